@@ -1,0 +1,155 @@
+"""fp64 CPU oracle for the Mamba-2 SSD scan (test infrastructure).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the
+benchmark's CPU-baseline leg are the only callers.  The HIP library and its
+Python binding never import this package, and this package imports nothing
+from them.
+
+The arithmetic lives in ``ssd_oracle.c`` (plain sequential recurrence in
+float64, see that file for the page citations).  This module only builds it
+with gcc, loads it with ctypes and marshals numpy arrays:
+
+* ``scan(x, dt, dt_bias, A, B, C, D, init)`` -> ``(y, final_state)``
+* ``step(state, x, delta, A, B, C, D)`` -> ``(y, new_state)``
+
+Every array argument is converted to contiguous float64 first; callers pass
+the values exactly as the device sees them (bf16 inputs upcast exactly).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssd_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libssd_oracle.so")
+_default = None
+
+
+def compile_source(src: str, out: str) -> str:
+    """Compile one oracle C source into a shared library with gcc + OpenMP."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+           "-Wall", "-Werror", src, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> str:
+    """Compile ssd_oracle.c into libssd_oracle.so."""
+    if force or not os.path.exists(_LIB_PATH):
+        compile_source(_SRC, _LIB_PATH)
+    return _LIB_PATH
+
+
+class Oracle:
+    """ctypes front end of one compiled oracle library."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        i64, vp = ctypes.c_int64, ctypes.c_void_p
+        lib.oracle_scan_f64.argtypes = [i64] * 6 + [vp] * 10
+        lib.oracle_scan_f64.restype = None
+        lib.oracle_step_f64.argtypes = [i64] * 5 + [vp] * 8
+        lib.oracle_step_f64.restype = None
+        lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        self.lib = lib
+
+    def num_threads(self) -> int:
+        return int(self.lib.oracle_num_threads())
+
+    def set_num_threads(self, n: int) -> None:
+        self.lib.oracle_set_num_threads(int(n))
+
+    def scan(self, *args, **kwargs):
+        return _scan(self.lib, *args, **kwargs)
+
+    def step(self, *args, **kwargs):
+        return _step(self.lib, *args, **kwargs)
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=False)
+        _default = Oracle(_LIB_PATH)
+    return _default
+
+
+def num_threads() -> int:
+    return default().num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    default().set_num_threads(n)
+
+
+def _f64(a):
+    if a is None:
+        return None
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def scan(x, dt, dt_bias, A, B, C, D=None, init=None, want_final=True):
+    """Sequential fp64 scan (see ``_scan``)."""
+    return default().scan(x, dt, dt_bias, A, B, C, D, init, want_final)
+
+
+def step(state, x, delta, A, B, C, D=None):
+    """One fp64 recurrent step (see ``_step``)."""
+    return default().step(state, x, delta, A, B, C, D)
+
+
+def _scan(lib, x, dt, dt_bias, A, B, C, D=None, init=None, want_final=True):
+    """Sequential fp64 scan.
+
+    x [b,L,H,P], dt [b,L,H] (raw, before softplus), dt_bias [H] or None,
+    A [H], B/C [b,L,G,N], D [H] or None, init [b,H,P,N] or None.
+    Returns (y [b,L,H,P], final_state [b,H,P,N] or None), float64.
+    """
+    x, dt, dt_bias, A, B, C, D, init = map(_f64, (x, dt, dt_bias, A, B, C, D, init))
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    assert dt.shape == (b, L, H) and A.shape == (H,)
+    assert B.shape == (b, L, G, N) and C.shape == (b, L, G, N)
+    assert H % G == 0
+    if dt_bias is not None:
+        assert dt_bias.shape == (H,)
+    if D is not None:
+        assert D.shape == (H,)
+    if init is not None:
+        assert init.shape == (b, H, P, N)
+    y = np.empty((b, L, H, P), np.float64)
+    fin = np.empty((b, H, P, N), np.float64) if want_final else None
+    lib.oracle_scan_f64(b, L, H, P, G, N, _ptr(x), _ptr(dt), _ptr(dt_bias),
+                        _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(init),
+                        _ptr(y), _ptr(fin))
+    return y, fin
+
+
+def _step(lib, state, x, delta, A, B, C, D=None):
+    """One fp64 recurrent step on a copy of ``state``.
+
+    state [b,H,P,N], x [b,H,P], delta [b,H] (already activated),
+    A [H], B/C [b,G,N], D [H] or None.  Returns (y [b,H,P], new_state).
+    """
+    S = np.array(state, dtype=np.float64, order="C", copy=True)
+    x, delta, A, B, C, D = map(_f64, (x, delta, A, B, C, D))
+    b, H, P, N = S.shape
+    G = B.shape[1]
+    assert x.shape == (b, H, P) and delta.shape == (b, H)
+    assert B.shape == (b, G, N) and C.shape == (b, G, N) and H % G == 0
+    y = np.empty((b, H, P), np.float64)
+    lib.oracle_step_f64(b, H, P, G, N, _ptr(S), _ptr(x), _ptr(delta),
+                        _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(y))
+    return y, S

@@ -1,0 +1,139 @@
+/*
+ * ssd_oracle.c -- fp64 CPU oracle for the Mamba-2 SSD selective scan.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the checker, not the product:
+ * only the test suite, the smoke check and the benchmark's CPU-baseline leg
+ * may build, load or call it.  It shares no code, header, table or helper
+ * with the HIP library and includes nothing from it.
+ *
+ * What it computes (written out from the definitions, no chunking, no
+ * reordering beyond the plain loops):
+ *
+ *   Mamba-3 deep dive ch. 2, "SSM foundations" (171host.com), section 2.1.2
+ *   (discretization): the discrete recurrence
+ *       h_t = exp(Delta_t * A) * h_{t-1} + Delta_t * B_t * x_t
+ *   with forget gate alpha_t = exp(Delta_t * A) and input gate gamma_t = Delta_t,
+ *   and the readout y_t = C_t^T h_t.  Section 2.1.1 (continuous dynamics) adds
+ *   the skip term D * x to the output equation.
+ *
+ *   Mamba paper-reading notes (sxlin0.github.io), section on the selective
+ *   mechanism: Delta = tau_Delta(parameter + s_Delta(x)).  Here the
+ *   parameter is dt_bias, s_Delta(x) is the given dt, and tau_Delta is
+ *   softplus(z) = log(1 + e^z).
+ *
+ *   "From Transformer to Mamba" (jsqmd.com), section 2.1: the single-step
+ *   shape ssm_step(x_t, h_prev, A, B, C) -> (y_t, h_t).
+ *
+ * Shapes and layouts (all arrays dense, row-major, float64):
+ *   x      [b, L, H, P]      dt  [b, L, H]      dt_bias, A, D  [H]
+ *   B, C   [b, L, G, N]      heads h use group g = floor(h * G / H)
+ *   state  [b, H, P, N]      the per-head state h_t is a P x N matrix whose
+ *                            row p is the N-vector state of channel p.
+ *
+ * Readings where the pages are silent (listed in the design notes as well):
+ *   - the initial state enters before the first token's decay, so
+ *     h_0 = alpha_0 * init + Delta_0 * B_0 * x_0;
+ *   - y_t reads the state after token t has been added (the matrix form's
+ *     mask has ones on its diagonal);
+ *   - the step call takes Delta itself (already activated), no bias.
+ *
+ * Parallelism: independent (batch, head) pairs are spread over OpenMP
+ * threads; the time loop of each pair is sequential.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* softplus(z) = log(1 + exp(z)), evaluated in a form that does not overflow:
+ * log(1 + e^z) = max(z, 0) + log1p(exp(-|z|)). */
+static double softplus_f64(double z) {
+    double m = z > 0.0 ? z : 0.0;
+    return m + log1p(exp(-fabs(z)));
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+/* One token of the recurrence for one (batch, head) pair, in place on S
+ * (P x N).  x_t: P values, B_t and C_t: N values.  Writes P outputs. */
+static void recurrence_token(int64_t P, int64_t N, double *S, double delta,
+                             double a_h, const double *x_t, const double *B_t,
+                             const double *C_t, double d_h, double *y_t) {
+    double alpha = exp(delta * a_h);           /* forget gate */
+    for (int64_t p = 0; p < P; ++p) {
+        double *row = S + p * N;
+        double in = delta * x_t[p];            /* input gate times input */
+        double acc = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            row[n] = alpha * row[n] + in * B_t[n];
+            acc += row[n] * C_t[n];
+        }
+        y_t[p] = acc + d_h * x_t[p];
+    }
+}
+
+/* Full-sequence scan.  dt_bias, D and init may be NULL (treated as zero);
+ * final_state may be NULL (not written). */
+void oracle_scan_f64(int64_t b, int64_t L, int64_t H, int64_t P, int64_t G,
+                     int64_t N, const double *x, const double *dt,
+                     const double *dt_bias, const double *A, const double *B,
+                     const double *C, const double *D, const double *init,
+                     double *y, double *final_state) {
+    int64_t pairs = b * H;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < pairs; ++bh) {
+        int64_t ib = bh / H, h = bh % H;
+        int64_t g = (h * G) / H;
+        double *S = (double *)malloc((size_t)(P * N) * sizeof(double));
+        if (init)
+            memcpy(S, init + bh * P * N, (size_t)(P * N) * sizeof(double));
+        else
+            memset(S, 0, (size_t)(P * N) * sizeof(double));
+        double bias = dt_bias ? dt_bias[h] : 0.0;
+        double d_h = D ? D[h] : 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+            int64_t tok = ib * L + t;
+            double delta = softplus_f64(dt[tok * H + h] + bias);
+            recurrence_token(P, N, S, delta, A[h], x + (tok * H + h) * P,
+                             B + (tok * G + g) * N, C + (tok * G + g) * N, d_h,
+                             y + (tok * H + h) * P);
+        }
+        if (final_state)
+            memcpy(final_state + bh * P * N, S, (size_t)(P * N) * sizeof(double));
+        free(S);
+    }
+}
+
+/* One recurrent step for every (batch, head) pair, state updated in place.
+ * x [b,H,P], delta [b,H] (already activated), B/C [b,G,N], y [b,H,P]. */
+void oracle_step_f64(int64_t b, int64_t H, int64_t P, int64_t G, int64_t N,
+                     double *state, const double *x, const double *delta,
+                     const double *A, const double *B, const double *C,
+                     const double *D, double *y) {
+    int64_t pairs = b * H;
+#pragma omp parallel for schedule(static)
+    for (int64_t bh = 0; bh < pairs; ++bh) {
+        int64_t ib = bh / H, h = bh % H;
+        int64_t g = (h * G) / H;
+        recurrence_token(P, N, state + bh * P * N, delta[bh], A[h], x + bh * P,
+                         B + (ib * G + g) * N, C + (ib * G + g) * N,
+                         D ? D[h] : 0.0, y + bh * P);
+    }
+}

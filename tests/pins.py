@@ -1,0 +1,299 @@
+"""Independent checks that pin the fp64 oracle to the pages and to mathematics.
+
+Each ``pin_*`` function takes an oracle object (``scan``/``step`` methods)
+and raises ``AssertionError`` when the oracle disagrees with a result that is
+fixed independently of the oracle's own loop:
+
+* ``pin_golden``      hand-worked examples (tests/golden/hand_examples.txt)
+* ``pin_quadratic``   brute-force matrix form Y = (L o C B^T) diag(Delta) X
+                      with the mask built as products of forget gates
+                      ("Mamba-3 deep dive ch. 2", section 2.2.1), plus the
+                      initial-state and D terms, and the final state
+* ``pin_no_decay``    A = 0 closed form: prefix sums of Delta x B^T
+* ``pin_scalar_state`` N = 1: scalar-decay linear attention
+                      (same page, section 2.2.2)
+* ``pin_split``       carried state: two half-scans equal one scan
+* ``pin_lti``         constant parameters: convolution with numpy.convolve
+                      (Mamba reading notes, LTI section; "Transformers are
+                      SSMs" summary, section 1.1)
+* ``pin_step_scan``   T single steps equal one T-token scan
+* ``pin_exact_int``   integer data with A = 0, Delta = 1: exact integers
+* ``pin_linearity``, ``pin_groups``, ``pin_head_perm``, ``pin_decay_bound``
+
+Softplus here is ``numpy.logaddexp(0, z)`` (a library routine).
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                      "hand_examples.txt")
+
+
+def softplus(z):
+    return np.logaddexp(0.0, z)
+
+
+def rand_case(rng, b, L, H, P, G, N, *, A_scale=1.0, init=True, dt_shift=-1.0):
+    """Generic float64 inputs for oracle self-checks."""
+    x = rng.standard_normal((b, L, H, P))
+    dt = 0.5 * rng.standard_normal((b, L, H))
+    dt_bias = dt_shift + 0.3 * rng.standard_normal(H)
+    A = -A_scale * np.exp(rng.uniform(0.0, np.log(4.0), H))
+    B = rng.standard_normal((b, L, G, N)) / np.sqrt(N)
+    C = rng.standard_normal((b, L, G, N)) / np.sqrt(N)
+    D = rng.standard_normal(H)
+    h0 = 0.5 * rng.standard_normal((b, H, P, N)) if init else None
+    return dict(x=x, dt=dt, dt_bias=dt_bias, A=A, B=B, C=C, D=D, init=h0)
+
+
+def _close(a, b, rtol, what):
+    a = np.asarray(a)
+    b = np.asarray(b)
+    err = np.max(np.abs(a - b) / (1.0 + np.abs(b))) if a.size else 0.0
+    assert err <= rtol, "%s: max rel err %.3e > %.1e" % (what, err, rtol)
+
+
+# --------------------------------------------------------------------------
+def read_golden(path=GOLDEN):
+    cases, cur = [], None
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        key, *vals = line.split()
+        if key == "case":
+            cur = {"name": vals[0]}
+            cases.append(cur)
+        else:
+            cur[key] = np.array([float(v) for v in vals])
+    out = []
+    for c in cases:
+        b, L, H, P, G, N = (int(v) for v in c["dims"])
+        out.append(dict(
+            name=c["name"], x=c["x"].reshape(b, L, H, P), dt=c["dt"].reshape(b, L, H),
+            dt_bias=c["dt_bias"].reshape(H), A=c["A"].reshape(H),
+            B=c["B"].reshape(b, L, G, N), C=c["C"].reshape(b, L, G, N),
+            D=c["D"].reshape(H),
+            init=c["init"].reshape(b, H, P, N) if "init" in c else None,
+            y=c["y"].reshape(b, L, H, P), final=c["final"].reshape(b, H, P, N)))
+    return out
+
+
+def pin_golden(o):
+    for c in read_golden():
+        y, fin = o.scan(c["x"], c["dt"], c["dt_bias"], c["A"], c["B"], c["C"],
+                        c["D"], c["init"])
+        _close(y, c["y"], 1e-12, "golden %s y" % c["name"])
+        _close(fin, c["final"], 1e-12, "golden %s final" % c["name"])
+
+
+# --------------------------------------------------------------------------
+def quadratic_form(x, dt, dt_bias, A, B, C, D, init):
+    """Brute-force matrix form, O(L^2) per (batch, head)."""
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    delta = softplus(dt + dt_bias[None, None, :])
+    alpha = np.exp(delta * A[None, None, :])
+    y = np.zeros((b, L, H, P))
+    fin = np.zeros((b, H, P, N))
+    for ib in range(b):
+        for h in range(H):
+            g = h * G // H
+            Bm, Cm = B[ib, :, g, :], C[ib, :, g, :]
+            al, de, X = alpha[ib, :, h], delta[ib, :, h], x[ib, :, h, :]
+            mask = np.zeros((L, L))
+            for i in range(L):
+                mask[i, i] = 1.0
+                for j in range(i - 1, -1, -1):
+                    mask[i, j] = mask[i, j + 1] * al[j + 1]
+            M = mask * (Cm @ Bm.T) * de[None, :]
+            Y = M @ X + D[h] * X
+            carry = np.array([np.prod(al[s + 1:]) for s in range(L)]) * de
+            F = (X * carry[:, None]).T @ Bm
+            if init is not None:
+                dec = np.array([np.prod(al[: i + 1]) for i in range(L)])
+                Y = Y + dec[:, None] * (Cm @ init[ib, h].T)
+                F = F + np.prod(al) * init[ib, h]
+            y[ib, :, h, :] = Y
+            fin[ib, h] = F
+    return y, fin
+
+
+def pin_quadratic(o, seed=11):
+    rng = np.random.default_rng(seed)
+    for (b, L, H, P, G, N) in [(1, 64, 2, 3, 1, 5), (2, 17, 4, 2, 2, 3), (1, 40, 3, 4, 3, 1)]:
+        c = rand_case(rng, b, L, H, P, G, N)
+        y, fin = o.scan(**c)
+        yq, fq = quadratic_form(**c)
+        _close(y, yq, 1e-12, "quadratic y %s" % ((b, L, H, P, G, N),))
+        _close(fin, fq, 1e-12, "quadratic final")
+
+
+def pin_no_decay(o, seed=12):
+    rng = np.random.default_rng(seed)
+    b, L, H, P, G, N = 2, 50, 2, 3, 1, 4
+    c = rand_case(rng, b, L, H, P, G, N)
+    c["A"] = np.zeros(H)
+    y, fin = o.scan(**c)
+    delta = softplus(c["dt"] + c["dt_bias"])
+    for ib in range(b):
+        for h in range(H):
+            Bm, Cm = c["B"][ib, :, 0, :], c["C"][ib, :, 0, :]
+            X = c["x"][ib, :, h, :]
+            outer = (delta[ib, :, h][:, None, None] * X[:, :, None]) * Bm[:, None, :]
+            Hs = c["init"][ib, h][None] + np.cumsum(outer, axis=0)     # [L,P,N]
+            Y = np.einsum("tpn,tn->tp", Hs, Cm) + c["D"][h] * X
+            _close(y[ib, :, h, :], Y, 1e-12, "A=0 y")
+            _close(fin[ib, h], Hs[-1], 1e-12, "A=0 final")
+
+
+def pin_scalar_state(o, seed=13):
+    rng = np.random.default_rng(seed)
+    b, L, H, P, G, N = 1, 48, 3, 4, 1, 1
+    c = rand_case(rng, b, L, H, P, G, N)
+    y, fin = o.scan(**c)
+    delta = softplus(c["dt"] + c["dt_bias"])
+    for h in range(H):
+        cum = np.cumsum(delta[0, :, h] * c["A"][h])      # log of the running decay
+        bb, cc = c["B"][0, :, 0, 0], c["C"][0, :, 0, 0]
+        X = c["x"][0, :, h, :]
+        q = cc * np.exp(cum)                            # query side
+        k = bb * np.exp(-cum) * delta[0, :, h]          # key side
+        Y = q[:, None] * np.cumsum(k[:, None] * X, axis=0)
+        Y += q[:, None] * c["init"][0, h][:, 0][None, :] + c["D"][h] * X
+        _close(y[0, :, h, :], Y, 1e-11, "N=1 linear attention")
+        F = np.exp(cum[-1]) * (np.sum(k[:, None] * X, axis=0) + c["init"][0, h][:, 0])
+        _close(fin[0, h, :, 0], F, 1e-11, "N=1 final")
+
+
+def pin_split(o, seed=14):
+    rng = np.random.default_rng(seed)
+    b, L, H, P, G, N = 2, 70, 4, 3, 2, 5
+    c = rand_case(rng, b, L, H, P, G, N)
+    y, fin = o.scan(**c)
+    for L1 in (1, 33, 69):
+        a = {k: v for k, v in c.items()}
+        a.update(x=c["x"][:, :L1], dt=c["dt"][:, :L1], B=c["B"][:, :L1], C=c["C"][:, :L1])
+        y1, h1 = o.scan(**a)
+        a.update(x=c["x"][:, L1:], dt=c["dt"][:, L1:], B=c["B"][:, L1:], C=c["C"][:, L1:],
+                 init=h1)
+        y2, h2 = o.scan(**a)
+        _close(np.concatenate([y1, y2], axis=1), y, 1e-12, "split y L1=%d" % L1)
+        _close(h2, fin, 1e-12, "split final L1=%d" % L1)
+
+
+def pin_lti(o, seed=15):
+    rng = np.random.default_rng(seed)
+    b, L, H, P, G, N = 1, 60, 2, 3, 1, 4
+    c = rand_case(rng, b, L, H, P, G, N, init=False)
+    c["dt"] = np.broadcast_to(c["dt"][:, :1, :], (b, L, H)).copy()
+    c["B"] = np.broadcast_to(c["B"][:, :1], (b, L, G, N)).copy()
+    c["C"] = np.broadcast_to(c["C"][:, :1], (b, L, G, N)).copy()
+    y, _ = o.scan(**c)
+    for h in range(H):
+        de = softplus(c["dt"][0, 0, h] + c["dt_bias"][h])
+        al = np.exp(de * c["A"][h])
+        cb = float(c["C"][0, 0, 0] @ c["B"][0, 0, 0])
+        kern = de * cb * al ** np.arange(L)
+        for p in range(P):
+            X = c["x"][0, :, h, p]
+            Y = np.convolve(kern, X)[:L] + c["D"][h] * X
+            _close(y[0, :, h, p], Y, 1e-12, "LTI convolution")
+
+
+def pin_step_scan(o, seed=16):
+    rng = np.random.default_rng(seed)
+    b, L, H, P, G, N = 2, 20, 4, 3, 2, 5
+    c = rand_case(rng, b, L, H, P, G, N)
+    y, fin = o.scan(**c)
+    delta = softplus(c["dt"] + c["dt_bias"][None, None, :])
+    S = c["init"]
+    for t in range(L):
+        yt, S = o.step(S, c["x"][:, t], delta[:, t], c["A"], c["B"][:, t], c["C"][:, t], c["D"])
+        _close(yt, y[:, t], 1e-12, "step vs scan y t=%d" % t)
+    _close(S, fin, 1e-12, "step vs scan final")
+
+
+def pin_exact_int(o, seed=17):
+    """A = 0, Delta = 1, small integers: every value is an exact integer."""
+    rng = np.random.default_rng(seed)
+    b, H, P, G, N, T = 2, 4, 3, 2, 6, 5
+    S = rng.integers(-3, 4, (b, H, P, N)).astype(np.int64)
+    A = np.zeros(H)
+    D = rng.integers(-2, 3, H).astype(np.int64)
+    S_f = S.astype(np.float64)
+    for _ in range(T):
+        x = rng.integers(-4, 5, (b, H, P))
+        Bm = rng.integers(-3, 4, (b, G, N))
+        Cm = rng.integers(-3, 4, (b, G, N))
+        y, S_f = o.step(S_f, x, np.ones((b, H)), A, Bm, Cm, D)
+        g = np.arange(H) * G // H
+        S = S + x[:, :, :, None] * Bm[:, g, None, :]
+        y_int = np.einsum("bhpn,bhn->bhp", S, Cm[:, g, :]) + D[None, :, None] * x
+        assert np.array_equal(y, y_int.astype(np.float64)), "exact integer y"
+        assert np.array_equal(S_f, S.astype(np.float64)), "exact integer state"
+
+
+def pin_linearity(o, seed=18):
+    rng = np.random.default_rng(seed)
+    c = rand_case(rng, 1, 33, 2, 3, 1, 4)
+    y, fin = o.scan(**c)
+    z = dict(c, init=None)
+    y0, f0 = o.scan(**z)
+    yh, fh = o.scan(**dict(c, x=np.zeros_like(c["x"]), D=np.zeros_like(c["D"])))
+    _close(y, y0 + yh, 1e-12, "linearity in (x, h0)")
+    _close(fin, f0 + fh, 1e-12, "linearity final")
+    y3, f3 = o.scan(**dict(z, x=-2.5 * c["x"]))
+    _close(y3, -2.5 * y0, 1e-12, "homogeneity y")
+    _close(f3, -2.5 * f0, 1e-12, "homogeneity final")
+
+
+def pin_groups(o, seed=19):
+    rng = np.random.default_rng(seed)
+    b, L, H, P, G, N = 2, 25, 6, 2, 3, 4
+    c = rand_case(rng, b, L, H, P, G, N)
+    y, fin = o.scan(**c)
+    g = np.arange(H) * G // H
+    r = dict(c, B=c["B"][:, :, g, :], C=c["C"][:, :, g, :])
+    yr, fr = o.scan(**r)
+    _close(y, yr, 0.0, "groups vs repeated")
+    _close(fin, fr, 0.0, "groups vs repeated final")
+    one = dict(c, B=np.repeat(c["B"][:, :, :1], G, 2), C=np.repeat(c["C"][:, :, :1], G, 2))
+    y1, _ = o.scan(**one)
+    y2, _ = o.scan(**dict(c, B=c["B"][:, :, :1], C=c["C"][:, :, :1]))
+    _close(y1, y2, 0.0, "equal groups vs G=1")
+
+
+def pin_head_perm(o, seed=20):
+    rng = np.random.default_rng(seed)
+    b, L, H, P, G, N = 1, 21, 5, 2, 1, 3
+    c = rand_case(rng, b, L, H, P, G, N)
+    y, fin = o.scan(**c)
+    perm = rng.permutation(H)
+    pc = dict(c, x=c["x"][:, :, perm], dt=c["dt"][:, :, perm], dt_bias=c["dt_bias"][perm],
+              A=c["A"][perm], D=c["D"][perm], init=c["init"][:, perm])
+    yp, fp = o.scan(**pc)
+    _close(yp, y[:, :, perm], 0.0, "head permutation")
+    _close(fp, fin[:, perm], 0.0, "head permutation final")
+
+
+def pin_decay_bound(o, seed=21):
+    rng = np.random.default_rng(seed)
+    c = rand_case(rng, 1, 30, 3, 2, 1, 4)
+    c["x"] = np.zeros_like(c["x"])
+    prev = np.abs(c["init"]).copy()
+    S = c["init"]
+    delta = softplus(c["dt"] + c["dt_bias"])
+    for t in range(30):
+        _, S = o.step(S, c["x"][:, t], delta[:, t], c["A"], c["B"][:, t], c["C"][:, t], c["D"])
+        assert np.all(np.abs(S) <= prev + 1e-15), "state grew with zero input"
+        assert np.all(np.abs(S) < prev + 1e-15) or np.all(prev == 0)
+        prev = np.abs(S)
+
+
+ALL_PINS = [pin_golden, pin_quadratic, pin_no_decay, pin_scalar_state, pin_split,
+            pin_lti, pin_step_scan, pin_exact_int, pin_linearity, pin_groups,
+            pin_head_perm, pin_decay_bound]

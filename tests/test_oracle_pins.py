@@ -1,0 +1,91 @@
+"""The fp64 oracle against results fixed independently of it (CPU only)."""
+import os
+import shutil
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+
+import oracle
+import pins
+
+ORACLE_SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                          "oracle", "ssd_oracle.c")
+
+
+@pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(oracle_lib, pin):
+    pin(oracle_lib)
+
+
+# Plausible mistakes planted in a copy of the oracle source; every one must be
+# caught by at least one pin.  (old text, new text, description)
+MUTATIONS = [
+    ("double alpha = exp(delta * a_h);", "double alpha = exp(a_h);", "decay without Delta"),
+    ("double alpha = exp(delta * a_h);", "double alpha = exp(-delta * a_h);", "decay sign"),
+    ("double in = delta * x_t[p];", "double in = x_t[p];", "input gate dropped"),
+    ("row[n] = alpha * row[n] + in * B_t[n];\n            acc += row[n] * C_t[n];",
+     "row[n] = alpha * row[n] + in * C_t[n];\n            acc += row[n] * B_t[n];",
+     "B and C swapped"),
+    ("row[n] = alpha * row[n] + in * B_t[n];\n            acc += row[n] * C_t[n];",
+     "acc += row[n] * C_t[n];\n            row[n] = alpha * row[n] + in * B_t[n];",
+     "readout before update"),
+    ("row[n] = alpha * row[n] + in * B_t[n];", "row[n] = alpha * (row[n] + in * B_t[n]);",
+     "new input decayed"),
+    ("y_t[p] = acc + d_h * x_t[p];", "y_t[p] = acc;", "D term dropped"),
+    ("    return m + log1p(exp(-fabs(z)));", "    (void)m;\n    return z;", "no softplus"),
+    ("dt[tok * H + h] + bias", "dt[tok * H + h] - bias", "bias sign"),
+    ("x + (tok * H + h) * P,", "x + (tok * H + (H - 1 - h)) * P,", "wrong head of x"),
+    ("int64_t g = (h * G) / H;\n        double *S", "int64_t g = h % G;\n        double *S",
+     "group map"),
+    ("B + (tok * G + g) * N, C + (tok * G + g) * N",
+     "B + (tok * G + g) * N, C + ((tok > 0 ? tok - 1 : 0) * G + g) * N", "C one token late"),
+    ("recurrence_token(P, N, state + bh * P * N, delta[bh],",
+     "recurrence_token(P, N, state + bh * P * N, softplus_f64(delta[bh]),",
+     "step applies softplus"),
+    ("memcpy(S, init + bh * P * N, (size_t)(P * N) * sizeof(double));",
+     "memset(S, 0, (size_t)(P * N) * sizeof(double));", "init ignored"),
+]
+
+
+@pytest.mark.parametrize("old,new,what", MUTATIONS, ids=[m[2] for m in MUTATIONS])
+def test_planted_mistake_is_caught(old, new, what):
+    src = open(ORACLE_SRC).read()
+    assert src.count(old) == 1, "mutation anchor not found: %s" % what
+    tmp = tempfile.mkdtemp(prefix="oracle_mut_")
+    try:
+        path = os.path.join(tmp, "mut.c")
+        open(path, "w").write(src.replace(old, new))
+        lib = oracle.compile_source(path, os.path.join(tmp, "libmut.so"))
+        mutant = oracle.Oracle(lib)
+        caught = []
+        for pin in pins.ALL_PINS:
+            try:
+                pin(mutant)
+            except AssertionError:
+                caught.append(pin.__name__)
+        assert caught, "planted mistake '%s' passed every pin" % what
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+
+
+def test_generator_bf16_rounding_matches_torch():
+    torch = pytest.importorskip("torch")
+    from mamba_ssd_scan_05_amd import inputs
+    rng = np.random.default_rng(0)
+    v = (rng.standard_normal(100000) * np.exp(rng.uniform(-20, 20, 100000))).astype(np.float32)
+    ours = inputs.f32_to_bf16_bits(v)
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+    back = inputs.bf16_bits_to_f32(ours)
+    assert np.array_equal(back, torch.from_numpy(v).to(torch.bfloat16).float().numpy())
+
+
+def test_generator_is_seeded():
+    from mamba_ssd_scan_05_amd import inputs
+    a = inputs.make_scan(1, 40, 4, 8, 2, 8, seed=7, init_std=0.1)
+    b = inputs.make_scan(1, 40, 4, 8, 2, 8, seed=7, init_std=0.1)
+    for k in ("x", "dt", "dt_bias", "A", "B", "C", "D", "init"):
+        assert np.array_equal(getattr(a, k), getattr(b, k))
+    assert np.all(a.A < 0)
