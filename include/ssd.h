@@ -1,0 +1,160 @@
+/*
+ * ssd.h -- C ABI of libssd, the Mamba-2 SSD selective scan for AMD MI355X
+ * (gfx950).
+ *
+ * The operation ("Mamba-3 deep dive ch. 2, SSM foundations", 171host.com,
+ * section 2.1.2, the discrete recurrence with forget gate alpha and input
+ * gate gamma, and section 2.1.1 for the skip term D):
+ *
+ *     Delta_t = softplus(dt_t + dt_bias_h)
+ *     h_t     = exp(Delta_t * A_h) * h_{t-1} + Delta_t * x_t B_t^T   (P x N)
+ *     y_t     = h_t C_t + D_h * x_t                                    (P)
+ *
+ * for every batch row and head h independently; head h reads the B/C group
+ * g = floor(h * G / H).  Section 2.2.1 of the same page shows the equal
+ * matrix form Y = (L o C B^T) X; the library evaluates it chunk by chunk
+ * ("Transformers are SSMs" summary, gongshangzheng.github.io, section 1.2:
+ * the quadratic path inside short blocks, the recurrent path across them).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Tensors are described by ssd_tensor.  Every tensor must be dense and
+ * row-major (strides, in elements, equal to the contiguous strides of its
+ * shape) with a 16-byte aligned data pointer.  All data pointers are device
+ * pointers (HIP device memory) except where noted.
+ *
+ * Ownership: the caller allocates every tensor and keeps it alive until the
+ * work queued on `stream` has finished.  The library keeps no pointer after
+ * a call returns.  Scratch space, when an algorithm needs it, is taken from
+ * the HIP stream-ordered allocator on `stream` and released on `stream`.
+ *
+ * Errors: every argument is validated on the host before any HIP call; a
+ * failed validation returns a nonzero status and queues nothing.  A failed
+ * kernel launch or allocation returns SSD_ERR_HIP / SSD_ERR_NOMEM.  Faults
+ * inside kernels surface at the caller's next synchronisation.  The text of
+ * the most recent error on the calling thread is returned by
+ * ssd_last_error().  Calls are asynchronous with respect to the host and
+ * ordered on `stream` (a hipStream_t; NULL is the default stream).  No call
+ * prints or throws.
+ */
+#ifndef SSD_H
+#define SSD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSD_VERSION 100 /* 1.0.0 */
+
+/* Element types. */
+enum { SSD_F32 = 0, SSD_BF16 = 1 };
+
+/* Status codes. */
+enum {
+  SSD_OK = 0,
+  SSD_ERR_NULL = 1,        /* a required tensor or data pointer is NULL      */
+  SSD_ERR_SHAPE = 2,       /* shapes disagree, H % G != 0, b or L is zero    */
+  SSD_ERR_DTYPE = 3,       /* unsupported or mismatched element type         */
+  SSD_ERR_LAYOUT = 4,      /* not dense row-major, or data not 16B aligned   */
+  SSD_ERR_UNSUPPORTED = 5, /* P, N or chunk outside the compiled set         */
+  SSD_ERR_ALIAS = 6,       /* an output overlaps an input it may not alias   */
+  SSD_ERR_NOMEM = 7,       /* scratch allocation failed                      */
+  SSD_ERR_HIP = 8          /* a HIP runtime call or kernel launch failed     */
+};
+
+/* Algorithms for ssd_scan_fwd_algo (results agree to rounding). */
+enum {
+  SSD_ALGO_AUTO = 0,    /* choose by shape                                    */
+  SSD_ALGO_FUSED = 1,   /* one kernel; each workgroup walks one (batch, head)
+                           sequence in order with the state in registers      */
+  SSD_ALGO_CHUNKED = 2  /* chunk-parallel: log-decay cumsum, chunk states,
+                           inter-chunk state passing, fused intra+output      */
+};
+
+/* Dense tensor descriptor.  shape/strides beyond ndim are ignored; strides
+ * are in elements. */
+typedef struct ssd_tensor {
+  void *data;
+  int32_t dtype; /* SSD_F32 or SSD_BF16 */
+  int32_t ndim;
+  int64_t shape[4];
+  int64_t strides[4];
+} ssd_tensor;
+
+/*
+ * ssd_scan_fwd -- forward scan over whole sequences.
+ *
+ *   x          [b, L, H, P]  f32 or bf16                         required
+ *   dt         [b, L, H]     f32, raw (before softplus)           required
+ *   dt_bias    [H]           f32, added to dt before softplus     NULL => 0
+ *   A          [H]           f32, the decay rate A_h (normally < 0) required
+ *   B, C       [b, L, G, N]  dtype of x                           required
+ *   D          [H]           f32, skip weight                     NULL => 0
+ *   init_state [b, H, P, N]  f32, state before token 0            NULL => 0
+ *   out        [b, L, H, P]  dtype of x, written                  required
+ *   final_state[b, H, P, N]  f32, state after token L-1           NULL => skip
+ *   chunk      64, 128 or 256: the inter-chunk state-passing granularity
+ *              of the chunked algorithm (a performance knob only)
+ *   stream     hipStream_t
+ *
+ * The state is stored with N fastest: state[b][h][p][n] is the n-th state
+ * entry of channel p (the transpose of the N x P product B x^T).
+ * Supported sizes: P in {16, 32, 64, 128}, N in {16, 32, 64, 128}, H % G == 0,
+ * b >= 1, L >= 1 (any L; the last chunk may be partial).
+ * Arithmetic: products on MFMA in the input dtype with fp32 accumulation,
+ * the state and all decay factors in fp32.  final_state may be the same
+ * tensor as init_state (updated in place); out may not overlap any input.
+ */
+int ssd_scan_fwd(const ssd_tensor *x, const ssd_tensor *dt,
+                 const ssd_tensor *dt_bias, const ssd_tensor *A,
+                 const ssd_tensor *B, const ssd_tensor *C, const ssd_tensor *D,
+                 const ssd_tensor *init_state, ssd_tensor *out,
+                 ssd_tensor *final_state, int chunk, void *stream);
+
+/* ssd_scan_fwd with an explicit algorithm (SSD_ALGO_*). Same contract. */
+int ssd_scan_fwd_algo(const ssd_tensor *x, const ssd_tensor *dt,
+                      const ssd_tensor *dt_bias, const ssd_tensor *A,
+                      const ssd_tensor *B, const ssd_tensor *C,
+                      const ssd_tensor *D, const ssd_tensor *init_state,
+                      ssd_tensor *out, ssd_tensor *final_state, int chunk,
+                      int algo, void *stream);
+
+/*
+ * ssd_step -- one recurrent step for every (batch, head), state in place
+ * ("From Transformer to Mamba", jsqmd.com, section 2.1: the single-step
+ * update ssm_step(x_t, h_prev, A, B, C) -> (y_t, h_t); "Mamba-3 deep dive
+ * ch. 2", section 2.2.2: recurrent mode with a constant-size cache).
+ *
+ *   state [b, H, P, N]  f32, read and overwritten with the new state
+ *   x     [b, H, P]     f32 or bf16
+ *   dt    [b, H]        f32, the step size Delta itself (already activated:
+ *                       no bias and no softplus are applied here)
+ *   A     [H]           f32                                     required
+ *   B, C  [b, G, N]     dtype of x                              required
+ *   D     [H]           f32                                     NULL => 0
+ *   out   [b, H, P]     dtype of x, written
+ *
+ * Supported sizes: N in {16, 32, 64, 128, 256}, any P >= 1, H % G == 0.
+ * All arithmetic in fp32; out is rounded to its dtype once.  out may not
+ * overlap any input or the state.
+ */
+int ssd_step(ssd_tensor *state, const ssd_tensor *x, const ssd_tensor *dt,
+             const ssd_tensor *A, const ssd_tensor *B, const ssd_tensor *C,
+             const ssd_tensor *D, ssd_tensor *out, void *stream);
+
+/* Static text for a status code. */
+const char *ssd_status_string(int status);
+
+/* Text of the most recent failure on the calling thread ("" if none). */
+const char *ssd_last_error(void);
+
+/* SSD_VERSION of the built library. */
+int ssd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_H */

@@ -1,0 +1,323 @@
+// ssd_api.hip -- the C ABI of libssd: argument validation, algorithm choice,
+// scratch management and kernel launches.  Declarations and the contract
+// are in include/ssd.h.
+//
+// Every check runs on the host before the first HIP call, so a rejected
+// call has no side effect on the device and can be exercised without a GPU.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+
+#include "ssd.h"
+#include "ssd_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int elem_size(int dtype) { return dtype == SSD_BF16 ? 2 : 4; }
+
+int64_t numel(const ssd_tensor *t) {
+  int64_t n = 1;
+  for (int i = 0; i < t->ndim; ++i) n *= t->shape[i];
+  return n;
+}
+
+struct Range {
+  uintptr_t lo = 0, hi = 0; // [lo, hi)
+  bool empty() const { return hi <= lo; }
+};
+
+Range range_of(const ssd_tensor *t) {
+  Range r;
+  if (!t || !t->data) return r;
+  r.lo = (uintptr_t)t->data;
+  r.hi = r.lo + (uintptr_t)(numel(t) * elem_size(t->dtype));
+  return r;
+}
+
+bool overlap(const Range &a, const Range &b) {
+  return !a.empty() && !b.empty() && a.lo < b.hi && b.lo < a.hi;
+}
+
+// Checks presence, dtype, rank, exact shape, dense row-major strides and
+// 16-byte alignment.  `want_dtype` < 0 accepts f32 or bf16.
+int check_tensor(const ssd_tensor *t, const char *name, int want_dtype, int ndim,
+                 const int64_t *shape) {
+  if (!t) return fail(SSD_ERR_NULL, "%s: descriptor is NULL", name);
+  if (!t->data) return fail(SSD_ERR_NULL, "%s: data pointer is NULL", name);
+  if (t->dtype != SSD_F32 && t->dtype != SSD_BF16)
+    return fail(SSD_ERR_DTYPE, "%s: unknown dtype %d", name, t->dtype);
+  if (want_dtype >= 0 && t->dtype != want_dtype)
+    return fail(SSD_ERR_DTYPE, "%s: dtype %s, expected %s", name,
+                t->dtype == SSD_BF16 ? "bf16" : "f32", want_dtype == SSD_BF16 ? "bf16" : "f32");
+  if (t->ndim != ndim)
+    return fail(SSD_ERR_SHAPE, "%s: rank %d, expected %d", name, t->ndim, ndim);
+  for (int i = 0; i < ndim; ++i)
+    if (t->shape[i] != shape[i])
+      return fail(SSD_ERR_SHAPE, "%s: dim %d is %lld, expected %lld", name, i,
+                  (long long)t->shape[i], (long long)shape[i]);
+  int64_t stride = 1;
+  for (int i = ndim - 1; i >= 0; --i) {
+    if (t->shape[i] != 1 && t->strides[i] != stride)
+      return fail(SSD_ERR_LAYOUT, "%s: stride of dim %d is %lld, expected %lld (dense row-major)",
+                  name, i, (long long)t->strides[i], (long long)stride);
+    stride *= t->shape[i];
+  }
+  if (((uintptr_t)t->data) % 16 != 0)
+    return fail(SSD_ERR_LAYOUT, "%s: data pointer is not 16-byte aligned", name);
+  return SSD_OK;
+}
+
+#define SSD_CHECK(expr)                                                                   \
+  do {                                                                                    \
+    int _s = (expr);                                                                      \
+    if (_s != SSD_OK) return _s;                                                          \
+  } while (0)
+
+bool valid_pn(int64_t v) { return v == 16 || v == 32 || v == 64 || v == 128; }
+
+struct ScanShape {
+  int64_t b, L, H, P, G, N;
+};
+
+int validate_scan(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bias,
+                  const ssd_tensor *A, const ssd_tensor *B, const ssd_tensor *C,
+                  const ssd_tensor *D, const ssd_tensor *init, const ssd_tensor *out,
+                  const ssd_tensor *fin, int chunk, ScanShape *s) {
+  if (!x) return fail(SSD_ERR_NULL, "x: descriptor is NULL");
+  if (!B) return fail(SSD_ERR_NULL, "B: descriptor is NULL");
+  if (x->ndim != 4) return fail(SSD_ERR_SHAPE, "x: rank %d, expected 4 [b,L,H,P]", x->ndim);
+  if (B->ndim != 4) return fail(SSD_ERR_SHAPE, "B: rank %d, expected 4 [b,L,G,N]", B->ndim);
+  s->b = x->shape[0]; s->L = x->shape[1]; s->H = x->shape[2]; s->P = x->shape[3];
+  s->G = B->shape[2]; s->N = B->shape[3];
+  if (s->b < 1 || s->L < 1 || s->H < 1 || s->G < 1)
+    return fail(SSD_ERR_SHAPE, "empty problem: b=%lld L=%lld H=%lld G=%lld", (long long)s->b,
+                (long long)s->L, (long long)s->H, (long long)s->G);
+  if (s->H % s->G != 0)
+    return fail(SSD_ERR_SHAPE, "H=%lld is not a multiple of G=%lld", (long long)s->H, (long long)s->G);
+  if (!valid_pn(s->P)) return fail(SSD_ERR_UNSUPPORTED, "P=%lld not in {16,32,64,128}", (long long)s->P);
+  if (!valid_pn(s->N)) return fail(SSD_ERR_UNSUPPORTED, "N=%lld not in {16,32,64,128}", (long long)s->N);
+  if (chunk != 64 && chunk != 128 && chunk != 256)
+    return fail(SSD_ERR_UNSUPPORTED, "chunk=%d not in {64,128,256}", chunk);
+  if (s->b * s->L * s->H * s->P > ((int64_t)1 << 40) || s->b * s->L > INT32_MAX / 2 ||
+      s->b * s->H * ((s->L + 63) / 64) > INT32_MAX / 2)
+    return fail(SSD_ERR_UNSUPPORTED, "problem too large for 32-bit workgroup indexing");
+  const int xd = x->dtype;
+  const int64_t sx[4] = {s->b, s->L, s->H, s->P}, sdt[3] = {s->b, s->L, s->H},
+                sh[1] = {s->H}, sbc[4] = {s->b, s->L, s->G, s->N},
+                sst[4] = {s->b, s->H, s->P, s->N};
+  SSD_CHECK(check_tensor(x, "x", -1, 4, sx));
+  SSD_CHECK(check_tensor(dt, "dt", SSD_F32, 3, sdt));
+  if (dt_bias) SSD_CHECK(check_tensor(dt_bias, "dt_bias", SSD_F32, 1, sh));
+  SSD_CHECK(check_tensor(A, "A", SSD_F32, 1, sh));
+  SSD_CHECK(check_tensor(B, "B", xd, 4, sbc));
+  SSD_CHECK(check_tensor(C, "C", xd, 4, sbc));
+  if (D) SSD_CHECK(check_tensor(D, "D", SSD_F32, 1, sh));
+  if (init) SSD_CHECK(check_tensor(init, "init_state", SSD_F32, 4, sst));
+  SSD_CHECK(check_tensor(out, "out", xd, 4, sx));
+  if (fin) SSD_CHECK(check_tensor(fin, "final_state", SSD_F32, 4, sst));
+
+  const Range ro = range_of(out), rf = range_of(fin);
+  const ssd_tensor *ins[] = {x, dt, dt_bias, A, B, C, D, init};
+  const char *names[] = {"x", "dt", "dt_bias", "A", "B", "C", "D", "init_state"};
+  for (int i = 0; i < 8; ++i) {
+    const Range ri = range_of(ins[i]);
+    if (overlap(ro, ri)) return fail(SSD_ERR_ALIAS, "out overlaps %s", names[i]);
+    if (i == 7 && fin && init && fin->data == init->data) continue; // in-place state
+    if (overlap(rf, ri)) return fail(SSD_ERR_ALIAS, "final_state overlaps %s", names[i]);
+  }
+  if (overlap(ro, rf)) return fail(SSD_ERR_ALIAS, "out overlaps final_state");
+  return SSD_OK;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+  return fail(SSD_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int run_fused(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bias,
+              const ssd_tensor *A, const ssd_tensor *B, const ssd_tensor *C,
+              const ssd_tensor *D, const ssd_tensor *init, ssd_tensor *out, ssd_tensor *fin,
+              const ScanShape &s, hipStream_t st) {
+  ssd::WalkParams p{};
+  p.x = x->data; p.dt = (const float *)dt->data;
+  p.dt_bias = dt_bias ? (const float *)dt_bias->data : nullptr;
+  p.A = (const float *)A->data; p.B = B->data; p.C = C->data;
+  p.D = D ? (const float *)D->data : nullptr;
+  p.init = init ? (const float *)init->data : nullptr;
+  p.out = out->data;
+  p.state_out = fin ? (float *)fin->data : nullptr;
+  p.b = (int)s.b; p.L = (int)s.L; p.H = (int)s.H; p.G = (int)s.G;
+  p.seg_len = (int)s.L; p.nseg = 1;
+  hipError_t e = ssd::launch_walk(x->dtype, (int)s.P, (int)s.N, ssd::kWalkFull, p, st);
+  return e == hipSuccess ? SSD_OK : hip_fail(e, "fused walk launch");
+}
+
+int run_chunked(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bias,
+                const ssd_tensor *A, const ssd_tensor *B, const ssd_tensor *C,
+                const ssd_tensor *D, const ssd_tensor *init, ssd_tensor *out,
+                ssd_tensor *fin, const ScanShape &s, int chunk, hipStream_t st) {
+  const int64_t nc = (s.L + chunk - 1) / chunk;
+  const int64_t PN = s.P * s.N;
+  const size_t n_tok = (size_t)(s.b * s.H * s.L);
+  const size_t bytes_delta = n_tok * sizeof(float);
+  const size_t bytes_states = (size_t)(s.b * s.H * nc * PN) * sizeof(float);
+  const size_t total = 2 * bytes_delta + bytes_states;
+  void *ws = nullptr;
+  hipError_t e = hipMallocAsync(&ws, total, st);
+  if (e != hipSuccess || !ws) {
+    (void)hipGetLastError();
+    return fail(SSD_ERR_NOMEM, "scratch of %zu bytes: %s", total, hipGetErrorString(e));
+  }
+  float *delta = (float *)ws;
+  float *cum = delta + n_tok;
+  float *states = cum + n_tok;
+  int status = SSD_OK;
+  do {
+    e = ssd::launch_cumsum((const float *)dt->data,
+                           dt_bias ? (const float *)dt_bias->data : nullptr,
+                           (const float *)A->data, delta, cum, (int)s.b, (int)s.L, (int)s.H,
+                           chunk, st);
+    if (e != hipSuccess) { status = hip_fail(e, "cumsum launch"); break; }
+
+    ssd::WalkParams p{};
+    p.x = x->data; p.dt = delta; p.dt_bias = nullptr; p.A = (const float *)A->data;
+    p.B = B->data; p.C = C->data; p.D = D ? (const float *)D->data : nullptr;
+    p.b = (int)s.b; p.L = (int)s.L; p.H = (int)s.H; p.G = (int)s.G;
+    p.seg_len = chunk; p.nseg = (int)nc;
+    p.init = nullptr; p.out = nullptr; p.state_out = states;
+    e = ssd::launch_walk(x->dtype, (int)s.P, (int)s.N, ssd::kWalkChunkState, p, st);
+    if (e != hipSuccess) { status = hip_fail(e, "chunk-state launch"); break; }
+
+    e = ssd::launch_state_pass(states, cum, init ? (const float *)init->data : nullptr,
+                               fin ? (float *)fin->data : nullptr, (int)s.b, (int)s.L,
+                               (int)s.H, (int)PN, chunk, st);
+    if (e != hipSuccess) { status = hip_fail(e, "state-pass launch"); break; }
+
+    p.init = states; p.out = out->data; p.state_out = nullptr;
+    e = ssd::launch_walk(x->dtype, (int)s.P, (int)s.N, ssd::kWalkChunkOut, p, st);
+    if (e != hipSuccess) { status = hip_fail(e, "chunk-output launch"); break; }
+  } while (0);
+  e = hipFreeAsync(ws, st);
+  if (e != hipSuccess && status == SSD_OK) status = hip_fail(e, "scratch free");
+  return status;
+}
+
+// Shape heuristic: the fused walk has one workgroup per (batch, head) and
+// needs enough of them to cover the 256 compute units; otherwise the
+// chunk-parallel pipeline exposes b*H*chunks workgroups.
+int choose_algo(const ScanShape &s, int chunk) {
+  (void)chunk;
+  return (s.b * s.H >= 192) ? SSD_ALGO_FUSED : SSD_ALGO_CHUNKED;
+}
+
+} // namespace
+
+extern "C" {
+
+int ssd_scan_fwd_algo(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bias,
+                      const ssd_tensor *A, const ssd_tensor *B, const ssd_tensor *C,
+                      const ssd_tensor *D, const ssd_tensor *init_state, ssd_tensor *out,
+                      ssd_tensor *final_state, int chunk, int algo, void *stream) {
+  g_last_error.clear();
+  ScanShape s;
+  SSD_CHECK(validate_scan(x, dt, dt_bias, A, B, C, D, init_state, out, final_state, chunk, &s));
+  if (algo != SSD_ALGO_AUTO && algo != SSD_ALGO_FUSED && algo != SSD_ALGO_CHUNKED)
+    return fail(SSD_ERR_UNSUPPORTED, "unknown algorithm %d", algo);
+  if (algo == SSD_ALGO_AUTO) algo = choose_algo(s, chunk);
+  hipStream_t st = (hipStream_t)stream;
+  if (algo == SSD_ALGO_FUSED)
+    return run_fused(x, dt, dt_bias, A, B, C, D, init_state, out, final_state, s, st);
+  return run_chunked(x, dt, dt_bias, A, B, C, D, init_state, out, final_state, s, chunk, st);
+}
+
+int ssd_scan_fwd(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bias,
+                 const ssd_tensor *A, const ssd_tensor *B, const ssd_tensor *C,
+                 const ssd_tensor *D, const ssd_tensor *init_state, ssd_tensor *out,
+                 ssd_tensor *final_state, int chunk, void *stream) {
+  return ssd_scan_fwd_algo(x, dt, dt_bias, A, B, C, D, init_state, out, final_state, chunk,
+                           SSD_ALGO_AUTO, stream);
+}
+
+int ssd_step(ssd_tensor *state, const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *A,
+             const ssd_tensor *B, const ssd_tensor *C, const ssd_tensor *D, ssd_tensor *out,
+             void *stream) {
+  g_last_error.clear();
+  if (!state) return fail(SSD_ERR_NULL, "state: descriptor is NULL");
+  if (!B) return fail(SSD_ERR_NULL, "B: descriptor is NULL");
+  if (state->ndim != 4) return fail(SSD_ERR_SHAPE, "state: rank %d, expected 4 [b,H,P,N]", state->ndim);
+  if (B->ndim != 3) return fail(SSD_ERR_SHAPE, "B: rank %d, expected 3 [b,G,N]", B->ndim);
+  const int64_t b = state->shape[0], H = state->shape[1], P = state->shape[2],
+                N = state->shape[3], G = B->shape[1];
+  if (b < 1 || H < 1 || P < 1 || G < 1)
+    return fail(SSD_ERR_SHAPE, "empty problem: b=%lld H=%lld P=%lld G=%lld", (long long)b,
+                (long long)H, (long long)P, (long long)G);
+  if (H % G != 0) return fail(SSD_ERR_SHAPE, "H=%lld is not a multiple of G=%lld", (long long)H, (long long)G);
+  if (N != 16 && N != 32 && N != 64 && N != 128 && N != 256)
+    return fail(SSD_ERR_UNSUPPORTED, "N=%lld not in {16,32,64,128,256}", (long long)N);
+  if (b * H > INT32_MAX / 2 || P > (1 << 20))
+    return fail(SSD_ERR_UNSUPPORTED, "problem too large");
+  if (!x) return fail(SSD_ERR_NULL, "x: descriptor is NULL");
+  const int xd = x->dtype;
+  const int64_t sst[4] = {b, H, P, N}, sx[3] = {b, H, P}, sdt[2] = {b, H}, sh[1] = {H},
+                sbc[3] = {b, G, N};
+  SSD_CHECK(check_tensor(state, "state", SSD_F32, 4, sst));
+  SSD_CHECK(check_tensor(x, "x", -1, 3, sx));
+  SSD_CHECK(check_tensor(dt, "dt", SSD_F32, 2, sdt));
+  SSD_CHECK(check_tensor(A, "A", SSD_F32, 1, sh));
+  SSD_CHECK(check_tensor(B, "B", xd, 3, sbc));
+  SSD_CHECK(check_tensor(C, "C", xd, 3, sbc));
+  if (D) SSD_CHECK(check_tensor(D, "D", SSD_F32, 1, sh));
+  SSD_CHECK(check_tensor(out, "out", xd, 3, sx));
+  const Range ro = range_of(out), rs = range_of(state);
+  const ssd_tensor *ins[] = {x, dt, A, B, C, D};
+  const char *names[] = {"x", "dt", "A", "B", "C", "D"};
+  for (int i = 0; i < 6; ++i) {
+    const Range ri = range_of(ins[i]);
+    if (overlap(ro, ri)) return fail(SSD_ERR_ALIAS, "out overlaps %s", names[i]);
+    if (overlap(rs, ri)) return fail(SSD_ERR_ALIAS, "state overlaps %s", names[i]);
+  }
+  if (overlap(ro, rs)) return fail(SSD_ERR_ALIAS, "out overlaps state");
+  hipError_t e = ssd::launch_step(xd, (int)N, (float *)state->data, x->data,
+                                  (const float *)dt->data, (const float *)A->data, B->data,
+                                  C->data, D ? (const float *)D->data : nullptr, out->data,
+                                  (int)b, (int)H, (int)P, (int)G, (hipStream_t)stream);
+  return e == hipSuccess ? SSD_OK : hip_fail(e, "step launch");
+}
+
+const char *ssd_status_string(int status) {
+  switch (status) {
+  case SSD_OK: return "ok";
+  case SSD_ERR_NULL: return "null pointer";
+  case SSD_ERR_SHAPE: return "shape mismatch";
+  case SSD_ERR_DTYPE: return "dtype mismatch";
+  case SSD_ERR_LAYOUT: return "layout not dense row-major or misaligned";
+  case SSD_ERR_UNSUPPORTED: return "unsupported size or option";
+  case SSD_ERR_ALIAS: return "output aliases an input";
+  case SSD_ERR_NOMEM: return "scratch allocation failed";
+  case SSD_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char *ssd_last_error(void) { return g_last_error.c_str(); }
+
+int ssd_version(void) { return SSD_VERSION; }
+
+} // extern "C"

@@ -1,0 +1,62 @@
+// ssd_internal.h -- launch interface between the C ABI (ssd_api.hip) and the
+// kernels (ssd_kernels.hip).  Not installed; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+// Tokens handled per step of a workgroup's walk along a sequence (the
+// sub-block on which the quadratic form is evaluated).
+constexpr int kSub = 64;
+
+// Parameters of the chunk-walk kernel family.  A workgroup owns one
+// (batch, head, segment); the segment covers tokens
+// [seg * seg_len, min(L, (seg + 1) * seg_len)).
+struct WalkParams {
+  const void *x;        // [b, L, H, P]  input dtype
+  const float *dt;      // delta_mode 0: raw dt [b, L, H]; 1: Delta [b, H, L]
+  const float *dt_bias; // [H] or null (delta_mode 0 only)
+  const float *A;       // [H]
+  const void *B;        // [b, L, G, N]
+  const void *C;        // [b, L, G, N]
+  const float *D;       // [H] or null
+  const float *init;    // state entering each segment, [(b*H + h)*nseg + seg][P][N]
+                        // or null for zero
+  void *out;            // [b, L, H, P] or null (state-only walk)
+  float *state_out;     // state leaving each segment, same indexing as init,
+                        // or null
+  int b, L, H, G, seg_len, nseg;
+};
+
+// Walk flavours.
+enum WalkMode {
+  kWalkFull = 0,      // outputs y; Delta from raw dt (+ bias, softplus)
+  kWalkChunkOut = 1,  // outputs y; Delta precomputed [b, H, L]
+  kWalkChunkState = 2 // no y; state only; Delta precomputed [b, H, L]
+};
+
+hipError_t launch_walk(int dtype, int P, int N, WalkMode mode,
+                       const WalkParams &p, hipStream_t stream);
+
+// Per-chunk log-decay: Delta [b,H,L] and chunk-local inclusive cumsum of
+// Delta*A [b,H,L].
+hipError_t launch_cumsum(const float *dt, const float *dt_bias, const float *A,
+                         float *delta, float *cum, int b, int L, int H,
+                         int chunk, hipStream_t stream);
+
+// Inter-chunk state passing over [b,H,nc,P,N] chunk states, in place: slot c
+// becomes the state entering chunk c.  final_state may be null.
+hipError_t launch_state_pass(float *states, const float *cum,
+                             const float *init, float *final_state, int b,
+                             int L, int H, int PN, int chunk,
+                             hipStream_t stream);
+
+// One recurrent step, state in place.
+hipError_t launch_step(int dtype, int N, float *state, const void *x,
+                       const float *dt, const float *A, const void *B,
+                       const void *C, const float *D, void *out, int b, int H,
+                       int P, int G, hipStream_t stream);
+
+} // namespace ssd

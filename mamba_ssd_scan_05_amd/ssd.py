@@ -1,0 +1,139 @@
+"""ctypes binding of libssd (include/ssd.h) for torch tensors.
+
+Argument marshalling only: every step of the scan and of the recurrent step
+runs in the HIP kernels of libssd.so.  There is no fallback: if the library
+is not built, loading it raises.
+
+    out, final = ssd_scan_fwd(x, dt, dt_bias, A, B, C, D, init_state, chunk=256)
+    y = ssd_step(state, x, dt, A, B, C, D)          # state updated in place
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libssd.so")
+
+SSD_F32, SSD_BF16 = 0, 1
+SSD_ALGO_AUTO, SSD_ALGO_FUSED, SSD_ALGO_CHUNKED = 0, 1, 2
+STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_DTYPE",
+          4: "SSD_ERR_LAYOUT", 5: "SSD_ERR_UNSUPPORTED", 6: "SSD_ERR_ALIAS",
+          7: "SSD_ERR_NOMEM", 8: "SSD_ERR_HIP"}
+
+
+class SsdTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4), ("strides", ctypes.c_int64 * 4)]
+
+
+class SsdError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s: %s" % (STATUS.get(status, status), message))
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load libssd.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libssd.so is not built (python -m mamba_ssd_scan_05_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER(SsdTensor)
+        L.ssd_scan_fwd.argtypes = [P] * 10 + [ctypes.c_int, ctypes.c_void_p]
+        L.ssd_scan_fwd.restype = ctypes.c_int
+        L.ssd_scan_fwd_algo.argtypes = [P] * 10 + [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        L.ssd_scan_fwd_algo.restype = ctypes.c_int
+        L.ssd_step.argtypes = [P] * 8 + [ctypes.c_void_p]
+        L.ssd_step.restype = ctypes.c_int
+        L.ssd_status_string.argtypes = [ctypes.c_int]
+        L.ssd_status_string.restype = ctypes.c_char_p
+        L.ssd_last_error.restype = ctypes.c_char_p
+        L.ssd_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SSD_F32
+    if t.dtype == torch.bfloat16:
+        return SSD_BF16
+    return 99  # rejected by the library as SSD_ERR_DTYPE
+
+
+def describe(t: Optional[torch.Tensor]):
+    """ssd_tensor descriptor of a torch tensor (None -> NULL pointer)."""
+    if t is None:
+        return None
+    if t.dim() > 4:
+        raise ValueError("ssd tensors have at most 4 dimensions")
+    d = SsdTensor()
+    d.data = t.data_ptr() if t.numel() else 0
+    d.dtype = _dtype_code(t)
+    d.ndim = t.dim()
+    for i, (s, st) in enumerate(zip(t.shape, t.stride())):
+        d.shape[i] = s
+        d.strides[i] = st
+    return ctypes.pointer(d)
+
+
+def _stream(stream, *tensors):
+    if stream is not None:
+        return stream
+    if any(t is not None and t.is_cuda for t in tensors):
+        return torch.cuda.current_stream().cuda_stream
+    return None
+
+
+def _check(status: int):
+    if status != 0:
+        raise SsdError(status, lib().ssd_last_error().decode())
+
+
+def ssd_scan_fwd(x, dt, dt_bias, A, B, C, D=None, init_state=None, out=None,
+                 final_state=None, chunk: int = 256, stream=None,
+                 algo: int = SSD_ALGO_AUTO, return_final_state: bool = True):
+    """Forward SSD scan; returns (out, final_state or None)."""
+    if out is None:
+        out = torch.empty_like(x)
+    if final_state is None and return_final_state:
+        final_state = torch.empty((x.shape[0], x.shape[2], x.shape[3], B.shape[3]),
+                                  dtype=torch.float32, device=x.device)
+    st = _stream(stream, x)
+    status = lib().ssd_scan_fwd_algo(
+        describe(x), describe(dt), describe(dt_bias), describe(A), describe(B), describe(C),
+        describe(D), describe(init_state), describe(out), describe(final_state),
+        int(chunk), int(algo), st)
+    _check(status)
+    return out, final_state
+
+
+def ssd_step(state, x, dt, A, B, C, D=None, out=None, stream=None):
+    """One recurrent step; ``state`` is updated in place; returns out."""
+    if out is None:
+        out = torch.empty_like(x)
+    st = _stream(stream, state)
+    status = lib().ssd_step(describe(state), describe(x), describe(dt), describe(A),
+                            describe(B), describe(C), describe(D), describe(out), st)
+    _check(status)
+    return out
+
+
+def ssd_status_string(status: int) -> str:
+    return lib().ssd_status_string(int(status)).decode()
+
+
+def ssd_last_error() -> str:
+    return lib().ssd_last_error().decode()
+
+
+def ssd_version() -> int:
+    return int(lib().ssd_version())
