@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""Benchmark of the SSD forward scan on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step is one ssd_scan_fwd call over the Mamba-2 2.7B layer-shape
+workload (b=4, L=4096, H=80, P=64, G=1, N=128, chunk 256, bf16 inputs,
+fp32 initial and final state), inputs resident in HBM.  W untimed steps,
+then exactly K timed steps between two device synchronisations; value =
+b*L*K / elapsed.  Each step is also bracketed by HIP events on the stream
+the library launches on, giving the kernel's average duration for the
+roofline figure.  Rank 0 prints one JSON line.
+
+Also reported (context, not the metric): the recurrent-step workload
+(b=256, H=80, P=64, N=128, 64 steps) and the fp64 oracle timed on the host
+cores (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "SSD fwd scan tokens/s and % of roofline, 2.7B layer shape L=4096, 1 GPU"
+WORKLOAD = "mamba2_2p7b_b4_L4096_H80_P64_N128"
+DECODE = "decode_step_b256_H80_P64_N128_T64"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # dense bf16 MFMA, 256 CU x 4096 FLOP/clk x 2.4 GHz
+ELEM = {"bf16": 2, "f32": 4}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "mamba_ssd_scan_05_amd", "csrc", "ssd_kernels.hip")
+
+
+def scan_bytes(b, L, H, P, G, N, dtype, init, final):
+    """Algorithmic bytes: every input read once, every output written once."""
+    e = ELEM[dtype]
+    n = 2 * b * L * H * P * e            # x in, y out
+    n += 2 * b * L * G * N * e           # B, C
+    n += b * L * H * 4 + 3 * H * 4       # dt; dt_bias, A, D
+    n += (int(init) + int(final)) * b * H * P * N * 4
+    return n
+
+
+def scan_flops(b, L, H, P, G, N, Q):
+    """Counted FLOPs of the chunked method: C B^T once per group and chunk,
+    causal half of the masked product, chunk states and the state term."""
+    nc = (L + Q - 1) // Q
+    return b * G * nc * Q * (Q + 1) * N + b * H * nc * (Q * (Q + 1) * P + 4 * Q * N * P)
+
+
+def step_bytes(b, H, P, G, N, dtype):
+    e = ELEM[dtype]
+    return 2 * b * H * P * N * 4 + 2 * b * H * P * e + 2 * b * G * N * e + b * H * 4 + 2 * H * 4
+
+
+def kernel_sha():
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(kernel, workload):
+    """HBM bytes per launch from committed counter runs, if the kernel source
+    is unchanged since they were taken; else None."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    rec = t.get(kernel, {}).get(workload)
+    if not rec or rec.get("kernel_source_sha") != kernel_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(si, reps):
+    """The fp64 oracle on the host cores over the whole workload."""
+    import oracle
+    f = si.f64()
+    b, L = si.x.shape[0], si.x.shape[1]
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        oracle.scan(**f)
+        times.append(time.perf_counter() - t0)
+    best = min(times)
+    return {"value": b * L / best, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "whole workload (b=4, L=4096, H=80, P=64, N=128, fp64), best of %d runs, "
+                      "%.2f s each" % (reps, best)}
+
+
+def bench_decode(ssd, staging, inputs, torch, dev):
+    sp = inputs.make_workload(DECODE)
+    t = staging.step_tensors(sp, dev)
+    T = sp.x.shape[0]
+    for k in range(4):  # warm-up on a copy of the state
+        st = t["state"].clone()
+        ssd.ssd_step(st, t["x"][k], t["dt"][k], t["A"], t["B"][k], t["C"][k], t["D"])
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(T + 1)]
+    ev[0].record()
+    for k in range(T):
+        ssd.ssd_step(t["state"], t["x"][k], t["dt"][k], t["A"], t["B"][k], t["C"][k], t["D"])
+        ev[k + 1].record()
+    torch.cuda.synchronize()
+    per = [ev[k].elapsed_time(ev[k + 1]) for k in range(T)]
+    avg_ms = float(np.mean(per))
+    b, H, P, N = sp.state.shape
+    G = sp.B.shape[2]
+    nbytes = step_bytes(b, H, P, G, N, sp.dtype)
+    return {"workload": DECODE, "tokens_per_s": b / (avg_ms * 1e-3), "ms_per_step": avg_ms,
+            "achieved_GBs": nbytes / (avg_ms * 1e-3) / 1e9, "peak_GBs": HBM_PEAK_GBS,
+            "frac": nbytes / (avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes_per_step": nbytes}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--algo", choices=["auto", "fused", "chunked"], default="auto")
+    ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-alt", action="store_true", help="skip timing the other algorithm")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a 1 GiB device copy (calibrates HBM byte counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the SSD scan here runs on a single MI355X "
+              "(no collectives); --gpus %d is not supported" % args.gpus, file=sys.stderr)
+        return 2
+
+    import torch
+    from mamba_ssd_scan_05_amd import inputs, ssd, staging
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    algo = {"auto": ssd.SSD_ALGO_AUTO, "fused": ssd.SSD_ALGO_FUSED,
+            "chunked": ssd.SSD_ALGO_CHUNKED}[args.algo]
+    si = inputs.make_workload(args.workload)
+    shp = si.shape
+    b, L, H, P, G, N = (shp[k] for k in ("b", "L", "H", "P", "G", "N"))
+    Q = si.chunk
+    t = staging.scan_tensors(si, dev)
+    out = torch.empty_like(t["x"])
+    fin = torch.empty((b, H, P, N), dtype=torch.float32, device=dev)
+
+    def one(a=algo):
+        ssd.ssd_scan_fwd(**t, out=out, final_state=fin, chunk=Q, algo=a)
+
+    print("bench: workload %s algo %s warmup %d steps %d" % (args.workload, args.algo,
+                                                              args.warmup, args.steps),
+          file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        one()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record()
+    for k in range(args.steps):
+        one()
+        ev[k + 1].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    per_ms = [ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps)]
+    kern_ms = float(np.mean(per_ms))
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens = b * L
+    value = tokens * args.steps / elapsed
+
+    nbytes = scan_bytes(b, L, H, P, G, N, si.dtype, si.init is not None, True)
+    flops = scan_flops(b, L, H, P, G, N, Q)
+    achieved = nbytes / (kern_ms * 1e-3) / 1e9
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    used_algo = args.algo
+    if args.algo == "auto":
+        used_algo = "fused" if b * H >= 192 else "chunked"
+    dominant = "walk_kernel<bf16,P64,N128,full>" if used_algo == "fused" else "chunked pipeline"
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS,
+                "traffic": load_traffic("walk_full", args.workload) if used_algo == "fused"
+                else None,
+                "kernel": dominant, "kernel_avg_ms": kern_ms,
+                "algorithmic_bytes_per_launch": nbytes, "bytes_per_token": nbytes / tokens,
+                "counted_flops": flops, "t_hbm_us": t_hbm * 1e6, "t_mfma_us": t_mfma * 1e6,
+                "roofline_tokens_per_s": tokens / max(t_hbm, t_mfma),
+                "mfma_frac": flops / (kern_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+
+    extra = {"p10_ms": float(np.percentile(per_ms, 10)), "p90_ms": float(np.percentile(per_ms, 90))}
+    if not args.no_alt:
+        other = ssd.SSD_ALGO_CHUNKED if used_algo == "fused" else ssd.SSD_ALGO_FUSED
+        for _ in range(3):
+            one(other)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            one(other)
+        e1.record()
+        torch.cuda.synchronize()
+        extra["other_algo"] = {"algo": "chunked" if other == ssd.SSD_ALGO_CHUNKED else "fused",
+                               "ms_per_step": e0.elapsed_time(e1) / 10}
+    if args.copy_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        extra["copy_probe_bytes"] = 2 * (1 << 30)
+    if not args.no_decode:
+        print("bench: decode step workload", file=sys.stderr, flush=True)
+        extra["decode_step"] = bench_decode(ssd, staging, inputs, torch, dev)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(si, reps=2)
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": si.dtype, "data": "synthetic",
+        "config": {"workload": args.workload, "b": b, "L": L, "H": H, "P": P, "G": G, "N": N,
+                   "chunk": Q, "init_state": si.init is not None, "algo": used_algo},
+        "roofline": roofline, "cpu_baseline": cpu, "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

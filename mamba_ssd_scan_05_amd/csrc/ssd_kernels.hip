@@ -125,34 +125,143 @@ template <> __device__ __forceinline__ void st4<float>(float *p, float a, float 
 __device__ __forceinline__ float to_f(__bf16 v) { return (float)v; }
 __device__ __forceinline__ float to_f(float v) { return v; }
 
-// softplus(z) = log(1 + e^z) = max(z, 0) + log1p(e^{-|z|}).
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Hardware base-2 exponential and logarithm (v_exp_f32, v_log_f32).
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// softplus(z) = log(1 + e^z) = max(z, 0) + log1p(u), u = e^{-|z|} in (0, 1].
+// log1p(u) = log(w) * u / (w - 1) with w = fl(1 + u) cancels the rounding of
+// 1 + u (the classic accurate-log1p identity); w == 1 means log1p(u) = u to
+// working precision.
 __device__ __forceinline__ float softplus_f(float z) {
-  return fmaxf(z, 0.f) + log1pf(__expf(-fabsf(z)));
+  const float u = hw_exp2(-fabsf(z) * kLog2e);
+  const float w = 1.f + u;
+  const float lp = (w == 1.f) ? u : hw_log2(w) * kLn2 * (u * __builtin_amdgcn_rcpf(w - 1.f));
+  return fmaxf(z, 0.f) + lp;
+}
+
+// Raw buffer access: reads past `bytes` return zero and writes past it are
+// dropped by the hardware range check.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ float4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ float bload4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+// Store four outputs (converted to T) at byte offset `off`.
+template <typename T> __device__ __forceinline__ void bstore4(__amdgpu_buffer_rsrc_t r, uint32_t off, float a, float b, float c, float d);
+template <> __device__ __forceinline__ void bstore4<__bf16>(__amdgpu_buffer_rsrc_t r, uint32_t off, float a, float b, float c, float d) {
+  bf16x4 v;
+  v[0] = (__bf16)a; v[1] = (__bf16)b; v[2] = (__bf16)c; v[3] = (__bf16)d;
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, v), r, (int)off, 0, 0);
+}
+template <> __device__ __forceinline__ void bstore4<float>(__amdgpu_buffer_rsrc_t r, uint32_t off, float a, float b, float c, float d) {
+  const float4 v = make_float4(a, b, c, d);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, (int)off, 0, 0);
+}
+
+// Transposed read of a row-major LDS tile: within each 16-lane group, lane li
+// receives column col0 + li of rows row0 .. row0+3 (gfx950
+// ds_read_b64_tr_b16; lane 4r+s of the group supplies the address of row r,
+// columns 4s .. 4s+3).
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 lds_bf16x4;
+__device__ __forceinline__ bf16x4 tr4(const __bf16 *tile, int ld, int row0, int col0, int li) {
+  const __bf16 *p = tile + (row0 + (li >> 2)) * ld + col0 + 4 * (li & 3);
+  auto q = (__attribute__((address_space(3))) lds_bf16x4 *)(p);
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(q));
+}
+// Fragment of eight K-values along the rows (tokens) of a row-major tile for
+// column col0 + li: rows row0+4g+{0..3} then row0+16+4g+{0..3}, g = lane/16
+// (this row set keeps the two reads of a half-wave on distinct LDS banks).
+__device__ __forceinline__ FragBF trfrag(const __bf16 *tile, int ld, int row0, int col0, int li, int lg) {
+  FragBF f;
+  f.v = __builtin_shufflevector(tr4(tile, ld, row0 + 4 * lg, col0, li),
+                                tr4(tile, ld, row0 + 16 + 4 * lg, col0, li), 0, 1, 2, 3, 4, 5, 6, 7);
+  return f;
+}
+__device__ __forceinline__ FragF32 trfrag(const float *tile, int ld, int row0, int col0, int li, int lg) {
+  FragF32 f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    f.v[k] = tile[(row0 + 4 * lg + k) * ld + col0 + li];
+    f.v[4 + k] = tile[(row0 + 16 + 4 * lg + k) * ld + col0 + li];
+  }
+  return f;
+}
+__device__ __forceinline__ float elem(const FragBF &f, int e) { return (float)f.v[e]; }
+__device__ __forceinline__ float elem(const FragF32 &f, int e) { return f.v[e]; }
+
+// Row stride (elements) of a tile read with transposed reads: at least
+// 16 bytes of padding and a byte stride that is an odd multiple of 32, so
+// the 8 rows read by a half-wave fall on distinct LDS banks.
+constexpr int tr_ld(int cols, int esize) {
+  int ld = cols + 16 / esize;
+  while ((ld * esize) % 64 != 32) ++ld;
+  return ld;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
+// row broadcasts (gfx9 data-parallel primitives).
+__device__ __forceinline__ float wave_incl_scan(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x111, 0xf, 0xf, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x112, 0xf, 0xf, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x114, 0xf, 0xf, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x118, 0xf, 0xf, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xa, 0xf, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0xc, 0xf, false));
+  return v;
+}
+
+// Masked-score tiles of a 64-token sub-block, enumerated row-tile major:
+// (it, jt) with jt <= it, plus the all-zero tile (it, it+1) for even it that
+// the 32-token K-steps of the intra-block product read.  Slots:
+// (0,0) (0,1z) (1,0) (1,1) (2,0) (2,1) (2,2) (2,3z) (3,0) (3,1) (3,2) (3,3)
+__host__ __device__ constexpr int mtile_it(int slot) { return slot < 4 ? slot / 2 : 2 + (slot - 4) / 4; }
+__host__ __device__ constexpr int mtile_jt(int slot) {
+  return slot - (mtile_it(slot) < 2 ? 2 * mtile_it(slot) : 4 * mtile_it(slot) - 4);
 }
 
 // ---------------------------------------------------------------------------
 // The chunk walk.
 template <typename T, int P, int N, int MODE>
-__global__ void __launch_bounds__(P / 16 * 64)
+__global__ void __launch_bounds__(P / 16 * 64, (sizeof(T) == 2 && P == 64) ? 2 : 1)
 walk_kernel(const WalkParams prm) {
+  static_assert(kSub == 64, "the tile tables assume 64-token sub-blocks");
   constexpr bool kOut = MODE != kWalkChunkState;
   constexpr int NW = P / 16;             // waves; wave w owns rows [16w, 16w+16)
   constexpr int NTH = NW * 64;
   constexpr int NP = (N + 31) / 32 * 32; // N padded to a K-step
   constexpr int NTILE = NP / 16;
   constexpr int KN = NP / 32;
-  constexpr int VEC = 16 / (int)sizeof(T); // elements per 16-byte access
-  constexpr int LDB = NP + VEC;            // row stride of the [token][n] tiles
-  constexpr int LDJ = kSub + VEC;          // row stride of the [.][token] tiles
-  constexpr int NTI = kSub / 16;           // token tiles per sub-block
+  constexpr int ES = (int)sizeof(T);
+  constexpr int VEC = 16 / ES;           // elements per 16-byte access
+  constexpr int LDB = tr_ld(NP, ES);     // B tile: row reads and transposed reads
+  constexpr int LDC = NP + VEC;          // C tile: row reads only
+  constexpr int LDX = tr_ld(P, ES);      // X tile: transposed reads and row reads
+  constexpr int LDM = kSub + 4;          // masked scores M[i][j]
+  constexpr int NTI = kSub / 16;         // token tiles per sub-block
+  constexpr int BRW = NP / VEC;          // 16-byte pieces per B/C row
+  constexpr int XRW = P / VEC;           // 16-byte pieces per X row
+  constexpr int BPT = (kSub * BRW + NTH - 1) / NTH;
+  constexpr int XPT = (kSub * XRW + NTH - 1) / NTH;
+  constexpr int NMT = 12;                // masked-score tile slots
+  constexpr int MPW = (NMT + NW - 1) / NW;
 
-  __shared__ __attribute__((aligned(16))) T sB[kOut ? kSub * LDB : VEC];
-  __shared__ __attribute__((aligned(16))) T sC[kOut ? kSub * LDB : VEC];
-  __shared__ __attribute__((aligned(16))) T sBt[NP * LDJ];
-  __shared__ __attribute__((aligned(16))) T sXt[P * LDJ];
-  __shared__ __attribute__((aligned(16))) T sM[kOut ? kSub * LDJ : VEC];
-  __shared__ float sCum[kSub];
-  __shared__ float sDel[kSub];
+  __shared__ __attribute__((aligned(16))) T sB[kSub * LDB];
+  __shared__ __attribute__((aligned(16))) T sC[kOut ? kSub * LDC : VEC];
+  __shared__ __attribute__((aligned(16))) T sX[kSub * LDX];
+  __shared__ __attribute__((aligned(16))) T sM[kOut ? kSub * LDM : VEC];
+  __shared__ float sC2[kSub]; // cum * log2(e)
+  __shared__ float sQ2[kSub]; // cum * log2(e) - log2(Delta)   (+inf where Delta = 0)
+  __shared__ float sW[kSub];  // exp(cum_last - cum_j) * Delta_j
 
   const int H = prm.H, G = prm.G, L = prm.L, nseg = prm.nseg;
   const int W = prm.b * H * nseg;
@@ -169,13 +278,10 @@ walk_kernel(const WalkParams prm) {
   const int t_end = min(L, t_begin + prm.seg_len);
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
-  const int prow = 16 * w + lr; // the state row this lane feeds as an operand
+  const int w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
+  const int prow = 16 * w + li; // the state row this lane feeds as an operand
 
-  const T *__restrict__ xg = reinterpret_cast<const T *>(prm.x);
-  const T *__restrict__ Bg = reinterpret_cast<const T *>(prm.B);
-  const T *__restrict__ Cg = reinterpret_cast<const T *>(prm.C);
-  const float a_h = prm.A[h];
+  const float a2 = prm.A[h] * kLog2e;
   const float d_h = prm.D ? prm.D[h] : 0.f;
   const float bias = (MODE == kWalkFull && prm.dt_bias) ? prm.dt_bias[h] : 0.f;
   const int64_t state_idx = ((int64_t)(ib * H + h) * nseg + seg) * P * N;
@@ -183,94 +289,137 @@ walk_kernel(const WalkParams prm) {
   // State S^T tiles: hs[nt][r] = S[p = prow][n = 16 nt + 4 lg + r].
   f32x4 hs[NTILE];
 #pragma unroll
-  for (int nt = 0; nt < NTILE; ++nt) {
-    const int n0 = 16 * nt + 4 * lg;
-    if (prm.init && n0 < N)
-      hs[nt] = *reinterpret_cast<const f32x4 *>(prm.init + state_idx + (int64_t)prow * N + n0);
-    else
-      hs[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int nt = 0; nt < NTILE; ++nt) hs[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (prm.init != nullptr) {
+    const float *src = prm.init + state_idx + (int64_t)prow * N;
+#pragma unroll
+    for (int nt = 0; nt < NTILE; ++nt)
+      if (16 * nt < N) hs[nt] = *reinterpret_cast<const f32x4 *>(src + 16 * nt + 4 * lg);
   }
 
-  for (int t0 = t_begin; t0 < t_end; t0 += kSub) {
-    const int nv = min(kSub, t_end - t0);
-    __syncthreads(); // previous sub-block is done with LDS
+  // Per-thread 16-byte pieces of the staged tiles: row and column within
+  // the sub-block are fixed for the whole walk; only the base moves.
+  const int64_t rowB = (int64_t)G * N;  // elements between consecutive tokens of B/C
+  const int64_t rowX = (int64_t)H * P;  // ... of x and y
+  const T *__restrict__ Bbase = reinterpret_cast<const T *>(prm.B) + ((int64_t)ib * L * G + g) * N;
+  const T *__restrict__ Cbase = reinterpret_cast<const T *>(prm.C) + ((int64_t)ib * L * G + g) * N;
+  const T *__restrict__ Xbase = reinterpret_cast<const T *>(prm.x) + (int64_t)ib * L * rowX + (int64_t)h * P;
+  T *__restrict__ Ybase = reinterpret_cast<T *>(prm.out) + (int64_t)ib * L * rowX + (int64_t)h * P;
+  const float *__restrict__ dtbase = (MODE == kWalkFull) ? prm.dt + (int64_t)ib * L * H + h
+                                                         : prm.dt + (int64_t)(ib * H + h) * L;
+  const int64_t dtstride = (MODE == kWalkFull) ? H : 1;
 
-    // ---- stage B (and B^T), C and X^T of this sub-block into LDS ----------
-    for (int idx = tid; idx < kSub * (NP / VEC); idx += NTH) {
-      const int j = idx / (NP / VEC), n0 = (idx % (NP / VEC)) * VEC;
-      float4 vb = make_float4(0.f, 0.f, 0.f, 0.f), vc = vb;
-      if (j < nv && n0 < N) {
-        const int64_t off = ((int64_t)(ib * L + t0 + j) * G + g) * N + n0;
-        vb = *reinterpret_cast<const float4 *>(Bg + off);
-        if (kOut) vc = *reinterpret_cast<const float4 *>(Cg + off);
-      }
-      if (kOut) {
-        *reinterpret_cast<float4 *>(&sB[j * LDB + n0]) = vb;
-        *reinterpret_cast<float4 *>(&sC[j * LDB + n0]) = vc;
-      }
-      const T *e = reinterpret_cast<const T *>(&vb);
+  float4 rB[BPT], rC[kOut ? BPT : 1], rX[XPT];
+  float rdt = 0.f;
+  // Loop-invariant byte offsets of this thread's 16-byte pieces inside a
+  // tile; column padding (N < NP) points past the range and reads zero.
+  constexpr uint32_t kOOB = 0x7ffffff0u;
+  uint32_t offB[BPT], offX[XPT];
 #pragma unroll
-      for (int q = 0; q < VEC; ++q) sBt[(n0 + q) * LDJ + j] = e[q];
-    }
-    for (int idx = tid; idx < kSub * (P / VEC); idx += NTH) {
-      const int j = idx / (P / VEC), p0 = (idx % (P / VEC)) * VEC;
-      float4 vx = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (j < nv) vx = *reinterpret_cast<const float4 *>(xg + ((int64_t)(ib * L + t0 + j) * H + h) * P + p0);
-      const T *e = reinterpret_cast<const T *>(&vx);
+  for (int q = 0; q < BPT; ++q) {
+    const int idx = tid + q * NTH;
+    const int n0 = (idx % BRW) * VEC;
+    offB[q] = (NP == N || n0 < N) ? (uint32_t)(((int64_t)(idx / BRW) * rowB + n0) * ES) : kOOB;
+  }
 #pragma unroll
-      for (int q = 0; q < VEC; ++q) sXt[(p0 + q) * LDJ + j] = e[q];
+  for (int q = 0; q < XPT; ++q) {
+    const int idx = tid + q * NTH;
+    offX[q] = (uint32_t)(((int64_t)(idx / XRW) * rowX + (idx % XRW) * VEC) * ES);
+  }
+  const uint32_t offDt = (uint32_t)(l * dtstride * 4);
+  const uint32_t offY = (uint32_t)(((int64_t)li * rowX + 16 * w + 4 * lg) * ES);
+  // Rows past the end of the segment read as zero (buffer range check).
+  auto fetch = [&](int t0, int nv) {
+    const auto rsB = make_rsrc(Bbase + (int64_t)t0 * rowB, (uint32_t)(((int64_t)(nv - 1) * rowB + N) * ES));
+    const auto rsC = make_rsrc(Cbase + (int64_t)t0 * rowB, (uint32_t)(((int64_t)(nv - 1) * rowB + N) * ES));
+    const auto rsX = make_rsrc(Xbase + (int64_t)t0 * rowX, (uint32_t)(((int64_t)(nv - 1) * rowX + P) * ES));
+    const auto rsD = make_rsrc(dtbase + (int64_t)t0 * dtstride, (uint32_t)(((int64_t)(nv - 1) * dtstride + 1) * 4));
+#pragma unroll
+    for (int q = 0; q < BPT; ++q) {
+      if (tid + q * NTH < kSub * BRW) {
+        rB[q] = bload16(rsB, offB[q]);
+        if (kOut) rC[q] = bload16(rsC, offB[q]);
+      }
     }
-    if (w == 0) {
+#pragma unroll
+    for (int q = 0; q < XPT; ++q)
+      if (tid + q * NTH < kSub * XRW) rX[q] = bload16(rsX, offX[q]);
+    rdt = bload4(rsD, offDt);
+  };
+
+  int t0 = t_begin;
+  int nv = min(kSub, t_end - t0);
+  if (t0 < t_end) fetch(t0, nv);
+  while (t0 < t_end) {
+    __syncthreads(); // the previous sub-block is done with LDS
+
+    // ---- stage the registers into row-major LDS tiles ---------------------
+#pragma unroll
+    for (int q = 0; q < BPT; ++q) {
+      const int idx = tid + q * NTH;
+      if (idx < kSub * BRW) {
+        const int j = idx / BRW, n0 = (idx % BRW) * VEC;
+        *reinterpret_cast<float4 *>(&sB[j * LDB + n0]) = rB[q];
+        if (kOut) *reinterpret_cast<float4 *>(&sC[j * LDC + n0]) = rC[q];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < XPT; ++q) {
+      const int idx = tid + q * NTH;
+      if (idx < kSub * XRW) {
+        const int j = idx / XRW, p0 = (idx % XRW) * VEC;
+        *reinterpret_cast<float4 *>(&sX[j * LDX + p0]) = rX[q];
+      }
+    }
+    {
       // Delta and the inclusive cumsum of Delta*A over the sub-block (wave
-      // scan, lane = token).  Padding tokens get Delta = 0: no decay, no
-      // contribution.
-      float dl = 0.f;
-      if (l < nv) {
-        if (MODE == kWalkFull)
-          dl = softplus_f(prm.dt[(int64_t)(ib * L + t0 + l) * H + h] + bias);
-        else
-          dl = prm.dt[(int64_t)(ib * H + h) * L + t0 + l];
-      }
-      float cum = dl * a_h;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float v = __shfl_up(cum, off, 64);
-        if (l >= off) cum += v;
-      }
-      sCum[l] = cum;
-      sDel[l] = dl;
+      // scan, lane = token), kept in log2 units.  Every wave computes the
+      // same values and stores them (no wave-dependent branch in the loop).
+      // Padding tokens get Delta = 0: no decay, no contribution.
+      float dl = (MODE == kWalkFull) ? softplus_f(rdt + bias) : rdt;
+      dl = (l < nv) ? dl : 0.f;
+      const float c2 = wave_incl_scan(dl * a2);
+      const float clast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, c2), 63));
+      sC2[l] = c2;
+      sQ2[l] = c2 - hw_log2(dl);
+      sW[l] = hw_exp2(clast - c2) * dl;
     }
     __syncthreads();
+
+    const int t_next = t0 + kSub;
+    const int nv_next = min(kSub, t_end - t_next);
+    if (t_next < t_end) fetch(t_next, nv_next);
 
     f32x4 yacc[NTI];
     if constexpr (kOut) {
       // ---- masked scores M[i][j] = (C_i . B_j) exp(cum_i - cum_j) Delta_j --
-      // Tiles (jt, it) with jt <= it, plus the all-zero tile above the
-      // diagonal that the K-step of 32 tokens reads for even it.
-      constexpr int NMT = NTI * (NTI + 1) / 2 + NTI / 2;
-      for (int tile = w; tile < NMT; tile += NW) {
-        int it = 0, rem = tile;
-        while (rem >= it + 1 + ((it & 1) == 0 ? 1 : 0)) {
-          rem -= it + 1 + ((it & 1) == 0 ? 1 : 0);
-          ++it;
-        }
-        const int jt = rem;
-        const int i = 16 * it + lr;
-        float m[4] = {0.f, 0.f, 0.f, 0.f};
-        if (jt <= it) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      //      = S^T[j][i] * exp2(c2_i - q2_j)
 #pragma unroll
-          for (int ks = 0; ks < KN; ++ks)
-            acc = mma(ld8(&sB[(16 * jt + lr) * LDB + 32 * ks + 8 * lg]),
-                      ld8(&sC[i * LDB + 32 * ks + 8 * lg]), acc);
-          const float ci = sCum[i];
+      for (int k = 0; k < MPW; ++k) {
+        const int slot = w + k * NW;
+        if (slot < NMT) {
+          const int it = mtile_it(slot), jt = mtile_jt(slot);
+          const int i = 16 * it + li;
+          float m[4] = {0.f, 0.f, 0.f, 0.f};
+          if (jt <= it) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int j = 16 * jt + 4 * lg + r;
-            m[r] = (j <= i) ? acc[r] * __expf(ci - sCum[j]) * sDel[j] : 0.f;
+            for (int ks = 0; ks < KN; ++ks)
+              acc = mma(ld8(&sB[(16 * jt + li) * LDB + 32 * ks + 8 * lg]),
+                        ld8(&sC[i * LDC + 32 * ks + 8 * lg]), acc);
+            const float ci = sC2[i];
+            const float4 q4 = *reinterpret_cast<const float4 *>(&sQ2[16 * jt + 4 * lg]);
+            m[0] = acc[0] * hw_exp2(ci - q4.x);
+            m[1] = acc[1] * hw_exp2(ci - q4.y);
+            m[2] = acc[2] * hw_exp2(ci - q4.z);
+            m[3] = acc[3] * hw_exp2(ci - q4.w);
+            if (jt == it) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) m[r] = (4 * lg + r <= li) ? m[r] : 0.f;
+            }
           }
+          st4<T>(&sM[i * LDM + 16 * jt + 4 * lg], m[0], m[1], m[2], m[3]);
         }
-        st4<T>(&sM[i * LDJ + 16 * jt + 4 * lg], m[0], m[1], m[2], m[3]);
       }
 
       // ---- state term: Y^T[p][i] = exp(cum_i) sum_n S[p][n] C[i][n] --------
@@ -287,62 +436,67 @@ walk_kernel(const WalkParams prm) {
       }
 #pragma unroll
       for (int it = 0; it < NTI; ++it) {
-        const int i = 16 * it + lr;
+        const int i = 16 * it + li;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KN; ++ks)
           acc = mma(hf[ks],
-                    ld4x2(&sC[i * LDB + 32 * ks + 4 * lg], &sC[i * LDB + 32 * ks + 16 + 4 * lg]),
+                    ld4x2(&sC[i * LDC + 32 * ks + 4 * lg], &sC[i * LDC + 32 * ks + 16 + 4 * lg]),
                     acc);
-        const float e = __expf(sCum[i]);
-        yacc[it] = acc * e;
+        yacc[it] = acc * hw_exp2(sC2[i]);
       }
+      __syncthreads(); // M complete
     }
-    __syncthreads(); // M complete
+
+    // X^T fragments (rows p = prow, K = tokens), shared by the intra-block
+    // product and the state update.
+    typename FragOf<T>::type xf[kSub / 32];
+#pragma unroll
+    for (int ks = 0; ks < kSub / 32; ++ks) xf[ks] = trfrag(sX, LDX, 32 * ks, 16 * w, li, lg);
 
     if constexpr (kOut) {
       // ---- intra-block term: Y^T[p][i] += sum_{j<=i} X^T[p][j] M[i][j] -----
 #pragma unroll
       for (int it = 0; it < NTI; ++it) {
+        const int i = 16 * it + li;
 #pragma unroll
         for (int ks = 0; ks < (16 * (it + 1) + 31) / 32; ++ks)
-          yacc[it] = mma(ld8(&sXt[prow * LDJ + 32 * ks + 8 * lg]),
-                         ld8(&sM[(16 * it + lr) * LDJ + 32 * ks + 8 * lg]), yacc[it]);
+          yacc[it] = mma(xf[ks],
+                         ld4x2(&sM[i * LDM + 32 * ks + 4 * lg], &sM[i * LDM + 32 * ks + 16 + 4 * lg]),
+                         yacc[it]);
       }
       // ---- epilogue: + D x, store y --------------------------------------
-      T *__restrict__ og = reinterpret_cast<T *>(prm.out);
+      // Rows past the end of the segment fall outside the store range.
+      const int p0 = 16 * w + 4 * lg;
+      const auto rsY = make_rsrc(Ybase + (int64_t)t0 * rowX, (uint32_t)(((int64_t)(nv - 1) * rowX + P) * ES));
 #pragma unroll
       for (int it = 0; it < NTI; ++it) {
-        const int i = 16 * it + lr;
-        if (i < nv) {
-          const int p0 = 16 * w + 4 * lg;
-          float y[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) y[r] = yacc[it][r] + d_h * to_f(sXt[(p0 + r) * LDJ + i]);
-          st4<T>(og + ((int64_t)(ib * L + t0 + i) * H + h) * P + p0, y[0], y[1], y[2], y[3]);
-        }
+        const int i = 16 * it + li;
+        const T *xr = &sX[i * LDX + p0];
+        bstore4<T>(rsY, offY + (uint32_t)(16 * it * rowX * ES),
+                   yacc[it][0] + d_h * to_f(xr[0]), yacc[it][1] + d_h * to_f(xr[1]),
+                   yacc[it][2] + d_h * to_f(xr[2]), yacc[it][3] + d_h * to_f(xr[3]));
       }
     }
 
-    // ---- state update: S^T = decay S^T + B^T (w o X), w_j = e^{cum_last-cum_j} Delta_j
-    const float clast = sCum[kSub - 1];
-    const float dec = __expf(clast);
+    // ---- state update: S^T = decay S^T + B^T (w o X) ------------------------
+    const float dec = hw_exp2(sC2[kSub - 1]);
 #pragma unroll
     for (int nt = 0; nt < NTILE; ++nt) hs[nt] *= dec;
 #pragma unroll
     for (int ks = 0; ks < kSub / 32; ++ks) {
-      float v[8];
-      const T *xp = &sXt[prow * LDJ + 32 * ks + 8 * lg];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = 32 * ks + 8 * lg + e;
-        v[e] = to_f(xp[e]) * (__expf(clast - sCum[j]) * sDel[j]);
-      }
+      const float4 wa = *reinterpret_cast<const float4 *>(&sW[32 * ks + 4 * lg]);
+      const float4 wb = *reinterpret_cast<const float4 *>(&sW[32 * ks + 16 + 4 * lg]);
+      const float v[8] = {elem(xf[ks], 0) * wa.x, elem(xf[ks], 1) * wa.y, elem(xf[ks], 2) * wa.z,
+                          elem(xf[ks], 3) * wa.w, elem(xf[ks], 4) * wb.x, elem(xf[ks], 5) * wb.y,
+                          elem(xf[ks], 6) * wb.z, elem(xf[ks], 7) * wb.w};
       const auto bx = pack8<T>(v);
 #pragma unroll
       for (int nt = 0; nt < NTILE; ++nt)
-        hs[nt] = mma(ld8(&sBt[(16 * nt + lr) * LDJ + 32 * ks + 8 * lg]), bx, hs[nt]);
+        hs[nt] = mma(trfrag(sB, LDB, 32 * ks, 16 * nt, li, lg), bx, hs[nt]);
     }
+    t0 = t_next;
+    nv = nv_next;
   }
 
   if (prm.state_out) {
@@ -357,27 +511,50 @@ walk_kernel(const WalkParams prm) {
 
 // ---------------------------------------------------------------------------
 // Per-chunk log-decay: Delta = softplus(dt + bias) and the chunk-local
-// inclusive cumsum of Delta * A.  One thread per (batch, chunk, head);
-// consecutive threads are consecutive heads, so the dt reads coalesce.
+// inclusive cumsum of Delta * A, written head-major ([b, H, L]).  One
+// workgroup per (batch, chunk, block of 64 heads) stages 64 tokens x 64
+// heads of dt through LDS (coalesced reads along heads), then each wave
+// scans whole heads with lane = token (coalesced writes along tokens).
 __global__ void __launch_bounds__(256)
 cumsum_kernel(const float *__restrict__ dt, const float *__restrict__ dt_bias,
               const float *__restrict__ A, float *__restrict__ delta,
               float *__restrict__ cum, int b, int L, int H, int chunk) {
+  __shared__ float tile[64 * 65];
+  __shared__ float carry[64];
   const int nc = (L + chunk - 1) / chunk;
-  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (id >= (int64_t)b * nc * H) return;
-  const int h = (int)(id % H);
-  const int c = (int)((id / H) % nc);
-  const int ib = (int)(id / ((int64_t)H * nc));
-  const float bias = dt_bias ? dt_bias[h] : 0.f;
-  const float a = A[h];
-  const int t_end = min(L, (c + 1) * chunk);
-  float run = 0.f;
-  for (int t = c * chunk; t < t_end; ++t) {
-    const float d = softplus_f(dt[((int64_t)ib * L + t) * H + h] + bias);
-    run += d * a;
-    delta[((int64_t)ib * H + h) * L + t] = d;
-    cum[((int64_t)ib * H + h) * L + t] = run;
+  const int nhb = (H + 63) / 64;
+  const int hb = blockIdx.x % nhb;
+  const int c = (blockIdx.x / nhb) % nc;
+  const int ib = blockIdx.x / (nhb * nc);
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int h0 = hb * 64, nh = min(64, H - h0);
+  if (tid < 64) carry[tid] = 0.f;
+  const int t_begin = c * chunk, t_end = min(L, t_begin + chunk);
+  for (int s0 = t_begin; s0 < t_end; s0 += 64) {
+    const int nv = min(64, t_end - s0);
+    __syncthreads();
+    for (int idx = tid; idx < 64 * 64; idx += 256) {
+      const int j = idx >> 6, hh = idx & 63;
+      tile[j * 65 + hh] = (j < nv && hh < nh) ? dt[((int64_t)ib * L + s0 + j) * H + h0 + hh] : 0.f;
+    }
+    __syncthreads();
+    for (int hh = w; hh < nh; hh += 4) {
+      const int h = h0 + hh;
+      const float d = (l < nv) ? softplus_f(tile[l * 65 + hh] + (dt_bias ? dt_bias[h] : 0.f)) : 0.f;
+      float run = d * A[h];
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float v = __shfl_up(run, off, 64);
+        if (l >= off) run += v;
+      }
+      run += carry[hh];
+      if (l < nv) {
+        delta[((int64_t)ib * H + h) * L + s0 + l] = d;
+        cum[((int64_t)ib * H + h) * L + s0 + l] = run;
+      }
+      const float last = __shfl(run, 63, 64);
+      if (l == 0) carry[hh] = last;
+    }
   }
 }
 
@@ -556,9 +733,9 @@ hipError_t launch_walk(int dtype, int P, int N, WalkMode mode, const WalkParams 
 hipError_t launch_cumsum(const float *dt, const float *dt_bias, const float *A, float *delta,
                          float *cum, int b, int L, int H, int chunk, hipStream_t stream) {
   const int nc = (L + chunk - 1) / chunk;
-  const int64_t n = (int64_t)b * nc * H;
-  hipLaunchKernelGGL(cumsum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, dt,
-                     dt_bias, A, delta, cum, b, L, H, chunk);
+  const int64_t n = (int64_t)b * nc * ((H + 63) / 64);
+  hipLaunchKernelGGL(cumsum_kernel, dim3((unsigned)n), dim3(256), 0, stream, dt, dt_bias, A,
+                     delta, cum, b, L, H, chunk);
   return hipGetLastError();
 }
 
