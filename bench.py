@@ -183,14 +183,21 @@ def main():
     achieved = nbytes / (kern_ms * 1e-3) / 1e9
     t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
     t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
-    used_algo = args.algo
+    used_algo, seg_len = args.algo, Q
     if args.algo == "auto":
-        used_algo = "fused" if b * H >= 192 else "chunked"
-    dominant = "walk_kernel<bf16,P64,N128,full>" if used_algo == "fused" else "chunked pipeline"
+        a, seg_len = ssd.ssd_scan_plan(b, L, H, P, G, N,
+                                       torch.cuda.get_device_properties(0).multi_processor_count)
+        used_algo = "fused" if a == ssd.SSD_ALGO_FUSED else "chunked"
+    if used_algo == "fused":
+        dominant = "walk_kernel (fused walk, one launch)"
+        seg_len = L
+    else:
+        dominant = ("ssd_scan_fwd chunked path, segment %d: cumsum + chunk-state walk + "
+                    "state pass + chunk-output walk (4 launches)" % seg_len)
+    plan_key = "%s_seg%d" % (used_algo, seg_len)
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS,
-                "traffic": load_traffic("walk_full", args.workload) if used_algo == "fused"
-                else None,
+                "traffic": load_traffic(plan_key, args.workload),
                 "kernel": dominant, "kernel_avg_ms": kern_ms,
                 "algorithmic_bytes_per_launch": nbytes, "bytes_per_token": nbytes / tokens,
                 "counted_flops": flops, "t_hbm_us": t_hbm * 1e6, "t_mfma_us": t_mfma * 1e6,
@@ -199,18 +206,23 @@ def main():
 
     extra = {"p10_ms": float(np.percentile(per_ms, 10)), "p90_ms": float(np.percentile(per_ms, 90))}
     if not args.no_alt:
-        other = ssd.SSD_ALGO_CHUNKED if used_algo == "fused" else ssd.SSD_ALGO_FUSED
-        for _ in range(3):
-            one(other)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(10):
-            one(other)
-        e1.record()
-        torch.cuda.synchronize()
-        extra["other_algo"] = {"algo": "chunked" if other == ssd.SSD_ALGO_CHUNKED else "fused",
-                               "ms_per_step": e0.elapsed_time(e1) / 10}
+        alts = {}
+        for name_a, a, q in (("fused", ssd.SSD_ALGO_FUSED, Q), ("chunked_256", ssd.SSD_ALGO_CHUNKED, 256),
+                             ("chunked_1024", ssd.SSD_ALGO_CHUNKED, 1024),
+                             ("chunked_2048", ssd.SSD_ALGO_CHUNKED, 2048)):
+            def run_alt():
+                ssd.ssd_scan_fwd(**t, out=out, final_state=fin, chunk=q, algo=a)
+            for _ in range(3):
+                run_alt()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(10):
+                run_alt()
+            e1.record()
+            torch.cuda.synchronize()
+            alts[name_a] = e0.elapsed_time(e1) / 10
+        extra["algorithms_ms"] = alts
     if args.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -233,7 +245,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": si.dtype, "data": "synthetic",
         "config": {"workload": args.workload, "b": b, "L": L, "H": H, "P": P, "G": G, "N": N,
-                   "chunk": Q, "init_state": si.init is not None, "algo": used_algo},
+                   "chunk": Q, "init_state": si.init is not None, "algo": used_algo,
+                   "segment": seg_len},
         "roofline": roofline, "cpu_baseline": cpu, "extra": extra,
     }
     print(json.dumps(line), flush=True)

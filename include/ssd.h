@@ -95,14 +95,18 @@ typedef struct ssd_tensor {
  *   init_state [b, H, P, N]  f32, state before token 0            NULL => 0
  *   out        [b, L, H, P]  dtype of x, written                  required
  *   final_state[b, H, P, N]  f32, state after token L-1           NULL => skip
- *   chunk      64, 128 or 256: the inter-chunk state-passing granularity
- *              of the chunked algorithm (a performance knob only)
+ *   chunk      a power of two in [64, 65536]: the segment length of the
+ *              chunked algorithm, i.e. the granularity at which states are
+ *              passed between segments.  A performance knob only: with
+ *              SSD_ALGO_AUTO the library chooses the algorithm and segment
+ *              length itself (see ssd_scan_plan) and chunk is not used.
  *   stream     hipStream_t
  *
  * The state is stored with N fastest: state[b][h][p][n] is the n-th state
  * entry of channel p (the transpose of the N x P product B x^T).
- * Supported sizes: P in {16, 32, 64, 128}, N in {16, 32, 64, 128}, H % G == 0,
- * b >= 1, L >= 1 (any L; the last chunk may be partial).
+ * Supported sizes: P in {16, 32, 64, 128} (bf16) or {16, 32, 64} (fp32),
+ * N in {16, 32, 64, 128}, H % G == 0, b >= 1, L >= 1 (any L; the last chunk
+ * may be partial).
  * Arithmetic: products on MFMA in the input dtype with fp32 accumulation,
  * the state and all decay factors in fp32.  final_state may be the same
  * tensor as init_state (updated in place); out may not overlap any input.
@@ -113,7 +117,8 @@ int ssd_scan_fwd(const ssd_tensor *x, const ssd_tensor *dt,
                  const ssd_tensor *init_state, ssd_tensor *out,
                  ssd_tensor *final_state, int chunk, void *stream);
 
-/* ssd_scan_fwd with an explicit algorithm (SSD_ALGO_*). Same contract. */
+/* ssd_scan_fwd with an explicit algorithm (SSD_ALGO_*). Same contract;
+ * SSD_ALGO_CHUNKED uses `chunk` as its segment length. */
 int ssd_scan_fwd_algo(const ssd_tensor *x, const ssd_tensor *dt,
                       const ssd_tensor *dt_bias, const ssd_tensor *A,
                       const ssd_tensor *B, const ssd_tensor *C,
@@ -143,6 +148,17 @@ int ssd_scan_fwd_algo(const ssd_tensor *x, const ssd_tensor *dt,
 int ssd_step(ssd_tensor *state, const ssd_tensor *x, const ssd_tensor *dt,
              const ssd_tensor *A, const ssd_tensor *B, const ssd_tensor *C,
              const ssd_tensor *D, ssd_tensor *out, void *stream);
+
+/*
+ * ssd_scan_plan -- the plan SSD_ALGO_AUTO uses for a shape on a device with
+ * `cus` compute units (host only, no HIP call): *algo is SSD_ALGO_FUSED or
+ * SSD_ALGO_CHUNKED and *seg_len the segment length (L for the fused walk).
+ * The choice trades the spread of (batch, head, segment) walks over the
+ * compute units against the extra state-only pass and state traffic of
+ * shorter segments.
+ */
+int ssd_scan_plan(int64_t b, int64_t L, int64_t H, int64_t P, int64_t G,
+                  int64_t N, int cus, int *algo, int *seg_len);
 
 /* Static text for a status code. */
 const char *ssd_status_string(int status);

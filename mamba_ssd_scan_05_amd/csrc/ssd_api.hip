@@ -114,8 +114,10 @@ int validate_scan(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *d
     return fail(SSD_ERR_SHAPE, "H=%lld is not a multiple of G=%lld", (long long)s->H, (long long)s->G);
   if (!valid_pn(s->P)) return fail(SSD_ERR_UNSUPPORTED, "P=%lld not in {16,32,64,128}", (long long)s->P);
   if (!valid_pn(s->N)) return fail(SSD_ERR_UNSUPPORTED, "N=%lld not in {16,32,64,128}", (long long)s->N);
-  if (chunk != 64 && chunk != 128 && chunk != 256)
-    return fail(SSD_ERR_UNSUPPORTED, "chunk=%d not in {64,128,256}", chunk);
+  if (x->dtype == SSD_F32 && s->P > 64)
+    return fail(SSD_ERR_UNSUPPORTED, "P=%lld with fp32 inputs: fp32 supports P in {16,32,64}", (long long)s->P);
+  if (chunk < 64 || chunk > 65536 || (chunk & (chunk - 1)) != 0)
+    return fail(SSD_ERR_UNSUPPORTED, "chunk=%d is not a power of two in [64, 65536]", chunk);
   if (s->b * s->L * s->H * s->P > ((int64_t)1 << 40) || s->b * s->L > INT32_MAX / 2 ||
       s->b * s->H * ((s->L + 63) / 64) > INT32_MAX / 2)
     return fail(SSD_ERR_UNSUPPORTED, "problem too large for 32-bit workgroup indexing");
@@ -176,9 +178,11 @@ int run_chunked(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_
   const int64_t nc = (s.L + chunk - 1) / chunk;
   const int64_t PN = s.P * s.N;
   const size_t n_tok = (size_t)(s.b * s.H * s.L);
-  const size_t bytes_delta = n_tok * sizeof(float);
-  const size_t bytes_states = (size_t)(s.b * s.H * nc * PN) * sizeof(float);
-  const size_t total = 2 * bytes_delta + bytes_states;
+  const size_t n_seg = (size_t)(s.b * s.H * nc);
+  // scratch: Delta [b,H,L] | chunk log2 decays [b,H,nc] (padded) | chunk states [b,H,nc,P,N]
+  const size_t off_dec = n_tok * sizeof(float);
+  const size_t off_states = off_dec + ((n_seg * sizeof(float) + 255) / 256) * 256;
+  const size_t total = off_states + n_seg * (size_t)PN * sizeof(float);
   void *ws = nullptr;
   hipError_t e = hipMallocAsync(&ws, total, st);
   if (e != hipSuccess || !ws) {
@@ -186,31 +190,38 @@ int run_chunked(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_
     return fail(SSD_ERR_NOMEM, "scratch of %zu bytes: %s", total, hipGetErrorString(e));
   }
   float *delta = (float *)ws;
-  float *cum = delta + n_tok;
-  float *states = cum + n_tok;
+  float *seg_decay = (float *)((char *)ws + off_dec);
+  float *states = (float *)((char *)ws + off_states);
   int status = SSD_OK;
   do {
-    e = ssd::launch_cumsum((const float *)dt->data,
-                           dt_bias ? (const float *)dt_bias->data : nullptr,
-                           (const float *)A->data, delta, cum, (int)s.b, (int)s.L, (int)s.H,
-                           chunk, st);
-    if (e != hipSuccess) { status = hip_fail(e, "cumsum launch"); break; }
+    // 1. step sizes Delta (head-major)
+    e = ssd::launch_delta((const float *)dt->data, dt_bias ? (const float *)dt_bias->data : nullptr,
+                          delta, (int)s.b, (int)s.L, (int)s.H, st);
+    if (e != hipSuccess) { status = hip_fail(e, "delta launch"); break; }
 
+    // 2. each chunk's own end state from a zero start, and its total decay
+    //    (all chunks but the last)
     ssd::WalkParams p{};
     p.x = x->data; p.dt = delta; p.dt_bias = nullptr; p.A = (const float *)A->data;
     p.B = B->data; p.C = C->data; p.D = D ? (const float *)D->data : nullptr;
     p.b = (int)s.b; p.L = (int)s.L; p.H = (int)s.H; p.G = (int)s.G;
     p.seg_len = chunk; p.nseg = (int)nc;
-    p.init = nullptr; p.out = nullptr; p.state_out = states;
-    e = ssd::launch_walk(x->dtype, (int)s.P, (int)s.N, ssd::kWalkChunkState, p, st);
-    if (e != hipSuccess) { status = hip_fail(e, "chunk-state launch"); break; }
+    p.init = nullptr; p.out = nullptr; p.state_out = states; p.final_state = nullptr;
+    p.seg_decay = seg_decay;
+    if (nc > 1) {
+      e = ssd::launch_walk(x->dtype, (int)s.P, (int)s.N, ssd::kWalkChunkState, p, st);
+      if (e != hipSuccess) { status = hip_fail(e, "chunk-state launch"); break; }
+    }
 
-    e = ssd::launch_state_pass(states, cum, init ? (const float *)init->data : nullptr,
-                               fin ? (float *)fin->data : nullptr, (int)s.b, (int)s.L,
-                               (int)s.H, (int)PN, chunk, st);
+    // 3. state entering every chunk (sequential over chunks)
+    e = ssd::launch_state_pass(states, seg_decay, init ? (const float *)init->data : nullptr,
+                               (int)s.b, (int)s.H, (int)PN, (int)nc, st);
     if (e != hipSuccess) { status = hip_fail(e, "state-pass launch"); break; }
 
-    p.init = states; p.out = out->data; p.state_out = nullptr;
+    // 4. outputs of every chunk from its entering state; the last chunk's
+    //    walk leaves the final state
+    p.init = states; p.out = out->data; p.state_out = nullptr; p.seg_decay = nullptr;
+    p.final_state = fin ? (float *)fin->data : nullptr;
     e = ssd::launch_walk(x->dtype, (int)s.P, (int)s.N, ssd::kWalkChunkOut, p, st);
     if (e != hipSuccess) { status = hip_fail(e, "chunk-output launch"); break; }
   } while (0);
@@ -219,12 +230,58 @@ int run_chunked(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_
   return status;
 }
 
-// Shape heuristic: the fused walk has one workgroup per (batch, head) and
-// needs enough of them to cover the 256 compute units; otherwise the
-// chunk-parallel pipeline exposes b*H*chunks workgroups.
-int choose_algo(const ScanShape &s, int chunk) {
-  (void)chunk;
-  return (s.b * s.H >= 192) ? SSD_ALGO_FUSED : SSD_ALGO_CHUNKED;
+// Compute units of the current device (queried once per device).
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int cu = 0;
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0)
+      cu = 256;
+    cache[dev] = cu;
+  }
+  return cache[dev];
+}
+
+// Plan for SSD_ALGO_AUTO, from measured costs on MI355X: a compute unit
+// retires about one 64-token sub-block of one (batch, head) walk every
+// 2 us whether it holds one walk or several, so a pass of W walks of n
+// sub-blocks costs ceil(W / CUs) * n * 2 us.  The fused single kernel is one
+// pass with W = b*H over the whole sequence.  Splitting sequences into S
+// segments gives a pass of b*H*S output walks, a state-only pass over S-1
+// segments (measured at 0.7 of an output walk), the step-size kernel, the
+// state-passing pass (2 * b*H*S*P*N*4 bytes at ~4 TB/s) and launch gaps.
+// The split is taken only when predicted at least 10% faster.
+struct Plan {
+  int algo;
+  int seg_len;
+};
+
+Plan choose_plan(const ScanShape &s, int cus) {
+  const double t_sub_us = 2.0;  // one sub-block of one walk on one compute unit
+  const double state_rel = 0.7; // state-only walk relative to an output walk
+  const double pass_bw = 4.0e12;
+  const double fixed_us = 10.0; // step-size kernel and extra launches
+  const int64_t units = s.b * s.H;
+  const int64_t nsub = (s.L + 63) / 64;
+  Plan best{SSD_ALGO_FUSED, (int)std::min<int64_t>(s.L, 65536)};
+  const double fused_t = (double)((units + cus - 1) / cus) * nsub * t_sub_us;
+  double best_t = 0.9 * fused_t;
+  for (int seg = 65536; seg >= 256; seg /= 2) {
+    const int64_t S = (s.L + seg - 1) / seg;
+    if (S < 2) continue;
+    const double sub = (double)(seg / 64);
+    const double walk = (double)((units * S + cus - 1) / cus) * sub * t_sub_us;
+    const double state = state_rel * (double)((units * (S - 1) + cus - 1) / cus) * sub * t_sub_us;
+    const double pass = 2.0 * units * S * s.P * s.N * 4.0 / pass_bw * 1e6;
+    const double t = walk + state + pass + fixed_us;
+    if (t < best_t) {
+      best_t = t;
+      best = Plan{SSD_ALGO_CHUNKED, seg};
+    }
+  }
+  return best;
 }
 
 } // namespace
@@ -240,7 +297,11 @@ int ssd_scan_fwd_algo(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tenso
   SSD_CHECK(validate_scan(x, dt, dt_bias, A, B, C, D, init_state, out, final_state, chunk, &s));
   if (algo != SSD_ALGO_AUTO && algo != SSD_ALGO_FUSED && algo != SSD_ALGO_CHUNKED)
     return fail(SSD_ERR_UNSUPPORTED, "unknown algorithm %d", algo);
-  if (algo == SSD_ALGO_AUTO) algo = choose_algo(s, chunk);
+  if (algo == SSD_ALGO_AUTO) {
+    const Plan plan = choose_plan(s, device_cus());
+    algo = plan.algo;
+    chunk = plan.seg_len;
+  }
   hipStream_t st = (hipStream_t)stream;
   if (algo == SSD_ALGO_FUSED)
     return run_fused(x, dt, dt_bias, A, B, C, D, init_state, out, final_state, s, st);
@@ -299,6 +360,20 @@ int ssd_step(ssd_tensor *state, const ssd_tensor *x, const ssd_tensor *dt, const
                                   C->data, D ? (const float *)D->data : nullptr, out->data,
                                   (int)b, (int)H, (int)P, (int)G, (hipStream_t)stream);
   return e == hipSuccess ? SSD_OK : hip_fail(e, "step launch");
+}
+
+int ssd_scan_plan(int64_t b, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, int cus,
+                  int *algo, int *seg_len) {
+  g_last_error.clear();
+  if (!algo || !seg_len) return fail(SSD_ERR_NULL, "algo/seg_len: NULL");
+  if (b < 1 || L < 1 || H < 1 || G < 1 || H % G != 0)
+    return fail(SSD_ERR_SHAPE, "invalid shape b=%lld L=%lld H=%lld G=%lld", (long long)b,
+                (long long)L, (long long)H, (long long)G);
+  ScanShape s{b, L, H, P, G, N};
+  const Plan plan = choose_plan(s, cus > 0 ? cus : 256);
+  *algo = plan.algo;
+  *seg_len = plan.seg_len;
+  return SSD_OK;
 }
 
 const char *ssd_status_string(int status) {

@@ -27,6 +27,9 @@ struct WalkParams {
   void *out;            // [b, L, H, P] or null (state-only walk)
   float *state_out;     // state leaving each segment, same indexing as init,
                         // or null
+  float *final_state;   // [b, H, P, N]: state leaving the last segment, or null
+  float *seg_decay;     // [b, H, nseg]: sum of Delta*A*log2(e) over each segment
+                        // (state-only walk), or null
   int b, L, H, G, seg_len, nseg;
 };
 
@@ -34,23 +37,22 @@ struct WalkParams {
 enum WalkMode {
   kWalkFull = 0,      // outputs y; Delta from raw dt (+ bias, softplus)
   kWalkChunkOut = 1,  // outputs y; Delta precomputed [b, H, L]
-  kWalkChunkState = 2 // no y; state only; Delta precomputed [b, H, L]
+  kWalkChunkState = 2 // no y; state only; Delta precomputed [b, H, L];
+                      // the last segment is skipped (nothing consumes it)
 };
 
 hipError_t launch_walk(int dtype, int P, int N, WalkMode mode,
                        const WalkParams &p, hipStream_t stream);
 
-// Per-chunk log-decay: Delta [b,H,L] and chunk-local inclusive cumsum of
-// Delta*A [b,H,L].
-hipError_t launch_cumsum(const float *dt, const float *dt_bias, const float *A,
-                         float *delta, float *cum, int b, int L, int H,
-                         int chunk, hipStream_t stream);
+// Step sizes: Delta [b,H,L] = softplus(dt [b,L,H] + dt_bias), head-major.
+hipError_t launch_delta(const float *dt, const float *dt_bias, float *delta,
+                        int b, int L, int H, hipStream_t stream);
 
 // Inter-chunk state passing over [b,H,nc,P,N] chunk states, in place: slot c
-// becomes the state entering chunk c.  final_state may be null.
-hipError_t launch_state_pass(float *states, const float *cum,
-                             const float *init, float *final_state, int b,
-                             int L, int H, int PN, int chunk,
+// becomes the state entering chunk c (slot nc-1's own state is not read).
+// seg_decay [b,H,nc] holds each chunk's log2 decay.
+hipError_t launch_state_pass(float *states, const float *seg_decay,
+                             const float *init, int b, int H, int PN, int nc,
                              hipStream_t stream);
 
 // One recurrent step, state in place.

@@ -231,22 +231,43 @@ __host__ __device__ constexpr int mtile_jt(int slot) {
 
 // ---------------------------------------------------------------------------
 // The chunk walk.
+//
+// Work split inside a workgroup: KH * P/16 waves (KH = 1 or 2).  Wave w
+// handles p-tile pt = w % (P/16) (state rows [16pt, 16pt+16)) and part
+// hv = w / (P/16) of KH: it owns the n-tiles [hv*NTILE/KH, (hv+1)*NTILE/KH)
+// of those state rows in registers and the output token tiles
+// [hv*4/KH, (hv+1)*4/KH) of each sub-block.  With KH = 2 the operand copy
+// of the whole state, which the state term needs, is exchanged through LDS
+// once per sub-block; with KH = 1 it comes straight from the registers.
+template <typename T, int P>
+constexpr int walk_halves() { return 1; }
+template <typename T, int P>
+constexpr int walk_waves() { return walk_halves<T, P>() * (P / 16); }
+template <typename T, int P>
+constexpr int walk_min_waves_per_eu() {
+  return (sizeof(T) == 2 && P == 64) ? (walk_halves<T, P>() == 2 ? 4 : 2) : 1;
+}
+
 template <typename T, int P, int N, int MODE>
-__global__ void __launch_bounds__(P / 16 * 64, (sizeof(T) == 2 && P == 64) ? 2 : 1)
+__global__ void __launch_bounds__((walk_waves<T, P>() * 64), (walk_min_waves_per_eu<T, P>()))
 walk_kernel(const WalkParams prm) {
   static_assert(kSub == 64, "the tile tables assume 64-token sub-blocks");
   constexpr bool kOut = MODE != kWalkChunkState;
-  constexpr int NW = P / 16;             // waves; wave w owns rows [16w, 16w+16)
+  constexpr int NPT = P / 16;            // p-tiles
+  constexpr int KH = walk_halves<T, P>();
+  constexpr int NW = walk_waves<T, P>(); // waves
   constexpr int NTH = NW * 64;
   constexpr int NP = (N + 31) / 32 * 32; // N padded to a K-step
   constexpr int NTILE = NP / 16;
+  constexpr int NTH2 = NTILE / KH;       // n-tiles per wave
   constexpr int KN = NP / 32;
   constexpr int ES = (int)sizeof(T);
   constexpr int VEC = 16 / ES;           // elements per 16-byte access
   constexpr int LDB = tr_ld(NP, ES);     // B tile: row reads and transposed reads
   constexpr int LDC = NP + VEC;          // C tile: row reads only
-  constexpr int LDX = tr_ld(P, ES);      // X tile: transposed reads and row reads
+  constexpr int LDX = tr_ld(P, ES);      // X tile: transposed reads
   constexpr int LDM = kSub + 4;          // masked scores M[i][j]
+  constexpr int LDH = NP + VEC;          // state copy for the state-term operand
   constexpr int NTI = kSub / 16;         // token tiles per sub-block
   constexpr int BRW = NP / VEC;          // 16-byte pieces per B/C row
   constexpr int XRW = P / VEC;           // 16-byte pieces per X row
@@ -254,11 +275,14 @@ walk_kernel(const WalkParams prm) {
   constexpr int XPT = (kSub * XRW + NTH - 1) / NTH;
   constexpr int NMT = 12;                // masked-score tile slots
   constexpr int MPW = (NMT + NW - 1) / NW;
+  constexpr int NIT = NTI / KH;          // output token tiles per wave
+  static_assert(NTILE % KH == 0 && NTI == 4, "tile split");
 
   __shared__ __attribute__((aligned(16))) T sB[kSub * LDB];
   __shared__ __attribute__((aligned(16))) T sC[kOut ? kSub * LDC : VEC];
   __shared__ __attribute__((aligned(16))) T sX[kSub * LDX];
   __shared__ __attribute__((aligned(16))) T sM[kOut ? kSub * LDM : VEC];
+  __shared__ __attribute__((aligned(16))) T sH[(kOut && KH == 2) ? P * LDH : VEC];
   __shared__ float sC2[kSub]; // cum * log2(e)
   __shared__ float sQ2[kSub]; // cum * log2(e) - log2(Delta)   (+inf where Delta = 0)
   __shared__ float sW[kSub];  // exp(cum_last - cum_j) * Delta_j
@@ -277,25 +301,39 @@ walk_kernel(const WalkParams prm) {
   const int t_begin = seg * prm.seg_len;
   const int t_end = min(L, t_begin + prm.seg_len);
 
+  if (MODE == kWalkChunkState && seg == nseg - 1) return; // no consumer
+
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
-  const int prow = 16 * w + li; // the state row this lane feeds as an operand
+  const int pt = w % NPT, hv = w / NPT;
+  const int prow = 16 * pt + li; // the state row this lane feeds as an operand
 
   const float a2 = prm.A[h] * kLog2e;
   const float d_h = prm.D ? prm.D[h] : 0.f;
   const float bias = (MODE == kWalkFull && prm.dt_bias) ? prm.dt_bias[h] : 0.f;
   const int64_t state_idx = ((int64_t)(ib * H + h) * nseg + seg) * P * N;
 
-  // State S^T tiles: hs[nt][r] = S[p = prow][n = 16 nt + 4 lg + r].
-  f32x4 hs[NTILE];
+  // State tiles of this wave: hs[k][r] = S[p = prow][n = 16 (hv NTH2 + k) + 4 lg + r].
+  f32x4 hs[NTH2];
 #pragma unroll
-  for (int nt = 0; nt < NTILE; ++nt) hs[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < NTH2; ++k) hs[k] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (prm.init != nullptr) {
     const float *src = prm.init + state_idx + (int64_t)prow * N;
 #pragma unroll
-    for (int nt = 0; nt < NTILE; ++nt)
-      if (16 * nt < N) hs[nt] = *reinterpret_cast<const f32x4 *>(src + 16 * nt + 4 * lg);
+    for (int k = 0; k < NTH2; ++k) {
+      const int n0 = 16 * (hv * NTH2 + k);
+      if (n0 < N) hs[k] = *reinterpret_cast<const f32x4 *>(src + n0 + 4 * lg);
+    }
   }
+  // Publish the operand copy of the state (read after the loop's first barrier).
+  auto publish_state = [&]() {
+    if constexpr (kOut && KH == 2) {
+#pragma unroll
+      for (int k = 0; k < NTH2; ++k)
+        st4<T>(&sH[prow * LDH + 16 * (hv * NTH2 + k) + 4 * lg], hs[k][0], hs[k][1], hs[k][2], hs[k][3]);
+    }
+  };
+  publish_state();
 
   // Per-thread 16-byte pieces of the staged tiles: row and column within
   // the sub-block are fixed for the whole walk; only the base moves.
@@ -327,29 +365,41 @@ walk_kernel(const WalkParams prm) {
     offX[q] = (uint32_t)(((int64_t)(idx / XRW) * rowX + (idx % XRW) * VEC) * ES);
   }
   const uint32_t offDt = (uint32_t)(l * dtstride * 4);
-  const uint32_t offY = (uint32_t)(((int64_t)li * rowX + 16 * w + 4 * lg) * ES);
-  // Rows past the end of the segment read as zero (buffer range check).
-  auto fetch = [&](int t0, int nv) {
-    const auto rsB = make_rsrc(Bbase + (int64_t)t0 * rowB, (uint32_t)(((int64_t)(nv - 1) * rowB + N) * ES));
-    const auto rsC = make_rsrc(Cbase + (int64_t)t0 * rowB, (uint32_t)(((int64_t)(nv - 1) * rowB + N) * ES));
+  const uint32_t offY = (uint32_t)(((int64_t)li * rowX + 16 * pt + 4 * lg) * ES);
+  // Loads of one sub-block, in three groups so that their issue spreads over
+  // the compute phases of the previous sub-block.  Rows past the end of the
+  // segment read as zero (buffer range check).
+  auto fetch_x = [&](int t0, int nv) {
     const auto rsX = make_rsrc(Xbase + (int64_t)t0 * rowX, (uint32_t)(((int64_t)(nv - 1) * rowX + P) * ES));
     const auto rsD = make_rsrc(dtbase + (int64_t)t0 * dtstride, (uint32_t)(((int64_t)(nv - 1) * dtstride + 1) * 4));
-#pragma unroll
-    for (int q = 0; q < BPT; ++q) {
-      if (tid + q * NTH < kSub * BRW) {
-        rB[q] = bload16(rsB, offB[q]);
-        if (kOut) rC[q] = bload16(rsC, offB[q]);
-      }
-    }
 #pragma unroll
     for (int q = 0; q < XPT; ++q)
       if (tid + q * NTH < kSub * XRW) rX[q] = bload16(rsX, offX[q]);
     rdt = bload4(rsD, offDt);
   };
+  auto fetch_b = [&](int t0, int nv) {
+    const auto rsB = make_rsrc(Bbase + (int64_t)t0 * rowB, (uint32_t)(((int64_t)(nv - 1) * rowB + N) * ES));
+#pragma unroll
+    for (int q = 0; q < BPT; ++q)
+      if (tid + q * NTH < kSub * BRW) rB[q] = bload16(rsB, offB[q]);
+  };
+  auto fetch_c = [&](int t0, int nv) {
+    if constexpr (kOut) {
+      const auto rsC = make_rsrc(Cbase + (int64_t)t0 * rowB, (uint32_t)(((int64_t)(nv - 1) * rowB + N) * ES));
+#pragma unroll
+      for (int q = 0; q < BPT; ++q)
+        if (tid + q * NTH < kSub * BRW) rC[q] = bload16(rsC, offB[q]);
+    }
+  };
 
+  float seg_log2 = 0.f; // log2 decay of the segment so far
   int t0 = t_begin;
   int nv = min(kSub, t_end - t0);
-  if (t0 < t_end) fetch(t0, nv);
+  if (t0 < t_end) {
+    fetch_x(t0, nv);
+    fetch_b(t0, nv);
+    fetch_c(t0, nv);
+  }
   while (t0 < t_end) {
     __syncthreads(); // the previous sub-block is done with LDS
 
@@ -388,101 +438,113 @@ walk_kernel(const WalkParams prm) {
 
     const int t_next = t0 + kSub;
     const int nv_next = min(kSub, t_end - t_next);
-    if (t_next < t_end) fetch(t_next, nv_next);
+    const bool more = t_next < t_end;
+    if (more) fetch_x(t_next, nv_next);
 
-    f32x4 yacc[NTI];
+    f32x4 yacc[NIT];
     if constexpr (kOut) {
       // ---- masked scores M[i][j] = (C_i . B_j) exp(cum_i - cum_j) Delta_j --
-      //      = S^T[j][i] * exp2(c2_i - q2_j)
+      //      = S^T[j][i] exp2(c2_i - q2_j); the diagonal also carries D, so
+      //      the intra-block product adds D x_i.
+      // All slots of a wave are computed without branches (the all-zero
+      // tiles too, then masked), so their MFMA chains interleave.
+      f32x4 macc[MPW];
+#pragma unroll
+      for (int k = 0; k < MPW; ++k) {
+        const int slot = min(w + k * NW, NMT - 1);
+        const int it = mtile_it(slot), jt = mtile_jt(slot);
+        macc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KN; ++ks)
+          macc[k] = mma(ld8(&sB[(16 * jt + li) * LDB + 32 * ks + 8 * lg]),
+                        ld8(&sC[(16 * it + li) * LDC + 32 * ks + 8 * lg]), macc[k]);
+      }
 #pragma unroll
       for (int k = 0; k < MPW; ++k) {
         const int slot = w + k * NW;
-        if (slot < NMT) {
+        if (NMT % NW == 0 || slot < NMT) {
           const int it = mtile_it(slot), jt = mtile_jt(slot);
           const int i = 16 * it + li;
-          float m[4] = {0.f, 0.f, 0.f, 0.f};
-          if (jt <= it) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          const float ci = sC2[i];
+          const float4 q4 = *reinterpret_cast<const float4 *>(&sQ2[16 * jt + 4 * lg]);
+          float m[4] = {macc[k][0] * hw_exp2(ci - q4.x), macc[k][1] * hw_exp2(ci - q4.y),
+                        macc[k][2] * hw_exp2(ci - q4.z), macc[k][3] * hw_exp2(ci - q4.w)};
+          // causal mask (row tile it vs column tile jt), D on the diagonal
 #pragma unroll
-            for (int ks = 0; ks < KN; ++ks)
-              acc = mma(ld8(&sB[(16 * jt + li) * LDB + 32 * ks + 8 * lg]),
-                        ld8(&sC[i * LDC + 32 * ks + 8 * lg]), acc);
-            const float ci = sC2[i];
-            const float4 q4 = *reinterpret_cast<const float4 *>(&sQ2[16 * jt + 4 * lg]);
-            m[0] = acc[0] * hw_exp2(ci - q4.x);
-            m[1] = acc[1] * hw_exp2(ci - q4.y);
-            m[2] = acc[2] * hw_exp2(ci - q4.z);
-            m[3] = acc[3] * hw_exp2(ci - q4.w);
-            if (jt == it) {
-#pragma unroll
-              for (int r = 0; r < 4; ++r) m[r] = (4 * lg + r <= li) ? m[r] : 0.f;
-            }
+          for (int r = 0; r < 4; ++r) {
+            const int dj = 16 * jt + 4 * lg + r, di = 16 * it + li;
+            m[r] = (dj < di) ? m[r] : (dj == di ? m[r] + d_h : 0.f);
           }
           st4<T>(&sM[i * LDM + 16 * jt + 4 * lg], m[0], m[1], m[2], m[3]);
         }
       }
+      if (more) fetch_b(t_next, nv_next);
 
       // ---- state term: Y^T[p][i] = exp(cum_i) sum_n S[p][n] C[i][n] --------
+      // A operand: the state rows of this p-tile, K = n in the order
+      // {32ks + 4g + r, 32ks + 16 + 4g + r} that the register tiles hold.
       typename FragOf<T>::type hf[KN];
 #pragma unroll
       for (int ks = 0; ks < KN; ++ks) {
-        float v[8];
+        if constexpr (KH == 1) {
+          float v[8];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          v[r] = hs[2 * ks][r];
-          v[4 + r] = hs[2 * ks + 1][r];
+          for (int r = 0; r < 4; ++r) {
+            v[r] = hs[2 * ks][r];
+            v[4 + r] = hs[2 * ks + 1][r];
+          }
+          hf[ks] = pack8<T>(v);
+        } else {
+          hf[ks] = ld4x2(&sH[prow * LDH + 32 * ks + 4 * lg], &sH[prow * LDH + 32 * ks + 16 + 4 * lg]);
         }
-        hf[ks] = pack8<T>(v);
       }
 #pragma unroll
-      for (int it = 0; it < NTI; ++it) {
-        const int i = 16 * it + li;
+      for (int u = 0; u < NIT; ++u) {
+        const int i = 16 * (NIT * hv + u) + li;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KN; ++ks)
-          acc = mma(hf[ks],
-                    ld4x2(&sC[i * LDC + 32 * ks + 4 * lg], &sC[i * LDC + 32 * ks + 16 + 4 * lg]),
+          acc = mma(hf[ks], ld4x2(&sC[i * LDC + 32 * ks + 4 * lg], &sC[i * LDC + 32 * ks + 16 + 4 * lg]),
                     acc);
-        yacc[it] = acc * hw_exp2(sC2[i]);
+        yacc[u] = acc * hw_exp2(sC2[i]);
       }
-      __syncthreads(); // M complete
+      if (more) fetch_c(t_next, nv_next);
+      __syncthreads(); // M complete; every wave has read the state copy
+    } else {
+      if (more) fetch_b(t_next, nv_next);
     }
 
     // X^T fragments (rows p = prow, K = tokens), shared by the intra-block
     // product and the state update.
     typename FragOf<T>::type xf[kSub / 32];
 #pragma unroll
-    for (int ks = 0; ks < kSub / 32; ++ks) xf[ks] = trfrag(sX, LDX, 32 * ks, 16 * w, li, lg);
+    for (int ks = 0; ks < kSub / 32; ++ks) xf[ks] = trfrag(sX, LDX, 32 * ks, 16 * pt, li, lg);
 
     if constexpr (kOut) {
       // ---- intra-block term: Y^T[p][i] += sum_{j<=i} X^T[p][j] M[i][j] -----
-#pragma unroll
-      for (int it = 0; it < NTI; ++it) {
-        const int i = 16 * it + li;
-#pragma unroll
-        for (int ks = 0; ks < (16 * (it + 1) + 31) / 32; ++ks)
-          yacc[it] = mma(xf[ks],
-                         ld4x2(&sM[i * LDM + 32 * ks + 4 * lg], &sM[i * LDM + 32 * ks + 16 + 4 * lg]),
-                         yacc[it]);
-      }
-      // ---- epilogue: + D x, store y --------------------------------------
-      // Rows past the end of the segment fall outside the store range.
-      const int p0 = 16 * w + 4 * lg;
+      //      then store y (rows past the segment end fall outside the range)
       const auto rsY = make_rsrc(Ybase + (int64_t)t0 * rowX, (uint32_t)(((int64_t)(nv - 1) * rowX + P) * ES));
 #pragma unroll
-      for (int it = 0; it < NTI; ++it) {
+      for (int u = 0; u < NIT; ++u) {
+        const int it = NIT * hv + u;
         const int i = 16 * it + li;
-        const T *xr = &sX[i * LDX + p0];
-        bstore4<T>(rsY, offY + (uint32_t)(16 * it * rowX * ES),
-                   yacc[it][0] + d_h * to_f(xr[0]), yacc[it][1] + d_h * to_f(xr[1]),
-                   yacc[it][2] + d_h * to_f(xr[2]), yacc[it][3] + d_h * to_f(xr[3]));
+        if (KH == 2 && hv == 0) {
+          yacc[u] = mma(xf[0], ld4x2(&sM[i * LDM + 4 * lg], &sM[i * LDM + 16 + 4 * lg]), yacc[u]);
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < (KH == 1 ? (16 * (u + 1) + 31) / 32 : 2); ++ks)
+            yacc[u] = mma(xf[ks], ld4x2(&sM[i * LDM + 32 * ks + 4 * lg], &sM[i * LDM + 32 * ks + 16 + 4 * lg]),
+                          yacc[u]);
+        }
+        bstore4<T>(rsY, offY + (uint32_t)(16 * it * rowX * ES), yacc[u][0], yacc[u][1], yacc[u][2], yacc[u][3]);
       }
     }
 
     // ---- state update: S^T = decay S^T + B^T (w o X) ------------------------
+    seg_log2 += sC2[kSub - 1];
     const float dec = hw_exp2(sC2[kSub - 1]);
 #pragma unroll
-    for (int nt = 0; nt < NTILE; ++nt) hs[nt] *= dec;
+    for (int k = 0; k < NTH2; ++k) hs[k] *= dec;
 #pragma unroll
     for (int ks = 0; ks < kSub / 32; ++ks) {
       const float4 wa = *reinterpret_cast<const float4 *>(&sW[32 * ks + 4 * lg]);
@@ -492,69 +554,52 @@ walk_kernel(const WalkParams prm) {
                           elem(xf[ks], 6) * wb.z, elem(xf[ks], 7) * wb.w};
       const auto bx = pack8<T>(v);
 #pragma unroll
-      for (int nt = 0; nt < NTILE; ++nt)
-        hs[nt] = mma(trfrag(sB, LDB, 32 * ks, 16 * nt, li, lg), bx, hs[nt]);
+      for (int k = 0; k < NTH2; ++k)
+        hs[k] = mma(trfrag(sB, LDB, 32 * ks, 16 * (hv * NTH2 + k), li, lg), bx, hs[k]);
     }
+    publish_state();
     t0 = t_next;
     nv = nv_next;
   }
 
-  if (prm.state_out) {
+  if (prm.seg_decay && tid == 0) prm.seg_decay[(int64_t)(ib * H + h) * nseg + seg] = seg_log2;
+  float *dst = prm.state_out ? prm.state_out + state_idx
+             : (prm.final_state && seg == nseg - 1) ? prm.final_state + (int64_t)(ib * H + h) * P * N
+                                                     : nullptr;
+  if (dst) {
 #pragma unroll
-    for (int nt = 0; nt < NTILE; ++nt) {
-      const int n0 = 16 * nt + 4 * lg;
-      if (n0 < N)
-        *reinterpret_cast<f32x4 *>(prm.state_out + state_idx + (int64_t)prow * N + n0) = hs[nt];
+    for (int k = 0; k < NTH2; ++k) {
+      const int n0 = 16 * (hv * NTH2 + k);
+      if (n0 < N) *reinterpret_cast<f32x4 *>(dst + (int64_t)prow * N + n0 + 4 * lg) = hs[k];
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Per-chunk log-decay: Delta = softplus(dt + bias) and the chunk-local
-// inclusive cumsum of Delta * A, written head-major ([b, H, L]).  One
-// workgroup per (batch, chunk, block of 64 heads) stages 64 tokens x 64
-// heads of dt through LDS (coalesced reads along heads), then each wave
-// scans whole heads with lane = token (coalesced writes along tokens).
+// Step sizes Delta = softplus(dt + bias), transposed to head-major [b, H, L]
+// (the selective step size of the Mamba reading notes, selective-mechanism
+// section).  One workgroup per (batch, 64-token tile, 64-head tile) stages
+// dt through LDS: reads coalesce along heads, writes along tokens.
 __global__ void __launch_bounds__(256)
-cumsum_kernel(const float *__restrict__ dt, const float *__restrict__ dt_bias,
-              const float *__restrict__ A, float *__restrict__ delta,
-              float *__restrict__ cum, int b, int L, int H, int chunk) {
+delta_kernel(const float *__restrict__ dt, const float *__restrict__ dt_bias,
+             float *__restrict__ delta, int b, int L, int H) {
   __shared__ float tile[64 * 65];
-  __shared__ float carry[64];
-  const int nc = (L + chunk - 1) / chunk;
-  const int nhb = (H + 63) / 64;
+  const int ntt = (L + 63) / 64, nhb = (H + 63) / 64;
   const int hb = blockIdx.x % nhb;
-  const int c = (blockIdx.x / nhb) % nc;
-  const int ib = blockIdx.x / (nhb * nc);
+  const int tt = (blockIdx.x / nhb) % ntt;
+  const int ib = blockIdx.x / (nhb * ntt);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int h0 = hb * 64, nh = min(64, H - h0);
-  if (tid < 64) carry[tid] = 0.f;
-  const int t_begin = c * chunk, t_end = min(L, t_begin + chunk);
-  for (int s0 = t_begin; s0 < t_end; s0 += 64) {
-    const int nv = min(64, t_end - s0);
-    __syncthreads();
-    for (int idx = tid; idx < 64 * 64; idx += 256) {
-      const int j = idx >> 6, hh = idx & 63;
-      tile[j * 65 + hh] = (j < nv && hh < nh) ? dt[((int64_t)ib * L + s0 + j) * H + h0 + hh] : 0.f;
-    }
-    __syncthreads();
-    for (int hh = w; hh < nh; hh += 4) {
-      const int h = h0 + hh;
-      const float d = (l < nv) ? softplus_f(tile[l * 65 + hh] + (dt_bias ? dt_bias[h] : 0.f)) : 0.f;
-      float run = d * A[h];
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float v = __shfl_up(run, off, 64);
-        if (l >= off) run += v;
-      }
-      run += carry[hh];
-      if (l < nv) {
-        delta[((int64_t)ib * H + h) * L + s0 + l] = d;
-        cum[((int64_t)ib * H + h) * L + s0 + l] = run;
-      }
-      const float last = __shfl(run, 63, 64);
-      if (l == 0) carry[hh] = last;
-    }
+  const int t0 = tt * 64, nv = min(64, L - t0);
+  for (int idx = tid; idx < 64 * 64; idx += 256) {
+    const int j = idx >> 6, hh = idx & 63;
+    tile[j * 65 + hh] = (j < nv && hh < nh) ? dt[((int64_t)ib * L + t0 + j) * H + h0 + hh] : 0.f;
+  }
+  __syncthreads();
+  for (int hh = w; hh < nh; hh += 4) {
+    const int h = h0 + hh;
+    if (l < nv)
+      delta[((int64_t)ib * H + h) * L + t0 + l] = softplus_f(tile[l * 65 + hh] + (dt_bias ? dt_bias[h] : 0.f));
   }
 }
 
@@ -563,13 +608,12 @@ cumsum_kernel(const float *__restrict__ dt, const float *__restrict__ dt_bias,
 // (batch, head, P*N/4): each thread carries four consecutive fp32 state
 // entries.  Slot c of `states` holds chunk c's own (zero-entry) end state on
 // input and the state entering chunk c on output.  The chunk decays
-// exp(cum at the chunk's last token) are read by lane c of a wave and
-// broadcast with wave shuffles.
+// exp2(seg_decay) are read by lane c of a wave and broadcast with wave
+// shuffles.  Four chunks' states are loaded before they are folded in, so
+// the loads overlap the dependent multiply-add chain.
 __global__ void __launch_bounds__(256)
-state_pass_kernel(float *__restrict__ states, const float *__restrict__ cum,
-                  const float *__restrict__ init, float *__restrict__ final_state,
-                  int b, int L, int H, int PN, int chunk) {
-  const int nc = (L + chunk - 1) / chunk;
+state_pass_kernel(float *__restrict__ states, const float *__restrict__ seg_decay,
+                  const float *__restrict__ init, int b, int H, int PN, int nc) {
   const int per_bh = PN / 4;
   const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t bh = id / per_bh;
@@ -579,17 +623,17 @@ state_pass_kernel(float *__restrict__ states, const float *__restrict__ cum,
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
   if (live && init) s = reinterpret_cast<const float4 *>(init + bh * PN)[e4];
   float4 *base = reinterpret_cast<float4 *>(states + (live ? bh : 0) * (int64_t)nc * PN) + e4;
-  const float *cb = cum + (live ? bh : 0) * (int64_t)L;
+  const float *db = seg_decay + (live ? bh : 0) * (int64_t)nc;
   for (int c0 = 0; c0 < nc; c0 += 64) {
     // lane k holds the decay of chunk c0 + k
-    float my_dec = 1.f;
-    if (c0 + lane < nc) my_dec = __expf(cb[min(L, (c0 + lane + 1) * chunk) - 1]);
+    const float my_dec = (c0 + lane < nc) ? hw_exp2(db[c0 + lane]) : 1.f;
     const int cnt = min(64, nc - c0);
     int k = 0;
     for (; k + 4 <= cnt; k += 4) {
       float4 v[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = live ? base[(int64_t)(c0 + k + u) * per_bh] : make_float4(0, 0, 0, 0);
+      for (int u = 0; u < 4; ++u)
+        v[u] = (live && c0 + k + u + 1 < nc) ? base[(int64_t)(c0 + k + u) * per_bh] : make_float4(0, 0, 0, 0);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const float d = __shfl(my_dec, k + u, 64);
@@ -599,14 +643,13 @@ state_pass_kernel(float *__restrict__ states, const float *__restrict__ cum,
       }
     }
     for (; k < cnt; ++k) {
-      const float4 v = live ? base[(int64_t)(c0 + k) * per_bh] : make_float4(0, 0, 0, 0);
+      const float4 v = (live && c0 + k + 1 < nc) ? base[(int64_t)(c0 + k) * per_bh] : make_float4(0, 0, 0, 0);
       const float d = __shfl(my_dec, k, 64);
       if (live) base[(int64_t)(c0 + k) * per_bh] = s;
       s.x = d * s.x + v.x; s.y = d * s.y + v.y;
       s.z = d * s.z + v.z; s.w = d * s.w + v.w;
     }
   }
-  if (live && final_state) reinterpret_cast<float4 *>(final_state + bh * PN)[e4] = s;
 }
 
 // ---------------------------------------------------------------------------
@@ -673,7 +716,7 @@ step_kernel(float *__restrict__ state, const T *__restrict__ x,
 
 template <typename T, int P, int N>
 hipError_t launch_walk_t(WalkMode mode, const WalkParams &p, hipStream_t st) {
-  const dim3 grid((unsigned)(p.b * p.H * p.nseg)), block(P / 16 * 64);
+  const dim3 grid((unsigned)(p.b * p.H * p.nseg)), block(walk_waves<T, P>() * 64);
   switch (mode) {
   case kWalkFull: hipLaunchKernelGGL((walk_kernel<T, P, N, kWalkFull>), grid, block, 0, st, p); break;
   case kWalkChunkOut: hipLaunchKernelGGL((walk_kernel<T, P, N, kWalkChunkOut>), grid, block, 0, st, p); break;
@@ -699,7 +742,10 @@ hipError_t launch_walk_p(int P, int N, WalkMode mode, const WalkParams &p, hipSt
   case 16: return launch_walk_n<T, 16>(N, mode, p, st);
   case 32: return launch_walk_n<T, 32>(N, mode, p, st);
   case 64: return launch_walk_n<T, 64>(N, mode, p, st);
-  case 128: return launch_walk_n<T, 128>(N, mode, p, st);
+  case 128:
+    // fp32 tiles for P = 128 exceed the 160 KB of LDS per workgroup.
+    if constexpr (sizeof(T) == 2) return launch_walk_n<T, 128>(N, mode, p, st);
+    return hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;
 }
@@ -730,21 +776,18 @@ hipError_t launch_walk(int dtype, int P, int N, WalkMode mode, const WalkParams 
                     : launch_walk_p<float>(P, N, mode, p, stream);
 }
 
-hipError_t launch_cumsum(const float *dt, const float *dt_bias, const float *A, float *delta,
-                         float *cum, int b, int L, int H, int chunk, hipStream_t stream) {
-  const int nc = (L + chunk - 1) / chunk;
-  const int64_t n = (int64_t)b * nc * ((H + 63) / 64);
-  hipLaunchKernelGGL(cumsum_kernel, dim3((unsigned)n), dim3(256), 0, stream, dt, dt_bias, A,
-                     delta, cum, b, L, H, chunk);
+hipError_t launch_delta(const float *dt, const float *dt_bias, float *delta, int b, int L, int H,
+                        hipStream_t stream) {
+  const int64_t n = (int64_t)b * ((L + 63) / 64) * ((H + 63) / 64);
+  hipLaunchKernelGGL(delta_kernel, dim3((unsigned)n), dim3(256), 0, stream, dt, dt_bias, delta, b, L, H);
   return hipGetLastError();
 }
 
-hipError_t launch_state_pass(float *states, const float *cum, const float *init,
-                             float *final_state, int b, int L, int H, int PN, int chunk,
-                             hipStream_t stream) {
+hipError_t launch_state_pass(float *states, const float *seg_decay, const float *init, int b, int H,
+                             int PN, int nc, hipStream_t stream) {
   const int64_t n = (int64_t)b * H * (PN / 4);
   hipLaunchKernelGGL(state_pass_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
-                     states, cum, init, final_state, b, L, H, PN, chunk);
+                     states, seg_decay, init, b, H, PN, nc);
   return hipGetLastError();
 }
 

@@ -57,6 +57,9 @@ def lib():
         L.ssd_status_string.restype = ctypes.c_char_p
         L.ssd_last_error.restype = ctypes.c_char_p
         L.ssd_version.restype = ctypes.c_int
+        L.ssd_scan_plan.argtypes = [ctypes.c_int64] * 6 + [ctypes.c_int, ctypes.POINTER(ctypes.c_int),
+                                                            ctypes.POINTER(ctypes.c_int)]
+        L.ssd_scan_plan.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -125,6 +128,13 @@ def ssd_step(state, x, dt, A, B, C, D=None, out=None, stream=None):
                             describe(B), describe(C), describe(D), describe(out), st)
     _check(status)
     return out
+
+
+def ssd_scan_plan(b, L, H, P, G, N, cus: int = 256):
+    """(algo, seg_len) that SSD_ALGO_AUTO uses for this shape."""
+    algo, seg = ctypes.c_int(), ctypes.c_int()
+    _check(lib().ssd_scan_plan(b, L, H, P, G, N, cus, ctypes.byref(algo), ctypes.byref(seg)))
+    return algo.value, seg.value
 
 
 def ssd_status_string(status: int) -> str:

@@ -27,8 +27,8 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(ssd):
     names = declared_functions()
-    assert {"ssd_scan_fwd", "ssd_step", "ssd_scan_fwd_algo", "ssd_status_string",
-            "ssd_last_error", "ssd_version"} <= set(names)
+    assert {"ssd_scan_fwd", "ssd_step", "ssd_scan_fwd_algo", "ssd_scan_plan",
+            "ssd_status_string", "ssd_last_error", "ssd_version"} <= set(names)
     raw = ctypes.CDLL(ssd.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -81,6 +81,10 @@ CASES = [
         x=torch.zeros(1 * 100 * 4 * 16 + 1, dtype=torch.bfloat16)[1:].view(1, 100, 4, 16)), 4),
     ("P_unsupported", lambda a: a.update(x=torch.zeros(1, 100, 4, 24, dtype=torch.bfloat16),
                                          out=torch.zeros(1, 100, 4, 24, dtype=torch.bfloat16)), 5),
+    ("P128_fp32_unsupported", lambda a: a.update(
+        x=torch.zeros(1, 100, 4, 128), out=torch.zeros(1, 100, 4, 128),
+        B=torch.zeros(1, 100, 2, 32), C=torch.zeros(1, 100, 2, 32),
+        init_state=torch.zeros(1, 4, 128, 32), final_state=torch.zeros(1, 4, 128, 32)), 5),
     ("N_unsupported", lambda a: a.update(B=torch.zeros(1, 100, 2, 48, dtype=torch.bfloat16),
                                          C=torch.zeros(1, 100, 2, 48, dtype=torch.bfloat16)), 5),
 ]
@@ -99,6 +103,7 @@ def test_scan_rejects_bad_chunk_and_algo(ssd):
     a = _scan_args()
     assert _call_scan(ssd, a, chunk=32)[0] == 5
     assert _call_scan(ssd, a, chunk=100)[0] == 5
+    assert _call_scan(ssd, a, chunk=131072)[0] == 5
     assert _call_scan(ssd, a, algo=7)[0] == 5
 
 
@@ -155,3 +160,25 @@ def test_python_binding_raises(ssd):
         ssd.ssd_scan_fwd(a["x"], a["dt"], a["dt_bias"], a["A"], a["B"], a["C"], a["D"],
                          a["init_state"], out=a["x"], chunk=64)
     assert e.value.status == 6
+
+
+def test_plan(ssd):
+    """The automatic plan: the fused walk when b*H covers the compute units,
+    segments otherwise; always a valid segment length."""
+    lib = ssd.lib()
+    import ctypes as ct
+    algo, seg = ct.c_int(), ct.c_int()
+    def plan(b, L, H, P=64, G=1, N=128, cus=256):
+        st = lib.ssd_scan_plan(b, L, H, P, G, N, cus, ct.byref(algo), ct.byref(seg))
+        assert st == 0
+        return algo.value, seg.value
+    assert plan(8, 2048, 32) == (1, 2048)            # 256 walks on 256 units
+    a, s = plan(4, 4096, 80)                          # 320 walks: 2 per busiest unit
+    assert (a, s) == (1, 4096)
+    a, s = plan(1, 65536, 32, G=8)                    # 32 walks: split into segments
+    assert a == 2 and 256 <= s <= 8192
+    a, s = plan(1, 4096, 16)                          # 16 walks on 256 units
+    assert a == 2
+    a, s = plan(1, 100, 2)
+    assert a in (1, 2) and s >= 64
+    assert lib.ssd_scan_plan(0, 10, 2, 64, 1, 128, 256, ct.byref(algo), ct.byref(seg)) == 2

@@ -197,10 +197,13 @@ def test_workload_decode_steps():
 def test_chunk_invariance():
     si = inputs.make_scan(2, 1000, 8, 64, 2, 128, dtype=inputs.BF16, seed=21, init_std=0.1)
     outs = []
-    for chunk in (64, 128, 256):
+    for chunk in (64, 128, 256, 512, 1024, 4096):
         say("chunk invariance", chunk)
         outs.append(gpu_scan(si, algo=ssd.SSD_ALGO_CHUNKED, chunk=chunk))
     outs.append(gpu_scan(si, algo=ssd.SSD_ALGO_FUSED))
+    yr, fr = oracle_scan(si)
+    check(outs[0][0], yr, 2e-2, "y chunk 64")
+    check(outs[0][1], fr, 2e-2, "final chunk 64")
     for y, f in outs[1:]:
         check(y, outs[0][0], 2e-2, "y across chunk sizes")
         check(f, outs[0][1], 2e-2, "final across chunk sizes")
@@ -265,3 +268,15 @@ def test_deterministic(algo):
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
     assert torch.equal(f1, f2)
+
+
+@pytest.mark.parametrize("chunk", [512, 2048])
+def test_long_segments_ragged(chunk):
+    """Segments of many sub-blocks with a ragged last segment."""
+    si = inputs.make_scan(1, 2 * chunk + 333, 4, 64, 2, 128, dtype=inputs.BF16, seed=chunk,
+                          init_std=0.2)
+    say("long segments", chunk)
+    y, fin = gpu_scan(si, algo=ssd.SSD_ALGO_CHUNKED, chunk=chunk)
+    yr, fr = oracle_scan(si)
+    check(y, yr, 2e-2, "y")
+    check(fin, fr, 2e-2, "final")
