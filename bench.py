@@ -37,7 +37,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # dense bf16 MFMA, 256 CU x 4096 FLOP/clk x 2.4 GHz
 ELEM = {"bf16": 2, "f32": 4}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCE = os.path.join(ROOT, "mamba_ssd_scan_05_amd", "csrc", "ssd_kernels.hip")
+CSRC = os.path.join(ROOT, "mamba_ssd_scan_05_amd", "csrc")
 
 
 def scan_bytes(b, L, H, P, G, N, dtype, init, final):
@@ -63,7 +63,14 @@ def step_bytes(b, H, P, G, N, dtype):
 
 
 def kernel_sha():
-    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+    """Hash of every kernel source: counter-derived traffic is used only for
+    the exact sources it was measured on."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            h.update(open(os.path.join(CSRC, name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(kernel, workload):
@@ -125,7 +132,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--algo", choices=["auto", "fused", "chunked"], default="auto")
+    ap.add_argument("--algo", choices=["auto", "fused", "chunked", "rows"], default="auto")
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
@@ -145,8 +152,9 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    names = {ssd.SSD_ALGO_FUSED: "fused", ssd.SSD_ALGO_CHUNKED: "chunked", ssd.SSD_ALGO_ROWS: "rows"}
     algo = {"auto": ssd.SSD_ALGO_AUTO, "fused": ssd.SSD_ALGO_FUSED,
-            "chunked": ssd.SSD_ALGO_CHUNKED}[args.algo]
+            "chunked": ssd.SSD_ALGO_CHUNKED, "rows": ssd.SSD_ALGO_ROWS}[args.algo]
     si = inputs.make_workload(args.workload)
     shp = si.shape
     b, L, H, P, G, N = (shp[k] for k in ("b", "L", "H", "P", "G", "N"))
@@ -185,11 +193,15 @@ def main():
     t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
     used_algo, seg_len = args.algo, Q
     if args.algo == "auto":
-        a, seg_len = ssd.ssd_scan_plan(b, L, H, P, G, N,
+        a, seg_len = ssd.ssd_scan_plan(b, L, H, P, G, N, t["x"].dtype,
                                        torch.cuda.get_device_properties(0).multi_processor_count)
-        used_algo = "fused" if a == ssd.SSD_ALGO_FUSED else "chunked"
+        used_algo = names[a]
     if used_algo == "fused":
         dominant = "walk_kernel (fused walk, one launch)"
+        seg_len = L
+    elif used_algo == "rows":
+        dominant = ("rwalk_kernel (row-sliced walk) with its scores_kernel precompute: the "
+                    "timed duration is the whole call, both launches")
         seg_len = L
     else:
         dominant = ("ssd_scan_fwd chunked path, segment %d: cumsum + chunk-state walk + "
@@ -207,7 +219,8 @@ def main():
     extra = {"p10_ms": float(np.percentile(per_ms, 10)), "p90_ms": float(np.percentile(per_ms, 90))}
     if not args.no_alt:
         alts = {}
-        for name_a, a, q in (("fused", ssd.SSD_ALGO_FUSED, Q), ("chunked_256", ssd.SSD_ALGO_CHUNKED, 256),
+        for name_a, a, q in (("rows", ssd.SSD_ALGO_ROWS, Q), ("fused", ssd.SSD_ALGO_FUSED, Q),
+                             ("chunked_256", ssd.SSD_ALGO_CHUNKED, 256),
                              ("chunked_1024", ssd.SSD_ALGO_CHUNKED, 1024),
                              ("chunked_2048", ssd.SSD_ALGO_CHUNKED, 2048)):
             def run_alt():

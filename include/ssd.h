@@ -69,8 +69,12 @@ enum {
   SSD_ALGO_AUTO = 0,    /* choose by shape                                    */
   SSD_ALGO_FUSED = 1,   /* one kernel; each workgroup walks one (batch, head)
                            sequence in order with the state in registers      */
-  SSD_ALGO_CHUNKED = 2  /* chunk-parallel: log-decay cumsum, chunk states,
+  SSD_ALGO_CHUNKED = 2, /* chunk-parallel: log-decay cumsum, chunk states,
                            inter-chunk state passing, fused intra+output      */
+  SSD_ALGO_ROWS = 3     /* bf16, N in {32, 64, 128}: the causal C B^T scores
+                           of each (batch, group, 64-token block) computed
+                           once and shared by the heads of the group; each
+                           wave walks 16 state rows of one head            */
 };
 
 /* Dense tensor descriptor.  shape/strides beyond ndim are ignored; strides
@@ -118,13 +122,31 @@ int ssd_scan_fwd(const ssd_tensor *x, const ssd_tensor *dt,
                  ssd_tensor *final_state, int chunk, void *stream);
 
 /* ssd_scan_fwd with an explicit algorithm (SSD_ALGO_*). Same contract;
- * SSD_ALGO_CHUNKED uses `chunk` as its segment length. */
+ * SSD_ALGO_CHUNKED uses `chunk` as its segment length; SSD_ALGO_ROWS
+ * returns SSD_ERR_UNSUPPORTED for fp32 inputs or N outside {32, 64, 128}.
+ * SSD_ALGO_ROWS and SSD_ALGO_CHUNKED take scratch from the stream-ordered
+ * allocator (ROWS: b*G*ceil(L/64)*8 KiB). */
 int ssd_scan_fwd_algo(const ssd_tensor *x, const ssd_tensor *dt,
                       const ssd_tensor *dt_bias, const ssd_tensor *A,
                       const ssd_tensor *B, const ssd_tensor *C,
                       const ssd_tensor *D, const ssd_tensor *init_state,
                       ssd_tensor *out, ssd_tensor *final_state, int chunk,
                       int algo, void *stream);
+
+/*
+ * ssd_scan_fwd_rows -- ssd_scan_fwd with SSD_ALGO_ROWS and an explicit
+ * workgroup size: `waves` in 1..8 waves per workgroup (16 state rows each),
+ * 0 = the size SSD_ALGO_AUTO would take.  For tuning and tests; the result
+ * does not depend on `waves` beyond rounding order (it does not at all:
+ * every state row is computed by the same instruction sequence).  bf16
+ * inputs and N in {32, 64, 128} only (else SSD_ERR_UNSUPPORTED).
+ */
+int ssd_scan_fwd_rows(const ssd_tensor *x, const ssd_tensor *dt,
+                      const ssd_tensor *dt_bias, const ssd_tensor *A,
+                      const ssd_tensor *B, const ssd_tensor *C,
+                      const ssd_tensor *D, const ssd_tensor *init_state,
+                      ssd_tensor *out, ssd_tensor *final_state, int waves,
+                      void *stream);
 
 /*
  * ssd_step -- one recurrent step for every (batch, head), state in place
@@ -151,14 +173,16 @@ int ssd_step(ssd_tensor *state, const ssd_tensor *x, const ssd_tensor *dt,
 
 /*
  * ssd_scan_plan -- the plan SSD_ALGO_AUTO uses for a shape on a device with
- * `cus` compute units (host only, no HIP call): *algo is SSD_ALGO_FUSED or
- * SSD_ALGO_CHUNKED and *seg_len the segment length (L for the fused walk).
+ * `cus` compute units for inputs of element type `dtype` (SSD_BF16 or
+ * SSD_F32), host only, no HIP call: *algo is SSD_ALGO_FUSED,
+ * SSD_ALGO_CHUNKED or SSD_ALGO_ROWS and *seg_len the segment length (L for
+ * the single-pass walks).
  * The choice trades the spread of (batch, head, segment) walks over the
  * compute units against the extra state-only pass and state traffic of
  * shorter segments.
  */
 int ssd_scan_plan(int64_t b, int64_t L, int64_t H, int64_t P, int64_t G,
-                  int64_t N, int cus, int *algo, int *seg_len);
+                  int64_t N, int dtype, int cus, int *algo, int *seg_len);
 
 /* Static text for a status code. */
 const char *ssd_status_string(int status);

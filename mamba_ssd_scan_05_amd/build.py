@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libssd.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-SOURCES = ["ssd_api.hip", "ssd_kernels.hip"]
+SOURCES = ["ssd_api.hip", "ssd_kernels.hip", "ssd_rwalk.hip"]
 
 COMMON = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",

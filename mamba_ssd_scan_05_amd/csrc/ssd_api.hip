@@ -230,6 +230,65 @@ int run_chunked(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_
   return status;
 }
 
+bool rows_supported(int dtype, int64_t N) {
+  return dtype == SSD_BF16 && (N == 32 || N == 64 || N == 128);
+}
+
+// Waves per workgroup of the row-sliced walk: the workgroups of a pass run
+// one per compute unit (LDS), and a workgroup of W waves retires a
+// sub-block in about 1 + 0.1 W units of time (shared LDS and issue), so
+// take the W with the fewest ceil(workgroups / CUs) * (1 + 0.1 W).
+int rows_waves(const ScanShape &s, int cus) {
+  const int64_t rg = (s.H / s.G) * s.P;
+  double best = 1e300;
+  int best_w = 4;
+  for (int W = 1; W <= 8; ++W) {
+    const int64_t nwg = s.b * s.G * ((rg + 16 * W - 1) / (16 * W));
+    const double t = (double)((nwg + cus - 1) / cus) * (1.0 + 0.1 * W);
+    if (t < best) {
+      best = t;
+      best_w = W;
+    }
+  }
+  return best_w;
+}
+
+int run_rows(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bias,
+             const ssd_tensor *A, const ssd_tensor *B, const ssd_tensor *C, const ssd_tensor *D,
+             const ssd_tensor *init, ssd_tensor *out, ssd_tensor *fin, const ScanShape &s,
+             int W, hipStream_t st) {
+  const int64_t nsub = (s.L + 63) / 64;
+  const size_t bytes = (size_t)(s.b * s.G * nsub) * 64 * 64 * 2;
+  void *ws = nullptr;
+  hipError_t e = hipMallocAsync(&ws, bytes, st);
+  if (e != hipSuccess || !ws) {
+    (void)hipGetLastError();
+    return fail(SSD_ERR_NOMEM, "scratch of %zu bytes: %s", bytes, hipGetErrorString(e));
+  }
+  int status = SSD_OK;
+  do {
+    e = ssd::launch_scores(B->data, C->data, ws, (int)s.b, (int)s.L, (int)s.G, (int)s.N, st);
+    if (e != hipSuccess) { status = hip_fail(e, "scores launch"); break; }
+    ssd::RWalkParams p{};
+    p.x = x->data; p.dt = (const float *)dt->data;
+    p.dt_bias = dt_bias ? (const float *)dt_bias->data : nullptr;
+    p.A = (const float *)A->data; p.B = B->data; p.C = C->data;
+    p.D = D ? (const float *)D->data : nullptr;
+    p.scores = ws;
+    p.init = init ? (const float *)init->data : nullptr;
+    p.out = out->data;
+    p.final_state = fin ? (float *)fin->data : nullptr;
+    p.b = (int)s.b; p.L = (int)s.L; p.H = (int)s.H; p.G = (int)s.G; p.P = (int)s.P;
+    p.rows_per_bg = (int)((s.H / s.G) * s.P);
+    p.wg_per_bg = (p.rows_per_bg + 16 * W - 1) / (16 * W);
+    e = ssd::launch_rwalk((int)s.N, W, p, st);
+    if (e != hipSuccess) { status = hip_fail(e, "row walk launch"); break; }
+  } while (0);
+  e = hipFreeAsync(ws, st);
+  if (e != hipSuccess && status == SSD_OK) status = hip_fail(e, "scratch free");
+  return status;
+}
+
 // Compute units of the current device (queried once per device).
 int device_cus() {
   static int cache[64] = {0};
@@ -244,21 +303,22 @@ int device_cus() {
   return cache[dev];
 }
 
-// Plan for SSD_ALGO_AUTO, from measured costs on MI355X: a compute unit
-// retires about one 64-token sub-block of one (batch, head) walk every
-// 2 us whether it holds one walk or several, so a pass of W walks of n
-// sub-blocks costs ceil(W / CUs) * n * 2 us.  The fused single kernel is one
-// pass with W = b*H over the whole sequence.  Splitting sequences into S
+// Plan for SSD_ALGO_AUTO, from measured costs on MI355X.  The walks of the
+// fused and chunked algorithms retire about one 64-token sub-block of one
+// (batch, head) walk per compute unit every 2 us whether a unit holds one
+// walk or several, so a pass of U walks of n sub-blocks costs
+// ceil(U / CUs) * n * 2 us.  The row-sliced walk (bf16) costs
+// ceil(workgroups / CUs) * n * t_rows(W).  Splitting sequences into S
 // segments gives a pass of b*H*S output walks, a state-only pass over S-1
-// segments (measured at 0.7 of an output walk), the step-size kernel, the
-// state-passing pass (2 * b*H*S*P*N*4 bytes at ~4 TB/s) and launch gaps.
-// The split is taken only when predicted at least 10% faster.
+// segments (0.7 of an output walk), the step-size kernel, the state-passing
+// pass (2 * b*H*S*P*N*4 bytes at ~4 TB/s) and launch gaps; a split is
+// taken only when predicted at least 10% faster than the single pass.
 struct Plan {
   int algo;
   int seg_len;
 };
 
-Plan choose_plan(const ScanShape &s, int cus) {
+Plan choose_plan(const ScanShape &s, int dtype, int cus) {
   const double t_sub_us = 2.0;  // one sub-block of one walk on one compute unit
   const double state_rel = 0.7; // state-only walk relative to an output walk
   const double pass_bw = 4.0e12;
@@ -266,8 +326,17 @@ Plan choose_plan(const ScanShape &s, int cus) {
   const int64_t units = s.b * s.H;
   const int64_t nsub = (s.L + 63) / 64;
   Plan best{SSD_ALGO_FUSED, (int)std::min<int64_t>(s.L, 65536)};
-  const double fused_t = (double)((units + cus - 1) / cus) * nsub * t_sub_us;
-  double best_t = 0.9 * fused_t;
+  double single_t = (double)((units + cus - 1) / cus) * nsub * t_sub_us;
+  if (rows_supported(dtype, s.N)) {
+    const int W = rows_waves(s, cus);
+    const int64_t nwg = s.b * s.G * (((s.H / s.G) * s.P + 16 * W - 1) / (16 * W));
+    const double rows_t = (double)((nwg + cus - 1) / cus) * nsub * (1.0 + 0.1 * W) * 0.5 + 5.0;
+    if (rows_t < single_t) {
+      single_t = rows_t;
+      best.algo = SSD_ALGO_ROWS;
+    }
+  }
+  double best_t = 0.9 * single_t;
   for (int seg = 65536; seg >= 256; seg /= 2) {
     const int64_t S = (s.L + seg - 1) / seg;
     if (S < 2) continue;
@@ -295,14 +364,20 @@ int ssd_scan_fwd_algo(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tenso
   g_last_error.clear();
   ScanShape s;
   SSD_CHECK(validate_scan(x, dt, dt_bias, A, B, C, D, init_state, out, final_state, chunk, &s));
-  if (algo != SSD_ALGO_AUTO && algo != SSD_ALGO_FUSED && algo != SSD_ALGO_CHUNKED)
+  if (algo != SSD_ALGO_AUTO && algo != SSD_ALGO_FUSED && algo != SSD_ALGO_CHUNKED &&
+      algo != SSD_ALGO_ROWS)
     return fail(SSD_ERR_UNSUPPORTED, "unknown algorithm %d", algo);
+  if (algo == SSD_ALGO_ROWS && !rows_supported(x->dtype, s.N))
+    return fail(SSD_ERR_UNSUPPORTED, "row-sliced walk needs bf16 inputs and N in {32,64,128}");
+  const int cus = device_cus();
   if (algo == SSD_ALGO_AUTO) {
-    const Plan plan = choose_plan(s, device_cus());
+    const Plan plan = choose_plan(s, x->dtype, cus);
     algo = plan.algo;
     chunk = plan.seg_len;
   }
   hipStream_t st = (hipStream_t)stream;
+  if (algo == SSD_ALGO_ROWS)
+    return run_rows(x, dt, dt_bias, A, B, C, D, init_state, out, final_state, s, rows_waves(s, cus), st);
   if (algo == SSD_ALGO_FUSED)
     return run_fused(x, dt, dt_bias, A, B, C, D, init_state, out, final_state, s, st);
   return run_chunked(x, dt, dt_bias, A, B, C, D, init_state, out, final_state, s, chunk, st);
@@ -314,6 +389,21 @@ int ssd_scan_fwd(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt
                  ssd_tensor *final_state, int chunk, void *stream) {
   return ssd_scan_fwd_algo(x, dt, dt_bias, A, B, C, D, init_state, out, final_state, chunk,
                            SSD_ALGO_AUTO, stream);
+}
+
+int ssd_scan_fwd_rows(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bias,
+                      const ssd_tensor *A, const ssd_tensor *B, const ssd_tensor *C,
+                      const ssd_tensor *D, const ssd_tensor *init_state, ssd_tensor *out,
+                      ssd_tensor *final_state, int waves, void *stream) {
+  g_last_error.clear();
+  ScanShape s;
+  SSD_CHECK(validate_scan(x, dt, dt_bias, A, B, C, D, init_state, out, final_state, 64, &s));
+  if (!rows_supported(x->dtype, s.N))
+    return fail(SSD_ERR_UNSUPPORTED, "row-sliced walk needs bf16 inputs and N in {32,64,128}");
+  if (waves < 0 || waves > 8) return fail(SSD_ERR_UNSUPPORTED, "waves=%d not in 0..8", waves);
+  const int W = waves ? waves : rows_waves(s, device_cus());
+  return run_rows(x, dt, dt_bias, A, B, C, D, init_state, out, final_state, s, W,
+                  (hipStream_t)stream);
 }
 
 int ssd_step(ssd_tensor *state, const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *A,
@@ -362,15 +452,16 @@ int ssd_step(ssd_tensor *state, const ssd_tensor *x, const ssd_tensor *dt, const
   return e == hipSuccess ? SSD_OK : hip_fail(e, "step launch");
 }
 
-int ssd_scan_plan(int64_t b, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, int cus,
-                  int *algo, int *seg_len) {
+int ssd_scan_plan(int64_t b, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, int dtype,
+                  int cus, int *algo, int *seg_len) {
   g_last_error.clear();
   if (!algo || !seg_len) return fail(SSD_ERR_NULL, "algo/seg_len: NULL");
   if (b < 1 || L < 1 || H < 1 || G < 1 || H % G != 0)
     return fail(SSD_ERR_SHAPE, "invalid shape b=%lld L=%lld H=%lld G=%lld", (long long)b,
                 (long long)L, (long long)H, (long long)G);
   ScanShape s{b, L, H, P, G, N};
-  const Plan plan = choose_plan(s, cus > 0 ? cus : 256);
+  if (dtype != SSD_F32 && dtype != SSD_BF16) return fail(SSD_ERR_DTYPE, "dtype %d", dtype);
+  const Plan plan = choose_plan(s, dtype, cus > 0 ? cus : 256);
   *algo = plan.algo;
   *seg_len = plan.seg_len;
   return SSD_OK;

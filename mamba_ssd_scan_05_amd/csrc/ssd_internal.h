@@ -44,6 +44,33 @@ enum WalkMode {
 hipError_t launch_walk(int dtype, int P, int N, WalkMode mode,
                        const WalkParams &p, hipStream_t stream);
 
+// Parameters of the row-sliced walk (bf16 inputs).  A workgroup of W waves
+// owns 16W consecutive state rows -- (head, p) pairs of the heads of one
+// group -- of one (batch, group); rows_per_bg = (H/G)*P, wg_per_bg =
+// ceil(rows_per_bg / (16W)).
+struct RWalkParams {
+  const void *x;        // [b, L, H, P] bf16
+  const float *dt;      // [b, L, H] raw
+  const float *dt_bias; // [H] or null
+  const float *A;       // [H]
+  const void *B;        // [b, L, G, N] bf16
+  const void *C;        // [b, L, G, N] bf16
+  const float *D;       // [H] or null
+  const void *scores;   // [b, G, ceil(L/64), 64, 64] bf16 from launch_scores
+  const float *init;    // [b, H, P, N] or null
+  void *out;            // [b, L, H, P] bf16
+  float *final_state;   // [b, H, P, N] or null
+  int b, L, H, G, P, rows_per_bg, wg_per_bg;
+};
+
+// Causal score tiles C_t . B_t' of every (batch, group, 64-token sub-block),
+// bf16, columns in the fragment order the row-sliced walk reads.
+hipError_t launch_scores(const void *B, const void *C, void *scores, int b, int L, int G,
+                         int N, hipStream_t stream);
+
+// Row-sliced walk with W waves per workgroup (1..8); N in {32, 64, 128}.
+hipError_t launch_rwalk(int N, int W, const RWalkParams &p, hipStream_t stream);
+
 // Step sizes: Delta [b,H,L] = softplus(dt [b,L,H] + dt_bias), head-major.
 hipError_t launch_delta(const float *dt, const float *dt_bias, float *delta,
                         int b, int L, int H, hipStream_t stream);

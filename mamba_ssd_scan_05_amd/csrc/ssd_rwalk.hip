@@ -1,0 +1,419 @@
+// ssd_rwalk.hip -- the row-sliced walk for bf16 inputs and the per-group
+// score precompute it reads.
+//
+// The method ("Mamba-3 deep dive ch. 2, SSM foundations", 171host.com,
+// section 2.1.2 recurrence, section 2.2.1 matrix form Y = (L o C B^T) X;
+// "Transformers are SSMs" summary, gongshangzheng.github.io, sections
+// 1.1-1.2: blocks evaluated with the quadratic form, linked through the
+// N-dimensional state).  For a 64-token sub-block after state S (P x N),
+// c_t = log2-scaled inclusive cumsum of Delta*A, q_t = c_t - log2(Delta_t):
+//
+//   y_t = 2^{c_t} S C_t + sum_{t'<=t} 2^{c_t - q_t'} (C_t . B_t') x_t' + D x_t
+//   S'  = 2^{c_last} S + sum_t 2^{c_last - q_t} x_t B_t^T
+//
+// Two observations shape this kernel:
+//
+// 1. The raw scores C_t . B_t' do not depend on the head, only on its B/C
+//    group.  scores_kernel computes them once per (batch, group, sub-block)
+//    as a causal 64x64 bf16 tile; every head of the group reads that tile.
+//
+// 2. The decay weight is separable: with a reference value m,
+//    2^{c_t - q_t'} = 2^{c_t - m} * 2^{m - q_t'}.  With m the midpoint of
+//    [min c, max c] (c is monotone, so that is c_last/2) both factors stay
+//    within 2^{+-span/2}, span = |c_last|.  Then
+//       y_t = 2^{c_t - m} [ (2^m S) C_t + sum_t' Score[t][t'] xs_t' ] + D x_t,
+//       xs_t' = 2^{m - q_t'} x_t'
+//       S'  = 2^{c_last - m} [ 2^m S + sum_t xs_t B_t^T ]
+//    so the intra-block product takes the shared score tile as it is and the
+//    decay becomes a per-token scale of x and of y.  Sub-blocks whose decay
+//    span exceeds kSpanMax take the per-element form instead (slow path).
+//
+// Work split: a workgroup of W waves owns 16W consecutive state rows of one
+// (batch, group) -- rows are (head, p) pairs of the heads in the group, 16
+// rows per wave, all in one head -- and walks the sequence in 64-token
+// sub-blocks.  The B and C tiles of a sub-block are staged once in LDS and
+// read by every wave; each wave holds its 16 x N state in MFMA accumulator
+// registers, stages its own 16 columns of x in a private LDS tile and loads
+// the score fragments straight from global memory (L2).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ssd_device.h"
+#include "ssd_internal.h"
+
+namespace ssd {
+namespace {
+
+// Decay span (log2 units) up to which the separable form is used: the
+// scale factors stay within 2^{+-kSpanMax/2}.
+constexpr float kSpanMax = 100.f;
+
+// Position of K-value j (0..7) of lane group g inside a 32-column group, in
+// the order the transposed fragments use: {4g .. 4g+3, 16+4g .. 16+4g+3}.
+// The score tile is stored with its columns permuted so that these eight
+// values are contiguous: column 32ks + 8g + j holds t' = 32ks + kperm(g, j).
+__host__ __device__ constexpr int kperm(int g, int j) { return j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4); }
+
+// ---------------------------------------------------------------------------
+// Scores: Sc[b][g][k][t][32ks + 8lg + j] = C_t . B_{t'} for t' = 32ks +
+// kperm(lg, j) <= t, 0 above the diagonal; t, t' are tokens of sub-block k.
+// One workgroup per (batch, group, sub-block); wave u computes query rows
+// [16u, 16u+16).  Tokens past L read as zero.
+template <int N>
+__global__ void __launch_bounds__(256) scores_kernel(const __bf16 *__restrict__ B, const __bf16 *__restrict__ C,
+                                                     __bf16 *__restrict__ Sc, int L, int G, int nsub) {
+  constexpr int KN = N / 32;
+  const int wg = blockIdx.x;
+  const int k = wg % nsub, bg = wg / nsub;
+  const int g = bg % G, ib = bg / G;
+  const int u = threadIdx.x >> 6, l = threadIdx.x & 63, li = l & 15, lg = l >> 4;
+  const int t0 = 64 * k, nv = min(64, L - t0);
+  const int64_t rowB = (int64_t)G * N;
+  const int64_t base = ((int64_t)ib * L + t0) * rowB + (int64_t)g * N;
+  const uint32_t bytes = (uint32_t)(((int64_t)(nv - 1) * rowB + N) * 2);
+  const auto rsB = make_rsrc(B + base, bytes);
+  const auto rsC = make_rsrc(C + base, bytes);
+
+  // B operand: C rows of the queries t = 16u + li, K = n.
+  FragBF cf[KN];
+#pragma unroll
+  for (int ks = 0; ks < KN; ++ks)
+    cf[ks].v = __builtin_bit_cast(bf16x8, bload16(rsC, (uint32_t)(((16 * u + li) * rowB + 32 * ks + 8 * lg) * 2)));
+  __bf16 *dst = Sc + ((int64_t)wg * 64 + 16 * u + li) * 64;
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (jt <= u) {
+      // A operand: B rows of the keys t' = 16jt + li; D[t'][t].
+#pragma unroll
+      for (int ks = 0; ks < KN; ++ks) {
+        FragBF bf;
+        bf.v = __builtin_bit_cast(bf16x8, bload16(rsB, (uint32_t)(((16 * jt + li) * rowB + 32 * ks + 8 * lg) * 2)));
+        acc = mma(bf, cf[ks], acc);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (16 * jt + 4 * lg + r > 16 * u + li) acc[r] = 0.f;
+    }
+    bf16x4 v;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = (__bf16)acc[r];
+    *reinterpret_cast<bf16x4 *>(dst + 32 * (jt / 2) + 8 * lg + 4 * (jt % 2)) = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The row-sliced walk.
+template <int N, int W>
+__global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
+  constexpr int NTH = W * 64;
+  constexpr int NT = N / 16;            // n-tiles of the state
+  constexpr int KN = N / 32;            // K-steps over n
+  constexpr int LDB = tr_ld(N, 2);      // B tile: transposed reads
+  constexpr int LDC = N + 8;            // C tile: row reads
+  constexpr int RW = N / 8;             // 16-byte pieces per B/C row
+  constexpr int PIECES = 64 * RW;       // per tile
+  constexpr int PPT = (PIECES + NTH - 1) / NTH;
+  constexpr int NSF = 6;                // score fragments per lane and sub-block
+
+  __shared__ __attribute__((aligned(16))) __bf16 sB[2][64 * LDB];
+  __shared__ __attribute__((aligned(16))) __bf16 sC[2][64 * LDC];
+  __shared__ __attribute__((aligned(16))) __bf16 sX[W][64 * 16]; // x[token][16 columns]
+  __shared__ __attribute__((aligned(16))) float sF0[W][64];      // xs scale (fast) / w (slow)
+  __shared__ __attribute__((aligned(16))) float sF1[W][64];      // y scale 2^{c - m}
+  __shared__ __attribute__((aligned(16))) float sCq[W][64];      // q (slow path)
+
+  const int H = prm.H, G = prm.G, L = prm.L, P = prm.P;
+  const int nwg = gridDim.x, bid = blockIdx.x;
+  // XCD-aware order: consecutive ids go round-robin to the 8 XCDs; give
+  // each XCD a contiguous range of logical ids so that the workgroups of one
+  // (batch, group) share its B/C/score tiles through one L2.
+  const int logical = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;
+  const int bg = logical / prm.wg_per_bg, wi = logical % prm.wg_per_bg;
+  const int g = bg % G, ib = bg / G;
+  const int tid = threadIdx.x, l = tid & 63, li = l & 15, lg = l >> 4;
+  // The wave index is uniform across the wave; readfirstlane makes that
+  // visible to the compiler, so that every per-wave address, buffer
+  // descriptor and branch below lives in scalar registers.
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int R = (wi * W + w) * 16;
+  const bool active = R < prm.rows_per_bg;
+  const int Rc = active ? R : 0;
+  const int h = g * (H / G) + Rc / P;
+  const int p0 = Rc % P;
+
+  const float a2 = prm.A[h] * kLog2e;
+  const float d_h = prm.D ? prm.D[h] : 0.f;
+  const float bias = prm.dt_bias ? prm.dt_bias[h] : 0.f;
+  const int64_t srow = ((int64_t)(ib * H + h) * P + p0 + li) * N; // state row p0 + li
+
+  // hs[k][r] = S[p0 + li][16k + 4lg + r]
+  f32x4 hs[NT];
+#pragma unroll
+  for (int k = 0; k < NT; ++k) hs[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (prm.init != nullptr && active) {
+#pragma unroll
+    for (int k = 0; k < NT; ++k) hs[k] = *reinterpret_cast<const f32x4 *>(prm.init + srow + 16 * k + 4 * lg);
+  }
+
+  const int64_t rowB = (int64_t)G * N, rowX = (int64_t)H * P;
+  const __bf16 *Bbase = reinterpret_cast<const __bf16 *>(prm.B) + ((int64_t)ib * L * G + g) * N;
+  const __bf16 *Cbase = reinterpret_cast<const __bf16 *>(prm.C) + ((int64_t)ib * L * G + g) * N;
+  const __bf16 *Xbase = reinterpret_cast<const __bf16 *>(prm.x) + (int64_t)ib * L * rowX + (int64_t)h * P + p0;
+  __bf16 *Ybase = reinterpret_cast<__bf16 *>(prm.out) + (int64_t)ib * L * rowX + (int64_t)h * P + p0;
+  const float *dtbase = prm.dt + (int64_t)ib * L * H + h;
+  const int nsub = (L + 63) / 64;
+  const __bf16 *Sbase = reinterpret_cast<const __bf16 *>(prm.scores) + (int64_t)bg * nsub * 4096;
+
+  // Loop-invariant offsets.  Every wave issues the same sequence of memory
+  // operations on every path through the loop (threads without a piece of
+  // their own repeat the last piece; fetches past the end use empty ranges
+  // and read zeros; stores of idle waves fall outside an empty range), so
+  // the compiler can wait for exactly the loads each step needs while
+  // later loads and the y stores stay in flight.
+  uint32_t offBC[PPT];
+  int ldsB[PPT], ldsC[PPT];
+#pragma unroll
+  for (int i = 0; i < PPT; ++i) {
+    const int q = min(tid + i * NTH, PIECES - 1);
+    const int j = q / RW, n0 = (q % RW) * 8;
+    offBC[i] = (uint32_t)((j * rowB + n0) * 2);
+    ldsB[i] = j * LDB + n0;
+    ldsC[i] = j * LDC + n0;
+  }
+  // x pieces of this wave: piece l + 64e = (token, half) -> 8 columns.
+  uint32_t offX[2];
+  int ldsX[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int pc = l + 64 * e, tok = pc >> 1, half = pc & 1;
+    offX[e] = (uint32_t)((tok * rowX + 8 * half) * 2);
+    ldsX[e] = tok * 16 + 8 * half;
+  }
+  // score fragments: (u, ks) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+  uint32_t offS[NSF];
+#pragma unroll
+  for (int f = 0; f < NSF; ++f) {
+    const int u = f < 2 ? f : 2 + (f - 2) / 2, ks = f < 2 ? 0 : (f - 2) % 2;
+    offS[f] = (uint32_t)(((16 * u + li) * 64 + 32 * ks + 8 * lg) * 2);
+  }
+  const uint32_t offY = (uint32_t)((li * rowX + 4 * lg) * 2);
+  const auto rsS = make_rsrc(Sbase, (uint32_t)nsub * 4096u * 2u);
+
+  float4 rB[PPT], rC[PPT], rX[2];
+  float rdt = 0.f;
+  auto fetch = [&](int k) {
+    const int t0 = 64 * k, nv = min(64, L - t0);
+    // step sizes first: they are needed first (top of the next step)
+    const auto rsD = make_rsrc(dtbase + (int64_t)t0 * H, nv > 0 ? (uint32_t)(((int64_t)(nv - 1) * H + 1) * 4) : 0u);
+    rdt = bload4(rsD, (uint32_t)(l * H * 4));
+    const uint32_t bcb = nv > 0 ? (uint32_t)(((int64_t)(nv - 1) * rowB + N) * 2) : 0u;
+    const auto rsB = make_rsrc(Bbase + (int64_t)t0 * rowB, bcb);
+    const auto rsC = make_rsrc(Cbase + (int64_t)t0 * rowB, bcb);
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      rB[i] = bload16(rsB, offBC[i]);
+      rC[i] = bload16(rsC, offBC[i]);
+    }
+    const auto rsX = make_rsrc(Xbase + (int64_t)t0 * rowX, nv > 0 ? (uint32_t)(((int64_t)(nv - 1) * rowX + 16) * 2) : 0u);
+    rX[0] = bload16(rsX, offX[0]);
+    rX[1] = bload16(rsX, offX[1]);
+  };
+  // Score fragments of sub-block k, issued right after the previous
+  // sub-block's intra-block product has consumed the registers.
+  FragBF sf[NSF];
+  auto fetch_scores = [&](int k) {
+#pragma unroll
+    for (int f = 0; f < NSF; ++f)
+      sf[f].v = __builtin_bit_cast(bf16x8, bload16(rsS, (uint32_t)k * 8192u + offS[f]));
+  };
+  auto stage = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      *reinterpret_cast<float4 *>(&sB[slot][ldsB[i]]) = rB[i];
+      *reinterpret_cast<float4 *>(&sC[slot][ldsC[i]]) = rC[i];
+    }
+    *reinterpret_cast<float4 *>(&sX[w][ldsX[0]]) = rX[0];
+    *reinterpret_cast<float4 *>(&sX[w][ldsX[1]]) = rX[1];
+  };
+
+  float pend = 1.f; // scale still to be applied to hs
+  fetch(0);
+  fetch_scores(0);
+  stage(0);
+  for (int k = 0; k < nsub; ++k) {
+    const int slot = k & 1;
+    const int t0 = 64 * k, nv = min(64, L - t0);
+    lds_barrier(); // B/C of sub-block k staged; slot ^ 1 no longer read
+
+    // ---- step sizes and decay factors of this wave's head (lane = token) --
+    float dl = softplus_f(rdt + bias);
+    dl = (l < nv) ? dl : 0.f;
+    const float c = wave_incl_scan(dl * a2);
+    const float clast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, c), 63));
+    const float q = c - hw_log2(dl); // +inf where Delta = 0
+    const bool fast = fabsf(clast) <= kSpanMax;
+    const float m = fast ? 0.5f * clast : 0.f;
+    sF0[w][l] = hw_exp2((fast ? m : clast) - q);
+    sF1[w][l] = hw_exp2(c - m);
+    sCq[w][l] = q;
+
+    fetch(k + 1);
+
+    const float pre = pend * hw_exp2(m);
+#pragma unroll
+    for (int kk = 0; kk < NT; ++kk) hs[kk] *= pre;
+
+    // ---- state term: Y[p][t] = sum_n S[p][n] C[t][n] --------------------------
+    FragBF hf[KN];
+#pragma unroll
+    for (int ks = 0; ks < KN; ++ks) {
+      float v[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        v[r] = hs[2 * ks][r];
+        v[4 + r] = hs[2 * ks + 1][r];
+      }
+      hf[ks] = pack8<__bf16>(v);
+    }
+    f32x4 yacc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const __bf16 *cr = &sC[slot][(16 * u + li) * LDC + 4 * lg];
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KN; ++ks) acc = mma(hf[ks], ld4x2(cr + 32 * ks, cr + 32 * ks + 16), acc);
+      yacc[u] = acc;
+    }
+
+    // x^T fragments (row p0 + li, K = tokens) scaled by the token factors
+    FragBF xr[2], xs[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      xr[ks] = trfrag(sX[w], 16, 32 * ks, 0, li, lg);
+      const float4 fa = *reinterpret_cast<const float4 *>(&sF0[w][32 * ks + 4 * lg]);
+      const float4 fb = *reinterpret_cast<const float4 *>(&sF0[w][32 * ks + 16 + 4 * lg]);
+      const float v[8] = {elem(xr[ks], 0) * fa.x, elem(xr[ks], 1) * fa.y, elem(xr[ks], 2) * fa.z,
+                          elem(xr[ks], 3) * fa.w, elem(xr[ks], 4) * fb.x, elem(xr[ks], 5) * fb.y,
+                          elem(xr[ks], 6) * fb.z, elem(xr[ks], 7) * fb.w};
+      xs[ks] = pack8<__bf16>(v);
+    }
+
+    // ---- intra-block term --------------------------------------------------
+    if (fast) {
+      // on the shared scores; y = 2^{c-m} (state + intra) below
+#pragma unroll
+      for (int f = 0; f < NSF; ++f) {
+        const int u = f < 2 ? f : 2 + (f - 2) / 2, ks = f < 2 ? 0 : (f - 2) % 2;
+        yacc[u] = mma(xs[ks], sf[f], yacc[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) yacc[u] *= sF1[w][16 * u + li];
+    } else {
+      // per-element decay M[t][t'] = Score[t][t'] 2^{c_t - q_t'} on raw x;
+      // the state term is scaled by 2^{c_t} first
+#pragma unroll
+      for (int u = 0; u < 4; ++u) yacc[u] *= sF1[w][16 * u + li];
+#pragma unroll
+      for (int f = 0; f < NSF; ++f) {
+        const int u = f < 2 ? f : 2 + (f - 2) / 2, ks = f < 2 ? 0 : (f - 2) % 2;
+        const int t = 16 * u + li;
+        const float ct = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * t, __builtin_bit_cast(int, c)));
+        const float4 qa = *reinterpret_cast<const float4 *>(&sCq[w][32 * ks + 4 * lg]);
+        const float4 qb = *reinterpret_cast<const float4 *>(&sCq[w][32 * ks + 16 + 4 * lg]);
+        const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int tp = 32 * ks + kperm(lg, e);
+          v[e] = (tp <= t) ? elem(sf[f], e) * hw_exp2(ct - qv[e]) : 0.f;
+        }
+        yacc[u] = mma(xr[ks], pack8<__bf16>(v), yacc[u]);
+      }
+    }
+    fetch_scores(min(k + 1, nsub - 1));
+
+    // ---- y = acc + D x; rows past the end (and idle waves) are dropped ------
+    {
+      const auto rsY = make_rsrc(Ybase + (int64_t)t0 * rowX,
+                                 active ? (uint32_t)(((int64_t)(nv - 1) * rowX + 16) * 2) : 0u);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(&sX[w][(16 * u + li) * 16 + 4 * lg]);
+        bstore4<__bf16>(rsY, offY + (uint32_t)(16 * u * rowX * 2), yacc[u][0] + d_h * (float)xv[0],
+                        yacc[u][1] + d_h * (float)xv[1], yacc[u][2] + d_h * (float)xv[2],
+                        yacc[u][3] + d_h * (float)xv[3]);
+      }
+    }
+
+    // ---- state update.  Fast path: S^T += B^T xs, the factor 2^{c_last-m}
+    //      is deferred to the next sub-block.  Slow path: S^T = 2^{c_last}
+    //      S^T + B^T (w o x), and xs holds w o x.
+    const float mid = fast ? 1.f : hw_exp2(clast);
+#pragma unroll
+    for (int kk = 0; kk < NT; ++kk) hs[kk] *= mid;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int kk = 0; kk < NT; ++kk) hs[kk] = mma(trfrag(sB[slot], LDB, 32 * ks, 16 * kk, li, lg), xs[ks], hs[kk]);
+    pend = fast ? hw_exp2(clast - m) : 1.f;
+
+    stage(slot ^ 1);
+  }
+
+  if (prm.final_state != nullptr && active) {
+#pragma unroll
+    for (int k = 0; k < NT; ++k) *reinterpret_cast<f32x4 *>(prm.final_state + srow + 16 * k + 4 * lg) = hs[k] * pend;
+  }
+}
+
+template <int N, int W>
+hipError_t launch_rwalk_t(const RWalkParams &p, int nwg, hipStream_t st) {
+  hipLaunchKernelGGL((rwalk_kernel<N, W>), dim3(nwg), dim3(W * 64), 0, st, p);
+  return hipGetLastError();
+}
+
+template <int N>
+hipError_t launch_rwalk_n(int W, const RWalkParams &p, int nwg, hipStream_t st) {
+  switch (W) {
+  case 1: return launch_rwalk_t<N, 1>(p, nwg, st);
+  case 2: return launch_rwalk_t<N, 2>(p, nwg, st);
+  case 3: return launch_rwalk_t<N, 3>(p, nwg, st);
+  case 4: return launch_rwalk_t<N, 4>(p, nwg, st);
+  case 5: return launch_rwalk_t<N, 5>(p, nwg, st);
+  case 6: return launch_rwalk_t<N, 6>(p, nwg, st);
+  case 7: return launch_rwalk_t<N, 7>(p, nwg, st);
+  case 8: return launch_rwalk_t<N, 8>(p, nwg, st);
+  default: return hipErrorInvalidValue;
+  }
+}
+
+} // namespace
+
+hipError_t launch_scores(const void *B, const void *C, void *scores_v, int b, int L, int G, int N,
+                         hipStream_t stream) {
+  const int nsub = (L + 63) / 64;
+  __bf16 *scores = reinterpret_cast<__bf16 *>(scores_v);
+  const dim3 grid((unsigned)(b * G * nsub));
+  const __bf16 *Bp = reinterpret_cast<const __bf16 *>(B);
+  const __bf16 *Cp = reinterpret_cast<const __bf16 *>(C);
+  switch (N) {
+  case 32: hipLaunchKernelGGL(scores_kernel<32>, grid, dim3(256), 0, stream, Bp, Cp, scores, L, G, nsub); break;
+  case 64: hipLaunchKernelGGL(scores_kernel<64>, grid, dim3(256), 0, stream, Bp, Cp, scores, L, G, nsub); break;
+  case 128: hipLaunchKernelGGL(scores_kernel<128>, grid, dim3(256), 0, stream, Bp, Cp, scores, L, G, nsub); break;
+  default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rwalk(int N, int W, const RWalkParams &p, hipStream_t stream) {
+  const int nwg = p.b * p.G * p.wg_per_bg;
+  switch (N) {
+  case 32: return launch_rwalk_n<32>(W, p, nwg, stream);
+  case 64: return launch_rwalk_n<64>(W, p, nwg, stream);
+  case 128: return launch_rwalk_n<128>(W, p, nwg, stream);
+  default: return hipErrorInvalidValue;
+  }
+}
+
+} // namespace ssd

@@ -19,7 +19,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libssd.so")
 
 SSD_F32, SSD_BF16 = 0, 1
-SSD_ALGO_AUTO, SSD_ALGO_FUSED, SSD_ALGO_CHUNKED = 0, 1, 2
+SSD_ALGO_AUTO, SSD_ALGO_FUSED, SSD_ALGO_CHUNKED, SSD_ALGO_ROWS = 0, 1, 2, 3
 STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_DTYPE",
           4: "SSD_ERR_LAYOUT", 5: "SSD_ERR_UNSUPPORTED", 6: "SSD_ERR_ALIAS",
           7: "SSD_ERR_NOMEM", 8: "SSD_ERR_HIP"}
@@ -51,13 +51,16 @@ def lib():
         L.ssd_scan_fwd.restype = ctypes.c_int
         L.ssd_scan_fwd_algo.argtypes = [P] * 10 + [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
         L.ssd_scan_fwd_algo.restype = ctypes.c_int
+        L.ssd_scan_fwd_rows.argtypes = [P] * 10 + [ctypes.c_int, ctypes.c_void_p]
+        L.ssd_scan_fwd_rows.restype = ctypes.c_int
         L.ssd_step.argtypes = [P] * 8 + [ctypes.c_void_p]
         L.ssd_step.restype = ctypes.c_int
         L.ssd_status_string.argtypes = [ctypes.c_int]
         L.ssd_status_string.restype = ctypes.c_char_p
         L.ssd_last_error.restype = ctypes.c_char_p
         L.ssd_version.restype = ctypes.c_int
-        L.ssd_scan_plan.argtypes = [ctypes.c_int64] * 6 + [ctypes.c_int, ctypes.POINTER(ctypes.c_int),
+        L.ssd_scan_plan.argtypes = [ctypes.c_int64] * 6 + [ctypes.c_int, ctypes.c_int,
+                                                            ctypes.POINTER(ctypes.c_int),
                                                             ctypes.POINTER(ctypes.c_int)]
         L.ssd_scan_plan.restype = ctypes.c_int
         _lib = L
@@ -119,6 +122,24 @@ def ssd_scan_fwd(x, dt, dt_bias, A, B, C, D=None, init_state=None, out=None,
     return out, final_state
 
 
+def ssd_scan_fwd_rows(x, dt, dt_bias, A, B, C, D=None, init_state=None, out=None,
+                      final_state=None, waves: int = 0, stream=None,
+                      return_final_state: bool = True):
+    """Row-sliced walk with `waves` waves per workgroup (0 = automatic)."""
+    if out is None:
+        out = torch.empty_like(x)
+    if final_state is None and return_final_state:
+        final_state = torch.empty((x.shape[0], x.shape[2], x.shape[3], B.shape[3]),
+                                  dtype=torch.float32, device=x.device)
+    st = _stream(stream, x)
+    status = lib().ssd_scan_fwd_rows(
+        describe(x), describe(dt), describe(dt_bias), describe(A), describe(B), describe(C),
+        describe(D), describe(init_state), describe(out), describe(final_state),
+        int(waves), st)
+    _check(status)
+    return out, final_state
+
+
 def ssd_step(state, x, dt, A, B, C, D=None, out=None, stream=None):
     """One recurrent step; ``state`` is updated in place; returns out."""
     if out is None:
@@ -130,10 +151,11 @@ def ssd_step(state, x, dt, A, B, C, D=None, out=None, stream=None):
     return out
 
 
-def ssd_scan_plan(b, L, H, P, G, N, cus: int = 256):
-    """(algo, seg_len) that SSD_ALGO_AUTO uses for this shape."""
+def ssd_scan_plan(b, L, H, P, G, N, dtype=torch.bfloat16, cus: int = 256):
+    """(algo, seg_len) that SSD_ALGO_AUTO uses for this shape and input dtype."""
     algo, seg = ctypes.c_int(), ctypes.c_int()
-    _check(lib().ssd_scan_plan(b, L, H, P, G, N, cus, ctypes.byref(algo), ctypes.byref(seg)))
+    code = SSD_BF16 if dtype in (torch.bfloat16, SSD_BF16) else SSD_F32
+    _check(lib().ssd_scan_plan(b, L, H, P, G, N, code, cus, ctypes.byref(algo), ctypes.byref(seg)))
     return algo.value, seg.value
 
 

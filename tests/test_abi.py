@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(ssd):
     names = declared_functions()
-    assert {"ssd_scan_fwd", "ssd_step", "ssd_scan_fwd_algo", "ssd_scan_plan",
+    assert {"ssd_scan_fwd", "ssd_step", "ssd_scan_fwd_algo", "ssd_scan_fwd_rows", "ssd_scan_plan",
             "ssd_status_string", "ssd_last_error", "ssd_version"} <= set(names)
     raw = ctypes.CDLL(ssd.LIB_PATH)
     for n in names:
@@ -163,22 +163,47 @@ def test_python_binding_raises(ssd):
 
 
 def test_plan(ssd):
-    """The automatic plan: the fused walk when b*H covers the compute units,
-    segments otherwise; always a valid segment length."""
+    """The automatic plan: the row-sliced walk for bf16 shapes whose rows fill
+    the compute units, the single walk per (batch, head) for fp32, segments
+    when (batch, head) pairs are few; always a valid segment length."""
     lib = ssd.lib()
     import ctypes as ct
     algo, seg = ct.c_int(), ct.c_int()
-    def plan(b, L, H, P=64, G=1, N=128, cus=256):
-        st = lib.ssd_scan_plan(b, L, H, P, G, N, cus, ct.byref(algo), ct.byref(seg))
+
+    def plan(b, L, H, P=64, G=1, N=128, dtype=1, cus=256):
+        st = lib.ssd_scan_plan(b, L, H, P, G, N, dtype, cus, ct.byref(algo), ct.byref(seg))
         assert st == 0
         return algo.value, seg.value
-    assert plan(8, 2048, 32) == (1, 2048)            # 256 walks on 256 units
-    a, s = plan(4, 4096, 80)                          # 320 walks: 2 per busiest unit
-    assert (a, s) == (1, 4096)
-    a, s = plan(1, 65536, 32, G=8)                    # 32 walks: split into segments
-    assert a == 2 and 256 <= s <= 8192
-    a, s = plan(1, 4096, 16)                          # 16 walks on 256 units
-    assert a == 2
+    assert plan(8, 2048, 32) == (ssd.SSD_ALGO_ROWS, 2048)    # 370M layer
+    assert plan(4, 4096, 80) == (ssd.SSD_ALGO_ROWS, 4096)    # 2.7B layer
+    assert plan(4, 4096, 80, dtype=0) == (ssd.SSD_ALGO_FUSED, 4096)
+    assert plan(4, 4096, 80, N=16) == (ssd.SSD_ALGO_FUSED, 4096)  # N=16: no row walk
+    a, s = plan(1, 65536, 32, G=8)                    # 32 (batch, head) pairs: segments
+    assert a == ssd.SSD_ALGO_CHUNKED and 256 <= s <= 8192
+    a, s = plan(1, 4096, 16, dtype=0)                 # 16 walks on 256 units
+    assert a == ssd.SSD_ALGO_CHUNKED
     a, s = plan(1, 100, 2)
-    assert a in (1, 2) and s >= 64
-    assert lib.ssd_scan_plan(0, 10, 2, 64, 1, 128, 256, ct.byref(algo), ct.byref(seg)) == 2
+    assert a in (1, 2, 3) and s >= 64
+    assert lib.ssd_scan_plan(0, 10, 2, 64, 1, 128, 1, 256, ct.byref(algo), ct.byref(seg)) == 2
+    assert lib.ssd_scan_plan(1, 10, 2, 64, 1, 128, 7, 256, ct.byref(algo), ct.byref(seg)) == 3
+
+
+def test_rows_rejections(ssd):
+    """The explicit row-sliced walk validates like the scan and rejects fp32,
+    N outside {32, 64, 128} and wave counts outside 0..8."""
+    lib = ssd.lib()
+    d = ssd.describe
+
+    def call(a, waves):
+        return lib.ssd_scan_fwd_rows(d(a["x"]), d(a["dt"]), d(a["dt_bias"]), d(a["A"]), d(a["B"]),
+                                     d(a["C"]), d(a["D"]), d(a["init_state"]), d(a["out"]),
+                                     d(a["final_state"]), waves, None)
+    assert call(_scan_args(dtype=torch.float32), 1) == 5
+    assert call(_scan_args(N=16), 1) == 5
+    assert call(_scan_args(), 9) == 5
+    assert call(_scan_args(), -1) == 5
+    a = _scan_args()
+    a["x"] = torch.zeros(1, 99, 4, 16, dtype=torch.bfloat16)   # L disagrees with dt
+    assert call(a, 1) == 2
+    assert _call_scan(ssd, _scan_args(dtype=torch.float32), algo=3)[0] == 5
+    assert _call_scan(ssd, _scan_args(), algo=4)[0] == 5

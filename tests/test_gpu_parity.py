@@ -158,12 +158,15 @@ def workload_with_reference(name):
     return _CACHE[name]
 
 
-@pytest.mark.parametrize("algo", [ssd.SSD_ALGO_AUTO, ssd.SSD_ALGO_FUSED, ssd.SSD_ALGO_CHUNKED])
+@pytest.mark.parametrize("algo", [ssd.SSD_ALGO_AUTO, ssd.SSD_ALGO_FUSED, ssd.SSD_ALGO_CHUNKED,
+                                  ssd.SSD_ALGO_ROWS])
 @pytest.mark.parametrize("name", SCANS)
 def test_workload_scan(name, algo):
     if name.startswith("long") and algo == ssd.SSD_ALGO_FUSED:
         pytest.skip("one workgroup per (batch, head) leaves most of the GPU idle here; "
                     "covered by the small-shape tests")
+    if algo == ssd.SSD_ALGO_ROWS and inputs.WORKLOADS[name]["dtype"] != inputs.BF16:
+        pytest.skip("the row-sliced walk takes bf16 inputs only")
     say("workload", name, "algo", algo)
     si, (yr, fr) = workload_with_reference(name)
     y, fin = gpu_scan(si, algo=algo)
@@ -201,6 +204,7 @@ def test_chunk_invariance():
         say("chunk invariance", chunk)
         outs.append(gpu_scan(si, algo=ssd.SSD_ALGO_CHUNKED, chunk=chunk))
     outs.append(gpu_scan(si, algo=ssd.SSD_ALGO_FUSED))
+    outs.append(gpu_scan(si, algo=ssd.SSD_ALGO_ROWS))
     yr, fr = oracle_scan(si)
     check(outs[0][0], yr, 2e-2, "y chunk 64")
     check(outs[0][1], fr, 2e-2, "final chunk 64")
@@ -209,7 +213,7 @@ def test_chunk_invariance():
         check(f, outs[0][1], 2e-2, "final across chunk sizes")
 
 
-@pytest.mark.parametrize("algo", [ssd.SSD_ALGO_FUSED, ssd.SSD_ALGO_CHUNKED])
+@pytest.mark.parametrize("algo", [ssd.SSD_ALGO_FUSED, ssd.SSD_ALGO_CHUNKED, ssd.SSD_ALGO_ROWS])
 @pytest.mark.parametrize("L1", [256, 300])
 def test_split_invariance(algo, L1):
     """Scanning [0, L1) then [L1, L) from the carried state equals one scan."""
@@ -235,7 +239,7 @@ def test_in_place_final_state():
     say("in-place final state")
     t = staging.scan_tensors(si, DEV)
     st = t["init_state"].clone()
-    for algo in (ssd.SSD_ALGO_FUSED, ssd.SSD_ALGO_CHUNKED):
+    for algo in (ssd.SSD_ALGO_FUSED, ssd.SSD_ALGO_CHUNKED, ssd.SSD_ALGO_ROWS):
         t2 = dict(t, init_state=st.clone())
         ssd.ssd_scan_fwd(**dict(t2, final_state=t2["init_state"]), chunk=64, algo=algo)
         torch.cuda.synchronize()
@@ -258,7 +262,7 @@ def test_step_matches_scan():
     check(staging.to_f64(st), staging.to_f64(f), 1e-4, "step state vs scan final")
 
 
-@pytest.mark.parametrize("algo", [ssd.SSD_ALGO_FUSED, ssd.SSD_ALGO_CHUNKED])
+@pytest.mark.parametrize("algo", [ssd.SSD_ALGO_FUSED, ssd.SSD_ALGO_CHUNKED, ssd.SSD_ALGO_ROWS])
 def test_deterministic(algo):
     si = inputs.make_scan(2, 777, 8, 64, 1, 128, dtype=inputs.BF16, seed=25, init_std=0.1)
     say("determinism", algo)
@@ -280,3 +284,86 @@ def test_long_segments_ragged(chunk):
     yr, fr = oracle_scan(si)
     check(y, yr, 2e-2, "y")
     check(fin, fr, 2e-2, "final")
+
+
+# ---------------------------------------------------------------------------
+# the row-sliced walk (bf16, N in {32, 64, 128}) at every workgroup size
+
+ROWS_SMALL = [c for c in SMALL if c[0] == inputs.BF16 and c[6] in (32, 64, 128)] + [
+    # heads per group not a multiple of the workgroup's rows; idle waves
+    (inputs.BF16, 2, 300, 6, 32, 2, 64, 64),
+    (inputs.BF16, 1, 200, 12, 16, 3, 128, 64),
+    (inputs.BF16, 3, 129, 5, 64, 5, 32, 64),
+]
+
+
+@pytest.mark.parametrize("waves", [1, 2, 3, 5, 8])
+@pytest.mark.parametrize("case", ROWS_SMALL, ids=lambda c: "%s-b%dL%dH%dP%dG%dN%dQ%d" % c)
+def test_rows_small(case, waves):
+    dtype, b, L, H, P, G, N, chunk = case
+    si = inputs.make_scan(b, L, H, P, G, N, dtype=dtype, chunk=chunk, seed=L + P + N + 1,
+                          init_std=0.5)
+    say("rows small", case, "waves", waves)
+    t = staging.scan_tensors(si, DEV)
+    out, fin = ssd.ssd_scan_fwd_rows(**t, waves=waves)
+    torch.cuda.synchronize()
+    yr, fr = oracle_scan(si)
+    check(staging.to_f64(out), yr, TOL[dtype], "y")
+    check(staging.to_f64(fin), fr, TOL[dtype], "final_state")
+
+
+def decay_spans(si):
+    """|sum of Delta*A*log2(e)| over each 64-token sub-block, per (b, h)."""
+    f = si.f64()
+    dl = np.logaddexp(0.0, f["dt"] + f["dt_bias"][None, None, :])
+    a = np.abs(dl * f["A"][None, None, :]) * np.log2(np.e)
+    b, L, H = a.shape
+    pad = (-L) % 64
+    a = np.concatenate([a, np.zeros((b, pad, H))], 1)
+    return a.reshape(b, -1, 64, H).sum(2)
+
+
+@pytest.mark.parametrize("waves", [1, 4, 5])
+def test_rows_strong_decay(waves):
+    """Sub-blocks whose decay span exceeds the separable range (per-element
+    path) next to ordinary ones, in the same workgroups."""
+    si = inputs.make_scan(2, 300, 8, 64, 2, 128, dtype=inputs.BF16, seed=31,
+                          dt_range=(0.01, 2.0), init_std=0.3)
+    spans = decay_spans(si)
+    assert (spans > 100).any() and (spans <= 100).any()
+    say("rows strong decay waves", waves, "slow share %.2f" % float((spans > 100).mean()))
+    t = staging.scan_tensors(si, DEV)
+    out, fin = ssd.ssd_scan_fwd_rows(**t, waves=waves)
+    torch.cuda.synchronize()
+    yr, fr = oracle_scan(si)
+    check(staging.to_f64(out), yr, 2e-2, "y")
+    check(staging.to_f64(fin), fr, 2e-2, "final_state")
+
+
+def test_rows_no_optional():
+    si = inputs.make_scan(2, 150, 4, 64, 2, 64, dtype=inputs.BF16, chunk=64, seed=9)
+    say("rows no-optional")
+    t = staging.scan_tensors(si, DEV)
+    out, _ = ssd.ssd_scan_fwd_rows(t["x"], t["dt"], None, t["A"], t["B"], t["C"], None, None,
+                                   waves=2, return_final_state=False)
+    torch.cuda.synchronize()
+    f = si.f64()
+    yr, _ = oracle.scan(f["x"], f["dt"], None, f["A"], f["B"], f["C"], None, None)
+    check(staging.to_f64(out), yr, 2e-2, "y without bias/D/init")
+
+
+def test_rows_waves_agree():
+    """Every state row is computed by the same instructions whatever the
+    workgroup size, so outputs agree bitwise across wave counts."""
+    si = inputs.make_scan(2, 400, 10, 64, 1, 128, dtype=inputs.BF16, seed=33, init_std=0.2)
+    t = staging.scan_tensors(si, DEV)
+    ref = None
+    for waves in range(1, 9):
+        say("rows waves agree", waves)
+        out, fin = ssd.ssd_scan_fwd_rows(**t, waves=waves)
+        torch.cuda.synchronize()
+        if ref is None:
+            ref = (out.clone(), fin.clone())
+        else:
+            assert torch.equal(out.view(torch.int16), ref[0].view(torch.int16)), waves
+            assert torch.equal(fin, ref[1]), waves
