@@ -165,6 +165,12 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
   const int nsub = (L + 63) / 64;
   const __bf16 *Sbase = reinterpret_cast<const __bf16 *>(prm.scores) + (int64_t)bg * nsub * 4096;
 
+  // The C tile is stored with the columns of each 32-column group permuted
+  // (column 32ks + 8g + j holds n = 32ks + kperm(g, j)), so that a state-term
+  // fragment is one 16-byte read.  A piece of 8 consecutive n, the m-th of
+  // its 32-column group, splits into two 4-column halves stored 8 columns
+  // apart, the first at column 16m (m < 2) or 16(m - 2) + 4 (m >= 2).
+  //
   // Loop-invariant offsets.  Every wave issues the same sequence of memory
   // operations on every path through the loop (threads without a piece of
   // their own repeat the last piece; fetches past the end use empty ranges
@@ -177,9 +183,10 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
   for (int i = 0; i < PPT; ++i) {
     const int q = min(tid + i * NTH, PIECES - 1);
     const int j = q / RW, n0 = (q % RW) * 8;
+    const int mq = (n0 % 32) / 8;
     offBC[i] = (uint32_t)((j * rowB + n0) * 2);
     ldsB[i] = j * LDB + n0;
-    ldsC[i] = j * LDC + n0;
+    ldsC[i] = j * LDC + (n0 / 32) * 32 + (mq < 2 ? 16 * mq : 16 * (mq - 2) + 4);
   }
   // x pieces of this wave: piece l + 64e = (token, half) -> 8 columns.
   uint32_t offX[2];
@@ -231,7 +238,8 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
       *reinterpret_cast<float4 *>(&sB[slot][ldsB[i]]) = rB[i];
-      *reinterpret_cast<float4 *>(&sC[slot][ldsC[i]]) = rC[i];
+      *reinterpret_cast<float2 *>(&sC[slot][ldsC[i]]) = make_float2(rC[i].x, rC[i].y);
+      *reinterpret_cast<float2 *>(&sC[slot][ldsC[i] + 8]) = make_float2(rC[i].z, rC[i].w);
     }
     *reinterpret_cast<float4 *>(&sX[w][ldsX[0]]) = rX[0];
     *reinterpret_cast<float4 *>(&sX[w][ldsX[1]]) = rX[1];
@@ -264,7 +272,8 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
 #pragma unroll
     for (int kk = 0; kk < NT; ++kk) hs[kk] *= pre;
 
-    // ---- state term: Y[p][t] = sum_n S[p][n] C[t][n] --------------------------
+    // ---- state term: Y[p][t] = sum_n S[p][n] C[t][n]; K-step outer, the four
+    //      token tiles of a step are independent MFMAs read together ---------
     FragBF hf[KN];
 #pragma unroll
     for (int ks = 0; ks < KN; ++ks) {
@@ -278,12 +287,14 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
     }
     f32x4 yacc[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const __bf16 *cr = &sC[slot][(16 * u + li) * LDC + 4 * lg];
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < 4; ++u) yacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KN; ++ks) acc = mma(hf[ks], ld4x2(cr + 32 * ks, cr + 32 * ks + 16), acc);
-      yacc[u] = acc;
+    for (int ks = 0; ks < KN; ++ks) {
+      FragBF cf[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) cf[u] = ld8(&sC[slot][(16 * u + li) * LDC + 8 * lg + 32 * ks]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) yacc[u] = mma(hf[ks], cf[u], yacc[u]);
     }
 
     // x^T fragments (row p0 + li, K = tokens) scaled by the token factors
