@@ -20,6 +20,10 @@ LIB = os.path.join(PKG, "libssd.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 SOURCES = ["ssd_api.hip", "ssd_kernels.hip", "ssd_rwalk.hip"]
+# Per-source flags.  The row walk keeps its MFMA accumulators (the state
+# tile) in ordinary VGPRs; otherwise the compiler places them in accumulator
+# registers and copies them to VGPRs and back on every sub-block.
+EXTRA = {"ssd_rwalk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 COMMON = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
@@ -32,7 +36,7 @@ COMMON = [
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + COMMON + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + COMMON + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))

@@ -17,16 +17,18 @@
 //    group.  scores_kernel computes them once per (batch, group, sub-block)
 //    as a causal 64x64 bf16 tile; every head of the group reads that tile.
 //
-// 2. The decay weight is separable: with a reference value m,
-//    2^{c_t - q_t'} = 2^{c_t - m} * 2^{m - q_t'}.  With m the midpoint of
-//    [min c, max c] (c is monotone, so that is c_last/2) both factors stay
-//    within 2^{+-span/2}, span = |c_last|.  Then
-//       y_t = 2^{c_t - m} [ (2^m S) C_t + sum_t' Score[t][t'] xs_t' ] + D x_t,
-//       xs_t' = 2^{m - q_t'} x_t'
-//       S'  = 2^{c_last - m} [ 2^m S + sum_t xs_t B_t^T ]
-//    so the intra-block product takes the shared score tile as it is and the
-//    decay becomes a per-token scale of x and of y.  Sub-blocks whose decay
-//    span exceeds kSpanMax take the per-element form instead (slow path).
+// 2. The decay weight is separable: 2^{c_t - q_t'} = 2^{c_t + e} 2^{-q_t' - e}
+//    for any reference e.  The kernel keeps the state as S = 2^e hs, where
+//    hs is the register tile and e a running wave-uniform exponent; then
+//       y_t = 2^{c_t + e} [ hs C_t + sum_t' Score[t][t'] xs_t' ] + D x_t,
+//       xs_t' = 2^{-q_t' - e} x_t',   hs' = hs + sum_t xs_t B_t^T,
+//       e' = e + c_last,
+//    so the intra-block product takes the shared score tile as it is, the
+//    decay becomes a per-token scale of x and of y, and the register tile is
+//    never rescaled except when e drifts out of range (an exact shift by
+//    whole octaves).  Both token factors stay within 2^{+-kExpLim} while the
+//    sub-block's decay span |c_last| is at most kSpanMax; longer spans take
+//    the per-element form (slow path).
 //
 // Work split: a workgroup of W waves owns 16W consecutive state rows of one
 // (batch, group) -- rows are (head, p) pairs of the heads in the group, 16
@@ -34,9 +36,15 @@
 // sub-blocks.  The B and C tiles of a sub-block are staged once in LDS and
 // read by every wave; each wave holds its 16 x N state in MFMA accumulator
 // registers, stages its own 16 columns of x in a private LDS tile and loads
-// the score fragments straight from global memory (L2).
+// the score fragments straight from global memory (L2).  Two schedules of
+// the same arithmetic (bitwise the same results): with at most four waves
+// every wave has a SIMD to itself and the plain order is fastest; with more,
+// the decay factors of the next sub-block are computed next to the products
+// of the current one.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "ssd_device.h"
 #include "ssd_internal.h"
@@ -44,9 +52,13 @@
 namespace ssd {
 namespace {
 
-// Decay span (log2 units) up to which the separable form is used: the
-// scale factors stay within 2^{+-kSpanMax/2}.
-constexpr float kSpanMax = 100.f;
+// Decay span |c_last| (log2 units) up to which a sub-block takes the
+// separable form, and the bound on the state exponent e: with e kept in
+// [|c_last| - kExpLim, kExpLim] every token factor 2^{c + e} and
+// 2^{log2 Delta - c - e} lies within 2^{+-kExpLim} (times Delta), far inside
+// the fp32 / bf16 exponent range, and so do the products they enter.
+constexpr float kSpanMax = 178.f;
+constexpr float kExpLim = 90.f;
 
 // Position of K-value j (0..7) of lane group g inside a 32-column group, in
 // the order the transposed fragments use: {4g .. 4g+3, 16+4g .. 16+4g+3}.
@@ -104,6 +116,9 @@ __global__ void __launch_bounds__(256) scores_kernel(const __bf16 *__restrict__ 
 
 // ---------------------------------------------------------------------------
 // The row-sliced walk.
+// This file is built with MFMA accumulators in ordinary VGPRs: with
+// accumulator registers the compiler parks the state tile there and copies
+// it to VGPRs and back every sub-block.
 template <int N, int W>
 __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
   constexpr int NTH = W * 64;
@@ -119,9 +134,10 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
   __shared__ __attribute__((aligned(16))) __bf16 sB[2][64 * LDB];
   __shared__ __attribute__((aligned(16))) __bf16 sC[2][64 * LDC];
   __shared__ __attribute__((aligned(16))) __bf16 sX[W][64 * 16]; // x[token][16 columns]
-  __shared__ __attribute__((aligned(16))) float sF0[W][64];      // xs scale (fast) / w (slow)
-  __shared__ __attribute__((aligned(16))) float sF1[W][64];      // y scale 2^{c - m}
-  __shared__ __attribute__((aligned(16))) float sCq[W][64];      // q (slow path)
+  // per-wave token factors, double-buffered: scan() fills the other slot
+  __shared__ __attribute__((aligned(16))) float sF0[2][W][64];   // xs scale (fast) / w (slow)
+  __shared__ __attribute__((aligned(16))) float sF1[2][W][64];   // y scale 2^{c + e}
+  __shared__ __attribute__((aligned(16))) float2 sQC[2][W][64];  // (q, c) for the slow path
 
   const int H = prm.H, G = prm.G, L = prm.L, P = prm.P;
   const int nwg = gridDim.x, bid = blockIdx.x;
@@ -208,12 +224,9 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
   const auto rsS = make_rsrc(Sbase, (uint32_t)nsub * 4096u * 2u);
 
   float4 rB[PPT], rC[PPT], rX[2];
-  float rdt = 0.f;
-  auto fetch = [&](int k) {
+  // B, C and x of sub-block k (loads past the end read zeros).
+  auto fetch_bcx = [&](int k) {
     const int t0 = 64 * k, nv = min(64, L - t0);
-    // step sizes first: they are needed first (top of the next step)
-    const auto rsD = make_rsrc(dtbase + (int64_t)t0 * H, nv > 0 ? (uint32_t)(((int64_t)(nv - 1) * H + 1) * 4) : 0u);
-    rdt = bload4(rsD, (uint32_t)(l * H * 4));
     const uint32_t bcb = nv > 0 ? (uint32_t)(((int64_t)(nv - 1) * rowB + N) * 2) : 0u;
     const auto rsB = make_rsrc(Bbase + (int64_t)t0 * rowB, bcb);
     const auto rsC = make_rsrc(Cbase + (int64_t)t0 * rowB, bcb);
@@ -225,6 +238,12 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
     const auto rsX = make_rsrc(Xbase + (int64_t)t0 * rowX, nv > 0 ? (uint32_t)(((int64_t)(nv - 1) * rowX + 16) * 2) : 0u);
     rX[0] = bload16(rsX, offX[0]);
     rX[1] = bload16(rsX, offX[1]);
+  };
+  // Raw step size of token l of sub-block k (zero past the end).
+  auto fetch_dt = [&](int k) {
+    const int t0 = 64 * k, nv = min(64, L - t0);
+    const auto rsD = make_rsrc(dtbase + (int64_t)t0 * H, nv > 0 ? (uint32_t)(((int64_t)(nv - 1) * H + 1) * 4) : 0u);
+    return bload4(rsD, (uint32_t)(l * H * 4));
   };
   // Score fragments of sub-block k, issued right after the previous
   // sub-block's intra-block product has consumed the registers.
@@ -245,35 +264,68 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
     *reinterpret_cast<float4 *>(&sX[w][ldsX[1]]) = rX[1];
   };
 
-  float pend = 1.f; // scale still to be applied to hs
-  fetch(0);
-  fetch_scores(0);
-  stage(0);
-  for (int k = 0; k < nsub; ++k) {
-    const int slot = k & 1;
-    const int t0 = 64 * k, nv = min(64, L - t0);
-    lds_barrier(); // B/C of sub-block k staged; slot ^ 1 no longer read
-
-    // ---- step sizes and decay factors of this wave's head (lane = token) --
+  // ---- decay factors of one sub-block (lane = token) ------------------------
+  // The state is kept as S = 2^e * hs with a wave-uniform exponent e, so that
+  // the separable path never rescales the register tile: with e_k the
+  // exponent in force during sub-block k,
+  //   y_t = 2^{c_t + e_k} [ hs C_t + sum_t' Score[t][t'] xs_t' ] + D x_t,
+  //   xs_t = 2^{-q_t - e_k} x_t,   hs' = hs + sum_t xs_t B_t^T,
+  //   e_{k+1} = e_k + c_last.
+  // e_k is the incoming exponent while it stays in [|c_last| - kExpLim,
+  // kExpLim]; otherwise hs is shifted by a whole number of octaves (an exact
+  // ldexp) to bring e_k just below kExpLim.  A per-element sub-block shifts
+  // e to within half an octave of 0 and uses
+  //   y_t = 2^{c_t + e_k} hs C_t + sum_t' Score[t][t'] 2^{c_t - q_t'} x_t' + D x_t,
+  //   hs' = 2^{c_last} hs + sum_t 2^{c_last - q_t - e_k} x_t B_t^T,  e_{k+1} = e_k.
+  // scan() writes the per-token factors of sub-block k to slot `sl` and sets
+  // the next_* scalars.
+  int next_fast = 1, next_shift = 0;
+  float next_clast = 0.f, next_eout = 0.f;
+  auto scan = [&](int k, float rdt, float e_in, int sl) {
+    const int nv = min(64, L - 64 * k);
     float dl = softplus_f(rdt + bias);
     dl = (l < nv) ? dl : 0.f;
     const float c = wave_incl_scan(dl * a2);
-    const float clast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, c), 63));
+    float clast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, c), 63));
+    // Keep the (wave-uniform) decisions below in vector registers: as
+    // per-lane selects they stay inside one basic block with the products
+    // they are scheduled against, instead of becoming scalar branches.
+    float e_v = e_in;
+    __asm__ volatile("" : "+v"(clast), "+v"(e_v));
     const float q = c - hw_log2(dl); // +inf where Delta = 0
     const bool fast = fabsf(clast) <= kSpanMax;
-    const float m = fast ? 0.5f * clast : 0.f;
-    sF0[w][l] = hw_exp2((fast ? m : clast) - q);
-    sF1[w][l] = hw_exp2(c - m);
-    sCq[w][l] = q;
+    const bool keep = e_v >= -clast - kExpLim && e_v <= kExpLim;
+    const float n = fast ? (keep ? 0.f : floorf(kExpLim - e_v)) : -rintf(e_v); // octaves
+    const float ek = e_v + n;
+    sF0[sl][w][l] = hw_exp2((fast ? 0.f : clast) - q - ek);
+    sF1[sl][w][l] = hw_exp2(c + ek);
+    sQC[sl][w][l] = make_float2(q, c);
+    next_fast = __builtin_amdgcn_readfirstlane((int)fast);
+    next_shift = __builtin_amdgcn_readfirstlane((int)n);
+    next_clast = clast;
+    next_eout = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, fast ? ek + clast : ek)));
+  };
 
-    fetch(k + 1);
-
-    const float pre = pend * hw_exp2(m);
+  // ---- the phases of one sub-block -------------------------------------------
+  // x^T fragments (row p0 + li, K = tokens), raw and scaled by the token
+  // factors of slot `slot`.
+  FragBF xr[2], xs[2];
+  auto scale_x = [&](int slot) {
 #pragma unroll
-    for (int kk = 0; kk < NT; ++kk) hs[kk] *= pre;
-
-    // ---- state term: Y[p][t] = sum_n S[p][n] C[t][n]; K-step outer, the four
-    //      token tiles of a step are independent MFMAs read together ---------
+    for (int ks = 0; ks < 2; ++ks) {
+      xr[ks] = trfrag(sX[w], 16, 32 * ks, 0, li, lg);
+      const float4 fa = *reinterpret_cast<const float4 *>(&sF0[slot][w][32 * ks + 4 * lg]);
+      const float4 fb = *reinterpret_cast<const float4 *>(&sF0[slot][w][32 * ks + 16 + 4 * lg]);
+      const float v[8] = {elem(xr[ks], 0) * fa.x, elem(xr[ks], 1) * fa.y, elem(xr[ks], 2) * fa.z,
+                          elem(xr[ks], 3) * fa.w, elem(xr[ks], 4) * fb.x, elem(xr[ks], 5) * fb.y,
+                          elem(xr[ks], 6) * fb.z, elem(xr[ks], 7) * fb.w};
+      xs[ks] = pack8<__bf16>(v);
+    }
+  };
+  // State term Y[p][t] = sum_n hs[p][n] C[t][n]; K-step outer, the four
+  // token tiles of a step are independent MFMAs read together.
+  f32x4 yacc[4];
+  auto state_term = [&](int slot) {
     FragBF hf[KN];
 #pragma unroll
     for (int ks = 0; ks < KN; ++ks) {
@@ -285,7 +337,6 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
       }
       hf[ks] = pack8<__bf16>(v);
     }
-    f32x4 yacc[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) yacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -296,85 +347,155 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) yacc[u] = mma(hf[ks], cf[u], yacc[u]);
     }
-
-    // x^T fragments (row p0 + li, K = tokens) scaled by the token factors
-    FragBF xr[2], xs[2];
+  };
+  // State update hs += B^T xs (after the state term has read hs).
+  auto update = [&](int slot) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      xr[ks] = trfrag(sX[w], 16, 32 * ks, 0, li, lg);
-      const float4 fa = *reinterpret_cast<const float4 *>(&sF0[w][32 * ks + 4 * lg]);
-      const float4 fb = *reinterpret_cast<const float4 *>(&sF0[w][32 * ks + 16 + 4 * lg]);
-      const float v[8] = {elem(xr[ks], 0) * fa.x, elem(xr[ks], 1) * fa.y, elem(xr[ks], 2) * fa.z,
-                          elem(xr[ks], 3) * fa.w, elem(xr[ks], 4) * fb.x, elem(xr[ks], 5) * fb.y,
-                          elem(xr[ks], 6) * fb.z, elem(xr[ks], 7) * fb.w};
-      xs[ks] = pack8<__bf16>(v);
-    }
-
-    // ---- intra-block term --------------------------------------------------
-    if (fast) {
-      // on the shared scores; y = 2^{c-m} (state + intra) below
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int kk = 0; kk < NT; ++kk) hs[kk] = mma(trfrag(sB[slot], LDB, 32 * ks, 16 * kk, li, lg), xs[ks], hs[kk]);
+  };
+  // Per-element path: decay the state by 2^{c_last} before its update (its xs
+  // holds 2^{c_last - q - e} x).
+  auto decay_state = [&](float clast) {
+    const float mid = hw_exp2(clast);
+#pragma unroll
+    for (int kk = 0; kk < NT; ++kk) hs[kk] *= mid;
+  };
+  // Exact renormalisation hs *= 2^{-n}.
+  auto shift_state = [&](int n) {
+#pragma unroll
+    for (int kk = 0; kk < NT; ++kk)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) hs[kk][r] = __builtin_amdgcn_ldexpf(hs[kk][r], -n);
+  };
+  // Intra-block term added to the state term, and the token factor of y.
+  auto intra = [&](int slot, auto fast_tag) {
+    if constexpr (decltype(fast_tag)::value) {
+      // on the shared scores; y = 2^{c + e} (state + intra)
 #pragma unroll
       for (int f = 0; f < NSF; ++f) {
         const int u = f < 2 ? f : 2 + (f - 2) / 2, ks = f < 2 ? 0 : (f - 2) % 2;
         yacc[u] = mma(xs[ks], sf[f], yacc[u]);
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) yacc[u] *= sF1[w][16 * u + li];
+      for (int u = 0; u < 4; ++u) yacc[u] *= sF1[slot][w][16 * u + li];
     } else {
-      // per-element decay M[t][t'] = Score[t][t'] 2^{c_t - q_t'} on raw x;
-      // the state term is scaled by 2^{c_t} first
+      // per-element decay M[t][t'] = Score[t][t'] 2^{c_t - q_t'} on raw x; the
+      // state term is scaled by 2^{c_t + e} first
 #pragma unroll
-      for (int u = 0; u < 4; ++u) yacc[u] *= sF1[w][16 * u + li];
+      for (int u = 0; u < 4; ++u) yacc[u] *= sF1[slot][w][16 * u + li];
 #pragma unroll
       for (int f = 0; f < NSF; ++f) {
         const int u = f < 2 ? f : 2 + (f - 2) / 2, ks = f < 2 ? 0 : (f - 2) % 2;
         const int t = 16 * u + li;
-        const float ct = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * t, __builtin_bit_cast(int, c)));
-        const float4 qa = *reinterpret_cast<const float4 *>(&sCq[w][32 * ks + 4 * lg]);
-        const float4 qb = *reinterpret_cast<const float4 *>(&sCq[w][32 * ks + 16 + 4 * lg]);
-        const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+        const float ct = sQC[slot][w][t].y;
         float v[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int tp = 32 * ks + kperm(lg, e);
-          v[e] = (tp <= t) ? elem(sf[f], e) * hw_exp2(ct - qv[e]) : 0.f;
+        for (int j = 0; j < 8; ++j) {
+          const int tp = 32 * ks + kperm(lg, j);
+          v[j] = (tp <= t) ? elem(sf[f], j) * hw_exp2(ct - sQC[slot][w][tp].x) : 0.f;
         }
         yacc[u] = mma(xr[ks], pack8<__bf16>(v), yacc[u]);
       }
     }
-    fetch_scores(min(k + 1, nsub - 1));
-
-    // ---- y = acc + D x; rows past the end (and idle waves) are dropped ------
-    {
-      const auto rsY = make_rsrc(Ybase + (int64_t)t0 * rowX,
-                                 active ? (uint32_t)(((int64_t)(nv - 1) * rowX + 16) * 2) : 0u);
+  };
+  // y = acc + D x; rows past the end (and idle waves) are dropped.
+  auto store_y = [&](int k) {
+    const int t0 = 64 * k, nv = min(64, L - t0);
+    const auto rsY = make_rsrc(Ybase + (int64_t)t0 * rowX,
+                               active ? (uint32_t)(((int64_t)(nv - 1) * rowX + 16) * 2) : 0u);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(&sX[w][(16 * u + li) * 16 + 4 * lg]);
-        bstore4<__bf16>(rsY, offY + (uint32_t)(16 * u * rowX * 2), yacc[u][0] + d_h * (float)xv[0],
-                        yacc[u][1] + d_h * (float)xv[1], yacc[u][2] + d_h * (float)xv[2],
-                        yacc[u][3] + d_h * (float)xv[3]);
-      }
+    for (int u = 0; u < 4; ++u) {
+      const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(&sX[w][(16 * u + li) * 16 + 4 * lg]);
+      bstore4<__bf16>(rsY, offY + (uint32_t)(16 * u * rowX * 2), yacc[u][0] + d_h * (float)xv[0],
+                      yacc[u][1] + d_h * (float)xv[1], yacc[u][2] + d_h * (float)xv[2],
+                      yacc[u][3] + d_h * (float)xv[3]);
     }
+  };
 
-    // ---- state update.  Fast path: S^T += B^T xs, the factor 2^{c_last-m}
-    //      is deferred to the next sub-block.  Slow path: S^T = 2^{c_last}
-    //      S^T + B^T (w o x), and xs holds w o x.
-    const float mid = fast ? 1.f : hw_exp2(clast);
-#pragma unroll
-    for (int kk = 0; kk < NT; ++kk) hs[kk] *= mid;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int kk = 0; kk < NT; ++kk) hs[kk] = mma(trfrag(sB[slot], LDB, 32 * ks, 16 * kk, li, lg), xs[ks], hs[kk]);
-    pend = fast ? hw_exp2(clast - m) : 1.f;
-
-    stage(slot ^ 1);
+  float e_final = 0.f;
+  if constexpr (W <= 4) {
+    // ---- one wave per SIMD: the wave's own latency sets the pace.  The
+    //      factors of sub-block k are computed at its start; the state term
+    //      runs first, the update last, and the renormalisation is applied
+    //      unconditionally (a shift by 0 is exact) so that the block has no
+    //      branch before the intra-block term.
+    float rdt = fetch_dt(0);
+    fetch_bcx(0);
+    fetch_scores(0);
+    stage(0);
+    float e = 0.f;
+    for (int k = 0; k < nsub; ++k) {
+      const int slot = k & 1;
+      lds_barrier(); // B/C/x of sub-block k staged; slot ^ 1 no longer read
+      scan(k, rdt, e, slot);
+      const int fast = next_fast;
+      rdt = fetch_dt(k + 1);
+      fetch_bcx(k + 1);
+      shift_state(next_shift);
+      state_term(slot);
+      scale_x(slot);
+      if (fast) {
+        intra(slot, std::true_type{});
+      } else {
+        intra(slot, std::false_type{});
+        decay_state(next_clast);
+      }
+      fetch_scores(min(k + 1, nsub - 1));
+      store_y(k);
+      update(slot);
+      stage(slot ^ 1);
+      e = next_eout;
+    }
+    e_final = e;
+  } else {
+    // ---- two waves on some SIMD: the factors of sub-block k + 1 are computed
+    //      during sub-block k, next to its products, the step sizes are
+    //      fetched two sub-blocks ahead, and each path (separable or
+    //      per-element) is one straight block.
+    float rdt_next = 0.f, rdt_next2 = 0.f;
+    float cur_clast = 0.f, cur_eout = 0.f;
+    auto body = [&](int k, auto fast_tag) {
+      constexpr bool FAST = decltype(fast_tag)::value;
+      const int slot = k & 1;
+      scale_x(slot);
+      state_term(slot);
+      if constexpr (!FAST) decay_state(cur_clast);
+      update(slot);
+      scan(k + 1, rdt_next, cur_eout, slot ^ 1);
+      intra(slot, fast_tag);
+      fetch_scores(min(k + 1, nsub - 1));
+      store_y(k);
+      stage(slot ^ 1);
+    };
+    fetch_bcx(0);
+    const float rdt0 = fetch_dt(0);
+    rdt_next = fetch_dt(1);
+    fetch_scores(0);
+    stage(0);
+    scan(0, rdt0, 0.f, 0);
+    for (int k = 0; k < nsub; ++k) {
+      lds_barrier(); // B/C/x of sub-block k staged; slot ^ 1 no longer read
+      fetch_bcx(k + 1);
+      rdt_next2 = fetch_dt(k + 2);
+      const int fast = next_fast;
+      cur_clast = next_clast;
+      cur_eout = next_eout;
+      if (__builtin_expect(next_shift != 0, 0)) shift_state(next_shift);
+      if (fast)
+        body(k, std::true_type{});
+      else
+        body(k, std::false_type{});
+      rdt_next = rdt_next2;
+    }
+    e_final = cur_eout;
   }
 
   if (prm.final_state != nullptr && active) {
+    const float sc = hw_exp2(e_final);
 #pragma unroll
-    for (int k = 0; k < NT; ++k) *reinterpret_cast<f32x4 *>(prm.final_state + srow + 16 * k + 4 * lg) = hs[k] * pend;
+    for (int k = 0; k < NT; ++k) *reinterpret_cast<f32x4 *>(prm.final_state + srow + 16 * k + 4 * lg) = hs[k] * sc;
   }
 }
 

@@ -326,12 +326,33 @@ def decay_spans(si):
 @pytest.mark.parametrize("waves", [1, 4, 5])
 def test_rows_strong_decay(waves):
     """Sub-blocks whose decay span exceeds the separable range (per-element
-    path) next to ordinary ones, in the same workgroups."""
+    path, span > 178 log2 units) next to wide separable ones (90 < span <=
+    178, renormalised every sub-block) and ordinary ones, in the same
+    workgroups."""
     si = inputs.make_scan(2, 300, 8, 64, 2, 128, dtype=inputs.BF16, seed=31,
                           dt_range=(0.01, 2.0), init_std=0.3)
     spans = decay_spans(si)
-    assert (spans > 100).any() and (spans <= 100).any()
-    say("rows strong decay waves", waves, "slow share %.2f" % float((spans > 100).mean()))
+    assert (spans > 178).any() and ((spans > 90) & (spans <= 178)).any() and (spans <= 90).any()
+    say("rows strong decay waves", waves, "slow share %.2f" % float((spans > 178).mean()))
+    t = staging.scan_tensors(si, DEV)
+    out, fin = ssd.ssd_scan_fwd_rows(**t, waves=waves)
+    torch.cuda.synchronize()
+    yr, fr = oracle_scan(si)
+    check(staging.to_f64(out), yr, 2e-2, "y")
+    check(staging.to_f64(fin), fr, 2e-2, "final_state")
+
+
+@pytest.mark.parametrize("waves", [1, 4, 5])
+def test_rows_exponent_renormalisation(waves):
+    """32 sub-blocks per head with decay spans from 34 to 183 log2 units: the
+    running state exponent is renormalised many times, one head alternates
+    between the separable and the per-element path, and the final state
+    carries the accumulated exponent."""
+    si = inputs.make_scan(1, 2048, 4, 64, 1, 64, dtype=inputs.BF16, seed=37,
+                          dt_range=(0.03, 0.4), A_range=(4.0, 16.0), init_std=0.3)
+    spans = decay_spans(si)
+    assert (spans > 178).any() and ((spans > 90) & (spans <= 178)).mean() > 0.3
+    say("rows exponent renormalisation waves", waves)
     t = staging.scan_tensors(si, DEV)
     out, fin = ssd.ssd_scan_fwd_rows(**t, waves=waves)
     torch.cuda.synchronize()
