@@ -127,6 +127,10 @@ __device__ __forceinline__ float bload4(__amdgpu_buffer_rsrc_t r, uint32_t off) 
 }
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+// Store 16 bytes at byte offset `off` (dropped past the range).
+__device__ __forceinline__ void bstore16(__amdgpu_buffer_rsrc_t r, uint32_t off, float4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, (int)off, 0, 0);
+}
 // Store four outputs (converted to T) at byte offset `off`.
 template <typename T> __device__ __forceinline__ void bstore4(__amdgpu_buffer_rsrc_t r, uint32_t off, float a, float b, float c, float d);
 template <> __device__ __forceinline__ void bstore4<__bf16>(__amdgpu_buffer_rsrc_t r, uint32_t off, float a, float b, float c, float d) {

@@ -138,6 +138,11 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
   __shared__ __attribute__((aligned(16))) float sF0[2][W][64];   // xs scale (fast) / w (slow)
   __shared__ __attribute__((aligned(16))) float sF1[2][W][64];   // y scale 2^{c + e}
   __shared__ __attribute__((aligned(16))) float2 sQC[2][W][64];  // (q, c) for the slow path
+  // With more than four waves: y of a sub-block for all rows of the
+  // workgroup, [token][row], written by each wave and stored after the next
+  // barrier as whole row runs.
+  constexpr int YLD = 16 * W + 8;
+  __shared__ __attribute__((aligned(16))) __bf16 sY[2][(W > 4 ? 64 : 1) * YLD];
 
   const int H = prm.H, G = prm.G, L = prm.L, P = prm.P;
   const int nwg = gridDim.x, bid = blockIdx.x;
@@ -176,7 +181,6 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
   const __bf16 *Bbase = reinterpret_cast<const __bf16 *>(prm.B) + ((int64_t)ib * L * G + g) * N;
   const __bf16 *Cbase = reinterpret_cast<const __bf16 *>(prm.C) + ((int64_t)ib * L * G + g) * N;
   const __bf16 *Xbase = reinterpret_cast<const __bf16 *>(prm.x) + (int64_t)ib * L * rowX + (int64_t)h * P + p0;
-  __bf16 *Ybase = reinterpret_cast<__bf16 *>(prm.out) + (int64_t)ib * L * rowX + (int64_t)h * P + p0;
   const float *dtbase = prm.dt + (int64_t)ib * L * H + h;
   const int nsub = (L + 63) / 64;
   const __bf16 *Sbase = reinterpret_cast<const __bf16 *>(prm.scores) + (int64_t)bg * nsub * 4096;
@@ -220,7 +224,6 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
     const int u = f < 2 ? f : 2 + (f - 2) / 2, ks = f < 2 ? 0 : (f - 2) % 2;
     offS[f] = (uint32_t)(((16 * u + li) * 64 + 32 * ks + 8 * lg) * 2);
   }
-  const uint32_t offY = (uint32_t)((li * rowX + 4 * lg) * 2);
   const auto rsS = make_rsrc(Sbase, (uint32_t)nsub * 4096u * 2u);
 
   float4 rB[PPT], rC[PPT], rX[2];
@@ -400,7 +403,10 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
       }
     }
   };
-  // y = acc + D x; rows past the end (and idle waves) are dropped.
+  // y = acc + D x stored directly; rows past the end (and idle waves) are
+  // dropped.
+  const uint32_t offY = (uint32_t)((li * rowX + 4 * lg) * 2);
+  __bf16 *Ybase = reinterpret_cast<__bf16 *>(prm.out) + (int64_t)ib * L * rowX + (int64_t)h * P + p0;
   auto store_y = [&](int k) {
     const int t0 = 64 * k, nv = min(64, L - t0);
     const auto rsY = make_rsrc(Ybase + (int64_t)t0 * rowX,
@@ -411,6 +417,38 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
       bstore4<__bf16>(rsY, offY + (uint32_t)(16 * u * rowX * 2), yacc[u][0] + d_h * (float)xv[0],
                       yacc[u][1] + d_h * (float)xv[1], yacc[u][2] + d_h * (float)xv[2],
                       yacc[u][3] + d_h * (float)xv[3]);
+    }
+  };
+  // With more than four waves: y = acc + D x of this wave's rows into the
+  // workgroup tile of slot `slot`.
+  auto put_y = [&](int slot) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = 16 * u + li;
+      const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(&sX[w][t * 16 + 4 * lg]);
+      bf16x4 v;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = (__bf16)(yacc[u][r] + d_h * (float)xv[r]);
+      *reinterpret_cast<bf16x4 *>(&sY[slot][t * YLD + 16 * w + 4 * lg]) = v;
+    }
+  };
+  // Store the tile of sub-block k (after a barrier).  For one token the
+  // workgroup's rows are one contiguous run of y (rows are (head, p) pairs,
+  // head-major, and y is [.., token, head, p]), so the tile goes out as
+  // aligned 16-byte pieces, two per thread; pieces of rows past the group's
+  // last row are dropped, as are tokens past L.  k < 0 stores nothing.
+  const int rows_valid = min(16 * W, prm.rows_per_bg - wi * 16 * W);
+  __bf16 *Ywg = reinterpret_cast<__bf16 *>(prm.out) + (int64_t)ib * L * rowX + (int64_t)g * (H / G) * P + wi * 16 * W;
+  auto flush_y = [&](int k) {
+    const int t0 = 64 * k, nv = min(64, L - t0);
+    const auto rs = make_rsrc(Ywg + (int64_t)max(t0, 0) * rowX,
+                              k >= 0 ? (uint32_t)(((int64_t)(nv - 1) * rowX + rows_valid) * 2) : 0u);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q = tid + i * NTH, t = q / (2 * W), j = q % (2 * W);
+      const float4 v = *reinterpret_cast<const float4 *>(&sY[k & 1][t * YLD + 8 * j]);
+      const uint32_t off = 8 * j < rows_valid ? (uint32_t)((t * rowX + 8 * j) * 2) : 0xfffffff0u;
+      bstore16(rs, off, v);
     }
   };
 
@@ -463,10 +501,11 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
       state_term(slot);
       if constexpr (!FAST) decay_state(cur_clast);
       update(slot);
+      flush_y(k - 1);
       scan(k + 1, rdt_next, cur_eout, slot ^ 1);
       intra(slot, fast_tag);
       fetch_scores(min(k + 1, nsub - 1));
-      store_y(k);
+      put_y(slot);
       stage(slot ^ 1);
     };
     fetch_bcx(0);
@@ -489,6 +528,8 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
         body(k, std::false_type{});
       rdt_next = rdt_next2;
     }
+    lds_barrier(); // y tile of the last sub-block complete
+    flush_y(nsub - 1);
     e_final = cur_eout;
   }
 
