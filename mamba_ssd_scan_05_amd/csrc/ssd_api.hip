@@ -11,6 +11,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <string>
 
 #include "ssd.h"
@@ -319,18 +320,27 @@ struct Plan {
 };
 
 Plan choose_plan(const ScanShape &s, int dtype, int cus) {
-  const double t_sub_us = 2.0;  // one sub-block of one walk on one compute unit
-  const double state_rel = 0.7; // state-only walk relative to an output walk
+  // Cost model in microseconds, fitted to MI355X measurements of the three
+  // plans.  Walks that share a compute unit (more walks than units) cost
+  // about 0.78 x ceil(walks per unit) of a lone walk.
+  const bool bf16 = dtype == SSD_BF16;
+  const double t_full = bf16 ? 3.3 : 11.0;  // one 64-token sub-block of a whole-sequence walk
+  const double t_seg = bf16 ? 2.3 : 9.2;    // the same inside a segment walk
+  const double state_rel = 0.7;             // state-only walk relative to an output walk
   const double pass_bw = 4.0e12;
-  const double fixed_us = 10.0; // step-size kernel and extra launches
+  const double fixed_us = 10.0;             // step-size kernel and extra launches
+  auto share = [](double n) { return n <= 1.0 ? 1.0 : 0.78 * std::ceil(n); };
   const int64_t units = s.b * s.H;
   const int64_t nsub = (s.L + 63) / 64;
   Plan best{SSD_ALGO_FUSED, (int)std::min<int64_t>(s.L, 65536)};
-  double single_t = (double)((units + cus - 1) / cus) * nsub * t_sub_us;
+  double single_t = share((double)units / cus) * nsub * t_full;
   if (rows_supported(dtype, s.N)) {
+    // row walk: one workgroup per unit and round; a sub-block takes longer
+    // with more waves per workgroup and with more units busy
     const int W = rows_waves(s, cus);
     const int64_t nwg = s.b * s.G * (((s.H / s.G) * s.P + 16 * W - 1) / (16 * W));
-    const double rows_t = (double)((nwg + cus - 1) / cus) * nsub * (1.0 + 0.1 * W) * 0.5 + 5.0;
+    const double fill = std::min(1.0, (double)nwg / cus);
+    const double rows_t = (double)((nwg + cus - 1) / cus) * nsub * (2.0 + 0.15 * W) * (0.55 + 0.45 * fill) + 6.0;
     if (rows_t < single_t) {
       single_t = rows_t;
       best.algo = SSD_ALGO_ROWS;
@@ -341,8 +351,8 @@ Plan choose_plan(const ScanShape &s, int dtype, int cus) {
     const int64_t S = (s.L + seg - 1) / seg;
     if (S < 2) continue;
     const double sub = (double)(seg / 64);
-    const double walk = (double)((units * S + cus - 1) / cus) * sub * t_sub_us;
-    const double state = state_rel * (double)((units * (S - 1) + cus - 1) / cus) * sub * t_sub_us;
+    const double walk = share((double)(units * S) / cus) * sub * t_seg;
+    const double state = state_rel * share((double)(units * (S - 1)) / cus) * sub * t_seg;
     const double pass = 2.0 * units * S * s.P * s.N * 4.0 / pass_bw * 1e6;
     const double t = walk + state + pass + fixed_us;
     if (t < best_t) {
