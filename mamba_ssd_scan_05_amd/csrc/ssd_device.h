@@ -131,6 +131,16 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void bstore16(__amdgpu_buffer_rsrc_t r, uint32_t off, float4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, (int)off, 0, 0);
 }
+// Streaming variants for data touched once (the non-temporal cache-policy
+// bit of the buffer access): keeps a stream that is read once and written
+// once from displacing reused lines.
+constexpr int kNonTemporal = 2;
+__device__ __forceinline__ float4 bload16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kNonTemporal));
+}
+__device__ __forceinline__ void bstore16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off, float4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, (int)off, 0, kNonTemporal);
+}
 // Store four outputs (converted to T) at byte offset `off`.
 template <typename T> __device__ __forceinline__ void bstore4(__amdgpu_buffer_rsrc_t r, uint32_t off, float a, float b, float c, float d);
 template <> __device__ __forceinline__ void bstore4<__bf16>(__amdgpu_buffer_rsrc_t r, uint32_t off, float a, float b, float c, float d) {

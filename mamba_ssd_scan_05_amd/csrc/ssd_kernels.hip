@@ -480,7 +480,25 @@ state_pass_kernel(float *__restrict__ states, const float *__restrict__ seg_deca
 // Recurrent step ("From Transformer to Mamba", section 2.1, single-step
 // update): one workgroup per (batch, head); N/4 threads per state row, each
 // owning four consecutive entries; the readout sum over n is a shuffle
-// reduction inside those N/4 lanes.
+// reduction inside those N/4 lanes.  State and x go through range-checked
+// buffer accesses (rows past P read zeros, their stores are dropped), so a
+// batch of rows is loaded without branches and all its loads are in flight
+// together; the state, read once and written once, streams non-temporally.
+template <typename T> __device__ __forceinline__ float bload_elem(__amdgpu_buffer_rsrc_t r, uint32_t off);
+template <> __device__ __forceinline__ float bload_elem<__bf16>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return (float)__builtin_bit_cast(__bf16, (unsigned short)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0));
+}
+template <> __device__ __forceinline__ float bload_elem<float>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return bload4(r, off);
+}
+template <typename T> __device__ __forceinline__ void bstore_elem(__amdgpu_buffer_rsrc_t r, uint32_t off, float v);
+template <> __device__ __forceinline__ void bstore_elem<__bf16>(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (__bf16)v), r, (int)off, 0, 0);
+}
+template <> __device__ __forceinline__ void bstore_elem<float>(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), r, (int)off, 0, 0);
+}
+
 template <typename T, int N>
 __global__ void __launch_bounds__(256)
 step_kernel(float *__restrict__ state, const T *__restrict__ x,
@@ -504,20 +522,17 @@ step_kernel(float *__restrict__ state, const T *__restrict__ x,
     bv[q] = to_f(B[((int64_t)ib * G + g) * N + 4 * c4 + q]);
     cv[q] = to_f(C[((int64_t)ib * G + g) * N + 4 * c4 + q]);
   }
-  float4 *srow = reinterpret_cast<float4 *>(state + (int64_t)bh * P * N);
+  const auto rsS = make_rsrc(state + (int64_t)bh * P * N, (uint32_t)P * N * 4u);
+  const auto rsX = make_rsrc(x + (int64_t)bh * P, (uint32_t)P * (uint32_t)sizeof(T));
+  const auto rsO = make_rsrc(out + (int64_t)bh * P, (uint32_t)P * (uint32_t)sizeof(T));
   for (int p0 = 0; p0 < P; p0 += RPP * BATCH) {
     float4 s[BATCH];
     float xv[BATCH];
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
       const int p = p0 + u * RPP + rp;
-      if (p < P) {
-        s[u] = srow[(int64_t)p * TPR + c4];
-        xv[u] = to_f(x[(int64_t)bh * P + p]);
-      } else {
-        s[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-        xv[u] = 0.f;
-      }
+      s[u] = bload16_nt(rsS, (uint32_t)(p * TPR + c4) * 16u);
+      xv[u] = bload_elem<T>(rsX, (uint32_t)p * (uint32_t)sizeof(T));
     }
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
@@ -530,10 +545,9 @@ step_kernel(float *__restrict__ state, const T *__restrict__ x,
       float acc = s[u].x * cv[0] + s[u].y * cv[1] + s[u].z * cv[2] + s[u].w * cv[3];
 #pragma unroll
       for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-      if (p < P) {
-        srow[(int64_t)p * TPR + c4] = s[u];
-        if (c4 == 0) out[(int64_t)bh * P + p] = (T)(acc + d_h * xv[u]);
-      }
+      bstore16_nt(rsS, (uint32_t)(p * TPR + c4) * 16u, s[u]);
+      // one lane per row writes y; the others aim past the range
+      bstore_elem<T>(rsO, c4 == 0 ? (uint32_t)p * (uint32_t)sizeof(T) : 0xfffffff0u, acc + d_h * xv[u]);
     }
   }
 }
