@@ -10,6 +10,8 @@ float64, see that file for the page citations).  This module only builds it
 with gcc, loads it with ctypes and marshals numpy arrays:
 
 * ``scan(x, dt, dt_bias, A, B, C, D, init)`` -> ``(y, final_state)``
+* ``scan_gated(x, dt, dt_bias, A, B, C, z, D, init)`` -> ``(y * silu(z), final_state)``
+* ``gate(y, z)`` -> ``y * silu(z)``
 * ``step(state, x, delta, A, B, C, D)`` -> ``(y, new_state)``
 
 Every array argument is converted to contiguous float64 first; callers pass
@@ -56,6 +58,8 @@ class Oracle:
         lib.oracle_scan_f64.restype = None
         lib.oracle_step_f64.argtypes = [i64] * 5 + [vp] * 8
         lib.oracle_step_f64.restype = None
+        lib.oracle_gate_f64.argtypes = [i64, vp, vp, vp]
+        lib.oracle_gate_f64.restype = None
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
         self.lib = lib
@@ -71,6 +75,9 @@ class Oracle:
 
     def step(self, *args, **kwargs):
         return _step(self.lib, *args, **kwargs)
+
+    def gate(self, y, z):
+        return _gate(self.lib, y, z)
 
 
 def default() -> Oracle:
@@ -108,6 +115,17 @@ def scan(x, dt, dt_bias, A, B, C, D=None, init=None, want_final=True):
 def step(state, x, delta, A, B, C, D=None):
     """One fp64 recurrent step (see ``_step``)."""
     return default().step(state, x, delta, A, B, C, D)
+
+
+def gate(y, z):
+    """Elementwise y * silu(z) in fp64 (see ``_gate``)."""
+    return default().gate(y, z)
+
+
+def scan_gated(x, dt, dt_bias, A, B, C, z, D=None, init=None, want_final=True):
+    """The scan followed by the output gate: (y * silu(z), final_state)."""
+    y, fin = scan(x, dt, dt_bias, A, B, C, D, init, want_final)
+    return gate(y, z), fin
 
 
 def _scan(lib, x, dt, dt_bias, A, B, C, D=None, init=None, want_final=True):
@@ -153,3 +171,12 @@ def _step(lib, state, x, delta, A, B, C, D=None):
     lib.oracle_step_f64(b, H, P, G, N, _ptr(S), _ptr(x), _ptr(delta),
                         _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(y))
     return y, S
+
+
+def _gate(lib, y, z):
+    """out = y * silu(z), silu(v) = v / (1 + e^-v), elementwise, float64."""
+    y, z = _f64(y), _f64(z)
+    assert y.shape == z.shape
+    out = np.empty_like(y)
+    lib.oracle_gate_f64(y.size, _ptr(y), _ptr(z), _ptr(out))
+    return out

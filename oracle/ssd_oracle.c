@@ -24,6 +24,14 @@
  *   "From Transformer to Mamba" (jsqmd.com), section 2.1: the single-step
  *   shape ssm_step(x_t, h_prev, A, B, C) -> (y_t, h_t).
  *
+ *   Gated output (oracle_gate_f64): the Mamba block follows the selective
+ *   SSM with a gate before its output projection (Mamba paper-reading
+ *   notes, sxlin0.github.io, the section on the simplified block), and the
+ *   main branch is a Linear+SiLU ("Transformers are SSMs" summary,
+ *   gongshangzheng.github.io, section 2.3, the correspondence table).  Read
+ *   as out = y * silu(z), silu(v) = v / (1 + e^{-v}), applied elementwise to
+ *   the scan output y (after the D term).
+ *
  * Shapes and layouts (all arrays dense, row-major, float64):
  *   x      [b, L, H, P]      dt  [b, L, H]      dt_bias, A, D  [H]
  *   B, C   [b, L, G, N]      heads h use group g = floor(h * G / H)
@@ -136,4 +144,11 @@ void oracle_step_f64(int64_t b, int64_t H, int64_t P, int64_t G, int64_t N,
                          B + (ib * G + g) * N, C + (ib * G + g) * N,
                          D ? D[h] : 0.0, y + bh * P);
     }
+}
+
+/* Gated output: out[i] = y[i] * silu(z[i]), silu(v) = v / (1 + exp(-v)),
+ * elementwise over n values. */
+void oracle_gate_f64(int64_t n, const double *y, const double *z, double *out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = y[i] * (z[i] / (1.0 + exp(-z[i])));
 }

@@ -19,6 +19,10 @@ fixed independently of the oracle's own loop:
 * ``pin_step_scan``   T single steps equal one T-token scan
 * ``pin_exact_int``   integer data with A = 0, Delta = 1: exact integers
 * ``pin_linearity``, ``pin_groups``, ``pin_head_perm``, ``pin_decay_bound``
+* ``pin_gate_closed_forms`` the output gate y * silu(z) at z = 0, +-ln 3
+                      (logistic 3/4 and 1/4) and +-40
+* ``pin_gate_expit``  the gate against ``scipy.special.expit`` (a library
+                      logistic)
 
 Softplus here is ``numpy.logaddexp(0, z)`` (a library routine).
 """
@@ -294,6 +298,29 @@ def pin_decay_bound(o, seed=21):
         prev = np.abs(S)
 
 
+def pin_gate_closed_forms(o):
+    # silu(v) = v * logistic(v); logistic(ln 3) = 3/4, logistic(-ln 3) = 1/4,
+    # logistic(0) = 1/2 (so silu(0) = 0 exactly); for v = 40 the logistic is 1
+    # to double precision, for v = -40 it is e^v / (1 + e^v)
+    l3 = np.log(3.0)
+    y = np.array([2.5, -1.5, 3.0, 0.7, -2.0, 1.25])
+    z = np.array([0.0, 0.0, l3, -l3, 40.0, -40.0])
+    want = np.array([0.0, 0.0, 3.0 * 0.75 * l3, 0.7 * 0.25 * -l3, -2.0 * 40.0,
+                     1.25 * -40.0 * np.exp(-40.0) / (1.0 + np.exp(-40.0))])
+    got = o.gate(y, z)
+    assert got[0] == 0.0 and got[1] == 0.0, "silu(0) must be exactly 0"
+    _close(got, want, 1e-15, "gate closed forms")
+    assert abs(got[5] - want[5]) <= 1e-15 * abs(want[5]), "gate far negative tail"
+
+
+def pin_gate_expit(o, seed=22):
+    from scipy.special import expit
+    rng = np.random.default_rng(seed)
+    y = rng.standard_normal((3, 17, 5))
+    z = 4.0 * rng.standard_normal((3, 17, 5))
+    _close(o.gate(y, z), y * z * expit(z), 1e-15, "gate vs scipy expit")
+
+
 ALL_PINS = [pin_golden, pin_quadratic, pin_no_decay, pin_scalar_state, pin_split,
             pin_lti, pin_step_scan, pin_exact_int, pin_linearity, pin_groups,
-            pin_head_perm, pin_decay_bound]
+            pin_head_perm, pin_decay_bound, pin_gate_closed_forms, pin_gate_expit]

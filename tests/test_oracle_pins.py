@@ -46,6 +46,12 @@ MUTATIONS = [
      "step applies softplus"),
     ("memcpy(S, init + bh * P * N, (size_t)(P * N) * sizeof(double));",
      "memset(S, 0, (size_t)(P * N) * sizeof(double));", "init ignored"),
+    ("out[i] = y[i] * (z[i] / (1.0 + exp(-z[i])));", "out[i] = y[i] * (z[i] / (1.0 + exp(z[i])));",
+     "gate logistic sign"),
+    ("out[i] = y[i] * (z[i] / (1.0 + exp(-z[i])));", "out[i] = y[i] * (1.0 / (1.0 + exp(-z[i])));",
+     "gate sigmoid instead of silu"),
+    ("out[i] = y[i] * (z[i] / (1.0 + exp(-z[i])));", "out[i] = (z[i] / (1.0 + exp(-z[i])));",
+     "gate drops y"),
 ]
 
 
