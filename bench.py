@@ -136,6 +136,8 @@ def main():
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-gated", action="store_true",
+                    help="skip the timing of the gated scan (out = y * silu(z))")
     ap.add_argument("--no-alt", action="store_true", help="skip timing the other algorithm")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 1 GiB device copy (calibrates HBM byte counters)")
@@ -241,6 +243,30 @@ def main():
             torch.cuda.synchronize()
             alts[name_a] = e0.elapsed_time(e1) / 10
         extra["algorithms_ms"] = alts
+    if not args.no_gated:
+        # the scan with the output gate fused (out = y * silu(z)): the same
+        # automatic plan, z read once more (the bytes of x)
+        z = staging.tensor(inputs.make_gate(si), si.dtype, dev)
+
+        def run_gated():
+            ssd.ssd_scan_fwd_gated(**t, z=z, out=out, final_state=fin, chunk=Q)
+        for _ in range(3):
+            run_gated()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            run_gated()
+        e1.record()
+        torch.cuda.synchronize()
+        g_ms = e0.elapsed_time(e1) / 20
+        g_bytes = nbytes + b * L * H * P * ELEM[si.dtype]
+        extra["gated"] = {"ms_per_step": g_ms, "tokens_per_s": tokens / (g_ms * 1e-3),
+                          "algorithmic_bytes": g_bytes,
+                          "achieved_GBs": g_bytes / (g_ms * 1e-3) / 1e9,
+                          "frac": g_bytes / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                          "ungated_ms_per_step": kern_ms}
+        del z
     if args.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

@@ -134,6 +134,35 @@ int ssd_scan_fwd_algo(const ssd_tensor *x, const ssd_tensor *dt,
                       int algo, void *stream);
 
 /*
+ * ssd_scan_fwd_gated -- the scan with the block's output gate fused into its
+ * output step.  The Mamba block follows the selective SSM with a gate before
+ * the output projection (Mamba paper-reading notes, sxlin0.github.io, the
+ * section on the simplified block), and its main branch is a Linear+SiLU
+ * ("Transformers are SSMs" summary, gongshangzheng.github.io, section 2.3,
+ * the correspondence table); read as
+ *
+ *     out_t = y_t * silu(z_t),   silu(v) = v / (1 + e^{-v})
+ *
+ * elementwise, with y_t exactly as ssd_scan_fwd computes it (D term
+ * included).  final_state is the same as ssd_scan_fwd's.
+ *
+ *   z   [b, L, H, P]  dtype of x, dense, 16-byte aligned     required
+ *
+ * Every other argument as ssd_scan_fwd_algo (any algorithm, any supported
+ * size).  out and final_state may not overlap z.  Arithmetic: y is formed
+ * as in ssd_scan_fwd and the gate in fp32; out is rounded once to the dtype
+ * of x, except that SSD_ALGO_ROWS with more than four waves per workgroup
+ * rounds y to bf16 before gating (a second rounding of the same size).
+ */
+int ssd_scan_fwd_gated(const ssd_tensor *x, const ssd_tensor *dt,
+                       const ssd_tensor *dt_bias, const ssd_tensor *A,
+                       const ssd_tensor *B, const ssd_tensor *C,
+                       const ssd_tensor *D, const ssd_tensor *z,
+                       const ssd_tensor *init_state, ssd_tensor *out,
+                       ssd_tensor *final_state, int chunk, int algo,
+                       void *stream);
+
+/*
  * ssd_scan_fwd_rows -- ssd_scan_fwd with SSD_ALGO_ROWS and an explicit
  * workgroup size: `waves` in 1..8 waves per workgroup (16 state rows each),
  * 0 = the size SSD_ALGO_AUTO would take.  For tuning and tests; the result

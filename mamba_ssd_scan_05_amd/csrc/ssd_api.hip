@@ -156,8 +156,8 @@ int hip_fail(hipError_t e, const char *what) {
 
 int run_fused(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bias,
               const ssd_tensor *A, const ssd_tensor *B, const ssd_tensor *C,
-              const ssd_tensor *D, const ssd_tensor *init, ssd_tensor *out, ssd_tensor *fin,
-              const ScanShape &s, hipStream_t st) {
+              const ssd_tensor *D, const ssd_tensor *z, const ssd_tensor *init, ssd_tensor *out,
+              ssd_tensor *fin, const ScanShape &s, hipStream_t st) {
   ssd::WalkParams p{};
   p.x = x->data; p.dt = (const float *)dt->data;
   p.dt_bias = dt_bias ? (const float *)dt_bias->data : nullptr;
@@ -165,6 +165,7 @@ int run_fused(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bi
   p.D = D ? (const float *)D->data : nullptr;
   p.init = init ? (const float *)init->data : nullptr;
   p.out = out->data;
+  p.z = z ? z->data : nullptr;
   p.state_out = fin ? (float *)fin->data : nullptr;
   p.b = (int)s.b; p.L = (int)s.L; p.H = (int)s.H; p.G = (int)s.G;
   p.seg_len = (int)s.L; p.nseg = 1;
@@ -174,7 +175,7 @@ int run_fused(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bi
 
 int run_chunked(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bias,
                 const ssd_tensor *A, const ssd_tensor *B, const ssd_tensor *C,
-                const ssd_tensor *D, const ssd_tensor *init, ssd_tensor *out,
+                const ssd_tensor *D, const ssd_tensor *z, const ssd_tensor *init, ssd_tensor *out,
                 ssd_tensor *fin, const ScanShape &s, int chunk, hipStream_t st) {
   const int64_t nc = (s.L + chunk - 1) / chunk;
   const int64_t PN = s.P * s.N;
@@ -221,7 +222,7 @@ int run_chunked(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_
 
     // 4. outputs of every chunk from its entering state; the last chunk's
     //    walk leaves the final state
-    p.init = states; p.out = out->data; p.state_out = nullptr; p.seg_decay = nullptr;
+    p.init = states; p.out = out->data; p.z = z ? z->data : nullptr; p.state_out = nullptr; p.seg_decay = nullptr;
     p.final_state = fin ? (float *)fin->data : nullptr;
     e = ssd::launch_walk(x->dtype, (int)s.P, (int)s.N, ssd::kWalkChunkOut, p, st);
     if (e != hipSuccess) { status = hip_fail(e, "chunk-output launch"); break; }
@@ -256,8 +257,8 @@ int rows_waves(const ScanShape &s, int cus) {
 
 int run_rows(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bias,
              const ssd_tensor *A, const ssd_tensor *B, const ssd_tensor *C, const ssd_tensor *D,
-             const ssd_tensor *init, ssd_tensor *out, ssd_tensor *fin, const ScanShape &s,
-             int W, hipStream_t st) {
+             const ssd_tensor *z, const ssd_tensor *init, ssd_tensor *out, ssd_tensor *fin,
+             const ScanShape &s, int W, hipStream_t st) {
   const int64_t nsub = (s.L + 63) / 64;
   const size_t bytes = (size_t)(s.b * s.G * nsub) * 64 * 64 * 2;
   void *ws = nullptr;
@@ -278,6 +279,7 @@ int run_rows(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bia
     p.scores = ws;
     p.init = init ? (const float *)init->data : nullptr;
     p.out = out->data;
+    p.z = z ? z->data : nullptr;
     p.final_state = fin ? (float *)fin->data : nullptr;
     p.b = (int)s.b; p.L = (int)s.L; p.H = (int)s.H; p.G = (int)s.G; p.P = (int)s.P;
     p.rows_per_bg = (int)((s.H / s.G) * s.P);
@@ -363,17 +365,11 @@ Plan choose_plan(const ScanShape &s, int dtype, int cus) {
   return best;
 }
 
-} // namespace
-
-extern "C" {
-
-int ssd_scan_fwd_algo(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bias,
-                      const ssd_tensor *A, const ssd_tensor *B, const ssd_tensor *C,
-                      const ssd_tensor *D, const ssd_tensor *init_state, ssd_tensor *out,
-                      ssd_tensor *final_state, int chunk, int algo, void *stream) {
-  g_last_error.clear();
-  ScanShape s;
-  SSD_CHECK(validate_scan(x, dt, dt_bias, A, B, C, D, init_state, out, final_state, chunk, &s));
+int scan_dispatch(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bias,
+                  const ssd_tensor *A, const ssd_tensor *B, const ssd_tensor *C,
+                  const ssd_tensor *D, const ssd_tensor *z, const ssd_tensor *init_state,
+                  ssd_tensor *out, ssd_tensor *final_state, const ScanShape &s, int chunk, int algo,
+                  void *stream) {
   if (algo != SSD_ALGO_AUTO && algo != SSD_ALGO_FUSED && algo != SSD_ALGO_CHUNKED &&
       algo != SSD_ALGO_ROWS)
     return fail(SSD_ERR_UNSUPPORTED, "unknown algorithm %d", algo);
@@ -387,10 +383,49 @@ int ssd_scan_fwd_algo(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tenso
   }
   hipStream_t st = (hipStream_t)stream;
   if (algo == SSD_ALGO_ROWS)
-    return run_rows(x, dt, dt_bias, A, B, C, D, init_state, out, final_state, s, rows_waves(s, cus), st);
+    return run_rows(x, dt, dt_bias, A, B, C, D, z, init_state, out, final_state, s, rows_waves(s, cus), st);
   if (algo == SSD_ALGO_FUSED)
-    return run_fused(x, dt, dt_bias, A, B, C, D, init_state, out, final_state, s, st);
-  return run_chunked(x, dt, dt_bias, A, B, C, D, init_state, out, final_state, s, chunk, st);
+    return run_fused(x, dt, dt_bias, A, B, C, D, z, init_state, out, final_state, s, st);
+  return run_chunked(x, dt, dt_bias, A, B, C, D, z, init_state, out, final_state, s, chunk, st);
+}
+
+// The gate input z: same shape and element type as x, dense; neither out
+// nor final_state may overlap it.
+int validate_gate(const ssd_tensor *z, const ssd_tensor *x, const ssd_tensor *out,
+                  const ssd_tensor *fin, const ScanShape &s) {
+  const int64_t sx[4] = {s.b, s.L, s.H, s.P};
+  SSD_CHECK(check_tensor(z, "z", x->dtype, 4, sx));
+  const Range rz = range_of(z);
+  if (overlap(range_of(out), rz)) return fail(SSD_ERR_ALIAS, "out overlaps z");
+  if (overlap(range_of(fin), rz)) return fail(SSD_ERR_ALIAS, "final_state overlaps z");
+  return SSD_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+int ssd_scan_fwd_algo(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bias,
+                      const ssd_tensor *A, const ssd_tensor *B, const ssd_tensor *C,
+                      const ssd_tensor *D, const ssd_tensor *init_state, ssd_tensor *out,
+                      ssd_tensor *final_state, int chunk, int algo, void *stream) {
+  g_last_error.clear();
+  ScanShape s;
+  SSD_CHECK(validate_scan(x, dt, dt_bias, A, B, C, D, init_state, out, final_state, chunk, &s));
+  return scan_dispatch(x, dt, dt_bias, A, B, C, D, nullptr, init_state, out, final_state, s, chunk, algo,
+                       stream);
+}
+
+int ssd_scan_fwd_gated(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bias,
+                       const ssd_tensor *A, const ssd_tensor *B, const ssd_tensor *C,
+                       const ssd_tensor *D, const ssd_tensor *z, const ssd_tensor *init_state,
+                       ssd_tensor *out, ssd_tensor *final_state, int chunk, int algo, void *stream) {
+  g_last_error.clear();
+  ScanShape s;
+  SSD_CHECK(validate_scan(x, dt, dt_bias, A, B, C, D, init_state, out, final_state, chunk, &s));
+  if (!z) return fail(SSD_ERR_NULL, "z: descriptor is NULL");
+  SSD_CHECK(validate_gate(z, x, out, final_state, s));
+  return scan_dispatch(x, dt, dt_bias, A, B, C, D, z, init_state, out, final_state, s, chunk, algo, stream);
 }
 
 int ssd_scan_fwd(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bias,
@@ -412,7 +447,7 @@ int ssd_scan_fwd_rows(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tenso
     return fail(SSD_ERR_UNSUPPORTED, "row-sliced walk needs bf16 inputs and N in {32,64,128}");
   if (waves < 0 || waves > 8) return fail(SSD_ERR_UNSUPPORTED, "waves=%d not in 0..8", waves);
   const int W = waves ? waves : rows_waves(s, device_cus());
-  return run_rows(x, dt, dt_bias, A, B, C, D, init_state, out, final_state, s, W,
+  return run_rows(x, dt, dt_bias, A, B, C, D, nullptr, init_state, out, final_state, s, W,
                   (hipStream_t)stream);
 }
 

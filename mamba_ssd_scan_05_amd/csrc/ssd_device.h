@@ -103,6 +103,12 @@ constexpr float kLn2 = 0.6931471805599453f;
 __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// silu(v) = v / (1 + e^{-v}); for v far below 0 the exponential is +inf
+// and the result a signed zero.
+__device__ __forceinline__ float silu_f(float v) {
+  return v * __builtin_amdgcn_rcpf(1.f + hw_exp2(-v * kLog2e));
+}
+
 // softplus(z) = log(1 + e^z) = max(z, 0) + log1p(u), u = e^{-|z|} in (0, 1].
 // log1p(u) = log(w) * u / (w - 1) with w = fl(1 + u) cancels the rounding of
 // 1 + u (the classic accurate-log1p identity); w == 1 means log1p(u) = u to
@@ -140,6 +146,16 @@ __device__ __forceinline__ float4 bload16_nt(__amdgpu_buffer_rsrc_t r, uint32_t 
 }
 __device__ __forceinline__ void bstore16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off, float4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, (int)off, 0, kNonTemporal);
+}
+// Load four consecutive elements of type T at byte offset `off` as floats
+// (zeros past the range).
+template <typename T> __device__ __forceinline__ float4 bload4x(__amdgpu_buffer_rsrc_t r, uint32_t off);
+template <> __device__ __forceinline__ float4 bload4x<__bf16>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const bf16x4 v = __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+  return make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
+}
+template <> __device__ __forceinline__ float4 bload4x<float>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return bload16(r, off);
 }
 // Store four outputs (converted to T) at byte offset `off`.
 template <typename T> __device__ __forceinline__ void bstore4(__amdgpu_buffer_rsrc_t r, uint32_t off, float a, float b, float c, float d);

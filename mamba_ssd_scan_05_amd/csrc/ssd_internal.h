@@ -25,6 +25,7 @@ struct WalkParams {
   const float *init;    // state entering each segment, [(b*H + h)*nseg + seg][P][N]
                         // or null for zero
   void *out;            // [b, L, H, P] or null (state-only walk)
+  const void *z;        // [b, L, H, P] gate input (out = y * silu(z)) or null
   float *state_out;     // state leaving each segment, same indexing as init,
                         // or null
   float *final_state;   // [b, H, P, N]: state leaving the last segment, or null
@@ -59,6 +60,7 @@ struct RWalkParams {
   const void *scores;   // [b, G, ceil(L/64), 64, 64] bf16 from launch_scores
   const float *init;    // [b, H, P, N] or null
   void *out;            // [b, L, H, P] bf16
+  const void *z;        // [b, L, H, P] bf16 gate input (out = y * silu(z)) or null
   float *final_state;   // [b, H, P, N] or null
   int b, L, H, G, P, rows_per_bg, wg_per_bg;
 };

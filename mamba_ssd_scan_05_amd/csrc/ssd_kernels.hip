@@ -167,6 +167,9 @@ walk_kernel(const WalkParams prm) {
   const T *__restrict__ Cbase = reinterpret_cast<const T *>(prm.C) + ((int64_t)ib * L * G + g) * N;
   const T *__restrict__ Xbase = reinterpret_cast<const T *>(prm.x) + (int64_t)ib * L * rowX + (int64_t)h * P;
   T *__restrict__ Ybase = reinterpret_cast<T *>(prm.out) + (int64_t)ib * L * rowX + (int64_t)h * P;
+  // gate input of the output (out = y * silu(z)), or null
+  const T *__restrict__ Zbase = prm.z ? reinterpret_cast<const T *>(prm.z) + (int64_t)ib * L * rowX + (int64_t)h * P
+                                      : nullptr;
   const float *__restrict__ dtbase = (MODE == kWalkFull) ? prm.dt + (int64_t)ib * L * H + h
                                                          : prm.dt + (int64_t)(ib * H + h) * L;
   const int64_t dtstride = (MODE == kWalkFull) ? H : 1;
@@ -348,6 +351,8 @@ walk_kernel(const WalkParams prm) {
       // ---- intra-block term: Y^T[p][i] += sum_{j<=i} X^T[p][j] M[i][j] -----
       //      then store y (rows past the segment end fall outside the range)
       const auto rsY = make_rsrc(Ybase + (int64_t)t0 * rowX, (uint32_t)(((int64_t)(nv - 1) * rowX + P) * ES));
+      const auto rsZ = make_rsrc(Zbase ? Zbase + (int64_t)t0 * rowX : Ybase,
+                                 Zbase ? (uint32_t)(((int64_t)(nv - 1) * rowX + P) * ES) : 0u);
 #pragma unroll
       for (int u = 0; u < NIT; ++u) {
         const int it = NIT * hv + u;
@@ -360,7 +365,15 @@ walk_kernel(const WalkParams prm) {
             yacc[u] = mma(xf[ks], ld4x2(&sM[i * LDM + 32 * ks + 4 * lg], &sM[i * LDM + 32 * ks + 16 + 4 * lg]),
                           yacc[u]);
         }
-        bstore4<T>(rsY, offY + (uint32_t)(16 * it * rowX * ES), yacc[u][0], yacc[u][1], yacc[u][2], yacc[u][3]);
+        f32x4 yv = yacc[u];
+        if (Zbase) {
+          const float4 zz = bload4x<T>(rsZ, offY + (uint32_t)(16 * it * rowX * ES));
+          yv[0] *= silu_f(zz.x);
+          yv[1] *= silu_f(zz.y);
+          yv[2] *= silu_f(zz.z);
+          yv[3] *= silu_f(zz.w);
+        }
+        bstore4<T>(rsY, offY + (uint32_t)(16 * it * rowX * ES), yv[0], yv[1], yv[2], yv[3]);
       }
     }
 

@@ -119,7 +119,8 @@ __global__ void __launch_bounds__(256) scores_kernel(const __bf16 *__restrict__ 
 // This file is built with MFMA accumulators in ordinary VGPRs: with
 // accumulator registers the compiler parks the state tile there and copies
 // it to VGPRs and back every sub-block.
-template <int N, int W>
+// GATED: out = y * silu(z) with z read next to y.
+template <int N, int W, bool GATED>
 __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
   constexpr int NTH = W * 64;
   constexpr int NT = N / 16;            // n-tiles of the state
@@ -407,6 +408,16 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
   // dropped.
   const uint32_t offY = (uint32_t)((li * rowX + 4 * lg) * 2);
   __bf16 *Ybase = reinterpret_cast<__bf16 *>(prm.out) + (int64_t)ib * L * rowX + (int64_t)h * P + p0;
+  // Gate input of this wave's y values of a sub-block (same positions).
+  const __bf16 *Zbase = GATED ? reinterpret_cast<const __bf16 *>(prm.z) + (int64_t)ib * L * rowX + (int64_t)h * P + p0
+                              : nullptr;
+  float4 zq[4];
+  auto fetch_z = [&](int k) {
+    const int t0 = 64 * k, nv = min(64, L - t0);
+    const auto rsZ = make_rsrc(Zbase + (int64_t)t0 * rowX, (uint32_t)(((int64_t)(nv - 1) * rowX + 16) * 2));
+#pragma unroll
+    for (int u = 0; u < 4; ++u) zq[u] = bload4x<__bf16>(rsZ, offY + (uint32_t)(16 * u * rowX * 2));
+  };
   auto store_y = [&](int k) {
     const int t0 = 64 * k, nv = min(64, L - t0);
     const auto rsY = make_rsrc(Ybase + (int64_t)t0 * rowX,
@@ -414,9 +425,16 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(&sX[w][(16 * u + li) * 16 + 4 * lg]);
-      bstore4<__bf16>(rsY, offY + (uint32_t)(16 * u * rowX * 2), yacc[u][0] + d_h * (float)xv[0],
-                      yacc[u][1] + d_h * (float)xv[1], yacc[u][2] + d_h * (float)xv[2],
-                      yacc[u][3] + d_h * (float)xv[3]);
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = yacc[u][r] + d_h * (float)xv[r];
+      if constexpr (GATED) {
+        v[0] *= silu_f(zq[u].x);
+        v[1] *= silu_f(zq[u].y);
+        v[2] *= silu_f(zq[u].z);
+        v[3] *= silu_f(zq[u].w);
+      }
+      bstore4<__bf16>(rsY, offY + (uint32_t)(16 * u * rowX * 2), v[0], v[1], v[2], v[3]);
     }
   };
   // With more than four waves: y = acc + D x of this wave's rows into the
@@ -439,6 +457,22 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
   // last row are dropped, as are tokens past L.  k < 0 stores nothing.
   const int rows_valid = min(16 * W, prm.rows_per_bg - wi * 16 * W);
   __bf16 *Ywg = reinterpret_cast<__bf16 *>(prm.out) + (int64_t)ib * L * rowX + (int64_t)g * (H / G) * P + wi * 16 * W;
+  // Gate input pieces matching the pieces flush_y stores for sub-block k
+  // (zeros for k < 0).
+  const __bf16 *Zwg = GATED ? reinterpret_cast<const __bf16 *>(prm.z) + (int64_t)ib * L * rowX +
+                                  (int64_t)g * (H / G) * P + wi * 16 * W
+                            : nullptr;
+  float4 zpc[2];
+  auto fetch_zpieces = [&](int k) {
+    const int t0 = 64 * k, nv = min(64, L - t0);
+    const auto rs = make_rsrc(Zwg + (int64_t)max(t0, 0) * rowX,
+                              k >= 0 ? (uint32_t)(((int64_t)(nv - 1) * rowX + rows_valid) * 2) : 0u);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q = tid + i * NTH, t = q / (2 * W), j = q % (2 * W);
+      zpc[i] = bload16(rs, 8 * j < rows_valid ? (uint32_t)((t * rowX + 8 * j) * 2) : 0xfffffff0u);
+    }
+  };
   auto flush_y = [&](int k) {
     const int t0 = 64 * k, nv = min(64, L - t0);
     const auto rs = make_rsrc(Ywg + (int64_t)max(t0, 0) * rowX,
@@ -446,7 +480,14 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int q = tid + i * NTH, t = q / (2 * W), j = q % (2 * W);
-      const float4 v = *reinterpret_cast<const float4 *>(&sY[k & 1][t * YLD + 8 * j]);
+      float4 v = *reinterpret_cast<const float4 *>(&sY[k & 1][t * YLD + 8 * j]);
+      if constexpr (GATED) {
+        const bf16x8 yb = __builtin_bit_cast(bf16x8, v), zb = __builtin_bit_cast(bf16x8, zpc[i]);
+        bf16x8 ob;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ob[e] = (__bf16)((float)yb[e] * silu_f((float)zb[e]));
+        v = __builtin_bit_cast(float4, ob);
+      }
       const uint32_t off = 8 * j < rows_valid ? (uint32_t)((t * rowX + 8 * j) * 2) : 0xfffffff0u;
       bstore16(rs, off, v);
     }
@@ -471,6 +512,7 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
       const int fast = next_fast;
       rdt = fetch_dt(k + 1);
       fetch_bcx(k + 1);
+      if constexpr (GATED) fetch_z(k);
       shift_state(next_shift);
       state_term(slot);
       scale_x(slot);
@@ -518,6 +560,7 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
       lds_barrier(); // B/C/x of sub-block k staged; slot ^ 1 no longer read
       fetch_bcx(k + 1);
       rdt_next2 = fetch_dt(k + 2);
+      if constexpr (GATED) fetch_zpieces(k - 1);
       const int fast = next_fast;
       cur_clast = next_clast;
       cur_eout = next_eout;
@@ -528,6 +571,7 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
         body(k, std::false_type{});
       rdt_next = rdt_next2;
     }
+    if constexpr (GATED) fetch_zpieces(nsub - 1);
     lds_barrier(); // y tile of the last sub-block complete
     flush_y(nsub - 1);
     e_final = cur_eout;
@@ -542,7 +586,10 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
 
 template <int N, int W>
 hipError_t launch_rwalk_t(const RWalkParams &p, int nwg, hipStream_t st) {
-  hipLaunchKernelGGL((rwalk_kernel<N, W>), dim3(nwg), dim3(W * 64), 0, st, p);
+  if (p.z)
+    hipLaunchKernelGGL((rwalk_kernel<N, W, true>), dim3(nwg), dim3(W * 64), 0, st, p);
+  else
+    hipLaunchKernelGGL((rwalk_kernel<N, W, false>), dim3(nwg), dim3(W * 64), 0, st, p);
   return hipGetLastError();
 }
 

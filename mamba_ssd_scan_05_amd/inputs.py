@@ -121,6 +121,14 @@ def make_scan(b, L, H, P, G, N, *, dtype=BF16, chunk=256, seed=0,
         init=None if init is None else init.astype(np.float32))
 
 
+def make_gate(si: ScanInputs, seed: int = 100, scale: float = 1.5) -> np.ndarray:
+    """Gate input z for a scan's output gate: the shape of x, drawn from
+    N(0, scale^2) (so both tails of silu are used), stored in the scan's
+    dtype (bf16 as uint16 bits)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return _store(scale * rng.standard_normal(si.x.shape), si.dtype)
+
+
 @dataclasses.dataclass
 class StepInputs:
     """Host arrays for T consecutive recurrent steps (bf16 as uint16 bits)."""

@@ -53,6 +53,8 @@ def lib():
         L.ssd_scan_fwd_algo.restype = ctypes.c_int
         L.ssd_scan_fwd_rows.argtypes = [P] * 10 + [ctypes.c_int, ctypes.c_void_p]
         L.ssd_scan_fwd_rows.restype = ctypes.c_int
+        L.ssd_scan_fwd_gated.argtypes = [P] * 11 + [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        L.ssd_scan_fwd_gated.restype = ctypes.c_int
         L.ssd_step.argtypes = [P] * 8 + [ctypes.c_void_p]
         L.ssd_step.restype = ctypes.c_int
         L.ssd_status_string.argtypes = [ctypes.c_int]
@@ -117,6 +119,25 @@ def ssd_scan_fwd(x, dt, dt_bias, A, B, C, D=None, init_state=None, out=None,
     status = lib().ssd_scan_fwd_algo(
         describe(x), describe(dt), describe(dt_bias), describe(A), describe(B), describe(C),
         describe(D), describe(init_state), describe(out), describe(final_state),
+        int(chunk), int(algo), st)
+    _check(status)
+    return out, final_state
+
+
+def ssd_scan_fwd_gated(x, dt, dt_bias, A, B, C, z, D=None, init_state=None, out=None,
+                       final_state=None, chunk: int = 256, stream=None,
+                       algo: int = SSD_ALGO_AUTO, return_final_state: bool = True):
+    """Forward scan with the output gate: out = y * silu(z); returns
+    (out, final_state or None)."""
+    if out is None:
+        out = torch.empty_like(x)
+    if final_state is None and return_final_state:
+        final_state = torch.empty((x.shape[0], x.shape[2], x.shape[3], B.shape[3]),
+                                  dtype=torch.float32, device=x.device)
+    st = _stream(stream, x)
+    status = lib().ssd_scan_fwd_gated(
+        describe(x), describe(dt), describe(dt_bias), describe(A), describe(B), describe(C),
+        describe(D), describe(z), describe(init_state), describe(out), describe(final_state),
         int(chunk), int(algo), st)
     _check(status)
     return out, final_state

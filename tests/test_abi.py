@@ -27,8 +27,8 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(ssd):
     names = declared_functions()
-    assert {"ssd_scan_fwd", "ssd_step", "ssd_scan_fwd_algo", "ssd_scan_fwd_rows", "ssd_scan_plan",
-            "ssd_status_string", "ssd_last_error", "ssd_version"} <= set(names)
+    assert {"ssd_scan_fwd", "ssd_step", "ssd_scan_fwd_algo", "ssd_scan_fwd_rows", "ssd_scan_fwd_gated",
+            "ssd_scan_plan", "ssd_status_string", "ssd_last_error", "ssd_version"} <= set(names)
     raw = ctypes.CDLL(ssd.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -211,3 +211,24 @@ def test_rows_rejections(ssd):
     assert call(a, 1) == 2
     assert _call_scan(ssd, _scan_args(dtype=torch.float32), algo=3)[0] == 5
     assert _call_scan(ssd, _scan_args(), algo=4)[0] == 5
+
+
+def test_gated_rejections(ssd):
+    """The gated scan validates like the scan, and z: present, the shape and
+    element type of x, dense, not overlapping out."""
+    lib, d = ssd.lib(), ssd.describe
+
+    def call(a, z, algo=0):
+        return lib.ssd_scan_fwd_gated(d(a["x"]), d(a["dt"]), d(a["dt_bias"]), d(a["A"]), d(a["B"]),
+                                      d(a["C"]), d(a["D"]), d(z), d(a["init_state"]), d(a["out"]),
+                                      d(a["final_state"]), 64, algo, None)
+    a = _scan_args()
+    assert call(a, None) == 1
+    assert call(a, torch.zeros(1, 99, 4, 16, dtype=torch.bfloat16)) == 2
+    assert call(a, torch.zeros(1, 100, 4, 16)) == 3
+    assert call(a, torch.zeros(1, 4, 100, 16, dtype=torch.bfloat16).transpose(1, 2)) == 4
+    assert call(a, a["out"]) == 6
+    assert call(a, torch.zeros(1, 100, 4, 16, dtype=torch.bfloat16), algo=4) == 5
+    b = _scan_args()
+    b["x"] = None
+    assert call(b, torch.zeros(1, 100, 4, 16, dtype=torch.bfloat16)) == 1

@@ -388,3 +388,81 @@ def test_rows_waves_agree():
         else:
             assert torch.equal(out.view(torch.int16), ref[0].view(torch.int16)), waves
             assert torch.equal(fin, ref[1]), waves
+
+
+# ---------------------------------------------------------------------------
+# the gated output out = y * silu(z), every algorithm
+
+def gated_case(si, seed):
+    z = inputs.make_gate(si, seed=seed)
+    return z, inputs.to_f64(z, si.dtype)
+
+
+def oracle_scan_gated(si, zf):
+    f = si.f64()
+    return oracle.scan_gated(f["x"], f["dt"], f["dt_bias"], f["A"], f["B"], f["C"], zf, f["D"], f["init"])
+
+
+GATED = [
+    # dtype, b, L, H, P, G, N, chunk
+    (inputs.F32, 1, 300, 2, 64, 2, 128, 128),
+    (inputs.F32, 2, 200, 4, 16, 1, 16, 64),
+    (inputs.BF16, 2, 517, 4, 64, 1, 128, 256),
+    (inputs.BF16, 1, 333, 4, 32, 4, 64, 128),
+]
+
+
+@pytest.mark.parametrize("algo", [ssd.SSD_ALGO_FUSED, ssd.SSD_ALGO_CHUNKED, ssd.SSD_ALGO_ROWS])
+@pytest.mark.parametrize("case", GATED, ids=lambda c: "%s-b%dL%dH%dP%dG%dN%dQ%d" % c)
+def test_gated_small(case, algo):
+    dtype, b, L, H, P, G, N, chunk = case
+    if algo == ssd.SSD_ALGO_ROWS and (dtype != inputs.BF16 or N == 16):
+        pytest.skip("the row-sliced walk takes bf16 inputs and N >= 32")
+    si = inputs.make_scan(b, L, H, P, G, N, dtype=dtype, chunk=chunk, seed=L + P + N + 7,
+                          init_std=0.5)
+    z, zf = gated_case(si, seed=L + 3)
+    say("gated small", case, "algo", algo)
+    t = staging.scan_tensors(si, DEV)
+    out, fin = ssd.ssd_scan_fwd_gated(**t, z=staging.tensor(z, dtype, DEV), chunk=chunk, algo=algo)
+    torch.cuda.synchronize()
+    yr, fr = oracle_scan_gated(si, zf)
+    check(staging.to_f64(out), yr, TOL[dtype], "gated y")
+    check(staging.to_f64(fin), fr, TOL[dtype], "final_state")
+
+
+# Shapes whose automatic workgroup size on a 256-unit MI355X is 1, 5 and 8
+# waves: the direct-store schedule and the staged-store schedule.
+GATED_ROWS = [
+    (3, 129, 5, 64, 5, 32),     # 1 wave per workgroup, idle rows, ragged tail
+    (4, 300, 80, 64, 1, 128),   # 5 waves
+    (4, 200, 128, 64, 1, 128),  # 8 waves
+]
+
+
+@pytest.mark.parametrize("case", GATED_ROWS, ids=lambda c: "b%dL%dH%dP%dG%dN%d" % c)
+def test_gated_rows_schedules(case):
+    b, L, H, P, G, N = case
+    si = inputs.make_scan(b, L, H, P, G, N, dtype=inputs.BF16, chunk=64, seed=41 + H, init_std=0.5)
+    z, zf = gated_case(si, seed=42 + H)
+    say("gated rows", case)
+    t = staging.scan_tensors(si, DEV)
+    out, fin = ssd.ssd_scan_fwd_gated(**t, z=staging.tensor(z, inputs.BF16, DEV), chunk=64,
+                                      algo=ssd.SSD_ALGO_ROWS)
+    torch.cuda.synchronize()
+    yr, fr = oracle_scan_gated(si, zf)
+    check(staging.to_f64(out), yr, 2e-2, "gated y")
+    check(staging.to_f64(fin), fr, 2e-2, "final_state")
+
+
+def test_gated_workload_2p7b():
+    """The 2.7B layer shape at full size, automatic plan (the benchmark's)."""
+    si, _ = workload_with_reference("mamba2_2p7b_b4_L4096_H80_P64_N128")
+    z, zf = gated_case(si, seed=5)
+    say("gated workload 2.7B")
+    t = staging.scan_tensors(si, DEV)
+    out, fin = ssd.ssd_scan_fwd_gated(**t, z=staging.tensor(z, si.dtype, DEV), chunk=si.chunk)
+    torch.cuda.synchronize()
+    yr, fr = oracle_scan_gated(si, zf)
+    ey = check(staging.to_f64(out), yr, 2e-2, "gated y")
+    ef = check(staging.to_f64(fin), fr, 2e-2, "final_state")
+    say("  max rel err y %.3e final %.3e" % (ey, ef))
