@@ -228,10 +228,20 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
   const auto rsS = make_rsrc(Sbase, (uint32_t)nsub * 4096u * 2u);
 
   float4 rB[PPT], rC[PPT], rX[2];
-  // B, C and x of sub-block k (loads past the end read zeros).
+  // B, C and x of sub-block k (loads past the end read zeros).  With more
+  // than four waves the byte counts are formed before the select, which
+  // makes the choice a scalar select and keeps the loop body one scheduling
+  // region; with one wave per SIMD the branch form schedules better (both
+  // measured).
   auto fetch_bcx = [&](int k) {
     const int t0 = 64 * k, nv = min(64, L - t0);
-    const uint32_t bcb = nv > 0 ? (uint32_t)(((int64_t)(nv - 1) * rowB + N) * 2) : 0u;
+    uint32_t bcb;
+    if constexpr (W > 4) {
+      const uint32_t bcb0 = (uint32_t)(((int64_t)(nv - 1) * rowB + N) * 2);
+      bcb = nv > 0 ? bcb0 : 0u;
+    } else {
+      bcb = nv > 0 ? (uint32_t)(((int64_t)(nv - 1) * rowB + N) * 2) : 0u;
+    }
     const auto rsB = make_rsrc(Bbase + (int64_t)t0 * rowB, bcb);
     const auto rsC = make_rsrc(Cbase + (int64_t)t0 * rowB, bcb);
 #pragma unroll
@@ -239,7 +249,14 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
       rB[i] = bload16(rsB, offBC[i]);
       rC[i] = bload16(rsC, offBC[i]);
     }
-    const auto rsX = make_rsrc(Xbase + (int64_t)t0 * rowX, nv > 0 ? (uint32_t)(((int64_t)(nv - 1) * rowX + 16) * 2) : 0u);
+    uint32_t nbX;
+    if constexpr (W > 4) {
+      const uint32_t nbX0 = (uint32_t)(((int64_t)(nv - 1) * rowX + 16) * 2);
+      nbX = nv > 0 ? nbX0 : 0u;
+    } else {
+      nbX = nv > 0 ? (uint32_t)(((int64_t)(nv - 1) * rowX + 16) * 2) : 0u;
+    }
+    const auto rsX = make_rsrc(Xbase + (int64_t)t0 * rowX, nbX);
     rX[0] = bload16(rsX, offX[0]);
     rX[1] = bload16(rsX, offX[1]);
   };
@@ -293,13 +310,15 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
     float clast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, c), 63));
     // Keep the (wave-uniform) decisions below in vector registers: as
     // per-lane selects they stay inside one basic block with the products
-    // they are scheduled against, instead of becoming scalar branches.
+    // they are scheduled against, instead of becoming scalar branches; every
+    // arm is computed before the choice so that none becomes a branch.
     float e_v = e_in;
-    __asm__ volatile("" : "+v"(clast), "+v"(e_v));
+    __asm__("" : "+v"(clast), "+v"(e_v));
     const float q = c - hw_log2(dl); // +inf where Delta = 0
     const bool fast = fabsf(clast) <= kSpanMax;
     const bool keep = e_v >= -clast - kExpLim && e_v <= kExpLim;
-    const float n = fast ? (keep ? 0.f : floorf(kExpLim - e_v)) : -rintf(e_v); // octaves
+    const float n_up = floorf(kExpLim - e_v), n_fast = keep ? 0.f : n_up, n_slow = -rintf(e_v);
+    const float n = fast ? n_fast : n_slow; // octaves
     const float ek = e_v + n;
     sF0[sl][w][l] = hw_exp2((fast ? 0.f : clast) - q - ek);
     sF1[sl][w][l] = hw_exp2(c + ek);
@@ -475,8 +494,9 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
   };
   auto flush_y = [&](int k) {
     const int t0 = 64 * k, nv = min(64, L - t0);
-    const auto rs = make_rsrc(Ywg + (int64_t)max(t0, 0) * rowX,
-                              k >= 0 ? (uint32_t)(((int64_t)(nv - 1) * rowX + rows_valid) * 2) : 0u);
+    // byte count before the select: a scalar select, not a branch
+    const uint32_t nbY = (uint32_t)(((int64_t)(nv - 1) * rowX + rows_valid) * 2);
+    const auto rs = make_rsrc(Ywg + (int64_t)max(t0, 0) * rowX, k >= 0 ? nbY : 0u);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int q = tid + i * NTH, t = q / (2 * W), j = q % (2 * W);
