@@ -58,7 +58,7 @@ enum {
   SSD_ERR_SHAPE = 2,       /* shapes disagree, H % G != 0, b or L is zero    */
   SSD_ERR_DTYPE = 3,       /* unsupported or mismatched element type         */
   SSD_ERR_LAYOUT = 4,      /* not dense row-major, or data not 16B aligned   */
-  SSD_ERR_UNSUPPORTED = 5, /* P, N or chunk outside the compiled set         */
+  SSD_ERR_UNSUPPORTED = 5, /* P, N, chunk or size outside the supported set  */
   SSD_ERR_ALIAS = 6,       /* an output overlaps an input it may not alias   */
   SSD_ERR_NOMEM = 7,       /* scratch allocation failed                      */
   SSD_ERR_HIP = 8          /* a HIP runtime call or kernel launch failed     */
@@ -109,8 +109,9 @@ typedef struct ssd_tensor {
  * The state is stored with N fastest: state[b][h][p][n] is the n-th state
  * entry of channel p (the transpose of the N x P product B x^T).
  * Supported sizes: P in {16, 32, 64, 128} (bf16) or {16, 32, 64} (fp32),
- * N in {16, 32, 64, 128}, H % G == 0, b >= 1, L >= 1 (any L; the last chunk
- * may be partial).
+ * N in {16, 32, 64, 128}, H % G == 0, b >= 1, 1 <= L <= 2^24 (any L in
+ * that range; the last chunk may be partial), H*P and G*N at most 2^22;
+ * larger problems are refused with SSD_ERR_UNSUPPORTED.
  * Arithmetic: products on MFMA in the input dtype with fp32 accumulation,
  * the state and all decay factors in fp32.  final_state may be the same
  * tensor as init_state (updated in place); out may not overlap any input.

@@ -94,6 +94,9 @@ int check_tensor(const ssd_tensor *t, const char *name, int want_dtype, int ndim
 
 bool valid_pn(int64_t v) { return v == 16 || v == 32 || v == 64 || v == 128; }
 
+constexpr int64_t kMaxL = (int64_t)1 << 24;   // tokens per sequence
+constexpr int64_t kMaxRow = (int64_t)1 << 22; // elements of x (H*P) or B/C (G*N) per token
+
 struct ScanShape {
   int64_t b, L, H, P, G, N;
 };
@@ -122,6 +125,14 @@ int validate_scan(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *d
   if (s->b * s->L * s->H * s->P > ((int64_t)1 << 40) || s->b * s->L > INT32_MAX / 2 ||
       s->b * s->H * ((s->L + 63) / 64) > INT32_MAX / 2)
     return fail(SSD_ERR_UNSUPPORTED, "problem too large for 32-bit workgroup indexing");
+  // Kernels address one 64-token tile (and the row walk one sequence of
+  // score tiles) through 32-bit byte ranges.
+  if (s->L > kMaxL)
+    return fail(SSD_ERR_UNSUPPORTED, "L=%lld above the supported %lld tokens", (long long)s->L,
+                (long long)kMaxL);
+  if (s->H * s->P > kMaxRow || s->G * s->N > kMaxRow)
+    return fail(SSD_ERR_UNSUPPORTED, "H*P=%lld or G*N=%lld above the supported %lld per token",
+                (long long)(s->H * s->P), (long long)(s->G * s->N), (long long)kMaxRow);
   const int xd = x->dtype;
   const int64_t sx[4] = {s->b, s->L, s->H, s->P}, sdt[3] = {s->b, s->L, s->H},
                 sh[1] = {s->H}, sbc[4] = {s->b, s->L, s->G, s->N},

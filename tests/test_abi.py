@@ -90,6 +90,41 @@ CASES = [
 ]
 
 
+def _fake(ssd, shape, dtype):
+    """A descriptor of a dense tensor at a fake aligned address (validation
+    only reads the descriptor)."""
+    t = ssd.SsdTensor()
+    t.data = 1 << 20
+    t.dtype = dtype
+    t.ndim = len(shape)
+    st = 1
+    for i in range(len(shape) - 1, -1, -1):
+        t.shape[i] = shape[i]
+        t.strides[i] = st
+        st *= shape[i]
+    return t
+
+
+@pytest.mark.parametrize("b,L,H,P,G,N", [(1, (1 << 24) + 64, 1, 16, 1, 16),
+                                         (1, 64, (1 << 18) + 1, 16, 1, 16),
+                                         (1, 64, 1 << 16, 16, 1 << 16, 128)],
+                         ids=["L_above_max", "HP_above_max", "GN_above_max"])
+def test_scan_rejects_oversized(ssd, b, L, H, P, G, N):
+    # shapes whose per-tile byte ranges would not fit 32 bits are refused
+    # on the host before any device call
+    bf, f32 = 1, 0
+    x = _fake(ssd, (b, L, H, P), bf)
+    args = [x, _fake(ssd, (b, L, H), f32), None, _fake(ssd, (H,), f32),
+            _fake(ssd, (b, L, G, N), bf), _fake(ssd, (b, L, G, N), bf), None, None,
+            _fake(ssd, (b, L, H, P), bf), None]
+    lib = ssd.lib()
+    P_ = ctypes.POINTER(ssd.SsdTensor)
+    ptrs = [ctypes.byref(a) if a is not None else None for a in args]
+    st = lib.ssd_scan_fwd_algo(*ptrs, 256, 0, None)
+    assert st == 5, (st, ssd.ssd_last_error())
+    assert "supported" in ssd.ssd_last_error()
+
+
 @pytest.mark.parametrize("name,mutate,status", CASES, ids=[c[0] for c in CASES])
 def test_scan_rejects(ssd, name, mutate, status):
     a = _scan_args()
