@@ -165,6 +165,31 @@ int hip_fail(hipError_t e, const char *what) {
   return fail(SSD_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Every tensor must be memory the current device can address: device memory
+// of the current device, managed memory, or pinned host memory.  Pageable
+// host memory or another device's memory is refused here, before any launch
+// (a kernel would fault on it).
+int check_addressable(const ssd_tensor *const *ts, const char *const *names, int n) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(SSD_ERR_LAYOUT, "no current HIP device");
+  }
+  for (int i = 0; i < n; ++i) {
+    if (!ts[i]) continue;
+    hipPointerAttribute_t a;
+    if (hipPointerGetAttributes(&a, ts[i]->data) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(SSD_ERR_LAYOUT, "%s: not memory a HIP device can address (pageable host memory?)", names[i]);
+    }
+    if (a.type == hipMemoryTypeUnregistered)
+      return fail(SSD_ERR_LAYOUT, "%s: not memory a HIP device can address (pageable host memory?)", names[i]);
+    if (a.type == hipMemoryTypeDevice && a.device != dev)
+      return fail(SSD_ERR_LAYOUT, "%s: on device %d, but device %d is current", names[i], a.device, dev);
+  }
+  return SSD_OK;
+}
+
 int run_fused(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bias,
               const ssd_tensor *A, const ssd_tensor *B, const ssd_tensor *C,
               const ssd_tensor *D, const ssd_tensor *z, const ssd_tensor *init, ssd_tensor *out,
@@ -386,6 +411,11 @@ int scan_dispatch(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *d
     return fail(SSD_ERR_UNSUPPORTED, "unknown algorithm %d", algo);
   if (algo == SSD_ALGO_ROWS && !rows_supported(x->dtype, s.N))
     return fail(SSD_ERR_UNSUPPORTED, "row-sliced walk needs bf16 inputs and N in {32,64,128}");
+  {
+    const ssd_tensor *ts[] = {x, dt, dt_bias, A, B, C, D, z, init_state, out, final_state};
+    const char *nm[] = {"x", "dt", "dt_bias", "A", "B", "C", "D", "z", "init_state", "out", "final_state"};
+    SSD_CHECK(check_addressable(ts, nm, 11));
+  }
   const int cus = device_cus();
   if (algo == SSD_ALGO_AUTO) {
     const Plan plan = choose_plan(s, x->dtype, cus);
@@ -457,6 +487,11 @@ int ssd_scan_fwd_rows(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tenso
   if (!rows_supported(x->dtype, s.N))
     return fail(SSD_ERR_UNSUPPORTED, "row-sliced walk needs bf16 inputs and N in {32,64,128}");
   if (waves < 0 || waves > 8) return fail(SSD_ERR_UNSUPPORTED, "waves=%d not in 0..8", waves);
+  {
+    const ssd_tensor *ts[] = {x, dt, dt_bias, A, B, C, D, init_state, out, final_state};
+    const char *nm[] = {"x", "dt", "dt_bias", "A", "B", "C", "D", "init_state", "out", "final_state"};
+    SSD_CHECK(check_addressable(ts, nm, 10));
+  }
   const int W = waves ? waves : rows_waves(s, device_cus());
   return run_rows(x, dt, dt_bias, A, B, C, D, nullptr, init_state, out, final_state, s, W,
                   (hipStream_t)stream);
@@ -501,6 +536,11 @@ int ssd_step(ssd_tensor *state, const ssd_tensor *x, const ssd_tensor *dt, const
     if (overlap(rs, ri)) return fail(SSD_ERR_ALIAS, "state overlaps %s", names[i]);
   }
   if (overlap(ro, rs)) return fail(SSD_ERR_ALIAS, "out overlaps state");
+  {
+    const ssd_tensor *ts[] = {state, x, dt, A, B, C, D, out};
+    const char *nm[] = {"state", "x", "dt", "A", "B", "C", "D", "out"};
+    SSD_CHECK(check_addressable(ts, nm, 8));
+  }
   hipError_t e = ssd::launch_step(xd, (int)N, (float *)state->data, x->data,
                                   (const float *)dt->data, (const float *)A->data, B->data,
                                   C->data, D ? (const float *)D->data : nullptr, out->data,

@@ -9,6 +9,7 @@ is not built, loading it raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional
@@ -93,11 +94,19 @@ def describe(t: Optional[torch.Tensor]):
     return ctypes.pointer(d)
 
 
-def _stream(stream, *tensors):
+def _on_device(t):
+    """Make t's device current for the call (the library launches on the
+    current device and refuses memory that device cannot address)."""
+    if t is not None and t.is_cuda:
+        return torch.cuda.device(t.device)
+    return contextlib.nullcontext()
+
+
+def _stream(stream, t):
     if stream is not None:
         return stream
-    if any(t is not None and t.is_cuda for t in tensors):
-        return torch.cuda.current_stream().cuda_stream
+    if t is not None and t.is_cuda:
+        return torch.cuda.current_stream(t.device).cuda_stream
     return None
 
 
@@ -115,11 +124,12 @@ def ssd_scan_fwd(x, dt, dt_bias, A, B, C, D=None, init_state=None, out=None,
     if final_state is None and return_final_state:
         final_state = torch.empty((x.shape[0], x.shape[2], x.shape[3], B.shape[3]),
                                   dtype=torch.float32, device=x.device)
-    st = _stream(stream, x)
-    status = lib().ssd_scan_fwd_algo(
-        describe(x), describe(dt), describe(dt_bias), describe(A), describe(B), describe(C),
-        describe(D), describe(init_state), describe(out), describe(final_state),
-        int(chunk), int(algo), st)
+    with _on_device(x):
+        st = _stream(stream, x)
+        status = lib().ssd_scan_fwd_algo(
+            describe(x), describe(dt), describe(dt_bias), describe(A), describe(B), describe(C),
+            describe(D), describe(init_state), describe(out), describe(final_state),
+            int(chunk), int(algo), st)
     _check(status)
     return out, final_state
 
@@ -134,11 +144,12 @@ def ssd_scan_fwd_gated(x, dt, dt_bias, A, B, C, z, D=None, init_state=None, out=
     if final_state is None and return_final_state:
         final_state = torch.empty((x.shape[0], x.shape[2], x.shape[3], B.shape[3]),
                                   dtype=torch.float32, device=x.device)
-    st = _stream(stream, x)
-    status = lib().ssd_scan_fwd_gated(
-        describe(x), describe(dt), describe(dt_bias), describe(A), describe(B), describe(C),
-        describe(D), describe(z), describe(init_state), describe(out), describe(final_state),
-        int(chunk), int(algo), st)
+    with _on_device(x):
+        st = _stream(stream, x)
+        status = lib().ssd_scan_fwd_gated(
+            describe(x), describe(dt), describe(dt_bias), describe(A), describe(B), describe(C),
+            describe(D), describe(z), describe(init_state), describe(out), describe(final_state),
+            int(chunk), int(algo), st)
     _check(status)
     return out, final_state
 
@@ -152,11 +163,12 @@ def ssd_scan_fwd_rows(x, dt, dt_bias, A, B, C, D=None, init_state=None, out=None
     if final_state is None and return_final_state:
         final_state = torch.empty((x.shape[0], x.shape[2], x.shape[3], B.shape[3]),
                                   dtype=torch.float32, device=x.device)
-    st = _stream(stream, x)
-    status = lib().ssd_scan_fwd_rows(
-        describe(x), describe(dt), describe(dt_bias), describe(A), describe(B), describe(C),
-        describe(D), describe(init_state), describe(out), describe(final_state),
-        int(waves), st)
+    with _on_device(x):
+        st = _stream(stream, x)
+        status = lib().ssd_scan_fwd_rows(
+            describe(x), describe(dt), describe(dt_bias), describe(A), describe(B), describe(C),
+            describe(D), describe(init_state), describe(out), describe(final_state),
+            int(waves), st)
     _check(status)
     return out, final_state
 
@@ -165,9 +177,10 @@ def ssd_step(state, x, dt, A, B, C, D=None, out=None, stream=None):
     """One recurrent step; ``state`` is updated in place; returns out."""
     if out is None:
         out = torch.empty_like(x)
-    st = _stream(stream, state)
-    status = lib().ssd_step(describe(state), describe(x), describe(dt), describe(A),
-                            describe(B), describe(C), describe(D), describe(out), st)
+    with _on_device(state):
+        st = _stream(stream, state)
+        status = lib().ssd_step(describe(state), describe(x), describe(dt), describe(A),
+                                describe(B), describe(C), describe(D), describe(out), st)
     _check(status)
     return out
 

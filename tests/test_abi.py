@@ -197,6 +197,23 @@ def test_python_binding_raises(ssd):
     assert e.value.status == 6
 
 
+def test_host_memory_refused(ssd):
+    # valid shapes in (pageable) host memory: refused before any launch,
+    # whether or not a device is present
+    a = _scan_args()
+    with pytest.raises(ssd.SsdError) as e:
+        ssd.ssd_scan_fwd(a["x"], a["dt"], a["dt_bias"], a["A"], a["B"], a["C"], a["D"],
+                         a["init_state"], out=a["out"], final_state=a["final_state"], chunk=64)
+    assert e.value.status == 4
+    b, H, P, G, N = 2, 4, 16, 2, 32
+    with pytest.raises(ssd.SsdError) as e:
+        ssd.ssd_step(torch.zeros(b, H, P, N), torch.zeros(b, H, P, dtype=torch.bfloat16),
+                     torch.zeros(b, H), -torch.ones(H), torch.zeros(b, G, N, dtype=torch.bfloat16),
+                     torch.zeros(b, G, N, dtype=torch.bfloat16), torch.zeros(H),
+                     out=torch.zeros(b, H, P, dtype=torch.bfloat16))
+    assert e.value.status == 4
+
+
 def test_plan(ssd):
     """The automatic plan, against plan timings measured on MI355X: the
     row-sliced walk for bf16 shapes whose rows fill the compute units,

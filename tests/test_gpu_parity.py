@@ -466,3 +466,25 @@ def test_gated_workload_2p7b():
     ey = check(staging.to_f64(out), yr, 2e-2, "gated y")
     ef = check(staging.to_f64(fin), fr, 2e-2, "final_state")
     say("  max rel err y %.3e final %.3e" % (ey, ef))
+
+
+def test_host_memory_refused_on_device():
+    # pageable host tensors, alone or mixed with device tensors, are refused
+    # on the host before any launch
+    b, L, H, P, G, N = 1, 100, 4, 16, 2, 32
+    bf = torch.bfloat16
+
+    def args(dev, B_dev):
+        return dict(x=torch.zeros(b, L, H, P, dtype=bf, device=dev), dt=torch.zeros(b, L, H, device=dev),
+                    dt_bias=torch.zeros(H, device=dev), A=-torch.ones(H, device=dev),
+                    B=torch.zeros(b, L, G, N, dtype=bf, device=B_dev),
+                    C=torch.zeros(b, L, G, N, dtype=bf, device=dev), D=torch.zeros(H, device=dev))
+    say("host memory refusal: all on the host, then B on the host")
+    for dev, B_dev, culprit in (("cpu", "cpu", "x"), (DEV, "cpu", "B")):
+        a = args(dev, B_dev)
+        out = torch.zeros(b, L, H, P, dtype=bf, device=dev)
+        with pytest.raises(ssd.SsdError) as e:
+            ssd.ssd_scan_fwd(**a, out=out, return_final_state=False, chunk=64)
+        assert e.value.status == 4, str(e.value)
+        assert ("%s:" % culprit) in str(e.value), str(e.value)
+    torch.cuda.synchronize()
