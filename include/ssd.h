@@ -20,16 +20,20 @@
  * ---------------------------------------
  * Tensors are described by ssd_tensor.  Every tensor must be dense and
  * row-major (strides, in elements, equal to the contiguous strides of its
- * shape) with a 16-byte aligned data pointer.  All data pointers are device
- * pointers (HIP device memory) except where noted.
+ * shape) with a 16-byte aligned data pointer.  All data pointers must be
+ * memory the current HIP device can address: its own device memory,
+ * managed memory, or pinned host memory (read over the bus, slowly).
+ * Pageable host memory and another device's memory are refused with
+ * SSD_ERR_LAYOUT (checked with hipPointerGetAttributes after every other
+ * argument check, before any launch).
  *
  * Ownership: the caller allocates every tensor and keeps it alive until the
  * work queued on `stream` has finished.  The library keeps no pointer after
  * a call returns.  Scratch space, when an algorithm needs it, is taken from
  * the HIP stream-ordered allocator on `stream` and released on `stream`.
  *
- * Errors: every argument is validated on the host before any HIP call; a
- * failed validation returns a nonzero status and queues nothing.  A failed
+ * Errors: every argument is validated on the host before any work is
+ * queued; a failed validation returns a nonzero status and queues nothing.  A failed
  * kernel launch or allocation returns SSD_ERR_HIP / SSD_ERR_NOMEM.  Faults
  * inside kernels surface at the caller's next synchronisation.  The text of
  * the most recent error on the calling thread is returned by
@@ -57,7 +61,8 @@ enum {
   SSD_ERR_NULL = 1,        /* a required tensor or data pointer is NULL      */
   SSD_ERR_SHAPE = 2,       /* shapes disagree, H % G != 0, b or L is zero    */
   SSD_ERR_DTYPE = 3,       /* unsupported or mismatched element type         */
-  SSD_ERR_LAYOUT = 4,      /* not dense row-major, or data not 16B aligned   */
+  SSD_ERR_LAYOUT = 4,      /* not dense row-major, not 16B aligned, or not
+                              memory the current device can address        */
   SSD_ERR_UNSUPPORTED = 5, /* P, N, chunk or size outside the supported set  */
   SSD_ERR_ALIAS = 6,       /* an output overlaps an input it may not alias   */
   SSD_ERR_NOMEM = 7,       /* scratch allocation failed                      */
