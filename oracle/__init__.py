@@ -60,6 +60,8 @@ class Oracle:
         lib.oracle_step_f64.restype = None
         lib.oracle_gate_f64.argtypes = [i64, vp, vp, vp]
         lib.oracle_gate_f64.restype = None
+        lib.oracle_sscan_f64.argtypes = [i64] * 5 + [vp] * 10
+        lib.oracle_sscan_f64.restype = None
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
         self.lib = lib
@@ -78,6 +80,9 @@ class Oracle:
 
     def gate(self, y, z):
         return _gate(self.lib, y, z)
+
+    def selective_scan(self, *args, **kwargs):
+        return _sscan(self.lib, *args, **kwargs)
 
 
 def default() -> Oracle:
@@ -120,6 +125,12 @@ def step(state, x, delta, A, B, C, D=None):
 def gate(y, z):
     """Elementwise y * silu(z) in fp64 (see ``_gate``)."""
     return default().gate(y, z)
+
+
+def selective_scan(x, dt, dt_bias, A, B, C, D=None, init=None, want_final=True):
+    """Sequential fp64 selective scan with a diagonal A per (channel, n)
+    (see ``_sscan``)."""
+    return default().selective_scan(x, dt, dt_bias, A, B, C, D, init, want_final)
 
 
 def scan_gated(x, dt, dt_bias, A, B, C, z, D=None, init=None, want_final=True):
@@ -180,3 +191,24 @@ def _gate(lib, y, z):
     out = np.empty_like(y)
     lib.oracle_gate_f64(y.size, _ptr(y), _ptr(z), _ptr(out))
     return out
+
+
+def _sscan(lib, x, dt, dt_bias, A, B, C, D=None, init=None, want_final=True):
+    """Sequential fp64 selective scan, diagonal A per (channel, state index).
+
+    x, dt [b,L,Dc] (dt raw, before softplus), dt_bias [Dc] or None,
+    A [Dc,N], B/C [b,L,G,N] (channel d reads group floor(d*G/Dc)),
+    D [Dc] or None, init [b,Dc,N] or None.  Returns (y [b,L,Dc],
+    final_state [b,Dc,N] or None) in float64.  Follows oracle_sscan_f64 in
+    ssd_oracle.c (Mamba paper-reading notes, selective mechanism)."""
+    x, dt, A, B, C = (_f64(v) for v in (x, dt, A, B, C))
+    dt_bias, D, init = _f64(dt_bias), _f64(D), _f64(init)
+    b, L, Dc = x.shape
+    G, N = B.shape[2], B.shape[3]
+    assert dt.shape == (b, L, Dc) and A.shape == (Dc, N)
+    assert B.shape == (b, L, G, N) and C.shape == B.shape
+    y = np.empty((b, L, Dc), dtype=np.float64)
+    fin = np.empty((b, Dc, N), dtype=np.float64) if want_final else None
+    lib.oracle_sscan_f64(b, L, Dc, G, N, _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(B),
+                         _ptr(C), _ptr(D), _ptr(init), _ptr(y), _ptr(fin))
+    return y, fin

@@ -152,3 +152,52 @@ void oracle_gate_f64(int64_t n, const double *y, const double *z, double *out) {
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) out[i] = y[i] * (z[i] / (1.0 + exp(-z[i])));
 }
+
+/* Selective scan with a per-channel step size and a diagonal A per
+ * (channel, state index): the Mamba-1 selective SSM (Mamba paper-reading
+ * notes, sxlin0.github.io, the selective-mechanism section: B, C and Delta
+ * are functions of the input, Delta = tau_Delta(parameter + s_Delta(x)),
+ * applied per channel; the "Transformers are SSMs" summary,
+ * gongshangzheng.github.io, section 1.3 table: Mamba-1 keeps a small state,
+ * N = 16).  For every batch row and channel d independently:
+ *
+ *   Delta_t     = softplus(dt[t][d] + dt_bias[d])
+ *   h_t[n]      = exp(Delta_t * A[d][n]) * h_{t-1}[n] + Delta_t * B_t[n] * x_t[d]
+ *   y_t[d]      = sum_n C_t[n] * h_t[n] + D[d] * x_t[d]
+ *
+ * Shapes (dense, row-major, float64): x, dt, y [b, L, Dc]; dt_bias, D [Dc];
+ * A [Dc, N]; B, C [b, L, G, N] with channel d reading group
+ * floor(d * G / Dc); init and final state [b, Dc, N].  dt_bias, D and init
+ * may be NULL (zero); final_state may be NULL (not written).  The initial
+ * state enters before the first token's decay, as in oracle_scan_f64. */
+void oracle_sscan_f64(int64_t b, int64_t L, int64_t Dc, int64_t G, int64_t N,
+                      const double *x, const double *dt, const double *dt_bias,
+                      const double *A, const double *B, const double *C,
+                      const double *D, const double *init, double *y,
+                      double *final_state) {
+    int64_t pairs = b * Dc;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t bd = 0; bd < pairs; ++bd) {
+        int64_t ib = bd / Dc, d = bd % Dc;
+        int64_t g = (d * G) / Dc;
+        double *h = (double *)malloc((size_t)N * sizeof(double));
+        for (int64_t n = 0; n < N; ++n) h[n] = init ? init[bd * N + n] : 0.0;
+        double bias = dt_bias ? dt_bias[d] : 0.0;
+        double d_d = D ? D[d] : 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+            int64_t tok = ib * L + t;
+            double delta = softplus_f64(dt[tok * Dc + d] + bias);
+            double xv = x[tok * Dc + d];
+            const double *B_t = B + (tok * G + g) * N, *C_t = C + (tok * G + g) * N;
+            double acc = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                h[n] = exp(delta * A[d * N + n]) * h[n] + delta * B_t[n] * xv;
+                acc += C_t[n] * h[n];
+            }
+            y[tok * Dc + d] = acc + d_d * xv;
+        }
+        if (final_state)
+            for (int64_t n = 0; n < N; ++n) final_state[bd * N + n] = h[n];
+        free(h);
+    }
+}

@@ -23,6 +23,14 @@ fixed independently of the oracle's own loop:
                       (logistic 3/4 and 1/4) and +-40
 * ``pin_gate_expit``  the gate against ``scipy.special.expit`` (a library
                       logistic)
+* ``pin_sscan_closed_form`` the selective scan with a diagonal A per
+                      (channel, n): per state index an explicit double sum
+                      of decays exp(A (S_t - S_s)), S the cumulative sum of
+                      Delta (Mamba reading notes, selective mechanism)
+* ``pin_sscan_reduces_to_ssd`` A constant over n: the selective scan equals
+                      the (separately pinned) SSD scan with one channel per
+                      head
+* ``pin_sscan_hand``  a hand-worked 3-token example with two state indices
 
 Softplus here is ``numpy.logaddexp(0, z)`` (a library routine).
 """
@@ -321,6 +329,86 @@ def pin_gate_expit(o, seed=22):
     _close(o.gate(y, z), y * z * expit(z), 1e-15, "gate vs scipy expit")
 
 
+def rand_sscan_case(rng, b, L, Dc, G, N):
+    """Generic float64 inputs for the selective scan (A distinct per
+    (channel, n))."""
+    return dict(x=rng.standard_normal((b, L, Dc)), dt=0.5 * rng.standard_normal((b, L, Dc)),
+                dt_bias=-1.0 + 0.3 * rng.standard_normal(Dc),
+                A=-np.exp(rng.uniform(np.log(0.5), np.log(4.0), (Dc, N))),
+                B=rng.standard_normal((b, L, G, N)) / np.sqrt(N),
+                C=rng.standard_normal((b, L, G, N)) / np.sqrt(N),
+                D=rng.standard_normal(Dc), init=0.5 * rng.standard_normal((b, Dc, N)))
+
+
+def sscan_closed_form(x, dt, dt_bias, A, B, C, D, init):
+    """Per state index n the selective recurrence is a scalar linear
+    recurrence with gate exp(A[d,n] Delta_t); unrolled,
+        h_t[n] = exp(A S_t) h0[n] + sum_{s<=t} exp(A (S_t - S_s)) Delta_s B_s[n] x_s
+    with S the inclusive cumulative sum of Delta.  Evaluated as an explicit
+    double sum (no recurrence)."""
+    b, L, Dc = x.shape
+    G, N = B.shape[2], B.shape[3]
+    delta = softplus(dt + dt_bias)
+    S = np.cumsum(delta, axis=1)
+    tri = np.tril(np.ones((L, L), dtype=bool))[:, :, None]
+    y = np.empty_like(x)
+    fin = np.empty((b, Dc, N))
+    for ib in range(b):
+        for d in range(Dc):
+            g = (d * G) // Dc
+            Sd = S[ib, :, d]
+            arg = A[d][None, None, :] * (Sd[:, None, None] - Sd[None, :, None])
+            dec = np.exp(np.where(tri, arg, -np.inf))                      # [t, s, N]
+            inp = (delta[ib, :, d] * x[ib, :, d])[:, None] * B[ib, :, g, :]  # [s, N]
+            Hs = np.einsum("tsn,sn->tn", dec, inp) + np.exp(A[d][None, :] * Sd[:, None]) * init[ib, d][None, :]
+            y[ib, :, d] = np.einsum("tn,tn->t", Hs, C[ib, :, g, :]) + D[d] * x[ib, :, d]
+            fin[ib, d] = Hs[-1]
+    return y, fin
+
+
+def pin_sscan_closed_form(o, seed=23):
+    rng = np.random.default_rng(seed)
+    for (b, L, Dc, G, N) in [(1, 40, 5, 1, 4), (2, 23, 6, 3, 3), (1, 31, 4, 2, 16)]:
+        c = rand_sscan_case(rng, b, L, Dc, G, N)
+        y, fin = o.selective_scan(**c)
+        yq, fq = sscan_closed_form(**c)
+        _close(y, yq, 1e-12, "selective scan closed form y %s" % ((b, L, Dc, G, N),))
+        _close(fin, fq, 1e-12, "selective scan closed form final")
+
+
+def pin_sscan_reduces_to_ssd(o, seed=24):
+    # with A[d, n] = a_d for every n the selective scan is the SSD scan with
+    # H = Dc heads of P = 1 channel each (same group map floor(h G / H))
+    rng = np.random.default_rng(seed)
+    b, L, Dc, G, N = 2, 37, 6, 2, 8
+    c = rand_sscan_case(rng, b, L, Dc, G, N)
+    a = -np.exp(rng.uniform(np.log(0.5), np.log(4.0), Dc))
+    c["A"] = np.repeat(a[:, None], N, axis=1)
+    y, fin = o.selective_scan(**c)
+    ys, fs = o.scan(c["x"][..., None], c["dt"], c["dt_bias"], a, c["B"], c["C"], c["D"],
+                    c["init"][:, :, None, :])
+    _close(y, ys[..., 0], 1e-13, "selective scan vs SSD y")
+    _close(fin, fs[:, :, 0, :], 1e-13, "selective scan vs SSD final")
+
+
+def pin_sscan_hand(o):
+    # One channel, N = 2, A = [-ln 2, 0], Delta = 1 (dt = ln(e - 1)), D = 0.5,
+    # h0 = [4, -2], x = [1, 2, 3], B = [[1,0],[0,1],[1,1]], C = [[1,1],[1,0],[0,1]].
+    # Gates exp(Delta A) = [1/2, 1]:
+    #   t0: h = [2 + 1, -2 + 0] = [3, -2];      y = 3 - 2 + 0.5 = 1.5
+    #   t1: h = [1.5 + 0, -2 + 2] = [1.5, 0];   y = 1.5 + 1.0  = 2.5
+    #   t2: h = [0.75 + 3, 0 + 3] = [3.75, 3];  y = 3 + 1.5    = 4.5
+    c = dict(x=np.array([[[1.0], [2.0], [3.0]]]), dt=np.full((1, 3, 1), np.log(np.e - 1.0)),
+             dt_bias=np.zeros(1), A=np.array([[-np.log(2.0), 0.0]]),
+             B=np.array([[[[1.0, 0.0]], [[0.0, 1.0]], [[1.0, 1.0]]]]),
+             C=np.array([[[[1.0, 1.0]], [[1.0, 0.0]], [[0.0, 1.0]]]]),
+             D=np.array([0.5]), init=np.array([[[4.0, -2.0]]]))
+    y, fin = o.selective_scan(**c)
+    _close(y[0, :, 0], [1.5, 2.5, 4.5], 1e-14, "selective scan hand example y")
+    _close(fin[0, 0], [3.75, 3.0], 1e-14, "selective scan hand example final")
+
+
 ALL_PINS = [pin_golden, pin_quadratic, pin_no_decay, pin_scalar_state, pin_split,
             pin_lti, pin_step_scan, pin_exact_int, pin_linearity, pin_groups,
-            pin_head_perm, pin_decay_bound, pin_gate_closed_forms, pin_gate_expit]
+            pin_head_perm, pin_decay_bound, pin_gate_closed_forms, pin_gate_expit,
+            pin_sscan_closed_form, pin_sscan_reduces_to_ssd, pin_sscan_hand]

@@ -52,6 +52,22 @@ MUTATIONS = [
      "gate sigmoid instead of silu"),
     ("out[i] = y[i] * (z[i] / (1.0 + exp(-z[i])));", "out[i] = (z[i] / (1.0 + exp(-z[i])));",
      "gate drops y"),
+    # selective scan (diagonal A per channel and state index)
+    ("h[n] = exp(delta * A[d * N + n]) * h[n]", "h[n] = exp(delta * A[n * Dc + d]) * h[n]",
+     "selective scan: A transposed"),
+    ("h[n] = exp(delta * A[d * N + n]) * h[n]", "h[n] = exp(delta * A[d * N]) * h[n]",
+     "selective scan: one A per channel"),
+    ("double delta = softplus_f64(dt[tok * Dc + d] + bias);",
+     "double delta = softplus_f64(dt[tok * Dc + g] + bias);", "selective scan: Delta of another channel"),
+    ("""                h[n] = exp(delta * A[d * N + n]) * h[n] + delta * B_t[n] * xv;
+                acc += C_t[n] * h[n];""", """                acc += C_t[n] * h[n];
+                h[n] = exp(delta * A[d * N + n]) * h[n] + delta * B_t[n] * xv;""",
+     "selective scan: readout before update"),
+    ("const double *B_t = B + (tok * G + g) * N, *C_t = C + (tok * G + g) * N;",
+     "const double *B_t = C + (tok * G + g) * N, *C_t = B + (tok * G + g) * N;",
+     "selective scan: B and C swapped"),
+    ("        int64_t g = (d * G) / Dc;\n        double *h", "        int64_t g = d % G;\n        double *h",
+     "selective scan: group map"),
 ]
 
 
