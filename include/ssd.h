@@ -207,6 +207,47 @@ int ssd_step(ssd_tensor *state, const ssd_tensor *x, const ssd_tensor *dt,
              const ssd_tensor *D, ssd_tensor *out, void *stream);
 
 /*
+ * ssd_selective_scan_fwd -- the selective scan with a per-channel step size
+ * and a diagonal A per (channel, state index), the Mamba-1 selective SSM
+ * (Mamba paper-reading notes, sxlin0.github.io, the selective-mechanism
+ * section: B, C and Delta depend on the input, Delta per channel; "Transformers
+ * are SSMs" summary, gongshangzheng.github.io, section 1.3 table: a small
+ * state, N = 16).  For every batch row and channel d:
+ *
+ *     Delta_t = softplus(dt[t][d] + dt_bias[d])
+ *     h_t[n]  = exp(Delta_t * A[d][n]) * h_{t-1}[n] + Delta_t * B_t[n] * x_t[d]
+ *     y_t[d]  = sum_n C_t[n] * h_t[n] + D[d] * x_t[d]
+ *
+ *   x           [b, L, D]     f32 or bf16                        required
+ *   dt          [b, L, D]     f32, raw (before bias and softplus) required
+ *   dt_bias     [D]           f32                                NULL => 0
+ *   A           [D, N]        f32, the values A[d][n]            required
+ *   B, C        [b, L, G, N]  dtype of x; channel d reads group
+ *                             floor(d * G / D)                   required
+ *   D           [D]           f32 (the skip term)                NULL => 0
+ *   init_state  [b, D, N]     f32, the state before token 0      NULL => 0
+ *   out         [b, L, D]     dtype of x, written
+ *   final_state [b, D, N]     f32, written; may be init_state    NULL => skip
+ *   segments    the sequence is cut into this many segments walked in
+ *               parallel (their entering states folded from a first
+ *               state-only pass); 0 chooses from the device size.  The
+ *               result does not depend on it beyond rounding order.
+ *
+ * Supported sizes: N in {4, 8, 16}, D/G a multiple of 64 (64 channels of
+ * one group per wave), 1 <= L <= 2^24.  The state and all arithmetic in
+ * fp32; out is rounded to its dtype once.  Scratch (segment end states,
+ * b * segments * D * (N + 1) floats) comes from the stream-ordered allocator
+ * when segments > 1.  out may not overlap any input; final_state may not
+ * overlap any input other than (exactly) init_state.
+ */
+int ssd_selective_scan_fwd(const ssd_tensor *x, const ssd_tensor *dt,
+                           const ssd_tensor *dt_bias, const ssd_tensor *A,
+                           const ssd_tensor *B, const ssd_tensor *C,
+                           const ssd_tensor *D, const ssd_tensor *init_state,
+                           ssd_tensor *out, ssd_tensor *final_state,
+                           int segments, void *stream);
+
+/*
  * ssd_scan_plan -- the plan SSD_ALGO_AUTO uses for a shape on a device with
  * `cus` compute units for inputs of element type `dtype` (SSD_BF16 or
  * SSD_F32), host only, no HIP call: *algo is SSD_ALGO_FUSED,

@@ -548,6 +548,109 @@ int ssd_step(ssd_tensor *state, const ssd_tensor *x, const ssd_tensor *dt, const
   return e == hipSuccess ? SSD_OK : hip_fail(e, "step launch");
 }
 
+int ssd_selective_scan_fwd(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bias,
+                           const ssd_tensor *A, const ssd_tensor *B, const ssd_tensor *C,
+                           const ssd_tensor *D, const ssd_tensor *init_state, ssd_tensor *out,
+                           ssd_tensor *final_state, int segments, void *stream) {
+  g_last_error.clear();
+  if (!x) return fail(SSD_ERR_NULL, "x: descriptor is NULL");
+  if (!A) return fail(SSD_ERR_NULL, "A: descriptor is NULL");
+  if (!B) return fail(SSD_ERR_NULL, "B: descriptor is NULL");
+  if (x->ndim != 3) return fail(SSD_ERR_SHAPE, "x: rank %d, expected 3 [b,L,D]", x->ndim);
+  if (A->ndim != 2) return fail(SSD_ERR_SHAPE, "A: rank %d, expected 2 [D,N]", A->ndim);
+  if (B->ndim != 4) return fail(SSD_ERR_SHAPE, "B: rank %d, expected 4 [b,L,G,N]", B->ndim);
+  const int64_t b = x->shape[0], L = x->shape[1], Dc = x->shape[2], G = B->shape[2],
+                N = B->shape[3];
+  if (b < 1 || L < 1 || Dc < 1 || G < 1)
+    return fail(SSD_ERR_SHAPE, "empty problem: b=%lld L=%lld D=%lld G=%lld", (long long)b,
+                (long long)L, (long long)Dc, (long long)G);
+  if (Dc % G != 0) return fail(SSD_ERR_SHAPE, "D=%lld is not a multiple of G=%lld", (long long)Dc, (long long)G);
+  if ((Dc / G) % 64 != 0)
+    return fail(SSD_ERR_UNSUPPORTED, "channels per group D/G=%lld is not a multiple of 64",
+                (long long)(Dc / G));
+  if (N != 4 && N != 8 && N != 16) return fail(SSD_ERR_UNSUPPORTED, "N=%lld not in {4,8,16}", (long long)N);
+  if (L > kMaxL) return fail(SSD_ERR_UNSUPPORTED, "L=%lld above the supported %lld tokens", (long long)L, (long long)kMaxL);
+  if (Dc > kMaxRow || b * L > INT32_MAX / 2 || b * (Dc / 64) > INT32_MAX / 64)
+    return fail(SSD_ERR_UNSUPPORTED, "problem too large");
+  if (segments < 0) return fail(SSD_ERR_UNSUPPORTED, "segments=%d is negative", segments);
+  const int xd = x->dtype;
+  const int64_t sx[3] = {b, L, Dc}, sd[1] = {Dc}, sa[2] = {Dc, N}, sbc[4] = {b, L, G, N},
+                sst[3] = {b, Dc, N};
+  SSD_CHECK(check_tensor(x, "x", -1, 3, sx));
+  SSD_CHECK(check_tensor(dt, "dt", SSD_F32, 3, sx));
+  if (dt_bias) SSD_CHECK(check_tensor(dt_bias, "dt_bias", SSD_F32, 1, sd));
+  SSD_CHECK(check_tensor(A, "A", SSD_F32, 2, sa));
+  SSD_CHECK(check_tensor(B, "B", xd, 4, sbc));
+  SSD_CHECK(check_tensor(C, "C", xd, 4, sbc));
+  if (D) SSD_CHECK(check_tensor(D, "D", SSD_F32, 1, sd));
+  if (init_state) SSD_CHECK(check_tensor(init_state, "init_state", SSD_F32, 3, sst));
+  SSD_CHECK(check_tensor(out, "out", xd, 3, sx));
+  if (final_state) SSD_CHECK(check_tensor(final_state, "final_state", SSD_F32, 3, sst));
+  {
+    const Range ro = range_of(out), rf = range_of(final_state);
+    const ssd_tensor *ins[] = {x, dt, dt_bias, A, B, C, D, init_state};
+    const char *names[] = {"x", "dt", "dt_bias", "A", "B", "C", "D", "init_state"};
+    for (int i = 0; i < 8; ++i) {
+      const Range ri = range_of(ins[i]);
+      if (overlap(ro, ri)) return fail(SSD_ERR_ALIAS, "out overlaps %s", names[i]);
+      if (i == 7 && final_state && init_state && final_state->data == init_state->data) continue;
+      if (overlap(rf, ri)) return fail(SSD_ERR_ALIAS, "final_state overlaps %s", names[i]);
+    }
+    if (overlap(ro, rf)) return fail(SSD_ERR_ALIAS, "out overlaps final_state");
+  }
+  {
+    const ssd_tensor *ts[] = {x, dt, dt_bias, A, B, C, D, init_state, out, final_state};
+    const char *nm[] = {"x", "dt", "dt_bias", "A", "B", "C", "D", "init_state", "out", "final_state"};
+    SSD_CHECK(check_addressable(ts, nm, 10));
+  }
+  // Segments: enough waves for several per SIMD (each wave owns 64 channels
+  // of one batch row); segments are whole 8-token steps.
+  const int64_t waves_per_seg = b * (Dc / 64);
+  const int64_t steps = (L + 7) / 8;
+  int64_t nseg = segments;
+  if (nseg == 0) {
+    const int64_t want = 4LL * 4 * device_cus();
+    nseg = std::max<int64_t>(1, (want + waves_per_seg - 1) / waves_per_seg);
+  }
+  nseg = std::min<int64_t>(std::min<int64_t>(nseg, steps), 1024);
+  const int64_t seg_len = ((steps + nseg - 1) / nseg) * 8;
+  nseg = (L + seg_len - 1) / seg_len;
+
+  ssd::SScanParams p{};
+  p.x = x->data; p.dt = (const float *)dt->data;
+  p.dt_bias = dt_bias ? (const float *)dt_bias->data : nullptr;
+  p.A = (const float *)A->data; p.B = B->data; p.C = C->data;
+  p.D = D ? (const float *)D->data : nullptr;
+  p.init = init_state ? (const float *)init_state->data : nullptr;
+  p.out = out->data; p.final_state = final_state ? (float *)final_state->data : nullptr;
+  p.b = (int)b; p.L = (int)L; p.Dc = (int)Dc; p.G = (int)G; p.seg_len = (int)seg_len; p.nseg = (int)nseg;
+  hipStream_t st = (hipStream_t)stream;
+  void *ws = nullptr;
+  if (nseg > 1) {
+    // scratch: segment end states [b,nseg,D,N] | segment Delta sums [b,nseg,D] | staged init [b,D,N]
+    const size_t n_end = (size_t)(b * nseg * Dc);
+    const size_t off_sd = ((n_end * N * sizeof(float) + 255) / 256) * 256;
+    const size_t off_hc = off_sd + ((n_end * sizeof(float) + 255) / 256) * 256;
+    const size_t total = off_hc + (size_t)(b * Dc * N) * sizeof(float);
+    hipError_t e = hipMallocAsync(&ws, total, st);
+    if (e != hipSuccess || !ws) {
+      (void)hipGetLastError();
+      return fail(SSD_ERR_NOMEM, "scratch of %zu bytes: %s", total, hipGetErrorString(e));
+    }
+    p.hend = (float *)ws;
+    p.sdelta = (float *)((char *)ws + off_sd);
+    p.hcopy = (float *)((char *)ws + off_hc);
+  }
+  int status = SSD_OK;
+  hipError_t e = ssd::launch_sscan(xd, (int)N, p, st);
+  if (e != hipSuccess) status = hip_fail(e, "selective scan launch");
+  if (ws) {
+    e = hipFreeAsync(ws, st);
+    if (e != hipSuccess && status == SSD_OK) status = hip_fail(e, "scratch free");
+  }
+  return status;
+}
+
 int ssd_scan_plan(int64_t b, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, int dtype,
                   int cus, int *algo, int *seg_len) {
   g_last_error.clear();

@@ -90,4 +90,27 @@ hipError_t launch_step(int dtype, int N, float *state, const void *x,
                        const void *C, const float *D, void *out, int b, int H,
                        int P, int G, hipStream_t stream);
 
+// Selective scan with a diagonal A per (channel, state index).  A wave owns
+// 64 channels of one batch row over one segment of seg_len tokens; channels
+// [64k, 64k+64) all read one B/C group (validated on the host).
+struct SScanParams {
+  const void *x;        // [b, L, Dc]  input dtype
+  const float *dt;      // [b, L, Dc]  raw
+  const float *dt_bias; // [Dc] or null
+  const float *A;       // [Dc, N]
+  const void *B;        // [b, L, G, N]
+  const void *C;        // [b, L, G, N]
+  const float *D;       // [Dc] or null
+  const float *init;    // [b, Dc, N] or null
+  void *out;            // [b, L, Dc]
+  float *final_state;   // [b, Dc, N] or null
+  float *hend;          // scratch [b, nseg, Dc, N]: segment end states (nseg > 1)
+  float *sdelta;        // scratch [b, nseg, Dc]: sum of Delta per segment
+  float *hcopy;         // scratch [b, Dc, N]: staged initial state
+  int b, L, Dc, G, seg_len, nseg;
+};
+
+// N in {4, 8, 16}; dtype 1 = bf16, 0 = fp32.
+hipError_t launch_sscan(int dtype, int N, const SScanParams &p, hipStream_t stream);
+
 } // namespace ssd

@@ -179,6 +179,68 @@ WORKLOADS = {
 WORKLOAD_ORDER = list(WORKLOADS)
 
 
+@dataclasses.dataclass
+class SScanInputs:
+    """Host arrays for one selective scan with a diagonal A per (channel,
+    state index).  bf16 tensors hold uint16 bits."""
+    dtype: str
+    x: np.ndarray          # [b,L,D]
+    dt: np.ndarray         # [b,L,D]  f32 (raw)
+    dt_bias: np.ndarray    # [D]      f32
+    A: np.ndarray          # [D,N]    f32
+    B: np.ndarray          # [b,L,G,N]
+    C: np.ndarray          # [b,L,G,N]
+    D: np.ndarray          # [D]      f32
+    init: Optional[np.ndarray]  # [b,D,N] f32 or None
+
+    @property
+    def shape(self):
+        b, L, Dc = self.x.shape
+        return dict(b=b, L=L, D=Dc, G=self.B.shape[2], N=self.B.shape[3])
+
+    def f64(self):
+        """Exact float64 copies, in oracle argument order."""
+        return dict(x=to_f64(self.x, self.dtype), dt=to_f64(self.dt, F32),
+                    dt_bias=to_f64(self.dt_bias, F32), A=to_f64(self.A, F32),
+                    B=to_f64(self.B, self.dtype), C=to_f64(self.C, self.dtype),
+                    D=to_f64(self.D, F32),
+                    init=None if self.init is None else to_f64(self.init, F32))
+
+
+def make_sscan(b, L, Dc, G, N, *, dtype=BF16, seed=5, dt_range=(1e-3, 0.1),
+               init_std: Optional[float] = None) -> SScanInputs:
+    """A[d, n] = -(n + 1) * exp(U(-0.5, 0.5)): the real diagonal A = -(1..N)
+    with a per-entry jitter, so that every (channel, n) has its own decay;
+    per-channel step sizes exp(U(log dt_range)) through dt_bias =
+    softplus^-1(dt); x ~ N(0,1); B, C ~ N(0,1)/sqrt(N); D ~ N(0,1)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    A = -(np.arange(1, N + 1)[None, :] * np.exp(rng.uniform(-0.5, 0.5, size=(Dc, N))))
+    dt_h = np.exp(rng.uniform(np.log(dt_range[0]), np.log(dt_range[1]), size=Dc))
+    D = rng.standard_normal(Dc)
+    x = rng.standard_normal((b, L, Dc))
+    dt_raw = 0.5 * rng.standard_normal((b, L, Dc))
+    Bm = rng.standard_normal((b, L, G, N)) / np.sqrt(N)
+    Cm = rng.standard_normal((b, L, G, N)) / np.sqrt(N)
+    init = None if init_std is None else init_std * rng.standard_normal((b, Dc, N))
+    return SScanInputs(dtype=dtype, x=_store(x, dtype), dt=dt_raw.astype(np.float32),
+                       dt_bias=_inv_softplus(dt_h).astype(np.float32), A=A.astype(np.float32),
+                       B=_store(Bm, dtype), C=_store(Cm, dtype), D=D.astype(np.float32),
+                       init=None if init is None else init.astype(np.float32))
+
+
+# The selective-scan workload: a Mamba-1 2.8B layer (inner width 5120,
+# N = 16) over 4 sequences of 2048 tokens.
+SSCAN_WORKLOADS = {
+    "mamba1_2p8b_b4_L2048_D5120_N16": dict(b=4, L=2048, Dc=5120, G=1, N=16, dtype=BF16, seed=5,
+                                           init_std=0.1),
+}
+
+
+def make_sscan_workload(name: str) -> SScanInputs:
+    w = dict(SSCAN_WORKLOADS[name])
+    return make_sscan(w.pop("b"), w.pop("L"), w.pop("Dc"), w.pop("G"), w.pop("N"), **w)
+
+
 def make_workload(name: str):
     w = dict(WORKLOADS[name])
     kind = w.pop("kind")

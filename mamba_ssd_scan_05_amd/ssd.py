@@ -56,6 +56,8 @@ def lib():
         L.ssd_scan_fwd_rows.restype = ctypes.c_int
         L.ssd_scan_fwd_gated.argtypes = [P] * 11 + [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
         L.ssd_scan_fwd_gated.restype = ctypes.c_int
+        L.ssd_selective_scan_fwd.argtypes = [P] * 10 + [ctypes.c_int, ctypes.c_void_p]
+        L.ssd_selective_scan_fwd.restype = ctypes.c_int
         L.ssd_step.argtypes = [P] * 8 + [ctypes.c_void_p]
         L.ssd_step.restype = ctypes.c_int
         L.ssd_status_string.argtypes = [ctypes.c_int]
@@ -169,6 +171,26 @@ def ssd_scan_fwd_rows(x, dt, dt_bias, A, B, C, D=None, init_state=None, out=None
             describe(x), describe(dt), describe(dt_bias), describe(A), describe(B), describe(C),
             describe(D), describe(init_state), describe(out), describe(final_state),
             int(waves), st)
+    _check(status)
+    return out, final_state
+
+
+def ssd_selective_scan_fwd(x, dt, dt_bias, A, B, C, D=None, init_state=None, out=None,
+                           final_state=None, segments: int = 0, stream=None,
+                           return_final_state: bool = True):
+    """Selective scan with a diagonal A [D, N] per (channel, state index);
+    x, dt [b, L, D]; returns (out, final_state or None)."""
+    if out is None:
+        out = torch.empty_like(x)
+    if final_state is None and return_final_state:
+        final_state = torch.empty((x.shape[0], x.shape[2], B.shape[3]), dtype=torch.float32,
+                                  device=x.device)
+    with _on_device(x):
+        st = _stream(stream, x)
+        status = lib().ssd_selective_scan_fwd(
+            describe(x), describe(dt), describe(dt_bias), describe(A), describe(B), describe(C),
+            describe(D), describe(init_state), describe(out), describe(final_state),
+            int(segments), st)
     _check(status)
     return out, final_state
 

@@ -4,7 +4,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from .inputs import BF16, ScanInputs, StepInputs
+from .inputs import BF16, ScanInputs, SScanInputs, StepInputs
 
 
 def tensor(a, dtype: str, device) -> torch.Tensor:
@@ -15,6 +15,16 @@ def tensor(a, dtype: str, device) -> torch.Tensor:
 
 
 def scan_tensors(si: ScanInputs, device) -> dict:
+    f = "f32"
+    return dict(
+        x=tensor(si.x, si.dtype, device), dt=tensor(si.dt, f, device),
+        dt_bias=tensor(si.dt_bias, f, device), A=tensor(si.A, f, device),
+        B=tensor(si.B, si.dtype, device), C=tensor(si.C, si.dtype, device),
+        D=tensor(si.D, f, device),
+        init_state=None if si.init is None else tensor(si.init, f, device))
+
+
+def sscan_tensors(si: SScanInputs, device) -> dict:
     f = "f32"
     return dict(
         x=tensor(si.x, si.dtype, device), dt=tensor(si.dt, f, device),

@@ -28,6 +28,7 @@ def declared_functions():
 def test_exports_every_declared_symbol(ssd):
     names = declared_functions()
     assert {"ssd_scan_fwd", "ssd_step", "ssd_scan_fwd_algo", "ssd_scan_fwd_rows", "ssd_scan_fwd_gated",
+            "ssd_selective_scan_fwd",
             "ssd_scan_plan", "ssd_status_string", "ssd_last_error", "ssd_version"} <= set(names)
     raw = ctypes.CDLL(ssd.LIB_PATH)
     for n in names:
@@ -284,3 +285,64 @@ def test_gated_rejections(ssd):
     b = _scan_args()
     b["x"] = None
     assert call(b, torch.zeros(1, 100, 4, 16, dtype=torch.bfloat16)) == 1
+
+
+def _sscan_args(b=1, L=50, Dc=128, G=1, N=16, dtype=torch.bfloat16):
+    return dict(x=torch.zeros(b, L, Dc, dtype=dtype), dt=torch.zeros(b, L, Dc),
+                dt_bias=torch.zeros(Dc), A=-torch.ones(Dc, N), B=torch.zeros(b, L, G, N, dtype=dtype),
+                C=torch.zeros(b, L, G, N, dtype=dtype), D=torch.zeros(Dc),
+                init_state=torch.zeros(b, Dc, N), out=torch.zeros(b, L, Dc, dtype=dtype),
+                final_state=torch.zeros(b, Dc, N))
+
+
+SSCAN_CASES = [
+    ("x_none", lambda a: a.update(x=None), 1),
+    ("A_none", lambda a: a.update(A=None), 1),
+    ("C_none", lambda a: a.update(C=None), 1),
+    ("out_none", lambda a: a.update(out=None), 1),
+    ("L_zero", lambda a: a.update(x=torch.zeros(1, 0, 128, dtype=torch.bfloat16)), 2),
+    ("x_rank4", lambda a: a.update(x=torch.zeros(1, 50, 2, 64, dtype=torch.bfloat16)), 2),
+    ("A_wrong_shape", lambda a: a.update(A=-torch.ones(16, 128)), 2),
+    ("dt_wrong_shape", lambda a: a.update(dt=torch.zeros(1, 49, 128)), 2),
+    ("D_not_multiple_of_G", lambda a: a.update(B=torch.zeros(1, 50, 3, 16, dtype=torch.bfloat16),
+                                               C=torch.zeros(1, 50, 3, 16, dtype=torch.bfloat16)), 2),
+    ("dt_bf16", lambda a: a.update(dt=torch.zeros(1, 50, 128, dtype=torch.bfloat16)), 3),
+    ("B_f32_with_bf16_x", lambda a: a.update(B=torch.zeros(1, 50, 1, 16)), 3),
+    ("x_noncontiguous", lambda a: a.update(
+        x=torch.zeros(1, 128, 50, dtype=torch.bfloat16).transpose(1, 2)), 4),
+    ("channels_per_group_not_64k", lambda a: a.update(
+        x=torch.zeros(1, 50, 96, dtype=torch.bfloat16), dt=torch.zeros(1, 50, 96), dt_bias=torch.zeros(96),
+        A=-torch.ones(96, 16), D=torch.zeros(96), init_state=torch.zeros(1, 96, 16),
+        out=torch.zeros(1, 50, 96, dtype=torch.bfloat16), final_state=torch.zeros(1, 96, 16)), 5),
+    ("N_unsupported", lambda a: a.update(A=-torch.ones(128, 32), B=torch.zeros(1, 50, 1, 32, dtype=torch.bfloat16),
+                                         C=torch.zeros(1, 50, 1, 32, dtype=torch.bfloat16),
+                                         init_state=torch.zeros(1, 128, 32), final_state=torch.zeros(1, 128, 32)), 5),
+    ("out_aliases_x", lambda a: a.update(out=a["x"]), 6),
+    ("final_overlaps_A", lambda a: a.update(final_state=a["A"].view(1, 128, 16)), 6),
+]
+
+
+@pytest.mark.parametrize("name,mutate,status", SSCAN_CASES, ids=[c[0] for c in SSCAN_CASES])
+def test_selective_scan_rejects(ssd, name, mutate, status):
+    a = _sscan_args()
+    mutate(a)
+    d = ssd.describe
+    st = ssd.lib().ssd_selective_scan_fwd(d(a["x"]), d(a["dt"]), d(a["dt_bias"]), d(a["A"]), d(a["B"]),
+                                          d(a["C"]), d(a["D"]), d(a["init_state"]), d(a["out"]),
+                                          d(a["final_state"]), 0, None)
+    assert st == status, (st, ssd.ssd_last_error())
+    assert ssd.ssd_last_error()
+
+
+def test_selective_scan_host_memory_and_segments(ssd):
+    a = _sscan_args()
+    d = ssd.describe
+    args = [d(a[k]) for k in ("x", "dt", "dt_bias", "A", "B", "C", "D", "init_state", "out", "final_state")]
+    assert ssd.lib().ssd_selective_scan_fwd(*args, -1, None) == 5      # negative segment count
+    st = ssd.lib().ssd_selective_scan_fwd(*args, 0, None)               # host memory: refused
+    assert st == 4, ssd.ssd_last_error()
+    # final state in place of the initial state passes validation (then the
+    # host memory is refused)
+    a["final_state"] = a["init_state"]
+    args = [d(a[k]) for k in ("x", "dt", "dt_bias", "A", "B", "C", "D", "init_state", "out", "final_state")]
+    assert ssd.lib().ssd_selective_scan_fwd(*args, 0, None) == 4
