@@ -33,6 +33,11 @@ if ROOT not in sys.path:
 METRIC = "SSD fwd scan tokens/s and % of roofline, 2.7B layer shape L=4096, 1 GPU"
 WORKLOAD = "mamba2_2p7b_b4_L4096_H80_P64_N128"
 DECODE = "decode_step_b256_H80_P64_N128_T64"
+SSCAN = "mamba1_2p8b_b4_L2048_D5120_N16"
+# Vector ALU of MI355X without packed fp32: 256 CUs x 4 SIMDs x 16 lanes at
+# 2.4 GHz = 39.3e12 full-rate lane operations per second; a transcendental
+# (exp2) occupies four full-rate slots.
+VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # dense bf16 MFMA, 256 CU x 4096 FLOP/clk x 2.4 GHz
 ELEM = {"bf16": 2, "f32": 4}
@@ -103,6 +108,44 @@ def cpu_baseline(si, reps):
                       "%.2f s each" % (reps, best)}
 
 
+def sscan_ops(b, L, Dc, N):
+    """Full-rate lane-operation equivalents of one selective scan, counted
+    for a single pass of the recurrence: per (token, channel) and state
+    index one Delta*A product, one exp2 (4 slots), Delta*x*B, the state
+    fma and the readout fma; softplus (two exp2/log2 and five more
+    operations) and D*x once per (token, channel)."""
+    per = N * (1 + 4 + 1 + 1 + 1) + (2 * 4 + 5) + 1
+    return b * L * Dc * per
+
+
+def bench_sscan(ssd, staging, inputs, torch, dev):
+    si = inputs.make_sscan_workload(SSCAN)
+    t = staging.sscan_tensors(si, dev)
+    out = torch.empty_like(t["x"])
+    b, L, Dc = si.x.shape
+    N = si.B.shape[3]
+    fin = torch.empty((b, Dc, N), dtype=torch.float32, device=dev)
+    for _ in range(3):
+        ssd.ssd_selective_scan_fwd(**t, out=out, final_state=fin)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record()
+    for _ in range(reps):
+        ssd.ssd_selective_scan_fwd(**t, out=out, final_state=fin)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    ops = sscan_ops(b, L, Dc, N)
+    nbytes = b * L * Dc * (2 * ELEM[si.dtype] + 4) + 2 * b * L * N * ELEM[si.dtype] + Dc * N * 4 \
+        + 2 * b * Dc * N * 4 + 2 * Dc * 4
+    return {"workload": SSCAN, "ms_per_step": ms, "tokens_per_s": b * L / (ms * 1e-3),
+            "roofline": {"bound": "alu", "achieved": ops / (ms * 1e-3) / 1e9,
+                         "peak": VALU_LANE_OPS / 1e9, "unit": "G lane-op/s",
+                         "frac": ops / (ms * 1e-3) / VALU_LANE_OPS, "ops_per_launch": ops},
+            "hbm_GBs": nbytes / (ms * 1e-3) / 1e9, "bytes_per_launch": nbytes}
+
+
 def bench_decode(ssd, staging, inputs, torch, dev):
     sp = inputs.make_workload(DECODE)
     t = staging.step_tensors(sp, dev)
@@ -136,6 +179,8 @@ def main():
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-sscan", action="store_true",
+                    help="skip the timing of the selective scan (diagonal A per channel)")
     ap.add_argument("--no-gated", action="store_true",
                     help="skip the timing of the gated scan (out = y * silu(z))")
     ap.add_argument("--no-alt", action="store_true", help="skip timing the other algorithm")
@@ -274,6 +319,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         extra["copy_probe_bytes"] = 2 * (1 << 30)
+    if not args.no_sscan:
+        print("bench: selective scan %s" % SSCAN, file=sys.stderr, flush=True)
+        extra["selective_scan"] = bench_sscan(ssd, staging, inputs, torch, dev)
     if not args.no_decode:
         print("bench: decode step workload", file=sys.stderr, flush=True)
         extra["decode_step"] = bench_decode(ssd, staging, inputs, torch, dev)

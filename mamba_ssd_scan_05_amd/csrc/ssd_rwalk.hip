@@ -232,11 +232,11 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
   // than four waves the byte counts are formed before the select, which
   // makes the choice a scalar select and keeps the loop body one scheduling
   // region; with one wave per SIMD the branch form schedules better (both
-  // measured).
+  // measured; the gated walk keeps the branch form as well).
   auto fetch_bcx = [&](int k) {
     const int t0 = 64 * k, nv = min(64, L - t0);
     uint32_t bcb;
-    if constexpr (W > 4) {
+    if constexpr (W > 4 && !GATED) {
       const uint32_t bcb0 = (uint32_t)(((int64_t)(nv - 1) * rowB + N) * 2);
       bcb = nv > 0 ? bcb0 : 0u;
     } else {
@@ -250,7 +250,7 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
       rC[i] = bload16(rsC, offBC[i]);
     }
     uint32_t nbX;
-    if constexpr (W > 4) {
+    if constexpr (W > 4 && !GATED) {
       const uint32_t nbX0 = (uint32_t)(((int64_t)(nv - 1) * rowX + 16) * 2);
       nbX = nv > 0 ? nbX0 : 0u;
     } else {
@@ -313,12 +313,22 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
     // they are scheduled against, instead of becoming scalar branches; every
     // arm is computed before the choice so that none becomes a branch.
     float e_v = e_in;
-    __asm__("" : "+v"(clast), "+v"(e_v));
+    if constexpr (GATED)
+      __asm__ volatile("" : "+v"(clast), "+v"(e_v));
+    else
+      __asm__("" : "+v"(clast), "+v"(e_v));
     const float q = c - hw_log2(dl); // +inf where Delta = 0
     const bool fast = fabsf(clast) <= kSpanMax;
     const bool keep = e_v >= -clast - kExpLim && e_v <= kExpLim;
-    const float n_up = floorf(kExpLim - e_v), n_fast = keep ? 0.f : n_up, n_slow = -rintf(e_v);
-    const float n = fast ? n_fast : n_slow; // octaves
+    float n; // octaves
+    if constexpr (GATED) {
+      // (the gated walk holds the gate inputs as well; with every arm
+      // computed up front it spills)
+      n = fast ? (keep ? 0.f : floorf(kExpLim - e_v)) : -rintf(e_v);
+    } else {
+      const float n_up = floorf(kExpLim - e_v), n_fast = keep ? 0.f : n_up, n_slow = -rintf(e_v);
+      n = fast ? n_fast : n_slow;
+    }
     const float ek = e_v + n;
     sF0[sl][w][l] = hw_exp2((fast ? 0.f : clast) - q - ek);
     sF1[sl][w][l] = hw_exp2(c + ek);
@@ -494,9 +504,16 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
   };
   auto flush_y = [&](int k) {
     const int t0 = 64 * k, nv = min(64, L - t0);
-    // byte count before the select: a scalar select, not a branch
-    const uint32_t nbY = (uint32_t)(((int64_t)(nv - 1) * rowX + rows_valid) * 2);
-    const auto rs = make_rsrc(Ywg + (int64_t)max(t0, 0) * rowX, k >= 0 ? nbY : 0u);
+    // byte count before the select: a scalar select, not a branch (the gated
+    // walk keeps the branch form, which schedules better there)
+    uint32_t nbY;
+    if constexpr (GATED) {
+      nbY = k >= 0 ? (uint32_t)(((int64_t)(nv - 1) * rowX + rows_valid) * 2) : 0u;
+    } else {
+      const uint32_t nbY0 = (uint32_t)(((int64_t)(nv - 1) * rowX + rows_valid) * 2);
+      nbY = k >= 0 ? nbY0 : 0u;
+    }
+    const auto rs = make_rsrc(Ywg + (int64_t)max(t0, 0) * rowX, nbY);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int q = tid + i * NTH, t = q / (2 * W), j = q % (2 * W);
