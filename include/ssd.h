@@ -230,7 +230,9 @@ int ssd_step(ssd_tensor *state, const ssd_tensor *x, const ssd_tensor *dt,
  *   final_state [b, D, N]     f32, written; may be init_state    NULL => skip
  *   segments    the sequence is cut into this many segments walked in
  *               parallel (their entering states folded from a first
- *               state-only pass); 0 chooses from the device size.  The
+ *               state-only pass); 0 chooses from the device size.  Raised
+ *               if needed so that one segment's x, dt or out stays under
+ *               2 GiB, capped at 1024 and at one segment per 8 tokens.  The
  *               result does not depend on it beyond rounding order.
  *
  * Supported sizes: N in {4, 8, 16}, D/G a multiple of 64 (64 channels of

@@ -598,11 +598,6 @@ int ssd_selective_scan_fwd(const ssd_tensor *x, const ssd_tensor *dt, const ssd_
     }
     if (overlap(ro, rf)) return fail(SSD_ERR_ALIAS, "out overlaps final_state");
   }
-  {
-    const ssd_tensor *ts[] = {x, dt, dt_bias, A, B, C, D, init_state, out, final_state};
-    const char *nm[] = {"x", "dt", "dt_bias", "A", "B", "C", "D", "init_state", "out", "final_state"};
-    SSD_CHECK(check_addressable(ts, nm, 10));
-  }
   // Segments: about five waves per SIMD (each wave owns 64 channels of one
   // batch row; the kernel is bound by the vector ALU, and a multiple of the
   // SIMD count avoids a partial last round -- measured on MI355X: 16
@@ -615,10 +610,21 @@ int ssd_selective_scan_fwd(const ssd_tensor *x, const ssd_tensor *dt, const ssd_
     const int64_t want = 20LL * device_cus();
     nseg = std::max<int64_t>(1, (want + waves_per_seg / 2) / waves_per_seg);
   }
+  // A wave addresses its segment of x, dt and out through 32-bit byte
+  // ranges: at least enough segments to keep one segment under 2 GiB.
+  const int64_t min_nseg = (L * Dc * 4 + ((int64_t)1 << 31) - 1) >> 31;
+  nseg = std::max<int64_t>(nseg, min_nseg);
   nseg = std::min<int64_t>(std::min<int64_t>(nseg, steps), 1024);
   const int64_t seg_len = ((steps + nseg - 1) / nseg) * 8;
   nseg = (L + seg_len - 1) / seg_len;
+  if (seg_len * Dc * 4 >= ((int64_t)1 << 31) || b * (Dc / 64) * nseg > INT32_MAX)
+    return fail(SSD_ERR_UNSUPPORTED, "problem too large");
 
+  {
+    const ssd_tensor *ts[] = {x, dt, dt_bias, A, B, C, D, init_state, out, final_state};
+    const char *nm[] = {"x", "dt", "dt_bias", "A", "B", "C", "D", "init_state", "out", "final_state"};
+    SSD_CHECK(check_addressable(ts, nm, 10));
+  }
   ssd::SScanParams p{};
   p.x = x->data; p.dt = (const float *)dt->data;
   p.dt_bias = dt_bias ? (const float *)dt_bias->data : nullptr;

@@ -91,11 +91,11 @@ CASES = [
 ]
 
 
-def _fake(ssd, shape, dtype):
+def _fake(ssd, shape, dtype, slot=0):
     """A descriptor of a dense tensor at a fake aligned address (validation
-    only reads the descriptor)."""
+    only reads the descriptor); distinct slots do not overlap."""
     t = ssd.SsdTensor()
-    t.data = 1 << 20
+    t.data = (1 << 20) + slot * (1 << 44)
     t.dtype = dtype
     t.ndim = len(shape)
     st = 1
@@ -346,3 +346,17 @@ def test_selective_scan_host_memory_and_segments(ssd):
     a["final_state"] = a["init_state"]
     args = [d(a[k]) for k in ("x", "dt", "dt_bias", "A", "B", "C", "D", "init_state", "out", "final_state")]
     assert ssd.lib().ssd_selective_scan_fwd(*args, 0, None) == 4
+
+
+def test_selective_scan_oversized(ssd):
+    # one 2^24-token sequence of 65536 channels: even 1024 segments leave a
+    # segment above the 32-bit byte range; refused on the host
+    b, L, Dc, G, N = 1, 1 << 24, 1 << 16, 1, 16
+    bf, f32 = 1, 0
+    ts = [_fake(ssd, (b, L, Dc), bf, 1), _fake(ssd, (b, L, Dc), f32, 2), None,
+          _fake(ssd, (Dc, N), f32, 3), _fake(ssd, (b, L, G, N), bf, 4), _fake(ssd, (b, L, G, N), bf, 5),
+          None, None, _fake(ssd, (b, L, Dc), bf, 6), None]
+    ptrs = [ctypes.byref(t) if t is not None else None for t in ts]
+    st = ssd.lib().ssd_selective_scan_fwd(*ptrs, 0, None)
+    assert st == 5, (st, ssd.ssd_last_error())
+    assert "too large" in ssd.ssd_last_error()
