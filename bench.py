@@ -175,7 +175,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--algo", choices=["auto", "fused", "chunked", "rows", "rows_seg"], default="auto")
+    ap.add_argument("--algo", choices=["auto", "fused", "chunked", "rows"], default="auto")
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
@@ -199,11 +199,9 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    names = {ssd.SSD_ALGO_FUSED: "fused", ssd.SSD_ALGO_CHUNKED: "chunked", ssd.SSD_ALGO_ROWS: "rows",
-             ssd.SSD_ALGO_ROWS_SEG: "rows_seg"}
+    names = {ssd.SSD_ALGO_FUSED: "fused", ssd.SSD_ALGO_CHUNKED: "chunked", ssd.SSD_ALGO_ROWS: "rows"}
     algo = {"auto": ssd.SSD_ALGO_AUTO, "fused": ssd.SSD_ALGO_FUSED,
-            "chunked": ssd.SSD_ALGO_CHUNKED, "rows": ssd.SSD_ALGO_ROWS,
-            "rows_seg": ssd.SSD_ALGO_ROWS_SEG}[args.algo]
+            "chunked": ssd.SSD_ALGO_CHUNKED, "rows": ssd.SSD_ALGO_ROWS}[args.algo]
     si = inputs.make_workload(args.workload)
     shp = si.shape
     b, L, H, P, G, N = (shp[k] for k in ("b", "L", "H", "P", "G", "N"))
@@ -252,9 +250,6 @@ def main():
         dominant = ("rwalk_kernel (row-sliced walk) with its scores_kernel precompute: the "
                     "timed duration is the whole call, both launches")
         seg_len = L
-    elif used_algo == "rows_seg":
-        dominant = ("ssd_scan_fwd row walk over segments of %d tokens: step sizes + segment-state walk + "
-                    "state pass + scores + row walk (5 launches)" % seg_len)
     else:
         dominant = ("ssd_scan_fwd chunked path, segment %d: cumsum + chunk-state walk + "
                     "state pass + chunk-output walk (4 launches)" % seg_len)
@@ -274,8 +269,7 @@ def main():
         for name_a, a, q in (("rows", ssd.SSD_ALGO_ROWS, Q), ("fused", ssd.SSD_ALGO_FUSED, Q),
                              ("chunked_256", ssd.SSD_ALGO_CHUNKED, 256),
                              ("chunked_1024", ssd.SSD_ALGO_CHUNKED, 1024),
-                             ("chunked_2048", ssd.SSD_ALGO_CHUNKED, 2048),
-                             ("rows_seg_1024", ssd.SSD_ALGO_ROWS_SEG, 1024)):
+                             ("chunked_2048", ssd.SSD_ALGO_CHUNKED, 2048)):
             def run_alt():
                 ssd.ssd_scan_fwd(**t, out=out, final_state=fin, chunk=q, algo=a)
             try:

@@ -76,15 +76,10 @@ enum {
                            sequence in order with the state in registers      */
   SSD_ALGO_CHUNKED = 2, /* chunk-parallel: log-decay cumsum, chunk states,
                            inter-chunk state passing, fused intra+output      */
-  SSD_ALGO_ROWS = 3,    /* bf16, N in {32, 64, 128}: the causal C B^T scores
+  SSD_ALGO_ROWS = 3     /* bf16, N in {32, 64, 128}: the causal C B^T scores
                            of each (batch, group, 64-token block) computed
                            once and shared by the heads of the group; each
                            wave walks 16 state rows of one head            */
-  SSD_ALGO_ROWS_SEG = 4 /* the row walk over segments of `chunk` tokens:
-                           segment end states (state-only walk), states
-                           entering the segments (state passing), then the
-                           row walk of every segment from its entering
-                           state (for long sequences with few rows)        */
 };
 
 /* Dense tensor descriptor.  shape/strides beyond ndim are ignored; strides
@@ -133,10 +128,8 @@ int ssd_scan_fwd(const ssd_tensor *x, const ssd_tensor *dt,
                  ssd_tensor *final_state, int chunk, void *stream);
 
 /* ssd_scan_fwd with an explicit algorithm (SSD_ALGO_*). Same contract;
- * SSD_ALGO_CHUNKED and SSD_ALGO_ROWS_SEG use `chunk` as their segment
- * length (ROWS_SEG with chunk >= L is one segment); SSD_ALGO_ROWS and
- * SSD_ALGO_ROWS_SEG return SSD_ERR_UNSUPPORTED for fp32 inputs or N outside
- * {32, 64, 128}.
+ * SSD_ALGO_CHUNKED uses `chunk` as its segment length; SSD_ALGO_ROWS
+ * returns SSD_ERR_UNSUPPORTED for fp32 inputs or N outside {32, 64, 128}.
  * SSD_ALGO_ROWS and SSD_ALGO_CHUNKED take scratch from the stream-ordered
  * allocator (ROWS: b*G*ceil(L/64)*8 KiB). */
 int ssd_scan_fwd_algo(const ssd_tensor *x, const ssd_tensor *dt,
@@ -260,7 +253,7 @@ int ssd_selective_scan_fwd(const ssd_tensor *x, const ssd_tensor *dt,
  * ssd_scan_plan -- the plan SSD_ALGO_AUTO uses for a shape on a device with
  * `cus` compute units for inputs of element type `dtype` (SSD_BF16 or
  * SSD_F32), host only, no HIP call: *algo is SSD_ALGO_FUSED,
- * SSD_ALGO_CHUNKED, SSD_ALGO_ROWS or SSD_ALGO_ROWS_SEG and *seg_len the segment length (L for
+ * SSD_ALGO_CHUNKED or SSD_ALGO_ROWS and *seg_len the segment length (L for
  * the single-pass walks).
  * The choice trades the spread of (batch, head, segment) walks over the
  * compute units against the extra state-only pass and state traffic of

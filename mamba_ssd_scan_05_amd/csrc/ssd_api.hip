@@ -320,78 +320,6 @@ int run_rows(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bia
     p.b = (int)s.b; p.L = (int)s.L; p.H = (int)s.H; p.G = (int)s.G; p.P = (int)s.P;
     p.rows_per_bg = (int)((s.H / s.G) * s.P);
     p.wg_per_bg = (p.rows_per_bg + 16 * W - 1) / (16 * W);
-    p.seg_len = (int)(nsub * 64);
-    p.nseg = 1;
-    e = ssd::launch_rwalk((int)s.N, W, p, st);
-    if (e != hipSuccess) { status = hip_fail(e, "row walk launch"); break; }
-  } while (0);
-  e = hipFreeAsync(ws, st);
-  if (e != hipSuccess && status == SSD_OK) status = hip_fail(e, "scratch free");
-  return status;
-}
-
-// The row walk over segments of seg_len tokens: each segment's end state
-// from a zero start (the state-only walk of the chunked pipeline), the
-// states entering the segments (state passing), the score tiles, then the
-// row walk of every segment from its entering state.
-int run_rows_seg(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bias,
-                 const ssd_tensor *A, const ssd_tensor *B, const ssd_tensor *C, const ssd_tensor *D,
-                 const ssd_tensor *z, const ssd_tensor *init, ssd_tensor *out, ssd_tensor *fin,
-                 const ScanShape &s, int W, int seg_len, hipStream_t st) {
-  const int64_t nsub = (s.L + 63) / 64;
-  const int64_t nseg = (s.L + seg_len - 1) / seg_len;
-  const int64_t PN = s.P * s.N;
-  const size_t n_tok = (size_t)(s.b * s.H * s.L);
-  const size_t n_seg = (size_t)(s.b * s.H * nseg);
-  // scratch: score tiles [b,G,nsub,64,64] bf16 | Delta [b,H,L] | segment
-  // log2 decays [b,H,nseg] (padded) | segment states [b,H,nseg,P,N]
-  const size_t off_delta = (size_t)(s.b * s.G * nsub) * 64 * 64 * 2;
-  const size_t off_dec = off_delta + ((n_tok * sizeof(float) + 255) / 256) * 256;
-  const size_t off_states = off_dec + ((n_seg * sizeof(float) + 255) / 256) * 256;
-  const size_t total = off_states + n_seg * (size_t)PN * sizeof(float);
-  void *ws = nullptr;
-  hipError_t e = hipMallocAsync(&ws, total, st);
-  if (e != hipSuccess || !ws) {
-    (void)hipGetLastError();
-    return fail(SSD_ERR_NOMEM, "scratch of %zu bytes: %s", total, hipGetErrorString(e));
-  }
-  float *delta = (float *)((char *)ws + off_delta);
-  float *seg_decay = (float *)((char *)ws + off_dec);
-  float *states = (float *)((char *)ws + off_states);
-  int status = SSD_OK;
-  do {
-    e = ssd::launch_delta((const float *)dt->data, dt_bias ? (const float *)dt_bias->data : nullptr,
-                          delta, (int)s.b, (int)s.L, (int)s.H, st);
-    if (e != hipSuccess) { status = hip_fail(e, "delta launch"); break; }
-    ssd::WalkParams w{};
-    w.x = x->data; w.dt = delta; w.dt_bias = nullptr; w.A = (const float *)A->data;
-    w.B = B->data; w.C = C->data; w.D = D ? (const float *)D->data : nullptr;
-    w.b = (int)s.b; w.L = (int)s.L; w.H = (int)s.H; w.G = (int)s.G;
-    w.seg_len = seg_len; w.nseg = (int)nseg;
-    w.init = nullptr; w.out = nullptr; w.state_out = states; w.final_state = nullptr;
-    w.seg_decay = seg_decay;
-    e = ssd::launch_walk(x->dtype, (int)s.P, (int)s.N, ssd::kWalkChunkState, w, st);
-    if (e != hipSuccess) { status = hip_fail(e, "segment-state launch"); break; }
-    e = ssd::launch_state_pass(states, seg_decay, init ? (const float *)init->data : nullptr,
-                               (int)s.b, (int)s.H, (int)PN, (int)nseg, st);
-    if (e != hipSuccess) { status = hip_fail(e, "state-pass launch"); break; }
-    e = ssd::launch_scores(B->data, C->data, ws, (int)s.b, (int)s.L, (int)s.G, (int)s.N, st);
-    if (e != hipSuccess) { status = hip_fail(e, "scores launch"); break; }
-    ssd::RWalkParams p{};
-    p.x = x->data; p.dt = (const float *)dt->data;
-    p.dt_bias = dt_bias ? (const float *)dt_bias->data : nullptr;
-    p.A = (const float *)A->data; p.B = B->data; p.C = C->data;
-    p.D = D ? (const float *)D->data : nullptr;
-    p.scores = ws;
-    p.init = states;
-    p.out = out->data;
-    p.z = z ? z->data : nullptr;
-    p.final_state = fin ? (float *)fin->data : nullptr;
-    p.b = (int)s.b; p.L = (int)s.L; p.H = (int)s.H; p.G = (int)s.G; p.P = (int)s.P;
-    p.rows_per_bg = (int)((s.H / s.G) * s.P);
-    p.wg_per_bg = (p.rows_per_bg + 16 * W - 1) / (16 * W);
-    p.seg_len = seg_len;
-    p.nseg = (int)nseg;
     e = ssd::launch_rwalk((int)s.N, W, p, st);
     if (e != hipSuccess) { status = hip_fail(e, "row walk launch"); break; }
   } while (0);
@@ -461,9 +389,9 @@ Plan choose_plan(const ScanShape &s, int dtype, int cus) {
     const int64_t S = (s.L + seg - 1) / seg;
     if (S < 2) continue;
     const double sub = (double)(seg / 64);
+    const double walk = share((double)(units * S) / cus) * sub * t_seg;
     const double state = state_rel * share((double)(units * (S - 1)) / cus) * sub * t_seg;
     const double pass = 2.0 * units * S * s.P * s.N * 4.0 / pass_bw * 1e6;
-    const double walk = share((double)(units * S) / cus) * sub * t_seg;
     const double t = walk + state + pass + fixed_us;
     if (t < best_t) {
       best_t = t;
@@ -479,9 +407,9 @@ int scan_dispatch(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *d
                   ssd_tensor *out, ssd_tensor *final_state, const ScanShape &s, int chunk, int algo,
                   void *stream) {
   if (algo != SSD_ALGO_AUTO && algo != SSD_ALGO_FUSED && algo != SSD_ALGO_CHUNKED &&
-      algo != SSD_ALGO_ROWS && algo != SSD_ALGO_ROWS_SEG)
+      algo != SSD_ALGO_ROWS)
     return fail(SSD_ERR_UNSUPPORTED, "unknown algorithm %d", algo);
-  if ((algo == SSD_ALGO_ROWS || algo == SSD_ALGO_ROWS_SEG) && !rows_supported(x->dtype, s.N))
+  if (algo == SSD_ALGO_ROWS && !rows_supported(x->dtype, s.N))
     return fail(SSD_ERR_UNSUPPORTED, "row-sliced walk needs bf16 inputs and N in {32,64,128}");
   {
     const ssd_tensor *ts[] = {x, dt, dt_bias, A, B, C, D, z, init_state, out, final_state};
@@ -495,15 +423,6 @@ int scan_dispatch(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *d
     chunk = plan.seg_len;
   }
   hipStream_t st = (hipStream_t)stream;
-  if (algo == SSD_ALGO_ROWS_SEG) {
-    if (chunk >= s.L)
-      return run_rows(x, dt, dt_bias, A, B, C, D, z, init_state, out, final_state, s, rows_waves(s, cus), st);
-    const int64_t nseg = (s.L + chunk - 1) / chunk;
-    ScanShape sp = s; // the segments are walked side by side, like more batch rows
-    sp.b = s.b * nseg;
-    return run_rows_seg(x, dt, dt_bias, A, B, C, D, z, init_state, out, final_state, s, rows_waves(sp, cus),
-                        chunk, st);
-  }
   if (algo == SSD_ALGO_ROWS)
     return run_rows(x, dt, dt_bias, A, B, C, D, z, init_state, out, final_state, s, rows_waves(s, cus), st);
   if (algo == SSD_ALGO_FUSED)

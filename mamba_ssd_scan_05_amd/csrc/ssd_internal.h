@@ -58,13 +58,11 @@ struct RWalkParams {
   const void *C;        // [b, L, G, N] bf16
   const float *D;       // [H] or null
   const void *scores;   // [b, G, ceil(L/64), 64, 64] bf16 from launch_scores
-  const float *init;    // state entering each segment, [b, H, nseg, P, N], or null
+  const float *init;    // [b, H, P, N] or null
   void *out;            // [b, L, H, P] bf16
   const void *z;        // [b, L, H, P] bf16 gate input (out = y * silu(z)) or null
   float *final_state;   // [b, H, P, N] or null
   int b, L, H, G, P, rows_per_bg, wg_per_bg;
-  int seg_len, nseg;    // the sequence in nseg segments of seg_len tokens
-                        // (a multiple of 64); one segment: seg_len >= L
 };
 
 // Causal score tiles C_t . B_t' of every (batch, group, 64-token sub-block),

@@ -145,20 +145,13 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
   constexpr int YLD = 16 * W + 8;
   __shared__ __attribute__((aligned(16))) __bf16 sY[2][(W > 4 ? 64 : 1) * YLD];
 
-  const int H = prm.H, G = prm.G, Ls = prm.L, P = prm.P;
+  const int H = prm.H, G = prm.G, L = prm.L, P = prm.P;
   const int nwg = gridDim.x, bid = blockIdx.x;
   // XCD-aware order: consecutive ids go round-robin to the 8 XCDs; give
   // each XCD a contiguous range of logical ids so that the workgroups of one
   // (batch, group) share its B/C/score tiles through one L2.
   const int logical = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;
-  // Segments of the sequence (one when the whole sequence is walked): the
-  // workgroup walks tokens [tb, tb + L) of its (batch, group) rows,
-  // starting from the state entering the segment.
-  const int per_seg = nwg / prm.nseg;
-  const int seg = logical / per_seg, lseg = logical % per_seg;
-  const int bg = lseg / prm.wg_per_bg, wi = lseg % prm.wg_per_bg;
-  const int tb = seg * prm.seg_len;
-  const int L = min(prm.seg_len, Ls - tb);
+  const int bg = logical / prm.wg_per_bg, wi = logical % prm.wg_per_bg;
   const int g = bg % G, ib = bg / G;
   const int tid = threadIdx.x, l = tid & 63, li = l & 15, lg = l >> 4;
   // The wave index is uniform across the wave; readfirstlane makes that
@@ -181,20 +174,17 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
 #pragma unroll
   for (int k = 0; k < NT; ++k) hs[k] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (prm.init != nullptr && active) {
-    const float *irow = prm.init + ((int64_t)(ib * H + h) * prm.nseg + seg) * P * N + (int64_t)(p0 + li) * N;
 #pragma unroll
-    for (int k = 0; k < NT; ++k) hs[k] = *reinterpret_cast<const f32x4 *>(irow + 16 * k + 4 * lg);
+    for (int k = 0; k < NT; ++k) hs[k] = *reinterpret_cast<const f32x4 *>(prm.init + srow + 16 * k + 4 * lg);
   }
 
   const int64_t rowB = (int64_t)G * N, rowX = (int64_t)H * P;
-  const int64_t tok0 = (int64_t)ib * Ls + tb; // first token of the walk
-  const __bf16 *Bbase = reinterpret_cast<const __bf16 *>(prm.B) + (tok0 * G + g) * N;
-  const __bf16 *Cbase = reinterpret_cast<const __bf16 *>(prm.C) + (tok0 * G + g) * N;
-  const __bf16 *Xbase = reinterpret_cast<const __bf16 *>(prm.x) + tok0 * rowX + (int64_t)h * P + p0;
-  const float *dtbase = prm.dt + tok0 * H + h;
+  const __bf16 *Bbase = reinterpret_cast<const __bf16 *>(prm.B) + ((int64_t)ib * L * G + g) * N;
+  const __bf16 *Cbase = reinterpret_cast<const __bf16 *>(prm.C) + ((int64_t)ib * L * G + g) * N;
+  const __bf16 *Xbase = reinterpret_cast<const __bf16 *>(prm.x) + (int64_t)ib * L * rowX + (int64_t)h * P + p0;
+  const float *dtbase = prm.dt + (int64_t)ib * L * H + h;
   const int nsub = (L + 63) / 64;
-  const __bf16 *Sbase = reinterpret_cast<const __bf16 *>(prm.scores) +
-                        ((int64_t)bg * ((Ls + 63) / 64) + tb / 64) * 4096;
+  const __bf16 *Sbase = reinterpret_cast<const __bf16 *>(prm.scores) + (int64_t)bg * nsub * 4096;
 
   // The C tile is stored with the columns of each 32-column group permuted
   // (column 32ks + 8g + j holds n = 32ks + kperm(g, j)), so that a state-term
@@ -446,9 +436,9 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
   // y = acc + D x stored directly; rows past the end (and idle waves) are
   // dropped.
   const uint32_t offY = (uint32_t)((li * rowX + 4 * lg) * 2);
-  __bf16 *Ybase = reinterpret_cast<__bf16 *>(prm.out) + tok0 * rowX + (int64_t)h * P + p0;
+  __bf16 *Ybase = reinterpret_cast<__bf16 *>(prm.out) + (int64_t)ib * L * rowX + (int64_t)h * P + p0;
   // Gate input of this wave's y values of a sub-block (same positions).
-  const __bf16 *Zbase = GATED ? reinterpret_cast<const __bf16 *>(prm.z) + tok0 * rowX + (int64_t)h * P + p0
+  const __bf16 *Zbase = GATED ? reinterpret_cast<const __bf16 *>(prm.z) + (int64_t)ib * L * rowX + (int64_t)h * P + p0
                               : nullptr;
   float4 zq[4];
   auto fetch_z = [&](int k) {
@@ -495,10 +485,10 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
   // aligned 16-byte pieces, two per thread; pieces of rows past the group's
   // last row are dropped, as are tokens past L.  k < 0 stores nothing.
   const int rows_valid = min(16 * W, prm.rows_per_bg - wi * 16 * W);
-  __bf16 *Ywg = reinterpret_cast<__bf16 *>(prm.out) + tok0 * rowX + (int64_t)g * (H / G) * P + wi * 16 * W;
+  __bf16 *Ywg = reinterpret_cast<__bf16 *>(prm.out) + (int64_t)ib * L * rowX + (int64_t)g * (H / G) * P + wi * 16 * W;
   // Gate input pieces matching the pieces flush_y stores for sub-block k
   // (zeros for k < 0).
-  const __bf16 *Zwg = GATED ? reinterpret_cast<const __bf16 *>(prm.z) + tok0 * rowX +
+  const __bf16 *Zwg = GATED ? reinterpret_cast<const __bf16 *>(prm.z) + (int64_t)ib * L * rowX +
                                   (int64_t)g * (H / G) * P + wi * 16 * W
                             : nullptr;
   float4 zpc[2];
@@ -624,7 +614,7 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
     e_final = cur_eout;
   }
 
-  if (prm.final_state != nullptr && active && seg == prm.nseg - 1) {
+  if (prm.final_state != nullptr && active) {
     const float sc = hw_exp2(e_final);
 #pragma unroll
     for (int k = 0; k < NT; ++k) *reinterpret_cast<f32x4 *>(prm.final_state + srow + 16 * k + 4 * lg) = hs[k] * sc;
@@ -674,7 +664,7 @@ hipError_t launch_scores(const void *B, const void *C, void *scores_v, int b, in
 }
 
 hipError_t launch_rwalk(int N, int W, const RWalkParams &p, hipStream_t stream) {
-  const int nwg = p.nseg * p.b * p.G * p.wg_per_bg;
+  const int nwg = p.b * p.G * p.wg_per_bg;
   switch (N) {
   case 32: return launch_rwalk_n<32>(W, p, nwg, stream);
   case 64: return launch_rwalk_n<64>(W, p, nwg, stream);

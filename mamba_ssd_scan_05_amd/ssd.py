@@ -20,7 +20,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libssd.so")
 
 SSD_F32, SSD_BF16 = 0, 1
-SSD_ALGO_AUTO, SSD_ALGO_FUSED, SSD_ALGO_CHUNKED, SSD_ALGO_ROWS, SSD_ALGO_ROWS_SEG = 0, 1, 2, 3, 4
+SSD_ALGO_AUTO, SSD_ALGO_FUSED, SSD_ALGO_CHUNKED, SSD_ALGO_ROWS = 0, 1, 2, 3
 STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_DTYPE",
           4: "SSD_ERR_LAYOUT", 5: "SSD_ERR_UNSUPPORTED", 6: "SSD_ERR_ALIAS",
           7: "SSD_ERR_NOMEM", 8: "SSD_ERR_HIP"}

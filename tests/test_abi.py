@@ -263,7 +263,7 @@ def test_rows_rejections(ssd):
     a["x"] = torch.zeros(1, 99, 4, 16, dtype=torch.bfloat16)   # L disagrees with dt
     assert call(a, 1) == 2
     assert _call_scan(ssd, _scan_args(dtype=torch.float32), algo=3)[0] == 5
-    assert _call_scan(ssd, _scan_args(), algo=5)[0] == 5
+    assert _call_scan(ssd, _scan_args(), algo=4)[0] == 5
 
 
 def test_gated_rejections(ssd):
@@ -281,7 +281,7 @@ def test_gated_rejections(ssd):
     assert call(a, torch.zeros(1, 100, 4, 16)) == 3
     assert call(a, torch.zeros(1, 4, 100, 16, dtype=torch.bfloat16).transpose(1, 2)) == 4
     assert call(a, a["out"]) == 6
-    assert call(a, torch.zeros(1, 100, 4, 16, dtype=torch.bfloat16), algo=5) == 5
+    assert call(a, torch.zeros(1, 100, 4, 16, dtype=torch.bfloat16), algo=4) == 5
     b = _scan_args()
     b["x"] = None
     assert call(b, torch.zeros(1, 100, 4, 16, dtype=torch.bfloat16)) == 1

@@ -159,13 +159,13 @@ def workload_with_reference(name):
 
 
 @pytest.mark.parametrize("algo", [ssd.SSD_ALGO_AUTO, ssd.SSD_ALGO_FUSED, ssd.SSD_ALGO_CHUNKED,
-                                  ssd.SSD_ALGO_ROWS, ssd.SSD_ALGO_ROWS_SEG])
+                                  ssd.SSD_ALGO_ROWS])
 @pytest.mark.parametrize("name", SCANS)
 def test_workload_scan(name, algo):
     if name.startswith("long") and algo == ssd.SSD_ALGO_FUSED:
         pytest.skip("one workgroup per (batch, head) leaves most of the GPU idle here; "
                     "covered by the small-shape tests")
-    if algo in (ssd.SSD_ALGO_ROWS, ssd.SSD_ALGO_ROWS_SEG) and inputs.WORKLOADS[name]["dtype"] != inputs.BF16:
+    if algo == ssd.SSD_ALGO_ROWS and inputs.WORKLOADS[name]["dtype"] != inputs.BF16:
         pytest.skip("the row-sliced walk takes bf16 inputs only")
     say("workload", name, "algo", algo)
     si, (yr, fr) = workload_with_reference(name)
@@ -488,52 +488,3 @@ def test_host_memory_refused_on_device():
         assert e.value.status == 4, str(e.value)
         assert ("%s:" % culprit) in str(e.value), str(e.value)
     torch.cuda.synchronize()
-
-
-
-# ---------------------------------------------------------------------------
-# the row walk over segments (SSD_ALGO_ROWS_SEG)
-
-ROWS_SEG = [
-    # b, L, H, P, G, N, segment length
-    (1, 300, 4, 64, 2, 128, 64),     # five segments, the last one partial
-    (2, 1000, 8, 64, 2, 128, 256),
-    (1, 130, 2, 32, 1, 64, 128),
-    (3, 777, 6, 16, 3, 32, 512),
-    (1, 2100, 32, 64, 8, 128, 1024),
-]
-
-
-@pytest.mark.parametrize("case", ROWS_SEG, ids=["b%dL%dH%dP%dG%dN%d_seg%d" % c for c in ROWS_SEG])
-@pytest.mark.parametrize("init", [True, False])
-def test_rows_segmented(case, init):
-    b, L, H, P, G, N, seg = case
-    si = inputs.make_scan(b, L, H, P, G, N, dtype=inputs.BF16, chunk=seg, seed=L + H + seg,
-                          init_std=0.5)
-    say("row walk over segments", case, "init", init)
-    y, f = gpu_scan(si, algo=ssd.SSD_ALGO_ROWS_SEG, chunk=seg, init=init)
-    yr, fr = oracle_scan(si, init=init)
-    check(y, yr, 2e-2, "y")
-    check(f, fr, 2e-2, "final state")
-
-
-def test_rows_segmented_in_place_and_gated():
-    # final state in place of the initial state, and the gated output, over
-    # segments
-    si = inputs.make_scan(2, 600, 8, 64, 2, 128, dtype=inputs.BF16, chunk=128, seed=61, init_std=0.5)
-    yr, fr = oracle_scan(si)
-    t = staging.scan_tensors(si, DEV)
-    say("row walk over segments: in place")
-    out, fin = ssd.ssd_scan_fwd(**t, final_state=t["init_state"], chunk=128, algo=ssd.SSD_ALGO_ROWS_SEG)
-    torch.cuda.synchronize()
-    check(staging.to_f64(out), yr, 2e-2, "y (in place)")
-    check(staging.to_f64(fin), fr, 2e-2, "final (in place)")
-    z, zf = gated_case(si, seed=62)
-    t = staging.scan_tensors(si, DEV)
-    say("row walk over segments: gated")
-    out, fin = ssd.ssd_scan_fwd_gated(**t, z=staging.tensor(z, si.dtype, DEV), chunk=128,
-                                      algo=ssd.SSD_ALGO_ROWS_SEG)
-    torch.cuda.synchronize()
-    yg, fg = oracle_scan_gated(si, zf)
-    check(staging.to_f64(out), yg, 2e-2, "gated y over segments")
-    check(staging.to_f64(fin), fg, 2e-2, "gated final over segments")
