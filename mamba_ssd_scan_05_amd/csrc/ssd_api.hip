@@ -11,6 +11,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <string>
 
@@ -329,17 +330,24 @@ int run_rows(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bia
 }
 
 // Compute units of the current device (queried once per device).
+// Safe to call from several threads at once (each slot is written with the
+// same value by whichever thread gets there first).
 int device_cus() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64] = {};
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int cu = 0;
-    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0)
-      cu = 256;
-    cache[dev] = cu;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
   }
-  return cache[dev];
+  int cu = cache[dev].load(std::memory_order_relaxed);
+  if (cu == 0) {
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0) {
+      (void)hipGetLastError();
+      cu = 256;
+    }
+    cache[dev].store(cu, std::memory_order_relaxed);
+  }
+  return cu;
 }
 
 // Plan for SSD_ALGO_AUTO, from measured costs on MI355X.  The walks of the

@@ -360,3 +360,31 @@ def test_selective_scan_oversized(ssd):
     st = ssd.lib().ssd_selective_scan_fwd(*ptrs, 0, None)
     assert st == 5, (st, ssd.ssd_last_error())
     assert "too large" in ssd.ssd_last_error()
+
+
+def test_last_error_is_per_thread(ssd):
+    # each thread sees the message of its own last call
+    import threading
+    msgs, errs = {}, []
+
+    def worker(i):
+        try:
+            for _ in range(50):
+                a = _scan_args()
+                if i % 2:
+                    a["x"] = None
+                    st, msg = _call_scan(ssd, a)
+                    assert st == 1 and "x" in msg, msg
+                else:
+                    st, msg = _call_scan(ssd, a, chunk=32)
+                    assert st == 5 and "chunk" in msg, msg
+            msgs[i] = msg
+        except AssertionError as e:
+            errs.append(str(e))
+    ts = [threading.Thread(target=worker, args=(i,)) for i in range(8)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert not errs, errs[:3]
+    assert len(msgs) == 8
