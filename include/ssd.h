@@ -28,9 +28,18 @@
  * argument check, before any launch).
  *
  * Ownership: the caller allocates every tensor and keeps it alive until the
- * work queued on `stream` has finished.  The library keeps no pointer after
- * a call returns.  Scratch space, when an algorithm needs it, is taken from
- * the HIP stream-ordered allocator on `stream` and released on `stream`.
+ * work queued on `stream` has finished.  The library keeps no pointer to
+ * caller memory after a call returns.
+ *
+ * Scratch: an algorithm that needs scratch space uses a device buffer the
+ * library keeps, one per (device, stream) handle, reused by every call on
+ * that stream in stream order and grown stream-ordered on `stream` when a
+ * call needs more (an event recorded after each call orders the next use if
+ * a handle is reused for another stream).  A request above 256 MiB is
+ * allocated and freed stream-ordered on `stream` for that call alone.  Kept
+ * buffers live until ssd_release_scratch() or the end of the process.
+ * Allocating scratch per call would make the host wait for the stream's
+ * earlier work; keeping it lets back-to-back calls queue ahead of the GPU.
  *
  * Errors: every argument is validated on the host before any work is
  * queued; a failed validation returns a nonzero status and queues nothing.  A failed
@@ -130,8 +139,8 @@ int ssd_scan_fwd(const ssd_tensor *x, const ssd_tensor *dt,
 /* ssd_scan_fwd with an explicit algorithm (SSD_ALGO_*). Same contract;
  * SSD_ALGO_CHUNKED uses `chunk` as its segment length; SSD_ALGO_ROWS
  * returns SSD_ERR_UNSUPPORTED for fp32 inputs or N outside {32, 64, 128}.
- * SSD_ALGO_ROWS and SSD_ALGO_CHUNKED take scratch from the stream-ordered
- * allocator (ROWS: b*G*ceil(L/64)*8 KiB). */
+ * SSD_ALGO_ROWS and SSD_ALGO_CHUNKED use scratch (see Scratch above; ROWS:
+ * b*G*ceil(L/64)*8 KiB). */
 int ssd_scan_fwd_algo(const ssd_tensor *x, const ssd_tensor *dt,
                       const ssd_tensor *dt_bias, const ssd_tensor *A,
                       const ssd_tensor *B, const ssd_tensor *C,
@@ -238,8 +247,8 @@ int ssd_step(ssd_tensor *state, const ssd_tensor *x, const ssd_tensor *dt,
  * Supported sizes: N in {4, 8, 16}, D/G a multiple of 64 (64 channels of
  * one group per wave), 1 <= L <= 2^24.  The state and all arithmetic in
  * fp32; out is rounded to its dtype once.  Scratch (segment end states,
- * b * segments * D * (N + 1) floats) comes from the stream-ordered allocator
- * when segments > 1.  out may not overlap any input; final_state may not
+ * b * segments * D * (N + 1) floats, plus b * D * N staged initial state)
+ * is used when segments > 1 (see Scratch above).  out may not overlap any input; final_state may not
  * overlap any input other than (exactly) init_state.
  */
 int ssd_selective_scan_fwd(const ssd_tensor *x, const ssd_tensor *dt,
@@ -270,6 +279,14 @@ const char *ssd_last_error(void);
 
 /* SSD_VERSION of the built library. */
 int ssd_version(void);
+
+/* Frees the scratch buffers the library keeps between calls (see Scratch
+ * above), after waiting for the queued work that uses them; the next call
+ * that needs scratch allocates it again.  Safe to call at any time from any
+ * thread (calls that take scratch meanwhile wait for it); returns SSD_OK, or
+ * SSD_ERR_HIP if a HIP call failed (the buffers are forgotten either way).
+ * Makes no HIP call when no buffer is kept. */
+int ssd_release_scratch(void);
 
 #ifdef __cplusplus
 }

@@ -64,6 +64,8 @@ def lib():
         L.ssd_status_string.restype = ctypes.c_char_p
         L.ssd_last_error.restype = ctypes.c_char_p
         L.ssd_version.restype = ctypes.c_int
+        L.ssd_release_scratch.restype = ctypes.c_int
+        L.ssd_release_scratch.argtypes = []
         L.ssd_scan_plan.argtypes = [ctypes.c_int64] * 6 + [ctypes.c_int, ctypes.c_int,
                                                             ctypes.POINTER(ctypes.c_int),
                                                             ctypes.POINTER(ctypes.c_int)]
@@ -225,3 +227,9 @@ def ssd_last_error() -> str:
 
 def ssd_version() -> int:
     return int(lib().ssd_version())
+
+
+def ssd_release_scratch() -> None:
+    """Frees the scratch buffers the library keeps between calls (waits for
+    the queued work that uses them)."""
+    _check(lib().ssd_release_scratch())

@@ -29,13 +29,20 @@ def test_exports_every_declared_symbol(ssd):
     names = declared_functions()
     assert {"ssd_scan_fwd", "ssd_step", "ssd_scan_fwd_algo", "ssd_scan_fwd_rows", "ssd_scan_fwd_gated",
             "ssd_selective_scan_fwd",
-            "ssd_scan_plan", "ssd_status_string", "ssd_last_error", "ssd_version"} <= set(names)
+            "ssd_scan_plan", "ssd_status_string", "ssd_last_error", "ssd_version",
+            "ssd_release_scratch"} <= set(names)
     raw = ctypes.CDLL(ssd.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
     out = os.popen("nm -D --defined-only %s" % ssd.LIB_PATH).read()
     for n in names:
         assert re.search(r"\bT %s\b" % n, out), n
+
+
+def test_release_scratch_with_nothing_kept(ssd):
+    # no call has taken scratch in this process: nothing to free, no HIP call
+    assert ssd.lib().ssd_release_scratch() == 0
+    ssd.ssd_release_scratch()
 
 
 def test_version_and_strings(ssd):

@@ -1,0 +1,94 @@
+"""Scratch buffers kept between calls: calls queued back to back on one
+stream (no synchronisation between them) reuse one buffer in stream order,
+grow it, share it across algorithms, and calls on two streams at once use
+two buffers.  Every result is checked against the fp64 oracle with the bf16
+bound |got - ref| <= 2e-2 (1 + |ref|).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mamba_ssd_scan_05_amd import inputs, ssd, staging
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL = 2e-2
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def check(got, ref, what):
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), "%s: non-finite values" % what
+    err = float(np.max(np.abs(got - ref) / (1.0 + np.abs(ref))))
+    assert err <= TOL, "%s: max |e|/(1+|ref|) = %.3e > %.1e" % (what, err, TOL)
+
+
+def scan_case(L, seed, b=2, H=4, P=64, G=1, N=64):
+    si = inputs.make_scan(b, L, H, P, G, N, dtype=inputs.BF16, seed=seed, init_std=0.3)
+    return si, staging.scan_tensors(si, DEV), oracle.scan(**si.f64())
+
+
+def sscan_case(L, seed):
+    si = inputs.make_sscan(2, L, 128, 1, 16, dtype=inputs.BF16, seed=seed, init_std=0.3)
+    a = si.f64()
+    ref = oracle.selective_scan(a["x"], a["dt"], a["dt_bias"], a["A"], a["B"], a["C"], a["D"], a["init"])
+    return si, staging.sscan_tensors(si, DEV), ref
+
+
+def test_back_to_back_reuse_grow_and_mix():
+    # rows (80 KiB), rows (2.3 MiB: the kept buffer grows), chunked, selective
+    # scan with segments, rows again: all queued before one synchronisation
+    cases = [("rows", scan_case(300, 81)), ("rows", scan_case(9000, 82)),
+             ("chunked", scan_case(2000, 83)), ("sscan", sscan_case(1500, 84)),
+             ("rows", scan_case(700, 85))]
+    torch.cuda.synchronize()
+    outs = []
+    for kind, (si, t, ref) in cases:
+        say("queue", kind, "L =", si.x.shape[1])
+        if kind == "sscan":
+            outs.append(ssd.ssd_selective_scan_fwd(**t, segments=9))
+        else:
+            algo = ssd.SSD_ALGO_ROWS if kind == "rows" else ssd.SSD_ALGO_CHUNKED
+            outs.append(ssd.ssd_scan_fwd(**t, chunk=256, algo=algo))
+    torch.cuda.synchronize()
+    for (kind, (si, t, ref)), (out, fin) in zip(cases, outs):
+        check(staging.to_f64(out), ref[0], "%s L=%d y" % (kind, si.x.shape[1]))
+        check(staging.to_f64(fin), ref[1], "%s L=%d final" % (kind, si.x.shape[1]))
+
+
+def test_two_streams_at_once():
+    a = scan_case(4000, 86)
+    b = scan_case(3000, 87, H=8)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    res = []
+    for rep in range(3):
+        say("two streams, repetition", rep)
+        with torch.cuda.stream(s1):
+            ra = ssd.ssd_scan_fwd(**a[1], algo=ssd.SSD_ALGO_ROWS)
+        with torch.cuda.stream(s2):
+            rb = ssd.ssd_scan_fwd(**b[1], algo=ssd.SSD_ALGO_ROWS)
+        res.append((ra, rb))
+    torch.cuda.synchronize()
+    for ra, rb in res:
+        check(staging.to_f64(ra[0]), a[2][0], "stream 1 y")
+        check(staging.to_f64(ra[1]), a[2][1], "stream 1 final")
+        check(staging.to_f64(rb[0]), b[2][0], "stream 2 y")
+        check(staging.to_f64(rb[1]), b[2][1], "stream 2 final")
+
+
+def test_release_between_calls():
+    si, t, ref = scan_case(1000, 88)
+    for rep in range(2):
+        say("release, repetition", rep)
+        out, fin = ssd.ssd_scan_fwd(**t, algo=ssd.SSD_ALGO_ROWS)
+        ssd.ssd_release_scratch()       # waits for the scan, frees its scratch
+        check(staging.to_f64(out), ref[0], "y")
+        check(staging.to_f64(fin), ref[1], "final")
+    ssd.ssd_release_scratch()           # nothing kept: no-op
