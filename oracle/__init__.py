@@ -13,6 +13,7 @@ with gcc, loads it with ctypes and marshals numpy arrays:
 * ``scan_gated(x, dt, dt_bias, A, B, C, z, D, init)`` -> ``(y * silu(z), final_state)``
 * ``gate(y, z)`` -> ``y * silu(z)``
 * ``step(state, x, delta, A, B, C, D)`` -> ``(y, new_state)``
+* ``scan_bwd(x, dt, dt_bias, A, B, C, D, init, dy, dfinal)`` -> dict of gradients
 
 Every array argument is converted to contiguous float64 first; callers pass
 the values exactly as the device sees them (bf16 inputs upcast exactly).
@@ -62,6 +63,8 @@ class Oracle:
         lib.oracle_gate_f64.restype = None
         lib.oracle_sscan_f64.argtypes = [i64] * 5 + [vp] * 10
         lib.oracle_sscan_f64.restype = None
+        lib.oracle_scan_bwd_f64.argtypes = [i64] * 6 + [vp] * 18
+        lib.oracle_scan_bwd_f64.restype = None
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
         self.lib = lib
@@ -83,6 +86,9 @@ class Oracle:
 
     def selective_scan(self, *args, **kwargs):
         return _sscan(self.lib, *args, **kwargs)
+
+    def scan_bwd(self, *args, **kwargs):
+        return _scan_bwd(self.lib, *args, **kwargs)
 
 
 def default() -> Oracle:
@@ -110,6 +116,10 @@ def _f64(a):
 
 def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def scan_bwd(x, dt, dt_bias, A, B, C, D, init, dy, dfinal=None):
+    return default().scan_bwd(x, dt, dt_bias, A, B, C, D, init, dy, dfinal)
 
 
 def scan(x, dt, dt_bias, A, B, C, D=None, init=None, want_final=True):
@@ -212,3 +222,29 @@ def _sscan(lib, x, dt, dt_bias, A, B, C, D=None, init=None, want_final=True):
     lib.oracle_sscan_f64(b, L, Dc, G, N, _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(B),
                          _ptr(C), _ptr(D), _ptr(init), _ptr(y), _ptr(fin))
     return y, fin
+
+
+def _scan_bwd(lib, x, dt, dt_bias, A, B, C, D, init, dy, dfinal=None):
+    """Gradients of the sequential fp64 scan (oracle_scan_bwd_f64 in
+    ssd_oracle.c: the chain rule through the recurrence, latest token first).
+
+    Arguments as for ``scan`` plus dy [b,L,H,P] (gradient at y) and dfinal
+    [b,H,P,N] or None (gradient at the final state).  Returns a dict of
+    float64 arrays: dx [b,L,H,P], ddt [b,L,H] (at the raw dt), ddt_bias,
+    dA and dD [H], dB and dC [b,L,G,N], dinit [b,H,P,N]."""
+    x, dt, dt_bias, A, B, C, D, init, dy, dfinal = map(
+        _f64, (x, dt, dt_bias, A, B, C, D, init, dy, dfinal))
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    assert dt.shape == (b, L, H) and A.shape == (H,) and H % G == 0
+    assert B.shape == (b, L, G, N) and C.shape == (b, L, G, N) and dy.shape == x.shape
+    if dfinal is not None:
+        assert dfinal.shape == (b, H, P, N)
+    out = dict(dx=np.empty((b, L, H, P)), ddt=np.empty((b, L, H)), ddt_bias=np.empty(H),
+               dA=np.empty(H), dB=np.empty((b, L, G, N)), dC=np.empty((b, L, G, N)),
+               dD=np.empty(H), dinit=np.empty((b, H, P, N)))
+    lib.oracle_scan_bwd_f64(b, L, H, P, G, N, _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(B),
+                            _ptr(C), _ptr(D), _ptr(init), _ptr(dy), _ptr(dfinal),
+                            _ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["ddt_bias"]), _ptr(out["dA"]),
+                            _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dinit"]))
+    return out

@@ -201,3 +201,131 @@ void oracle_sscan_f64(int64_t b, int64_t L, int64_t Dc, int64_t G, int64_t N,
         free(h);
     }
 }
+
+/* Gradients of the full-sequence scan (oracle_scan_f64) by the chain rule,
+ * taken through the recurrence one token at a time, latest token first.
+ * Training needs them.  The Mamba paper-reading notes (sxlin0.github.io,
+ * the section on the hardware-aware selective scan) describe the backward
+ * pass as recomputing the states it needs rather than storing them; this
+ * checker simply keeps every state of one head in memory.
+ *
+ * Scalar objective: Lobj = sum_t <dy_t, y_t> + <dfinal, h_{L-1}>, so dy is
+ * the gradient arriving at y and dfinal the one arriving at the final state.
+ * With z_t = dt_t + dt_bias, Delta_t = softplus(z_t) and
+ * alpha_t = exp(Delta_t * A), walking t = L-1 down to 0 with the adjoint
+ * g = dLobj/dh_t (P x N, starting from dfinal):
+ *
+ *   g        += dy_t C_t^T                      (y_t reads h_t)
+ *   dC_t     += h_t^T dy_t                      (summed over the group's heads)
+ *   dx_t[p]   = D dy_t[p] + Delta_t sum_n g[p][n] B_t[n]
+ *   dB_t[n]  += Delta_t sum_p x_t[p] g[p][n]    (summed over the group's heads)
+ *   dDelta_t  = sum_{p,n} g[p][n] (A alpha_t h_{t-1}[p][n] + x_t[p] B_t[n])
+ *   dA       += Delta_t alpha_t sum_{p,n} g[p][n] h_{t-1}[p][n]
+ *   dD       += sum_p dy_t[p] x_t[p]
+ *   ddt_t     = dDelta_t * sigmoid(z_t)         (softplus' = sigmoid)
+ *   ddt_bias += ddt_t
+ *   g         = alpha_t g                       (now dLobj/dh_{t-1})
+ *
+ * and dinit = g after t = 0.  Shapes as in oracle_scan_f64; dy like y,
+ * dfinal like the state (NULL: zero).  Every output is written in full:
+ * dx [b,L,H,P], ddt [b,L,H], dA [H], dB and dC [b,L,G,N]; ddt_bias and dD [H]
+ * and dinit [b,H,P,N] may be NULL (not written).  Independent (batch, group)
+ * pairs run on OpenMP threads; within a pair the group's heads run in order.
+ * Per-(batch, head) partial sums of dA, dD and ddt_bias are added over the
+ * batch afterwards, in batch order. */
+void oracle_scan_bwd_f64(int64_t b, int64_t L, int64_t H, int64_t P, int64_t G,
+                         int64_t N, const double *x, const double *dt,
+                         const double *dt_bias, const double *A, const double *B,
+                         const double *C, const double *D, const double *init,
+                         const double *dy, const double *dfinal, double *dx,
+                         double *ddt, double *ddt_bias, double *dA, double *dB,
+                         double *dC, double *dD, double *dinit) {
+    int64_t PN = P * N, hpg = H / G;
+    memset(dB, 0, (size_t)(b * L * G * N) * sizeof(double));
+    memset(dC, 0, (size_t)(b * L * G * N) * sizeof(double));
+    double *part = (double *)calloc((size_t)(3 * b * H), sizeof(double));
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bg = 0; bg < b * G; ++bg) {
+        int64_t ib = bg / G, g = bg % G;
+        /* hist[t + 1] = hv, hist[0] = the initial state */
+        double *hist = (double *)malloc((size_t)((L + 1) * PN) * sizeof(double));
+        double *adj = (double *)malloc((size_t)PN * sizeof(double));
+        for (int64_t h = g * hpg; h < (g + 1) * hpg; ++h) {
+            int64_t bh = ib * H + h;
+            double bias = dt_bias ? dt_bias[h] : 0.0;
+            double d_h = D ? D[h] : 0.0;
+            if (init)
+                memcpy(hist, init + bh * PN, (size_t)PN * sizeof(double));
+            else
+                memset(hist, 0, (size_t)PN * sizeof(double));
+            for (int64_t t = 0; t < L; ++t) {       /* forward: every state */
+                int64_t tok = ib * L + t;
+                double delta = softplus_f64(dt[tok * H + h] + bias);
+                double alpha = exp(delta * A[h]);
+                const double *xv = x + (tok * H + h) * P, *Bv = B + (tok * G + g) * N;
+                const double *prev = hist + t * PN;
+                double *cur = hist + (t + 1) * PN;
+                for (int64_t p = 0; p < P; ++p)
+                    for (int64_t n = 0; n < N; ++n)
+                        cur[p * N + n] = alpha * prev[p * N + n] + delta * xv[p] * Bv[n];
+            }
+            if (dfinal)
+                memcpy(adj, dfinal + bh * PN, (size_t)PN * sizeof(double));
+            else
+                memset(adj, 0, (size_t)PN * sizeof(double));
+            for (int64_t t = L - 1; t >= 0; --t) {  /* backward */
+                int64_t tok = ib * L + t;
+                double z = dt[tok * H + h] + bias;
+                double delta = softplus_f64(z);
+                double alpha = exp(delta * A[h]);
+                const double *xv = x + (tok * H + h) * P, *dyv = dy + (tok * H + h) * P;
+                const double *Bv = B + (tok * G + g) * N, *Cv = C + (tok * G + g) * N;
+                const double *hv = hist + (t + 1) * PN, *hp = hist + t * PN;
+                double *dBv = dB + (tok * G + g) * N, *dCv = dC + (tok * G + g) * N;
+                for (int64_t p = 0; p < P; ++p)
+                    for (int64_t n = 0; n < N; ++n) {
+                        adj[p * N + n] += dyv[p] * Cv[n];
+                        dCv[n] += dyv[p] * hv[p * N + n];
+                    }
+                double d_delta = 0.0, decay_dot = 0.0, skip_dot = 0.0;
+                for (int64_t p = 0; p < P; ++p) {
+                    double gb = 0.0;
+                    for (int64_t n = 0; n < N; ++n) {
+                        gb += adj[p * N + n] * Bv[n];
+                        decay_dot += adj[p * N + n] * hp[p * N + n];
+                    }
+                    dx[(tok * H + h) * P + p] = d_h * dyv[p] + delta * gb;
+                    d_delta += xv[p] * gb;
+                    skip_dot += dyv[p] * xv[p];
+                }
+                for (int64_t n = 0; n < N; ++n) {
+                    double xg = 0.0;
+                    for (int64_t p = 0; p < P; ++p) xg += xv[p] * adj[p * N + n];
+                    dBv[n] += delta * xg;
+                }
+                d_delta += A[h] * alpha * decay_dot;
+                double ddt_t = d_delta / (1.0 + exp(-z));
+                ddt[tok * H + h] = ddt_t;
+                part[3 * bh] += delta * alpha * decay_dot;
+                part[3 * bh + 1] += skip_dot;
+                part[3 * bh + 2] += ddt_t;
+                for (int64_t e = 0; e < PN; ++e) adj[e] *= alpha;
+            }
+            if (dinit) memcpy(dinit + bh * PN, adj, (size_t)PN * sizeof(double));
+        }
+        free(adj);
+        free(hist);
+    }
+    for (int64_t h = 0; h < H; ++h) {
+        double sa = 0.0, sd = 0.0, sb = 0.0;
+        for (int64_t ib = 0; ib < b; ++ib) {
+            sa += part[3 * (ib * H + h)];
+            sd += part[3 * (ib * H + h) + 1];
+            sb += part[3 * (ib * H + h) + 2];
+        }
+        dA[h] = sa;
+        if (dD) dD[h] = sd;
+        if (ddt_bias) ddt_bias[h] = sb;
+    }
+    free(part);
+}

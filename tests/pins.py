@@ -31,6 +31,11 @@ fixed independently of the oracle's own loop:
                       the (separately pinned) SSD scan with one channel per
                       head
 * ``pin_sscan_hand``  a hand-worked 3-token example with two state indices
+* ``pin_bwd_finite_difference`` every gradient of the scan against central
+                      differences of the forward scan along random directions
+* ``pin_bwd_transpose`` dx, dinit, dD exactly as transposes of the explicit
+                      L x L operator (the forward is linear in x and h0)
+* ``pin_bwd_hand``    a one-token gradient example worked by hand
 
 Softplus here is ``numpy.logaddexp(0, z)`` (a library routine).
 """
@@ -408,7 +413,101 @@ def pin_sscan_hand(o):
     _close(fin[0, 0], [3.75, 3.0], 1e-14, "selective scan hand example final")
 
 
+# --------------------------------------------------------------------------
+# Gradients of the scan (oracle ``scan_bwd``).  Objective
+# Lobj = sum <dy, y> + <dfinal, final state>.
+
+BWD_KEYS = ["x", "dt", "dt_bias", "A", "B", "C", "D", "init"]
+GRAD_OF = dict(x="dx", dt="ddt", dt_bias="ddt_bias", A="dA", B="dB", C="dC", D="dD", init="dinit")
+
+
+def _objective(o, case, dy, dfinal):
+    y, fin = o.scan(**case)
+    return float(np.sum(dy * y) + (np.sum(dfinal * fin) if dfinal is not None else 0.0))
+
+
+def pin_bwd_finite_difference(o, seed=25):
+    """Every gradient against central differences of the (separately pinned)
+    forward scan along a random direction: (Lobj(p + e v) - Lobj(p - e v)) / 2e
+    equals <grad, v> up to O(e^2) (e = 1e-5, fp64)."""
+    rng = np.random.default_rng(seed)
+    for (b, L, H, P, G, N, init, fin) in [(2, 9, 4, 3, 2, 5, True, True), (1, 6, 2, 2, 1, 3, False, False)]:
+        case = rand_case(rng, b, L, H, P, G, N, init=init)
+        if case["init"] is None:
+            case["init"] = np.zeros((b, H, P, N))
+        dy = rng.standard_normal((b, L, H, P))
+        dfinal = rng.standard_normal((b, H, P, N)) if fin else None
+        grads = o.scan_bwd(**case, dy=dy, dfinal=dfinal)
+        eps = 1e-5
+        for k in BWD_KEYS:
+            v = rng.standard_normal(case[k].shape)
+            plus = dict(case, **{k: case[k] + eps * v})
+            minus = dict(case, **{k: case[k] - eps * v})
+            fd = (_objective(o, plus, dy, dfinal) - _objective(o, minus, dy, dfinal)) / (2 * eps)
+            an = float(np.sum(grads[GRAD_OF[k]] * v))
+            assert abs(fd - an) <= 1e-6 * (1.0 + abs(fd)), (k, fd, an)
+
+
+def pin_bwd_transpose(o, seed=26):
+    """dx, dinit and dD exactly: y and the final state are linear in x and in
+    the initial state, so these gradients are the transposes of the explicit
+    L x L operator M = mask o (C B^T) diag(Delta) (mask entries: products of
+    forget gates), of the decay read-out of the initial state and of the
+    final-state carry, applied to dy and dfinal."""
+    rng = np.random.default_rng(seed)
+    b, L, H, P, G, N = 2, 11, 4, 3, 2, 4
+    c = rand_case(rng, b, L, H, P, G, N)
+    dy = rng.standard_normal((b, L, H, P))
+    dfinal = rng.standard_normal((b, H, P, N))
+    grads = o.scan_bwd(**c, dy=dy, dfinal=dfinal)
+    delta = softplus(c["dt"] + c["dt_bias"][None, None, :])
+    alpha = np.exp(delta * c["A"][None, None, :])
+    dx = np.zeros_like(c["x"])
+    dinit = np.zeros_like(c["init"])
+    dD = np.zeros(H)
+    for ib in range(b):
+        for h in range(H):
+            g = h * G // H
+            Bm, Cm = c["B"][ib, :, g, :], c["C"][ib, :, g, :]
+            al, de = alpha[ib, :, h], delta[ib, :, h]
+            mask = np.zeros((L, L))
+            for i in range(L):
+                mask[i, i] = 1.0
+                for j in range(i - 1, -1, -1):
+                    mask[i, j] = mask[i, j + 1] * al[j + 1]
+            M = mask * (Cm @ Bm.T) * de[None, :]
+            carry = np.array([np.prod(al[s + 1:]) for s in range(L)]) * de      # final state: sum_s carry_s x_s B_s^T
+            dec = np.array([np.prod(al[: i + 1]) for i in range(L)])            # y_i gets dec_i * init C_i
+            Y = dy[ib, :, h, :]
+            dx[ib, :, h, :] = M.T @ Y + c["D"][h] * Y + carry[:, None] * (Bm @ dfinal[ib, h].T)
+            dinit[ib, h] = (dec[:, None] * Y).T @ Cm + np.prod(al) * dfinal[ib, h]
+            dD[h] += np.sum(Y * c["x"][ib, :, h, :])
+    _close(grads["dx"], dx, 1e-12, "dx vs transposed operator")
+    _close(grads["dinit"], dinit, 1e-12, "dinit vs transposed operator")
+    _close(grads["dD"], dD, 1e-12, "dD")
+
+
+def pin_bwd_hand(o):
+    """One token, one head, P = N = 1, worked by hand.  h = alpha h0 + Delta x B,
+    y = h C + D x, Lobj = dy y + df h.  With u = dy C + df (all that reaches h):
+    dx = D dy + Delta B u, dB = Delta x u, dC = dy h, dD = dy x, dh0 = alpha u,
+    dDelta = u (A alpha h0 + x B), dA = u Delta alpha h0, ddt = dDelta sigmoid(z).
+    Values: z = ln(e - 1) (so Delta = 1), A = -ln 2 (alpha = 1/2), x = 2, B = 3,
+    C = 5, D = 7, h0 = 4, dy = 1, df = 10: h = 8, u = 15, sigmoid(z) = (e-1)/e."""
+    e = np.e
+    case = dict(x=np.full((1, 1, 1, 1), 2.0), dt=np.full((1, 1, 1), np.log(e - 1.0)),
+                dt_bias=np.zeros(1), A=np.full(1, -np.log(2.0)), B=np.full((1, 1, 1, 1), 3.0),
+                C=np.full((1, 1, 1, 1), 5.0), D=np.full(1, 7.0), init=np.full((1, 1, 1, 1), 4.0))
+    g = o.scan_bwd(**case, dy=np.ones((1, 1, 1, 1)), dfinal=np.full((1, 1, 1, 1), 10.0))
+    d_delta = 15.0 * (-np.log(2.0) * 0.5 * 4.0 + 2.0 * 3.0)
+    want = dict(dx=7.0 + 45.0, dB=30.0, dC=8.0, dD=2.0, dinit=7.5, dA=30.0,
+                ddt=d_delta * (e - 1.0) / e, ddt_bias=d_delta * (e - 1.0) / e)
+    for k, v in want.items():
+        _close(g[k].ravel(), np.array([v]), 1e-12, "hand " + k)
+
+
 ALL_PINS = [pin_golden, pin_quadratic, pin_no_decay, pin_scalar_state, pin_split,
             pin_lti, pin_step_scan, pin_exact_int, pin_linearity, pin_groups,
             pin_head_perm, pin_decay_bound, pin_gate_closed_forms, pin_gate_expit,
-            pin_sscan_closed_form, pin_sscan_reduces_to_ssd, pin_sscan_hand]
+            pin_sscan_closed_form, pin_sscan_reduces_to_ssd, pin_sscan_hand,
+            pin_bwd_finite_difference, pin_bwd_transpose, pin_bwd_hand]

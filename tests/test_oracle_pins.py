@@ -35,8 +35,9 @@ MUTATIONS = [
      "new input decayed"),
     ("y_t[p] = acc + d_h * x_t[p];", "y_t[p] = acc;", "D term dropped"),
     ("    return m + log1p(exp(-fabs(z)));", "    (void)m;\n    return z;", "no softplus"),
-    ("dt[tok * H + h] + bias", "dt[tok * H + h] - bias", "bias sign"),
-    ("x + (tok * H + h) * P,", "x + (tok * H + (H - 1 - h)) * P,", "wrong head of x"),
+    ("softplus_f64(dt[tok * H + h] + bias);\n            recurrence_token(",
+     "softplus_f64(dt[tok * H + h] - bias);\n            recurrence_token(", "bias sign"),
+    ("A[h], x + (tok * H + h) * P,", "A[h], x + (tok * H + (H - 1 - h)) * P,", "wrong head of x"),
     ("int64_t g = (h * G) / H;\n        double *S", "int64_t g = h % G;\n        double *S",
      "group map"),
     ("B + (tok * G + g) * N, C + (tok * G + g) * N",
@@ -68,6 +69,25 @@ MUTATIONS = [
      "selective scan: B and C swapped"),
     ("        int64_t g = (d * G) / Dc;\n        double *h", "        int64_t g = d % G;\n        double *h",
      "selective scan: group map"),
+    # gradients of the scan
+    ("adj[p * N + n] += dyv[p] * Cv[n];", "adj[p * N + n] += dyv[p] * Bv[n] + 0.0 * Cv[n];",
+     "backward: adjoint reads B for C"),
+    ("dCv[n] += dyv[p] * hv[p * N + n];", "dCv[n] += dyv[p] * hp[p * N + n] + 0.0 * hv[0];",
+     "backward: dC from the previous state"),
+    ("dx[(tok * H + h) * P + p] = d_h * dyv[p] + delta * gb;",
+     "dx[(tok * H + h) * P + p] = 0.0 * d_h + delta * gb;", "backward: dx without the D term"),
+    ("d_delta += A[h] * alpha * decay_dot;", "d_delta += alpha * decay_dot;",
+     "backward: dDelta decay term without A"),
+    ("double ddt_t = d_delta / (1.0 + exp(-z));", "double ddt_t = d_delta + 0.0 * z;",
+     "backward: softplus derivative dropped"),
+    ("for (int64_t e = 0; e < PN; ++e) adj[e] *= alpha;", "for (int64_t e = 0; e < PN; ++e) adj[e] *= 1.0;",
+     "backward: adjoint not decayed"),
+    ("dBv[n] += delta * xg;", "dBv[n] += xg;", "backward: dB without Delta"),
+    ("part[3 * bh] += delta * alpha * decay_dot;", "part[3 * bh] += alpha * decay_dot;",
+     "backward: dA without Delta"),
+    ("decay_dot += adj[p * N + n] * hp[p * N + n];", "decay_dot += adj[p * N + n] * hv[p * N + n] + 0.0 * hp[0];",
+     "backward: decay term with the current state"),
+    ("xg += xv[p] * adj[p * N + n];", "xg += dyv[p] * adj[p * N + n] + 0.0 * xv[0];", "backward: dB from dy"),
 ]
 
 
