@@ -146,6 +146,51 @@ def bench_sscan(ssd, staging, inputs, torch, dev):
             "hbm_GBs": nbytes / (ms * 1e-3) / 1e9, "bytes_per_launch": nbytes}
 
 
+MFMA_F32 = 157.3e12  # MI355X dense fp32 matrix peak, FLOP/s
+
+
+def bwd_flops(b, L, H, P, G, N, Q=64):
+    """Matrix-product FLOPs of the chunked backward as built: per (batch, head,
+    64-token chunk) dY X^T and M^T dY (Q*Q*P each), dY H, B G^T, X G and the
+    chunk's own adjoint state (Q*P*N each), (DX o E) B and (DX o E)^T C
+    (Q*Q*N each); per (batch, group, chunk) S = C B^T (Q*Q*N); the forward
+    chunk-state walk that recomputes the states (Q*P*N per (batch, head,
+    chunk)); 2 FLOPs per multiply-add."""
+    nc = -(-L // Q)
+    per_head = 2 * Q * Q * P + 5 * Q * P * N + 2 * Q * Q * N
+    return 2 * (b * H * nc * per_head + b * G * nc * Q * Q * N)
+
+
+def bench_bwd(ssd, staging, inputs, torch, dev):
+    si = inputs.make_workload(WORKLOAD)
+    t = staging.scan_tensors(si, dev)
+    b, L, H, P = si.x.shape
+    G, N = si.B.shape[2], si.B.shape[3]
+    g = torch.Generator(device="cpu").manual_seed(1)
+    dy = torch.randn((b, L, H, P), generator=g).to(t["x"].dtype).to(dev)
+    df = torch.randn((b, H, P, N), generator=g).to(dev)
+    out = ssd.ssd_scan_bwd(**t, dout=dy, dfinal_state=df)
+    for _ in range(2):
+        ssd.ssd_scan_bwd(**t, dout=dy, dfinal_state=df, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        ssd.ssd_scan_bwd(**t, dout=dy, dfinal_state=df, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    fl = bwd_flops(b, L, H, P, G, N)
+    el = ELEM[si.dtype]
+    nbytes = b * L * H * P * (2 * el + 4) + b * L * H * 8 + 2 * b * L * G * N * (el + 4) + 3 * b * H * P * N * 4
+    return {"workload": WORKLOAD, "ms_per_step": ms, "tokens_per_s": b * L / (ms * 1e-3),
+            "roofline": {"bound": "mfma", "achieved": fl / (ms * 1e-3) / 1e12, "peak": MFMA_F32 / 1e12,
+                         "unit": "TFLOP/s", "frac": fl / (ms * 1e-3) / MFMA_F32, "flops_per_launch": fl,
+                         "dtype": "f32"},
+            "hbm_GBs": nbytes / (ms * 1e-3) / 1e9, "bytes_per_launch": nbytes}
+
+
 def bench_decode(ssd, staging, inputs, torch, dev):
     sp = inputs.make_workload(DECODE)
     t = staging.step_tensors(sp, dev)
@@ -179,6 +224,7 @@ def main():
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward (gradients) leg")
     ap.add_argument("--no-sscan", action="store_true",
                     help="skip the timing of the selective scan (diagonal A per channel)")
     ap.add_argument("--no-gated", action="store_true",
@@ -319,6 +365,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         extra["copy_probe_bytes"] = 2 * (1 << 30)
+    if not args.no_bwd:
+        print("bench: backward", WORKLOAD, file=sys.stderr, flush=True)
+        extra["backward"] = bench_bwd(ssd, staging, inputs, torch, dev)
     if not args.no_sscan:
         print("bench: selective scan %s" % SSCAN, file=sys.stderr, flush=True)
         extra["selective_scan"] = bench_sscan(ssd, staging, inputs, torch, dev)

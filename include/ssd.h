@@ -259,6 +259,50 @@ int ssd_selective_scan_fwd(const ssd_tensor *x, const ssd_tensor *dt,
                            int segments, void *stream);
 
 /*
+ * ssd_scan_bwd -- gradients of ssd_scan_fwd with respect to all its inputs.
+ *
+ * Training needs them.  The Mamba paper-reading notes (sxlin0.github.io, the
+ * section on the hardware-aware selective scan) describe the backward pass
+ * as recomputing the states it needs instead of storing them.  This call
+ * recomputes the states at 64-token chunk boundaries from the inputs and
+ * rebuilds everything inside a chunk on chip.  No forward-pass residue is
+ * needed.
+ *
+ * The gradients are those of the scalar sum <dout, y> + <dfinal_state, h_last>,
+ * where y and h_last are what ssd_scan_fwd computes from the same inputs.
+ * dout is the gradient arriving at the output and dfinal_state the one
+ * arriving at the final state.
+ *
+ * Inputs: x, dt, dt_bias, A, B, C, D and init_state exactly as for
+ * ssd_scan_fwd (dt_bias, D, init_state may be NULL: zero).  dout
+ * [b,L,H,P] has the dtype of x.  dfinal_state [b,H,P,N] f32 may be NULL
+ * (zero).
+ *
+ * Outputs, all f32, written in full (nothing is accumulated into them):
+ *   dx [b,L,H,P]         ddt [b,L,H] (gradient at the raw dt, before
+ *                         dt_bias and softplus)
+ *   dA [H]               dB, dC [b,L,G,N] (summed over the heads of a group)
+ *   ddt_bias [H], dD [H], dinit_state [b,H,P,N]: each may be NULL (not
+ *                         computed).
+ *
+ * Supported: P in {32, 64}, N in {32, 64, 128}, either input dtype, the
+ * size limits of ssd_scan_fwd.  No output may overlap an input or another
+ * output (SSD_ERR_ALIAS).  Arithmetic in fp32 (matrix products on the
+ * matrix cores from fp32 operands).  Sums over heads, chunks and batch run
+ * in a fixed order, so the result does not vary from run to run.  Scratch:
+ * b*H*(L + 2*ceil(L/64)*P*N) floats and a little more (see Scratch above;
+ * above 256 MiB it is allocated per call).
+ */
+int ssd_scan_bwd(const ssd_tensor *x, const ssd_tensor *dt,
+                 const ssd_tensor *dt_bias, const ssd_tensor *A,
+                 const ssd_tensor *B, const ssd_tensor *C, const ssd_tensor *D,
+                 const ssd_tensor *init_state, const ssd_tensor *dout,
+                 const ssd_tensor *dfinal_state, ssd_tensor *dx,
+                 ssd_tensor *ddt, ssd_tensor *ddt_bias, ssd_tensor *dA,
+                 ssd_tensor *dB, ssd_tensor *dC, ssd_tensor *dD,
+                 ssd_tensor *dinit_state, void *stream);
+
+/*
  * ssd_scan_plan -- the plan SSD_ALGO_AUTO uses for a shape on a device with
  * `cus` compute units for inputs of element type `dtype` (SSD_BF16 or
  * SSD_F32), host only, no HIP call: *algo is SSD_ALGO_FUSED,

@@ -107,7 +107,8 @@ struct ScanShape {
 int validate_scan(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bias,
                   const ssd_tensor *A, const ssd_tensor *B, const ssd_tensor *C,
                   const ssd_tensor *D, const ssd_tensor *init, const ssd_tensor *out,
-                  const ssd_tensor *fin, int chunk, ScanShape *s) {
+                  const ssd_tensor *fin, int chunk, ScanShape *s, const char *out_name = "out",
+                  bool out_written = true) {
   if (!x) return fail(SSD_ERR_NULL, "x: descriptor is NULL");
   if (!B) return fail(SSD_ERR_NULL, "B: descriptor is NULL");
   if (x->ndim != 4) return fail(SSD_ERR_SHAPE, "x: rank %d, expected 4 [b,L,H,P]", x->ndim);
@@ -148,8 +149,9 @@ int validate_scan(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *d
   SSD_CHECK(check_tensor(C, "C", xd, 4, sbc));
   if (D) SSD_CHECK(check_tensor(D, "D", SSD_F32, 1, sh));
   if (init) SSD_CHECK(check_tensor(init, "init_state", SSD_F32, 4, sst));
-  SSD_CHECK(check_tensor(out, "out", xd, 4, sx));
+  SSD_CHECK(check_tensor(out, out_name, xd, 4, sx));
   if (fin) SSD_CHECK(check_tensor(fin, "final_state", SSD_F32, 4, sst));
+  if (!out_written) return SSD_OK;
 
   const Range ro = range_of(out), rf = range_of(fin);
   const ssd_tensor *ins[] = {x, dt, dt_bias, A, B, C, D, init};
@@ -768,6 +770,97 @@ int ssd_selective_scan_fwd(const ssd_tensor *x, const ssd_tensor *dt, const ssd_
   int status = SSD_OK;
   hipError_t e = ssd::launch_sscan(xd, (int)N, p, st);
   if (e != hipSuccess) status = hip_fail(e, "selective scan launch");
+  const int fs = scratch.finish();
+  return status != SSD_OK ? status : fs;
+}
+
+int ssd_scan_bwd(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bias,
+                 const ssd_tensor *A, const ssd_tensor *B, const ssd_tensor *C,
+                 const ssd_tensor *D, const ssd_tensor *init_state, const ssd_tensor *dout,
+                 const ssd_tensor *dfinal_state, ssd_tensor *dx, ssd_tensor *ddt,
+                 ssd_tensor *ddt_bias, ssd_tensor *dA, ssd_tensor *dB, ssd_tensor *dC,
+                 ssd_tensor *dD, ssd_tensor *dinit_state, void *stream) {
+  g_last_error.clear();
+  ScanShape s;
+  SSD_CHECK(validate_scan(x, dt, dt_bias, A, B, C, D, init_state, dout, nullptr, 64, &s, "dout", false));
+  if (s.P != 32 && s.P != 64)
+    return fail(SSD_ERR_UNSUPPORTED, "backward: P=%lld not in {32,64}", (long long)s.P);
+  if (s.N != 32 && s.N != 64 && s.N != 128)
+    return fail(SSD_ERR_UNSUPPORTED, "backward: N=%lld not in {32,64,128}", (long long)s.N);
+  const int64_t sx[4] = {s.b, s.L, s.H, s.P}, sdt[3] = {s.b, s.L, s.H}, sh[1] = {s.H},
+                sbc[4] = {s.b, s.L, s.G, s.N}, sst[4] = {s.b, s.H, s.P, s.N};
+  if (dfinal_state) SSD_CHECK(check_tensor(dfinal_state, "dfinal_state", SSD_F32, 4, sst));
+  SSD_CHECK(check_tensor(dx, "dx", SSD_F32, 4, sx));
+  SSD_CHECK(check_tensor(ddt, "ddt", SSD_F32, 3, sdt));
+  if (ddt_bias) SSD_CHECK(check_tensor(ddt_bias, "ddt_bias", SSD_F32, 1, sh));
+  SSD_CHECK(check_tensor(dA, "dA", SSD_F32, 1, sh));
+  SSD_CHECK(check_tensor(dB, "dB", SSD_F32, 4, sbc));
+  SSD_CHECK(check_tensor(dC, "dC", SSD_F32, 4, sbc));
+  if (dD) SSD_CHECK(check_tensor(dD, "dD", SSD_F32, 1, sh));
+  if (dinit_state) SSD_CHECK(check_tensor(dinit_state, "dinit_state", SSD_F32, 4, sst));
+  const ssd_tensor *ts[] = {x, dt, dt_bias, A, B, C, D, init_state, dout, dfinal_state,
+                            dx, ddt, ddt_bias, dA, dB, dC, dD, dinit_state};
+  const char *nm[] = {"x", "dt", "dt_bias", "A", "B", "C", "D", "init_state", "dout", "dfinal_state",
+                      "dx", "ddt", "ddt_bias", "dA", "dB", "dC", "dD", "dinit_state"};
+  // no output may overlap an input or another output
+  for (int i = 10; i < 18; ++i) {
+    const Range ri = range_of(ts[i]);
+    for (int j = 0; j < 18; ++j)
+      if (j != i && overlap(ri, range_of(ts[j])))
+        return fail(SSD_ERR_ALIAS, "%s overlaps %s", nm[i], nm[j]);
+  }
+  SSD_CHECK(check_addressable(ts, nm, 18));
+
+  const int64_t nc = (s.L + 63) / 64, PN = s.P * s.N, nbh = s.b * s.H;
+  auto al = [](size_t v) { return (v + 255) / 256 * 256; };
+  const size_t o_fdec = al((size_t)(nbh * s.L) * 4);
+  const size_t o_states = o_fdec + al((size_t)(nbh * nc) * 4);
+  const size_t o_adj = o_states + al((size_t)(nbh * nc * PN) * 4);
+  const size_t o_rdec = o_adj + al((size_t)(nbh * nc * PN) * 4);
+  const size_t o_dec0 = o_rdec + al((size_t)(nbh * nc) * 4);
+  const size_t o_part = o_dec0 + al((size_t)nbh * 4);
+  const size_t total = o_part + al((size_t)(nbh * nc * 3) * 4);
+  hipStream_t st = (hipStream_t)stream;
+  Scratch scratch(st);
+  void *ws = nullptr;
+  SSD_CHECK(scratch.get(total, &ws));
+  char *base = (char *)ws;
+  float *delta = (float *)base, *fdec = (float *)(base + o_fdec), *states = (float *)(base + o_states);
+  int status = SSD_OK;
+  hipError_t e;
+  do {
+    // states entering every 64-token chunk, recomputed by the forward chunk walk
+    e = ssd::launch_delta((const float *)dt->data, dt_bias ? (const float *)dt_bias->data : nullptr, delta,
+                          (int)s.b, (int)s.L, (int)s.H, st);
+    if (e != hipSuccess) { status = hip_fail(e, "delta launch"); break; }
+    if (nc > 1) {
+      ssd::WalkParams wp{};
+      wp.x = x->data; wp.dt = delta; wp.A = (const float *)A->data; wp.B = B->data; wp.C = C->data;
+      wp.b = (int)s.b; wp.L = (int)s.L; wp.H = (int)s.H; wp.G = (int)s.G;
+      wp.seg_len = 64; wp.nseg = (int)nc; wp.state_out = states; wp.seg_decay = fdec;
+      e = ssd::launch_walk(x->dtype, (int)s.P, (int)s.N, ssd::kWalkChunkState, wp, st);
+      if (e != hipSuccess) { status = hip_fail(e, "chunk-state launch"); break; }
+    }
+    e = ssd::launch_state_pass(states, fdec, init_state ? (const float *)init_state->data : nullptr,
+                               (int)s.b, (int)s.H, (int)PN, (int)nc, st);
+    if (e != hipSuccess) { status = hip_fail(e, "state-pass launch"); break; }
+    ssd::BwdParams bp{};
+    bp.x = x->data; bp.dt = (const float *)dt->data;
+    bp.dt_bias = dt_bias ? (const float *)dt_bias->data : nullptr;
+    bp.A = (const float *)A->data; bp.B = B->data; bp.C = C->data;
+    bp.D = D ? (const float *)D->data : nullptr;
+    bp.dy = dout->data; bp.dfinal = dfinal_state ? (const float *)dfinal_state->data : nullptr;
+    bp.states = states; bp.adj = (float *)(base + o_adj); bp.rdecay = (float *)(base + o_rdec);
+    bp.dec0 = (float *)(base + o_dec0); bp.part = (float *)(base + o_part);
+    bp.dx = (float *)dx->data; bp.ddt = (float *)ddt->data; bp.dB = (float *)dB->data;
+    bp.dC = (float *)dC->data; bp.dA = (float *)dA->data;
+    bp.dD = dD ? (float *)dD->data : nullptr;
+    bp.ddt_bias = ddt_bias ? (float *)ddt_bias->data : nullptr;
+    bp.dinit = dinit_state ? (float *)dinit_state->data : nullptr;
+    bp.b = (int)s.b; bp.L = (int)s.L; bp.H = (int)s.H; bp.G = (int)s.G; bp.nc = (int)nc;
+    e = ssd::launch_bwd(x->dtype, (int)s.P, (int)s.N, bp, st);
+    if (e != hipSuccess) { status = hip_fail(e, "backward launch"); break; }
+  } while (0);
   const int fs = scratch.finish();
   return status != SSD_OK ? status : fs;
 }

@@ -1,0 +1,525 @@
+// ssd_bwd.hip -- gradients of the SSD scan on MI355X (gfx950).
+//
+// Training needs the gradients of the scan with respect to all of its
+// inputs.  The Mamba paper-reading notes (sxlin0.github.io, the section on
+// the hardware-aware selective scan) describe the backward pass as
+// recomputing the states it needs instead of keeping them from the forward
+// pass; here the states at 64-token chunk boundaries are recomputed by the
+// forward chunk walk, and everything inside a chunk is rebuilt on chip.
+//
+// Notation per (batch, head), chunk of Q = 64 tokens starting at t0, local
+// index i: a_i = Delta_i A (log decay), cum_i = a_0 + ... + a_i,
+// e_in_i = exp(cum_i), e_out_i = exp(cum_last - cum_i).  H is the state
+// entering the chunk, G the gradient arriving at the chunk's last state from
+// later tokens and the final state.  Unrolling the recurrence over the chunk
+// ("Mamba-3 deep dive ch. 2", section 2.2.1: the mask of the matrix form is
+// a product of forget gates) gives, with S = C B^T, E_ij = exp(cum_i - cum_j)
+// for i >= j (else 0), M = S o E and DX = dY X^T:
+//
+//   bracket_t = (M^T dY)_t + e_out_t G B_t            (the adjoint times B_t)
+//   dx_t      = D dy_t + Delta_t bracket_t
+//   dC_t     += e_in_t H^T dy_t + ((DX o E) diag(Delta) B)_t        (all heads)
+//   dB_t     += Delta_t (e_out_t G^T x_t + ((DX o E)^T C)_t)         (all heads)
+//   dDelta_t  = x_t . bracket_t + A da_t
+//   da_k      = sum_{i >= k > j} W_ij + sum_{i >= k} u_i + sum_{j < k} v_j + w
+//
+// where W_ij = M_ij DX_ij Delta_j (token j's input reaching output i), u_i =
+// e_in_i dy_i . (H C_i) (the entering state reaching output i), v_j =
+// e_out_j Delta_j x_j . (G B_j) (input j reaching later tokens) and w =
+// exp(cum_last) <G, H>: da_k collects every path whose decay product
+// contains a_k.  The first double sum is R_k with R_0 = 0 and
+// R_{k+1} = R_k + colsum_k(W) - rowsum_k(W) (W is strictly lower triangular).
+//
+// The chunk-boundary adjoints G follow the same state passing as the forward
+// states, run backwards: G_{c-1} = exp(cum_last^(c)) G_c + Gh_c with
+// Gh_c = sum_i e_in_i dy_i C_i^T, starting from the final-state gradient;
+// the gradient of the initial state is Gh_0 + exp(cum_last^(0)) G_0.
+//
+// Kernels: bwd_dstate_kernel (Gh_c per (batch, head, chunk), written in
+// reversed chunk order so the forward state pass runs the recursion),
+// bwd_chunk_kernel (one workgroup per (batch, group, chunk), all heads of
+// the group in turn: dB and dC stay in registers across heads, so no atomics
+// and a fixed summation order), bwd_dinit_kernel and bwd_param_kernel (sums
+// of the per-(batch, head, chunk) partials of dA, dD and d dt_bias).
+//
+// All matrix products run on the matrix cores in fp32 (16x16x4 MFMA) from
+// fp32 LDS tiles; bf16 inputs are widened when staged.
+#include "ssd_device.h"
+#include "ssd_internal.h"
+
+namespace ssd {
+namespace {
+
+constexpr int kQ = 64;
+
+// Staging of a row of `cols` elements of type T into fp32 LDS, four at a time.
+template <typename T>
+__device__ __forceinline__ void stage_rows(float *dst, int ld, const T *src, int64_t row_stride, int rows,
+                                           int valid_rows, int cols, int tid, int nthreads) {
+  const int c4 = cols / 4;
+  for (int idx = tid; idx < rows * c4; idx += nthreads) {
+    const int r = idx / c4, c = (idx % c4) * 4;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (r < valid_rows) {
+      const T *s = src + (int64_t)r * row_stride + c;
+      v = make_float4(to_f(s[0]), to_f(s[1]), to_f(s[2]), to_f(s[3]));
+    }
+    *reinterpret_cast<float4 *>(dst + r * ld + c) = v;
+  }
+}
+
+// Fragment of a row-major fp32 LDS tile whose K index runs along the row
+// (contiguous): row `row`, K-values k0 + {4g .. 4g+3, 16+4g .. 16+4g+3}.
+__device__ __forceinline__ FragF32 frag_k_contig(const float *tile, int ld, int row, int k0, int lg) {
+  const float *p = tile + row * ld + k0 + 4 * lg;
+  return ld4x2(p, p + 16);
+}
+
+__device__ __forceinline__ float sum16(float v) { // over the 16 lanes of a lane group
+  v += __shfl_xor(v, 1, 64);
+  v += __shfl_xor(v, 2, 64);
+  v += __shfl_xor(v, 4, 64);
+  v += __shfl_xor(v, 8, 64);
+  return v;
+}
+__device__ __forceinline__ float sum_lg(float v) { // over the 4 lane groups
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) { return sum_lg(sum16(v)); }
+
+// Per-chunk decay quantities for one (batch, head), computed by one wave:
+// lane k holds token t0 + k.  Returns Delta; writes cum (log2 units), e_in,
+// e_out and sigmoid(dt + bias) (the derivative of softplus) for lane k.
+struct ChunkDecay {
+  float delta, cum2, e_in, e_out, sig, cum2_last;
+};
+__device__ __forceinline__ ChunkDecay chunk_decay(const float *dt, const float *dt_bias, const float *A, int b_, int L,
+                                                  int H, int h, int t0, int lane) {
+  ChunkDecay d;
+  const int t = t0 + lane;
+  const bool valid = t < L;
+  const float z = valid ? dt[((int64_t)b_ * L + t) * H + h] + (dt_bias ? dt_bias[h] : 0.f) : 0.f;
+  d.delta = valid ? softplus_f(z) : 0.f;
+  d.sig = valid ? __builtin_amdgcn_rcpf(1.f + hw_exp2(-z * kLog2e)) : 0.f;
+  d.cum2 = wave_incl_scan(d.delta * A[h] * kLog2e);
+  d.cum2_last = __shfl(d.cum2, 63, 64);
+  d.e_in = hw_exp2(d.cum2);
+  d.e_out = hw_exp2(d.cum2_last - d.cum2);
+  return d;
+}
+
+// ---------------------------------------------------------------------------
+// Gh_c[p][n] = sum_i e_in_i dy_i[p] C_i[n] for one (batch, head, chunk c).
+// c >= 1 goes to slot nc-1-c of `adj` with its log2 decay in rdecay; c = 0
+// goes to dinit (if wanted) with its log2 decay in dec0.
+template <typename T, int P, int N>
+__global__ void __launch_bounds__(256) bwd_dstate_kernel(const BwdParams p) {
+  constexpr int LX = P + 4, LB = N + 4;
+  __shared__ __attribute__((aligned(16))) float sDY[kQ * LX];
+  __shared__ __attribute__((aligned(16))) float sC[kQ * LB];
+  __shared__ float sEin[kQ];
+  const int nc = p.nc;
+  const int c = blockIdx.x % nc;
+  const int bh = blockIdx.x / nc;
+  const int b_ = bh / p.H, h = bh % p.H, g = (int)(((int64_t)h * p.G) / p.H);
+  if (c == 0 && !p.dinit) return;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+  const int t0 = c * kQ, nv = min(kQ, p.L - t0);
+  if (w == 0) {
+    const ChunkDecay d = chunk_decay(p.dt, p.dt_bias, p.A, b_, p.L, p.H, h, t0, lane);
+    sEin[lane] = d.e_in;
+    if (lane == 0) {
+      if (c > 0) p.rdecay[(int64_t)bh * nc + (nc - 1 - c)] = d.cum2_last;
+      else p.dec0[bh] = d.cum2_last;
+    }
+  }
+  const T *dy = reinterpret_cast<const T *>(p.dy) + (((int64_t)b_ * p.L + t0) * p.H + h) * P;
+  const T *Cg = reinterpret_cast<const T *>(p.C) + (((int64_t)b_ * p.L + t0) * p.G + g) * N;
+  stage_rows<T>(sC, LB, Cg, (int64_t)p.G * N, kQ, nv, N, tid, 256);
+  stage_rows<T>(sDY, LX, dy, (int64_t)p.H * P, kQ, nv, P, tid, 256);
+  __syncthreads();
+  for (int idx = tid; idx < kQ * P; idx += 256) sDY[(idx / P) * LX + idx % P] *= sEin[idx / P];
+  __syncthreads();
+  float *dst = c > 0 ? p.adj + ((int64_t)bh * nc + (nc - 1 - c)) * (P * N) : p.dinit + (int64_t)bh * (P * N);
+  constexpr int PT = P / 16, NT = N / 16;
+  for (int tile = w; tile < PT * NT; tile += 4) {
+    const int pt = tile % PT, nt = tile / PT;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k0 = 0; k0 < kQ; k0 += 32)
+      acc = mma(trfrag(sDY, LX, k0, pt * 16, li, lg), trfrag(sC, LB, k0, nt * 16, li, lg), acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dst[(pt * 16 + 4 * lg + r) * N + nt * 16 + li] = acc[r];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// One workgroup per (batch, group, chunk); 8 waves.  Tile maps (16x16 tiles,
+// id -> row tile id % 4, column tile id / 4; wave w takes ids w, w+8, ...):
+// every wave owns one row tile (w % 4) of a Q x X product and the column
+// tiles w/4, w/4 + 2, ...
+template <typename T, int P, int N>
+__global__ void __launch_bounds__(512) bwd_chunk_kernel(const BwdParams p) {
+  constexpr int LB = N + 4, LX = P + 4, LQ = kQ + 4, LS = N + 4;
+  constexpr int PT = P / 16, NT = N / 16;
+  __shared__ __attribute__((aligned(16))) float sB[kQ * LB];
+  __shared__ __attribute__((aligned(16))) float sC[kQ * LB];
+  __shared__ __attribute__((aligned(16))) float sX[kQ * LX];
+  __shared__ __attribute__((aligned(16))) float sDY[kQ * LX];
+  __shared__ __attribute__((aligned(16))) float sM[kQ * LQ];
+  __shared__ __attribute__((aligned(16))) float sSt[P * LS];
+  __shared__ float sCum[kQ], sDel[kQ], sEin[kQ], sEout[kQ], sSig[kQ];
+  __shared__ float rowW[2][kQ], colW[4][kQ], uP[2][kQ], vP[2][kQ], dinP[2][kQ], sDiag[kQ];
+  __shared__ float sRed[9]; // [0]: log2 decay of the chunk; [1 + w]: wave w's share of <G, H>
+
+  const int nc = p.nc, G = p.G, H = p.H, L = p.L;
+  const int c = blockIdx.x % nc;
+  const int bg = blockIdx.x / nc;
+  const int b_ = bg / G, g = bg % G;
+  const int hpg = H / G;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+  const int rt = w & 3, ct0 = w >> 2;
+  const int t0 = c * kQ, nv = min(kQ, L - t0);
+  const int PN = P * N;
+
+  // B and C of the group's chunk, and S = C B^T (two 16x16 tiles per wave)
+  const T *Bg = reinterpret_cast<const T *>(p.B) + (((int64_t)b_ * L + t0) * G + g) * N;
+  const T *Cg = reinterpret_cast<const T *>(p.C) + (((int64_t)b_ * L + t0) * G + g) * N;
+  stage_rows<T>(sB, LB, Bg, (int64_t)G * N, kQ, nv, N, tid, 512);
+  stage_rows<T>(sC, LB, Cg, (int64_t)G * N, kQ, nv, N, tid, 512);
+  __syncthreads();
+  f32x4 S[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int ct = ct0 + 2 * k;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k0 = 0; k0 < N; k0 += 32)
+      acc = mma(frag_k_contig(sC, LB, rt * 16 + li, k0, lg), frag_k_contig(sB, LB, ct * 16 + li, k0, lg), acc);
+    S[k] = acc;
+  }
+
+  f32x4 dBacc[NT / 2], dCacc[NT / 2];
+#pragma unroll
+  for (int k = 0; k < NT / 2; ++k) {
+    dBacc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dCacc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  for (int h = g * hpg; h < (g + 1) * hpg; ++h) {
+    const int64_t bh = (int64_t)b_ * H + h;
+    const float Ah = p.A[h], Dh = p.D ? p.D[h] : 0.f;
+    // --- stage: decays, x, dy, entering state H
+    if (w == 0) {
+      const ChunkDecay d = chunk_decay(p.dt, p.dt_bias, p.A, b_, L, H, h, t0, lane);
+      sCum[lane] = d.cum2;
+      sDel[lane] = d.delta;
+      sEin[lane] = d.e_in;
+      sEout[lane] = d.e_out;
+      sSig[lane] = d.sig;
+      if (lane == 0) sRed[0] = d.cum2_last;
+    }
+    const T *xh = reinterpret_cast<const T *>(p.x) + (((int64_t)b_ * L + t0) * H + h) * P;
+    const T *dyh = reinterpret_cast<const T *>(p.dy) + (((int64_t)b_ * L + t0) * H + h) * P;
+    stage_rows<T>(sX, LX, xh, (int64_t)H * P, kQ, nv, P, tid, 512);
+    stage_rows<T>(sDY, LX, dyh, (int64_t)H * P, kQ, nv, P, tid, 512);
+    const float *Hs = p.states + (bh * nc + c) * PN;
+    for (int idx = tid; idx < PN / 4; idx += 512) {
+      const int r = (idx * 4) / N, col = (idx * 4) % N;
+      *reinterpret_cast<float4 *>(sSt + r * LS + col) = reinterpret_cast<const float4 *>(Hs)[idx];
+    }
+    __syncthreads();
+    const float cum_last2 = sRed[0];
+
+    // --- DX = dY X^T, M = S o E (to LDS), P2 = DX o E, W sums, diag(DX)
+    f32x4 P2[2];
+    float rsum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int ct = ct0 + 2 * k;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k0 = 0; k0 < P; k0 += 32)
+        acc = mma(frag_k_contig(sDY, LX, rt * 16 + li, k0, lg), frag_k_contig(sX, LX, ct * 16 + li, k0, lg), acc);
+      const int j = ct * 16 + li;
+      const float cj = sCum[j], dj = sDel[j];
+      float csum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = rt * 16 + 4 * lg + r;
+        const float e = (i >= j) ? hw_exp2(sCum[i] - cj) : 0.f;
+        const float m = S[k][r] * e;
+        sM[i * LQ + j] = m;
+        P2[k][r] = acc[r] * e;
+        const float wv = (i > j) ? m * acc[r] * dj : 0.f;
+        rsum[r] += wv;
+        csum += wv;
+        if (i == j) sDiag[i] = acc[r];
+      }
+      csum = sum_lg(csum);
+      if (lg == 0) colW[rt][j] = csum;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float v = sum16(rsum[r]);
+      if (li == 0) rowW[ct0][rt * 16 + 4 * lg + r] = v;
+    }
+
+    // --- dY H (K = P): dC += e_in o (dY H); u_i = e_in_i sum_n C_in (dY H)_in
+    {
+      float up[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < NT / 2; ++k) {
+        const int ct = ct0 + 2 * k;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k0 = 0; k0 < P; k0 += 32)
+          acc = mma(frag_k_contig(sDY, LX, rt * 16 + li, k0, lg), trfrag(sSt, LS, k0, ct * 16, li, lg), acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = rt * 16 + 4 * lg + r;
+          const float v = sEin[i] * acc[r];
+          dCacc[k][r] += v;
+          up[r] += sC[i * LB + ct * 16 + li] * v;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = sum16(up[r]);
+        if (li == 0) uP[ct0][rt * 16 + 4 * lg + r] = v;
+      }
+    }
+    __syncthreads();
+
+    // --- replace H by G (the gradient at the chunk's last state); <G, H>
+    {
+      const float *Gs = p.adj + (bh * nc + (nc - 1 - c)) * PN;
+      float gh = 0.f;
+      for (int idx = tid; idx < PN / 4; idx += 512) {
+        const int r = (idx * 4) / N, col = (idx * 4) % N;
+        float4 *d = reinterpret_cast<float4 *>(sSt + r * LS + col);
+        const float4 hv = *d, gv = reinterpret_cast<const float4 *>(Gs)[idx];
+        gh += hv.x * gv.x + hv.y * gv.y + hv.z * gv.z + hv.w * gv.w;
+        *d = gv;
+      }
+      gh = wave_sum(gh);
+      if (lane == 0) sRed[1 + w] = gh;
+    }
+    __syncthreads();
+
+    // --- bracket = M^T dY + e_out o (B G^T); dx; x . bracket
+    {
+      float dp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < PT / 2; ++k) {
+        const int ct = ct0 + 2 * k;
+        f32x4 a3 = {0.f, 0.f, 0.f, 0.f}, b3 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k0 = 0; k0 < kQ; k0 += 32)
+          a3 = mma(trfrag(sM, LQ, k0, rt * 16, li, lg), trfrag(sDY, LX, k0, ct * 16, li, lg), a3);
+#pragma unroll
+        for (int k0 = 0; k0 < N; k0 += 32)
+          b3 = mma(frag_k_contig(sB, LB, rt * 16 + li, k0, lg), frag_k_contig(sSt, LS, ct * 16 + li, k0, lg), b3);
+        const int pc = ct * 16 + li;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = rt * 16 + 4 * lg + r;
+          const float br = a3[r] + sEout[t] * b3[r];
+          if (t < nv)
+            p.dx[(((int64_t)b_ * L + t0 + t) * H + h) * P + pc] = Dh * sDY[t * LX + pc] + sDel[t] * br;
+          dp[r] += sX[t * LX + pc] * br;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = sum16(dp[r]);
+        if (li == 0) dinP[ct0][rt * 16 + 4 * lg + r] = v;
+      }
+    }
+
+    // --- X G (K = P): dB part e_out o (X G); v_j = e_out_j Delta_j sum_n B_jn (X G)_jn
+    f32x4 acc6[NT / 2];
+    {
+      float vp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < NT / 2; ++k) {
+        const int ct = ct0 + 2 * k;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k0 = 0; k0 < P; k0 += 32)
+          acc = mma(frag_k_contig(sX, LX, rt * 16 + li, k0, lg), trfrag(sSt, LS, k0, ct * 16, li, lg), acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = rt * 16 + 4 * lg + r;
+          vp[r] += sB[t * LB + ct * 16 + li] * acc[r];
+          acc6[k][r] = sEout[t] * acc[r];
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = sum16(vp[r]);
+        if (li == 0) vP[ct0][rt * 16 + 4 * lg + r] = v;
+      }
+    }
+    __syncthreads();
+
+    // --- P2 = DX o E to LDS; dB += Delta o (e_out o XG + P2^T C)
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sM[(rt * 16 + 4 * lg + r) * LQ + (ct0 + 2 * k) * 16 + li] = P2[k][r];
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NT / 2; ++k) {
+      const int ct = ct0 + 2 * k;
+      f32x4 acc = acc6[k];
+#pragma unroll
+      for (int k0 = 0; k0 < kQ; k0 += 32)
+        acc = mma(trfrag(sM, LQ, k0, rt * 16, li, lg), trfrag(sC, LB, k0, ct * 16, li, lg), acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dBacc[k][r] += sDel[rt * 16 + 4 * lg + r] * acc[r];
+    }
+    __syncthreads();
+
+    // --- P1 = P2 diag(Delta) to LDS; dC += P1 B
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int j = (ct0 + 2 * k) * 16 + li;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sM[(rt * 16 + 4 * lg + r) * LQ + j] = P2[k][r] * sDel[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NT / 2; ++k) {
+      const int ct = ct0 + 2 * k;
+      f32x4 acc = dCacc[k];
+#pragma unroll
+      for (int k0 = 0; k0 < kQ; k0 += 32)
+        acc = mma(frag_k_contig(sM, LQ, rt * 16 + li, k0, lg), trfrag(sB, LB, k0, ct * 16, li, lg), acc);
+      dCacc[k] = acc;
+    }
+
+    // --- da, ddt and the head's partial sums (wave 0, lane k = token)
+    if (w == 0) {
+      const int k = lane;
+      const float colsum = colW[0][k] + colW[1][k] + colW[2][k] + colW[3][k];
+      const float rowsum = rowW[0][k] + rowW[1][k];
+      const float dlt = colsum - rowsum;
+      const float R = wave_incl_scan(dlt) - dlt;           // sum over m < k
+      const float u = uP[0][k] + uP[1][k];
+      const float u_incl = wave_incl_scan(u);
+      const float U = __shfl(u_incl, 63, 64) - u_incl + u;  // sum over i >= k
+      const float v = sEout[k] * sDel[k] * (vP[0][k] + vP[1][k]);
+      const float V = wave_incl_scan(v) - v;               // sum over j < k
+      float gh = 0.f;
+#pragma unroll
+      for (int q = 1; q <= 8; ++q) gh += sRed[q];
+      const float da = R + U + V + hw_exp2(cum_last2) * gh;
+      const float din = dinP[0][k] + dinP[1][k];
+      const float ddt = (din + Ah * da) * sSig[k];
+      const bool valid = k < nv;
+      if (valid) p.ddt[((int64_t)b_ * L + t0 + k) * H + h] = ddt;
+      const float pa = wave_sum(valid ? sDel[k] * da : 0.f);
+      const float pd = wave_sum(valid ? sDiag[k] : 0.f);
+      const float pb = wave_sum(valid ? ddt : 0.f);
+      if (lane == 0) {
+        float *q = p.part + (bh * nc + c) * 3;
+        q[0] = pa;
+        q[1] = pd;
+        q[2] = pb;
+      }
+    }
+    __syncthreads();
+  }
+
+  // dB, dC of the group's chunk (fp32)
+#pragma unroll
+  for (int k = 0; k < NT / 2; ++k) {
+    const int n = (ct0 + 2 * k) * 16 + li;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = rt * 16 + 4 * lg + r;
+      if (t < nv) {
+        const int64_t o = (((int64_t)b_ * L + t0 + t) * G + g) * N + n;
+        p.dB[o] = dBacc[k][r];
+        p.dC[o] = dCacc[k][r];
+      }
+    }
+  }
+}
+
+// dinit += exp2(dec0) * G_0 (G_0 = slot nc-1 of adj after the reverse pass).
+__global__ void __launch_bounds__(256) bwd_dinit_kernel(float *__restrict__ dinit, const float *__restrict__ adj,
+                                                        const float *__restrict__ dec0, int64_t nbh, int PN, int nc) {
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= nbh * PN) return;
+  const int64_t bh = id / PN;
+  const int e = (int)(id % PN);
+  dinit[id] += hw_exp2(dec0[bh]) * adj[(bh * nc + nc - 1) * PN + e];
+}
+
+// dA, dD, d dt_bias per head: sums of the (batch, chunk) partials in a fixed order.
+__global__ void __launch_bounds__(64) bwd_param_kernel(const float *__restrict__ part, float *__restrict__ dA,
+                                                       float *__restrict__ dD, float *__restrict__ ddt_bias,
+                                                       int b, int H, int nc) {
+  const int h = blockIdx.x * 64 + threadIdx.x;
+  if (h >= H) return;
+  float sa = 0.f, sd = 0.f, sb = 0.f;
+  for (int ib = 0; ib < b; ++ib)
+    for (int c = 0; c < nc; ++c) {
+      const float *q = part + (((int64_t)ib * H + h) * nc + c) * 3;
+      sa += q[0];
+      sd += q[1];
+      sb += q[2];
+    }
+  dA[h] = sa;
+  if (dD) dD[h] = sd;
+  if (ddt_bias) ddt_bias[h] = sb;
+}
+
+template <typename T, int P, int N> hipError_t launch_bwd_t(const BwdParams &p, hipStream_t st) {
+  hipLaunchKernelGGL((bwd_dstate_kernel<T, P, N>), dim3((unsigned)(p.b * p.H * p.nc)), dim3(256), 0, st, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_state_pass(p.adj, p.rdecay, p.dfinal, p.b, p.H, P * N, p.nc, st);
+  if (e != hipSuccess) return e;
+  if (p.dinit) {
+    const int64_t n = (int64_t)p.b * p.H * P * N;
+    hipLaunchKernelGGL(bwd_dinit_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p.dinit, p.adj,
+                       p.dec0, (int64_t)p.b * p.H, P * N, p.nc);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((bwd_chunk_kernel<T, P, N>), dim3((unsigned)(p.b * p.G * p.nc)), dim3(512), 0, st, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_param_kernel, dim3((unsigned)((p.H + 63) / 64)), dim3(64), 0, st, p.part, p.dA, p.dD,
+                     p.ddt_bias, p.b, p.H, p.nc);
+  return hipGetLastError();
+}
+
+template <typename T, int P> hipError_t launch_bwd_n(int N, const BwdParams &p, hipStream_t st) {
+  switch (N) {
+  case 32: return launch_bwd_t<T, P, 32>(p, st);
+  case 64: return launch_bwd_t<T, P, 64>(p, st);
+  case 128: return launch_bwd_t<T, P, 128>(p, st);
+  }
+  return hipErrorInvalidValue;
+}
+template <typename T> hipError_t launch_bwd_p(int P, int N, const BwdParams &p, hipStream_t st) {
+  switch (P) {
+  case 32: return launch_bwd_n<T, 32>(N, p, st);
+  case 64: return launch_bwd_n<T, 64>(N, p, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+} // namespace
+
+hipError_t launch_bwd(int dtype, int P, int N, const BwdParams &p, hipStream_t st) {
+  return dtype == 1 ? launch_bwd_p<__bf16>(P, N, p, st) : launch_bwd_p<float>(P, N, p, st);
+}
+
+} // namespace ssd

@@ -113,4 +113,32 @@ struct SScanParams {
 // N in {4, 8, 16}; dtype 1 = bf16, 0 = fp32.
 hipError_t launch_sscan(int dtype, int N, const SScanParams &p, hipStream_t stream);
 
+// Gradients of the scan (64-token chunks).  The caller has filled `states`
+// with the state entering every chunk; launch_bwd computes the rest.
+struct BwdParams {
+  const void *x;        // [b, L, H, P] input dtype
+  const float *dt;      // [b, L, H] raw
+  const float *dt_bias; // [H] or null
+  const float *A;       // [H]
+  const void *B;        // [b, L, G, N]
+  const void *C;        // [b, L, G, N]
+  const float *D;       // [H] or null
+  const void *dy;       // [b, L, H, P] input dtype: gradient at the output
+  const float *dfinal;  // [b, H, P, N] or null: gradient at the final state
+  const float *states;  // scratch [b, H, nc, P, N]: state entering each chunk
+  float *adj;           // scratch [b, H, nc, P, N]: slot nc-1-c ends as the
+                        // gradient at chunk c's last state
+  float *rdecay;        // scratch [b, H, nc]: log2 decays in reversed chunk order
+  float *dec0;          // scratch [b, H]: log2 decay of chunk 0
+  float *part;          // scratch [b, H, nc, 3]: partial dA, dD, d dt_bias
+  float *dx;            // [b, L, H, P]
+  float *ddt;           // [b, L, H]
+  float *dB, *dC;       // [b, L, G, N]
+  float *dA;            // [H]
+  float *dD, *ddt_bias; // [H] or null
+  float *dinit;         // [b, H, P, N] or null
+  int b, L, H, G, nc;
+};
+// P in {32, 64}, N in {32, 64, 128}; dtype 1 = bf16, 0 = fp32.
+hipError_t launch_bwd(int dtype, int P, int N, const BwdParams &p, hipStream_t stream);
 } // namespace ssd

@@ -59,6 +59,8 @@ def lib():
         L.ssd_selective_scan_fwd.argtypes = [P] * 10 + [ctypes.c_int, ctypes.c_void_p]
         L.ssd_selective_scan_fwd.restype = ctypes.c_int
         L.ssd_step.argtypes = [P] * 8 + [ctypes.c_void_p]
+        L.ssd_scan_bwd.argtypes = [P] * 18 + [ctypes.c_void_p]
+        L.ssd_scan_bwd.restype = ctypes.c_int
         L.ssd_step.restype = ctypes.c_int
         L.ssd_status_string.argtypes = [ctypes.c_int]
         L.ssd_status_string.restype = ctypes.c_char_p
@@ -136,6 +138,37 @@ def ssd_scan_fwd(x, dt, dt_bias, A, B, C, D=None, init_state=None, out=None,
             int(chunk), int(algo), st)
     _check(status)
     return out, final_state
+
+
+def ssd_scan_bwd(x, dt, dt_bias, A, B, C, D, init_state, dout, dfinal_state=None, *,
+                 want_dt_bias: bool = True, want_D: bool = True, want_init: bool = True,
+                 out: dict = None, stream=None):
+    """Gradients of ssd_scan_fwd for the objective <dout, y> + <dfinal_state, final state>.
+
+    Returns a dict of fp32 tensors: dx, ddt (at the raw dt), dA, dB, dC and,
+    when asked for, ddt_bias, dD, dinit.  ``out`` may hold preallocated
+    tensors under those names."""
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    dev = x.device
+    shapes = dict(dx=(b, L, H, P), ddt=(b, L, H), dA=(H,), dB=(b, L, G, N), dC=(b, L, G, N),
+                  ddt_bias=(H,) if want_dt_bias else None, dD=(H,) if want_D else None,
+                  dinit=(b, H, P, N) if want_init else None)
+    g = dict(out or {})
+    for k, shp in shapes.items():
+        if shp is not None and g.get(k) is None:
+            g[k] = torch.empty(shp, dtype=torch.float32, device=dev)
+        elif shp is None:
+            g[k] = None
+    with _on_device(x):
+        st = _stream(stream, x)
+        status = lib().ssd_scan_bwd(
+            describe(x), describe(dt), describe(dt_bias), describe(A), describe(B), describe(C),
+            describe(D), describe(init_state), describe(dout), describe(dfinal_state),
+            describe(g["dx"]), describe(g["ddt"]), describe(g["ddt_bias"]), describe(g["dA"]),
+            describe(g["dB"]), describe(g["dC"]), describe(g["dD"]), describe(g["dinit"]), st)
+    _check(status)
+    return g
 
 
 def ssd_scan_fwd_gated(x, dt, dt_bias, A, B, C, z, D=None, init_state=None, out=None,
