@@ -813,54 +813,31 @@ int ssd_scan_bwd(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt
 
   const int64_t nc = (s.L + 63) / 64, PN = s.P * s.N, nbh = s.b * s.H;
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
-  const size_t o_fdec = al((size_t)(nbh * s.L) * 4);
-  const size_t o_states = o_fdec + al((size_t)(nbh * nc) * 4);
-  const size_t o_adj = o_states + al((size_t)(nbh * nc * PN) * 4);
-  const size_t o_rdec = o_adj + al((size_t)(nbh * nc * PN) * 4);
-  const size_t o_dec0 = o_rdec + al((size_t)(nbh * nc) * 4);
-  const size_t o_part = o_dec0 + al((size_t)nbh * 4);
+  const size_t o_adj = al((size_t)(nbh * nc * PN) * 4);
+  const size_t o_part = o_adj + al((size_t)(nbh * nc * PN) * 4);
   const size_t total = o_part + al((size_t)(nbh * nc * 3) * 4);
   hipStream_t st = (hipStream_t)stream;
   Scratch scratch(st);
   void *ws = nullptr;
   SSD_CHECK(scratch.get(total, &ws));
   char *base = (char *)ws;
-  float *delta = (float *)base, *fdec = (float *)(base + o_fdec), *states = (float *)(base + o_states);
+  ssd::BwdParams bp{};
+  bp.x = x->data; bp.dt = (const float *)dt->data;
+  bp.dt_bias = dt_bias ? (const float *)dt_bias->data : nullptr;
+  bp.A = (const float *)A->data; bp.B = B->data; bp.C = C->data;
+  bp.D = D ? (const float *)D->data : nullptr;
+  bp.dy = dout->data; bp.dfinal = dfinal_state ? (const float *)dfinal_state->data : nullptr;
+  bp.states_init = init_state ? (const float *)init_state->data : nullptr;
+  bp.states = (float *)base; bp.adj = (float *)(base + o_adj); bp.part = (float *)(base + o_part);
+  bp.dx = (float *)dx->data; bp.ddt = (float *)ddt->data; bp.dB = (float *)dB->data;
+  bp.dC = (float *)dC->data; bp.dA = (float *)dA->data;
+  bp.dD = dD ? (float *)dD->data : nullptr;
+  bp.ddt_bias = ddt_bias ? (float *)ddt_bias->data : nullptr;
+  bp.dinit = dinit_state ? (float *)dinit_state->data : nullptr;
+  bp.b = (int)s.b; bp.L = (int)s.L; bp.H = (int)s.H; bp.G = (int)s.G; bp.nc = (int)nc;
   int status = SSD_OK;
-  hipError_t e;
-  do {
-    // states entering every 64-token chunk, recomputed by the forward chunk walk
-    e = ssd::launch_delta((const float *)dt->data, dt_bias ? (const float *)dt_bias->data : nullptr, delta,
-                          (int)s.b, (int)s.L, (int)s.H, st);
-    if (e != hipSuccess) { status = hip_fail(e, "delta launch"); break; }
-    if (nc > 1) {
-      ssd::WalkParams wp{};
-      wp.x = x->data; wp.dt = delta; wp.A = (const float *)A->data; wp.B = B->data; wp.C = C->data;
-      wp.b = (int)s.b; wp.L = (int)s.L; wp.H = (int)s.H; wp.G = (int)s.G;
-      wp.seg_len = 64; wp.nseg = (int)nc; wp.state_out = states; wp.seg_decay = fdec;
-      e = ssd::launch_walk(x->dtype, (int)s.P, (int)s.N, ssd::kWalkChunkState, wp, st);
-      if (e != hipSuccess) { status = hip_fail(e, "chunk-state launch"); break; }
-    }
-    e = ssd::launch_state_pass(states, fdec, init_state ? (const float *)init_state->data : nullptr,
-                               (int)s.b, (int)s.H, (int)PN, (int)nc, st);
-    if (e != hipSuccess) { status = hip_fail(e, "state-pass launch"); break; }
-    ssd::BwdParams bp{};
-    bp.x = x->data; bp.dt = (const float *)dt->data;
-    bp.dt_bias = dt_bias ? (const float *)dt_bias->data : nullptr;
-    bp.A = (const float *)A->data; bp.B = B->data; bp.C = C->data;
-    bp.D = D ? (const float *)D->data : nullptr;
-    bp.dy = dout->data; bp.dfinal = dfinal_state ? (const float *)dfinal_state->data : nullptr;
-    bp.states = states; bp.adj = (float *)(base + o_adj); bp.rdecay = (float *)(base + o_rdec);
-    bp.dec0 = (float *)(base + o_dec0); bp.part = (float *)(base + o_part);
-    bp.dx = (float *)dx->data; bp.ddt = (float *)ddt->data; bp.dB = (float *)dB->data;
-    bp.dC = (float *)dC->data; bp.dA = (float *)dA->data;
-    bp.dD = dD ? (float *)dD->data : nullptr;
-    bp.ddt_bias = ddt_bias ? (float *)ddt_bias->data : nullptr;
-    bp.dinit = dinit_state ? (float *)dinit_state->data : nullptr;
-    bp.b = (int)s.b; bp.L = (int)s.L; bp.H = (int)s.H; bp.G = (int)s.G; bp.nc = (int)nc;
-    e = ssd::launch_bwd(x->dtype, (int)s.P, (int)s.N, bp, st);
-    if (e != hipSuccess) { status = hip_fail(e, "backward launch"); break; }
-  } while (0);
+  const hipError_t e = ssd::launch_bwd(x->dtype, (int)s.P, (int)s.N, bp, st);
+  if (e != hipSuccess) status = hip_fail(e, "backward launch");
   const int fs = scratch.finish();
   return status != SSD_OK ? status : fs;
 }

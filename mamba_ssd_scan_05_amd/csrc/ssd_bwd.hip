@@ -30,20 +30,23 @@
 // contains a_k.  The first double sum is R_k with R_0 = 0 and
 // R_{k+1} = R_k + colsum_k(W) - rowsum_k(W) (W is strictly lower triangular).
 //
-// The chunk-boundary adjoints G follow the same state passing as the forward
-// states, run backwards: G_{c-1} = exp(cum_last^(c)) G_c + Gh_c with
-// Gh_c = sum_i e_in_i dy_i C_i^T, starting from the final-state gradient;
-// the gradient of the initial state is Gh_0 + exp(cum_last^(0)) G_0.
+// The chunk-boundary states H and adjoints G are sequential over chunks:
+// H_{c+1} = exp(cum_last^(c)) H_c + sum_j e_out_j Delta_j x_j B_j^T from the
+// initial state, and, backwards from the final-state gradient,
+// G_{c-1} = exp(cum_last^(c)) G_c + sum_i e_in_i dy_i C_i^T; the gradient of
+// the initial state is the last of these, G_{-1}.
 //
-// Kernels: bwd_dstate_kernel (Gh_c per (batch, head, chunk), written in
-// reversed chunk order so the forward state pass runs the recursion),
-// bwd_chunk_kernel (one workgroup per (batch, group, chunk), all heads of
-// the group in turn: dB and dC stay in registers across heads, so no atomics
-// and a fixed summation order), bwd_dinit_kernel and bwd_param_kernel (sums
-// of the per-(batch, head, chunk) partials of dA, dD and d dt_bias).
+// Kernels: bwd_state_scan_kernel (both recursions, one workgroup per
+// (batch, head) walking the chunks with the state in matrix-core
+// accumulators), bwd_chunk_kernel (one workgroup per (batch, group, chunk),
+// all heads of the group in turn: dB and dC stay in registers across heads,
+// so no atomics and a fixed summation order), bwd_param_kernel (sums of the
+// per-(batch, head, chunk) partials of dA, dD and d dt_bias).
 //
-// All matrix products run on the matrix cores in fp32 (16x16x4 MFMA) from
-// fp32 LDS tiles; bf16 inputs are widened when staged.
+// Matrix products run on the matrix cores: for fp32 inputs in fp32 (16x16x4
+// MFMA) from fp32 LDS tiles; for bf16 inputs in bf16 (16x16x32 MFMA), with
+// every fp32 operand carried as a bf16 high part plus a bf16 remainder
+// (bwd_chunk_bf16_kernel).
 #include "ssd_device.h"
 #include "ssd_internal.h"
 
@@ -111,47 +114,135 @@ __device__ __forceinline__ ChunkDecay chunk_decay(const float *dt, const float *
 }
 
 // ---------------------------------------------------------------------------
-// Gh_c[p][n] = sum_i e_in_i dy_i[p] C_i[n] for one (batch, head, chunk c).
-// c >= 1 goes to slot nc-1-c of `adj` with its log2 decay in rdecay; c = 0
-// goes to dinit (if wanted) with its log2 decay in dec0.
-template <typename T, int P, int N>
-__global__ void __launch_bounds__(256) bwd_dstate_kernel(const BwdParams p) {
-  constexpr int LX = P + 4, LB = N + 4;
-  __shared__ __attribute__((aligned(16))) float sDY[kQ * LX];
-  __shared__ __attribute__((aligned(16))) float sC[kQ * LB];
-  __shared__ float sEin[kQ];
-  const int nc = p.nc;
-  const int c = blockIdx.x % nc;
-  const int bh = blockIdx.x / nc;
-  const int b_ = bh / p.H, h = bh % p.H, g = (int)(((int64_t)h * p.G) / p.H);
-  if (c == 0 && !p.dinit) return;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
-  const int t0 = c * kQ, nv = min(kQ, p.L - t0);
-  if (w == 0) {
-    const ChunkDecay d = chunk_decay(p.dt, p.dt_bias, p.A, b_, p.L, p.H, h, t0, lane);
-    sEin[lane] = d.e_in;
-    if (lane == 0) {
-      if (c > 0) p.rdecay[(int64_t)bh * nc + (nc - 1 - c)] = d.cum2_last;
-      else p.dec0[bh] = d.cum2_last;
+// Chunk-boundary states of one (batch, head), walking the chunks in order
+// with the P x N state held in matrix-core accumulators (4 waves, (P/16) *
+// (N/16) 16x16 tiles, wave w owning tiles w, w+4, ...):
+//
+//   forward (REV = false): S = init; for c = 0 .. nc-1: states[c] = S;
+//            S = e_tot_c S + sum_j (e_out_j Delta_j x_j) B_j^T
+//   reverse (REV = true):  S = dfinal; for c = nc-1 .. 0: adj[c] = S;
+//            S = e_tot_c S + sum_i (e_in_i dy_i) C_i^T;  dinit = S at the end
+//
+// so states[c] is the state entering chunk c and adj[c] the gradient at
+// chunk c's last state (from later tokens and the final state); the final S
+// of the reverse walk is the gradient of the initial state.  The next
+// chunk's inputs are loaded into registers while the current chunk's
+// products run; the per-token weights are applied to the A fragments.
+template <typename T, int COLS> struct RowPrefetch {
+  // one 64-row tile of COLS elements of T, 16 bytes per load, 256 threads
+  static constexpr int kPerRow = COLS * (int)sizeof(T) / 16;
+  static constexpr int kLoads = (kQ * kPerRow + 255) / 256;
+  uint4 v[kLoads];
+  __device__ __forceinline__ void load(const T *src, int64_t row_stride, int valid_rows, int tid) {
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) {
+      const int idx = tid + 256 * k, r = idx / kPerRow, c = idx % kPerRow;
+      v[k] = make_uint4(0u, 0u, 0u, 0u);
+      if (idx < kQ * kPerRow && r < valid_rows)
+        v[k] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(src + (int64_t)r * row_stride) + 16 * c);
     }
   }
-  const T *dy = reinterpret_cast<const T *>(p.dy) + (((int64_t)b_ * p.L + t0) * p.H + h) * P;
-  const T *Cg = reinterpret_cast<const T *>(p.C) + (((int64_t)b_ * p.L + t0) * p.G + g) * N;
-  stage_rows<T>(sC, LB, Cg, (int64_t)p.G * N, kQ, nv, N, tid, 256);
-  stage_rows<T>(sDY, LX, dy, (int64_t)p.H * P, kQ, nv, P, tid, 256);
-  __syncthreads();
-  for (int idx = tid; idx < kQ * P; idx += 256) sDY[(idx / P) * LX + idx % P] *= sEin[idx / P];
-  __syncthreads();
-  float *dst = c > 0 ? p.adj + ((int64_t)bh * nc + (nc - 1 - c)) * (P * N) : p.dinit + (int64_t)bh * (P * N);
-  constexpr int PT = P / 16, NT = N / 16;
-  for (int tile = w; tile < PT * NT; tile += 4) {
-    const int pt = tile % PT, nt = tile / PT;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // widen to fp32 rows of `ld` floats
+  __device__ __forceinline__ void store(float *dst, int ld, int tid) const {
+    constexpr int per16 = 16 / (int)sizeof(T);
 #pragma unroll
-    for (int k0 = 0; k0 < kQ; k0 += 32)
-      acc = mma(trfrag(sDY, LX, k0, pt * 16, li, lg), trfrag(sC, LB, k0, nt * 16, li, lg), acc);
+    for (int k = 0; k < kLoads; ++k) {
+      const int idx = tid + 256 * k, r = idx / kPerRow, c = idx % kPerRow;
+      if (idx >= kQ * kPerRow) continue;
+      float *d = dst + r * ld + c * per16;
+      if constexpr (sizeof(T) == 2) {
+        const __bf16 *e = reinterpret_cast<const __bf16 *>(&v[k]);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dst[(pt * 16 + 4 * lg + r) * N + nt * 16 + li] = acc[r];
+        for (int q = 0; q < 8; ++q) d[q] = (float)e[q];
+      } else {
+        *reinterpret_cast<uint4 *>(d) = v[k];
+      }
+    }
+  }
+};
+
+template <typename T, int P, int N, bool REV>
+__global__ void __launch_bounds__(256) bwd_state_scan_kernel(const BwdParams p) {
+  constexpr int LX = P + 4, LB = N + 4, PT = P / 16, NT = N / 16, TILES = PT * NT / 4;
+  __shared__ __attribute__((aligned(16))) float sL[kQ * LX]; // x (forward) or dy (reverse), [token][p]
+  __shared__ __attribute__((aligned(16))) float sR[kQ * LB]; // B (forward) or C (reverse), [token][n]
+  __shared__ float sW[kQ];
+  __shared__ float sTot[1];
+  const int nc = p.nc, H = p.H, G = p.G, L = p.L;
+  const int bh = blockIdx.x, b_ = bh / H, h = bh % H, g = (int)(((int64_t)h * G) / H);
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+  const int PN = P * N;
+  const T *lsrc = reinterpret_cast<const T *>(REV ? p.dy : p.x) + ((int64_t)b_ * L * H + h) * P;
+  const T *rsrc = reinterpret_cast<const T *>(REV ? p.C : p.B) + ((int64_t)b_ * L * G + g) * N;
+  const float *s0 = REV ? p.dfinal : p.states_init;
+  float *out = (REV ? p.adj : p.states) + (int64_t)bh * nc * PN;
+
+  f32x4 S[TILES];
+#pragma unroll
+  for (int k = 0; k < TILES; ++k) {
+    const int tile = w + 4 * k, pt = tile % PT, nt = tile / PT;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      S[k][r] = s0 ? s0[(int64_t)bh * PN + (pt * 16 + 4 * lg + r) * N + nt * 16 + li] : 0.f;
+  }
+
+  RowPrefetch<T, P> pl;
+  RowPrefetch<T, N> pr;
+  auto fetch = [&](int c) {
+    const int t0 = c * kQ, nv = min(kQ, L - t0);
+    pl.load(lsrc + (int64_t)t0 * H * P, (int64_t)H * P, nv, tid);
+    pr.load(rsrc + (int64_t)t0 * G * N, (int64_t)G * N, nv, tid);
+  };
+  fetch(REV ? nc - 1 : 0);
+  for (int step = 0; step < nc; ++step) {
+    const int c = REV ? nc - 1 - step : step;
+    // the state at this chunk boundary
+#pragma unroll
+    for (int k = 0; k < TILES; ++k) {
+      const int tile = w + 4 * k, pt = tile % PT, nt = tile / PT;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) out[(int64_t)c * PN + (pt * 16 + 4 * lg + r) * N + nt * 16 + li] = S[k][r];
+    }
+    pl.store(sL, LX, tid);
+    pr.store(sR, LB, tid);
+    if (w == 0) {
+      const ChunkDecay d = chunk_decay(p.dt, p.dt_bias, p.A, b_, L, H, h, c * kQ, lane);
+      sW[lane] = REV ? d.e_in : d.e_out * d.delta;
+      if (lane == 0) sTot[0] = hw_exp2(d.cum2_last);
+    }
+    __syncthreads();
+    if (step + 1 < nc) fetch(REV ? c - 1 : c + 1);
+    const float tot = sTot[0];
+    float wk[2][8];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        wk[kk][q] = sW[32 * kk + 4 * lg + q];
+        wk[kk][4 + q] = sW[32 * kk + 16 + 4 * lg + q];
+      }
+#pragma unroll
+    for (int k = 0; k < TILES; ++k) {
+      const int tile = w + 4 * k, pt = tile % PT, nt = tile / PT;
+      f32x4 acc = S[k] * tot;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        FragF32 a = trfrag(sL, LX, 32 * kk, pt * 16, li, lg);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) a.v[q] *= wk[kk][q];
+        acc = mma(a, trfrag(sR, LB, 32 * kk, nt * 16, li, lg), acc);
+      }
+      S[k] = acc;
+    }
+    __syncthreads();
+  }
+  if (REV && p.dinit) {
+#pragma unroll
+    for (int k = 0; k < TILES; ++k) {
+      const int tile = w + 4 * k, pt = tile % PT, nt = tile / PT;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p.dinit[(int64_t)bh * PN + (pt * 16 + 4 * lg + r) * N + nt * 16 + li] = S[k][r];
+    }
   }
 }
 
@@ -295,7 +386,7 @@ __global__ void __launch_bounds__(512) bwd_chunk_kernel(const BwdParams p) {
 
     // --- replace H by G (the gradient at the chunk's last state); <G, H>
     {
-      const float *Gs = p.adj + (bh * nc + (nc - 1 - c)) * PN;
+      const float *Gs = p.adj + (bh * nc + c) * PN;
       float gh = 0.f;
       for (int idx = tid; idx < PN / 4; idx += 512) {
         const int r = (idx * 4) / N, col = (idx * 4) % N;
@@ -450,53 +541,402 @@ __global__ void __launch_bounds__(512) bwd_chunk_kernel(const BwdParams p) {
   }
 }
 
-// dinit += exp2(dec0) * G_0 (G_0 = slot nc-1 of adj after the reverse pass).
-__global__ void __launch_bounds__(256) bwd_dinit_kernel(float *__restrict__ dinit, const float *__restrict__ adj,
-                                                        const float *__restrict__ dec0, int64_t nbh, int PN, int nc) {
-  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (id >= nbh * PN) return;
-  const int64_t bh = id / PN;
-  const int e = (int)(id % PN);
-  dinit[id] += hw_exp2(dec0[bh]) * adj[(bh * nc + nc - 1) * PN + e];
+// ---------------------------------------------------------------------------
+// The same chunk step for bf16 inputs on the bf16 matrix cores.  Every
+// product pairs an input operand (x, dy, B or C: exact in bf16) with either
+// another input or an fp32 quantity (M, DX o E, the states H and G).  An
+// fp32 operand v is kept in LDS as two bf16 planes, hi = bf16(v) and
+// lo = bf16(v - hi), and each product is two bf16 MFMAs, input * hi +
+// input * lo, accumulated in fp32: relative error at most about 2^-18 per
+// product (lo carries the next 8 bits of v), against 2^-24 for fp32 MFMA,
+// at a quarter of the matrix-core time.  Tile maps as in bwd_chunk_kernel.
+__device__ __forceinline__ void put_split(__bf16 *hi, __bf16 *lo, int off, float v) {
+  const __bf16 h = (__bf16)v;
+  hi[off] = h;
+  lo[off] = (__bf16)(v - (float)h);
+}
+__device__ __forceinline__ FragBF kc16(const __bf16 *tile, int ld, int row, int k0, int lg) {
+  const __bf16 *p = tile + row * ld + k0 + 4 * lg;
+  return ld4x2(p, p + 16);
+}
+// copy `rows` rows of `cols` bf16 (16 B at a time), zero rows >= valid_rows
+__device__ __forceinline__ void stage_bf16(__bf16 *dst, int ld, const __bf16 *src, int64_t row_stride, int rows,
+                                           int valid_rows, int cols, int tid, int nthreads) {
+  const int c8 = cols / 8;
+  for (int idx = tid; idx < rows * c8; idx += nthreads) {
+    const int r = idx / c8, c = (idx % c8) * 8;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (r < valid_rows) v = *reinterpret_cast<const uint4 *>(src + (int64_t)r * row_stride + c);
+    *reinterpret_cast<uint4 *>(dst + r * ld + c) = v;
+  }
+}
+// fp32 P x N state from global into hi/lo planes; returns this thread's share
+// of <state, other> when `other` is given (exact fp32 values from global)
+template <int N>
+__device__ __forceinline__ float stage_state_split(__bf16 *hi, __bf16 *lo, int ld, const float *src,
+                                                   const float *other, int PN, int tid) {
+  float dot = 0.f;
+  for (int idx = tid; idx < PN / 4; idx += 512) {
+    const int r = (idx * 4) / N, col = (idx * 4) % N;
+    const float4 v = reinterpret_cast<const float4 *>(src)[idx];
+    if (other) {
+      const float4 o = reinterpret_cast<const float4 *>(other)[idx];
+      dot += v.x * o.x + v.y * o.y + v.z * o.z + v.w * o.w;
+    }
+    const int off = r * ld + col;
+    put_split(hi, lo, off, v.x);
+    put_split(hi, lo, off + 1, v.y);
+    put_split(hi, lo, off + 2, v.z);
+    put_split(hi, lo, off + 3, v.w);
+  }
+  return dot;
 }
 
-// dA, dD, d dt_bias per head: sums of the (batch, chunk) partials in a fixed order.
-__global__ void __launch_bounds__(64) bwd_param_kernel(const float *__restrict__ part, float *__restrict__ dA,
-                                                       float *__restrict__ dD, float *__restrict__ ddt_bias,
-                                                       int b, int H, int nc) {
-  const int h = blockIdx.x * 64 + threadIdx.x;
-  if (h >= H) return;
-  float sa = 0.f, sd = 0.f, sb = 0.f;
-  for (int ib = 0; ib < b; ++ib)
-    for (int c = 0; c < nc; ++c) {
-      const float *q = part + (((int64_t)ib * H + h) * nc + c) * 3;
-      sa += q[0];
-      sd += q[1];
-      sb += q[2];
+template <int P, int N>
+__global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) {
+  constexpr int LB = tr_ld(N, 2), LX = tr_ld(P, 2), LQ = tr_ld(kQ, 2), LS = tr_ld(N, 2);
+  constexpr int PT = P / 16, NT = N / 16;
+  __shared__ __attribute__((aligned(16))) __bf16 sB[kQ * LB];
+  __shared__ __attribute__((aligned(16))) __bf16 sC[kQ * LB];
+  __shared__ __attribute__((aligned(16))) __bf16 sX[kQ * LX];
+  __shared__ __attribute__((aligned(16))) __bf16 sDY[kQ * LX];
+  __shared__ __attribute__((aligned(16))) __bf16 sMh[kQ * LQ];
+  __shared__ __attribute__((aligned(16))) __bf16 sMl[kQ * LQ];
+  __shared__ __attribute__((aligned(16))) __bf16 sSh[P * LS];
+  __shared__ __attribute__((aligned(16))) __bf16 sSl[P * LS];
+  __shared__ float sCum[kQ], sDel[kQ], sEin[kQ], sEout[kQ], sSig[kQ];
+  __shared__ float rowW[2][kQ], colW[4][kQ], uP[2][kQ], vP[2][kQ], dinP[2][kQ], sDiag[kQ];
+  __shared__ float sRed[9]; // [0]: log2 decay of the chunk; [1 + w]: wave w's share of <G, H>
+
+  const int nc = p.nc, G = p.G, H = p.H, L = p.L;
+  const int c = blockIdx.x % nc;
+  const int bg = blockIdx.x / nc;
+  const int b_ = bg / G, g = bg % G;
+  const int hpg = H / G;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+  const int rt = w & 3, ct0 = w >> 2;
+  const int t0 = c * kQ, nv = min(kQ, L - t0);
+  const int PN = P * N;
+
+  const __bf16 *Bg = reinterpret_cast<const __bf16 *>(p.B) + (((int64_t)b_ * L + t0) * G + g) * N;
+  const __bf16 *Cg = reinterpret_cast<const __bf16 *>(p.C) + (((int64_t)b_ * L + t0) * G + g) * N;
+  stage_bf16(sB, LB, Bg, (int64_t)G * N, kQ, nv, N, tid, 512);
+  stage_bf16(sC, LB, Cg, (int64_t)G * N, kQ, nv, N, tid, 512);
+  __syncthreads();
+  f32x4 S[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int ct = ct0 + 2 * k;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k0 = 0; k0 < N; k0 += 32)
+      acc = mma(kc16(sC, LB, rt * 16 + li, k0, lg), kc16(sB, LB, ct * 16 + li, k0, lg), acc);
+    S[k] = acc;
+  }
+
+  f32x4 dBacc[NT / 2], dCacc[NT / 2];
+#pragma unroll
+  for (int k = 0; k < NT / 2; ++k) {
+    dBacc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dCacc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  for (int h = g * hpg; h < (g + 1) * hpg; ++h) {
+    const int64_t bh = (int64_t)b_ * H + h;
+    const float Ah = p.A[h], Dh = p.D ? p.D[h] : 0.f;
+    if (w == 0) {
+      const ChunkDecay d = chunk_decay(p.dt, p.dt_bias, p.A, b_, L, H, h, t0, lane);
+      sCum[lane] = d.cum2;
+      sDel[lane] = d.delta;
+      sEin[lane] = d.e_in;
+      sEout[lane] = d.e_out;
+      sSig[lane] = d.sig;
+      if (lane == 0) sRed[0] = d.cum2_last;
     }
-  dA[h] = sa;
-  if (dD) dD[h] = sd;
-  if (ddt_bias) ddt_bias[h] = sb;
+    const __bf16 *xh = reinterpret_cast<const __bf16 *>(p.x) + (((int64_t)b_ * L + t0) * H + h) * P;
+    const __bf16 *dyh = reinterpret_cast<const __bf16 *>(p.dy) + (((int64_t)b_ * L + t0) * H + h) * P;
+    stage_bf16(sX, LX, xh, (int64_t)H * P, kQ, nv, P, tid, 512);
+    stage_bf16(sDY, LX, dyh, (int64_t)H * P, kQ, nv, P, tid, 512);
+    const float *Hs = p.states + (bh * nc + c) * PN;
+    const float *Gs = p.adj + (bh * nc + c) * PN;
+    stage_state_split<N>(sSh, sSl, LS, Hs, nullptr, PN, tid);
+    __syncthreads();
+    const float cum_last2 = sRed[0];
+
+    // --- DX = dY X^T, M = S o E (split to LDS), P2 = DX o E, W sums, diag(DX)
+    f32x4 P2[2];
+    float rsum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int ct = ct0 + 2 * k;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k0 = 0; k0 < P; k0 += 32)
+        acc = mma(kc16(sDY, LX, rt * 16 + li, k0, lg), kc16(sX, LX, ct * 16 + li, k0, lg), acc);
+      const int j = ct * 16 + li;
+      const float cj = sCum[j], dj = sDel[j];
+      float csum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = rt * 16 + 4 * lg + r;
+        const float e = (i >= j) ? hw_exp2(sCum[i] - cj) : 0.f;
+        const float m = S[k][r] * e;
+        put_split(sMh, sMl, i * LQ + j, m);
+        P2[k][r] = acc[r] * e;
+        const float wv = (i > j) ? m * acc[r] * dj : 0.f;
+        rsum[r] += wv;
+        csum += wv;
+        if (i == j) sDiag[i] = acc[r];
+      }
+      csum = sum_lg(csum);
+      if (lg == 0) colW[rt][j] = csum;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float v = sum16(rsum[r]);
+      if (li == 0) rowW[ct0][rt * 16 + 4 * lg + r] = v;
+    }
+
+    // --- dY H: dC += e_in o (dY H); u_i = e_in_i sum_n C_in (dY H)_in
+    {
+      float up[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < NT / 2; ++k) {
+        const int ct = ct0 + 2 * k;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k0 = 0; k0 < P; k0 += 32) {
+          const FragBF a = kc16(sDY, LX, rt * 16 + li, k0, lg);
+          acc = mma(a, trfrag(sSh, LS, k0, ct * 16, li, lg), acc);
+          acc = mma(a, trfrag(sSl, LS, k0, ct * 16, li, lg), acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = rt * 16 + 4 * lg + r;
+          const float v = sEin[i] * acc[r];
+          dCacc[k][r] += v;
+          up[r] += (float)sC[i * LB + ct * 16 + li] * v;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = sum16(up[r]);
+        if (li == 0) uP[ct0][rt * 16 + 4 * lg + r] = v;
+      }
+    }
+    __syncthreads();
+
+    // --- replace H by G; <G, H> from the fp32 values in global memory
+    {
+      const float gh = wave_sum(stage_state_split<N>(sSh, sSl, LS, Gs, Hs, PN, tid));
+      if (lane == 0) sRed[1 + w] = gh;
+    }
+    __syncthreads();
+
+    // --- bracket = M^T dY + e_out o (B G^T); dx; x . bracket
+    {
+      float dp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < PT / 2; ++k) {
+        const int ct = ct0 + 2 * k;
+        f32x4 a3 = {0.f, 0.f, 0.f, 0.f}, b3 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k0 = 0; k0 < kQ; k0 += 32) {
+          const FragBF bb = trfrag(sDY, LX, k0, ct * 16, li, lg);
+          a3 = mma(trfrag(sMh, LQ, k0, rt * 16, li, lg), bb, a3);
+          a3 = mma(trfrag(sMl, LQ, k0, rt * 16, li, lg), bb, a3);
+        }
+#pragma unroll
+        for (int k0 = 0; k0 < N; k0 += 32) {
+          const FragBF a = kc16(sB, LB, rt * 16 + li, k0, lg);
+          b3 = mma(a, kc16(sSh, LS, ct * 16 + li, k0, lg), b3);
+          b3 = mma(a, kc16(sSl, LS, ct * 16 + li, k0, lg), b3);
+        }
+        const int pc = ct * 16 + li;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = rt * 16 + 4 * lg + r;
+          const float br = a3[r] + sEout[t] * b3[r];
+          if (t < nv)
+            p.dx[(((int64_t)b_ * L + t0 + t) * H + h) * P + pc] = Dh * (float)sDY[t * LX + pc] + sDel[t] * br;
+          dp[r] += (float)sX[t * LX + pc] * br;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = sum16(dp[r]);
+        if (li == 0) dinP[ct0][rt * 16 + 4 * lg + r] = v;
+      }
+    }
+
+    // --- X G: dB part e_out o (X G); v_j = e_out_j Delta_j sum_n B_jn (X G)_jn
+    f32x4 acc6[NT / 2];
+    {
+      float vp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < NT / 2; ++k) {
+        const int ct = ct0 + 2 * k;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k0 = 0; k0 < P; k0 += 32) {
+          const FragBF a = kc16(sX, LX, rt * 16 + li, k0, lg);
+          acc = mma(a, trfrag(sSh, LS, k0, ct * 16, li, lg), acc);
+          acc = mma(a, trfrag(sSl, LS, k0, ct * 16, li, lg), acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = rt * 16 + 4 * lg + r;
+          vp[r] += (float)sB[t * LB + ct * 16 + li] * acc[r];
+          acc6[k][r] = sEout[t] * acc[r];
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = sum16(vp[r]);
+        if (li == 0) vP[ct0][rt * 16 + 4 * lg + r] = v;
+      }
+    }
+    __syncthreads();
+
+    // --- P2 = DX o E (split) to LDS; dB += Delta o (e_out o XG + P2^T C)
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        put_split(sMh, sMl, (rt * 16 + 4 * lg + r) * LQ + (ct0 + 2 * k) * 16 + li, P2[k][r]);
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NT / 2; ++k) {
+      const int ct = ct0 + 2 * k;
+      f32x4 acc = acc6[k];
+#pragma unroll
+      for (int k0 = 0; k0 < kQ; k0 += 32) {
+        const FragBF bb = trfrag(sC, LB, k0, ct * 16, li, lg);
+        acc = mma(trfrag(sMh, LQ, k0, rt * 16, li, lg), bb, acc);
+        acc = mma(trfrag(sMl, LQ, k0, rt * 16, li, lg), bb, acc);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dBacc[k][r] += sDel[rt * 16 + 4 * lg + r] * acc[r];
+    }
+    __syncthreads();
+
+    // --- P1 = P2 diag(Delta) (split) to LDS; dC += P1 B
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int j = (ct0 + 2 * k) * 16 + li;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) put_split(sMh, sMl, (rt * 16 + 4 * lg + r) * LQ + j, P2[k][r] * sDel[j]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NT / 2; ++k) {
+      const int ct = ct0 + 2 * k;
+      f32x4 acc = dCacc[k];
+#pragma unroll
+      for (int k0 = 0; k0 < kQ; k0 += 32) {
+        const FragBF bb = trfrag(sB, LB, k0, ct * 16, li, lg);
+        acc = mma(kc16(sMh, LQ, rt * 16 + li, k0, lg), bb, acc);
+        acc = mma(kc16(sMl, LQ, rt * 16 + li, k0, lg), bb, acc);
+      }
+      dCacc[k] = acc;
+    }
+
+    // --- da, ddt and the head's partial sums (wave 0, lane k = token)
+    if (w == 0) {
+      const int k = lane;
+      const float colsum = colW[0][k] + colW[1][k] + colW[2][k] + colW[3][k];
+      const float rowsum = rowW[0][k] + rowW[1][k];
+      const float dlt = colsum - rowsum;
+      const float R = wave_incl_scan(dlt) - dlt;
+      const float u = uP[0][k] + uP[1][k];
+      const float u_incl = wave_incl_scan(u);
+      const float U = __shfl(u_incl, 63, 64) - u_incl + u;
+      const float v = sEout[k] * sDel[k] * (vP[0][k] + vP[1][k]);
+      const float V = wave_incl_scan(v) - v;
+      float gh = 0.f;
+#pragma unroll
+      for (int q = 1; q <= 8; ++q) gh += sRed[q];
+      const float da = R + U + V + hw_exp2(cum_last2) * gh;
+      const float din = dinP[0][k] + dinP[1][k];
+      const float ddt = (din + Ah * da) * sSig[k];
+      const bool valid = k < nv;
+      if (valid) p.ddt[((int64_t)b_ * L + t0 + k) * H + h] = ddt;
+      const float pa = wave_sum(valid ? sDel[k] * da : 0.f);
+      const float pd = wave_sum(valid ? sDiag[k] : 0.f);
+      const float pb = wave_sum(valid ? ddt : 0.f);
+      if (lane == 0) {
+        float *q = p.part + (bh * nc + c) * 3;
+        q[0] = pa;
+        q[1] = pd;
+        q[2] = pb;
+      }
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int k = 0; k < NT / 2; ++k) {
+    const int n = (ct0 + 2 * k) * 16 + li;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = rt * 16 + 4 * lg + r;
+      if (t < nv) {
+        const int64_t o = (((int64_t)b_ * L + t0 + t) * G + g) * N + n;
+        p.dB[o] = dBacc[k][r];
+        p.dC[o] = dCacc[k][r];
+      }
+    }
+  }
+}
+
+// dA, dD, d dt_bias per head: one workgroup per head sums the (batch, chunk)
+// partials, each thread a fixed strided subset, then a fixed shuffle tree and
+// a fixed order over the four waves, so the result is the same every run.
+__global__ void __launch_bounds__(256) bwd_param_kernel(const float *__restrict__ part, float *__restrict__ dA,
+                                                        float *__restrict__ dD, float *__restrict__ ddt_bias,
+                                                        int b, int H, int nc) {
+  __shared__ float red[3][4];
+  const int h = blockIdx.x, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  float sa = 0.f, sd = 0.f, sb = 0.f;
+  for (int k = tid; k < b * nc; k += 256) {
+    const int ib = k / nc, c = k % nc;
+    const float *q = part + (((int64_t)ib * H + h) * nc + c) * 3;
+    sa += q[0];
+    sd += q[1];
+    sb += q[2];
+  }
+  sa = wave_sum(sa);
+  sd = wave_sum(sd);
+  sb = wave_sum(sb);
+  if (lane == 0) {
+    red[0][w] = sa;
+    red[1][w] = sd;
+    red[2][w] = sb;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    dA[h] = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
+    if (dD) dD[h] = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+    if (ddt_bias) ddt_bias[h] = (red[2][0] + red[2][1]) + (red[2][2] + red[2][3]);
+  }
 }
 
 template <typename T, int P, int N> hipError_t launch_bwd_t(const BwdParams &p, hipStream_t st) {
-  hipLaunchKernelGGL((bwd_dstate_kernel<T, P, N>), dim3((unsigned)(p.b * p.H * p.nc)), dim3(256), 0, st, p);
+  const dim3 grid_bh((unsigned)(p.b * p.H));
+  hipLaunchKernelGGL((bwd_state_scan_kernel<T, P, N, false>), grid_bh, dim3(256), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = launch_state_pass(p.adj, p.rdecay, p.dfinal, p.b, p.H, P * N, p.nc, st);
-  if (e != hipSuccess) return e;
-  if (p.dinit) {
-    const int64_t n = (int64_t)p.b * p.H * P * N;
-    hipLaunchKernelGGL(bwd_dinit_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p.dinit, p.adj,
-                       p.dec0, (int64_t)p.b * p.H, P * N, p.nc);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL((bwd_chunk_kernel<T, P, N>), dim3((unsigned)(p.b * p.G * p.nc)), dim3(512), 0, st, p);
+  hipLaunchKernelGGL((bwd_state_scan_kernel<T, P, N, true>), grid_bh, dim3(256), 0, st, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_param_kernel, dim3((unsigned)((p.H + 63) / 64)), dim3(64), 0, st, p.part, p.dA, p.dD,
-                     p.ddt_bias, p.b, p.H, p.nc);
+  if constexpr (sizeof(T) == 2)
+    hipLaunchKernelGGL((bwd_chunk_bf16_kernel<P, N>), dim3((unsigned)(p.b * p.G * p.nc)), dim3(512), 0, st, p);
+  else
+    hipLaunchKernelGGL((bwd_chunk_kernel<T, P, N>), dim3((unsigned)(p.b * p.G * p.nc)), dim3(512), 0, st, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_param_kernel, dim3((unsigned)p.H), dim3(256), 0, st, p.part, p.dA, p.dD, p.ddt_bias,
+                     p.b, p.H, p.nc);
   return hipGetLastError();
 }
 

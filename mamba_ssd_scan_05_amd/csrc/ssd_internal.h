@@ -113,8 +113,7 @@ struct SScanParams {
 // N in {4, 8, 16}; dtype 1 = bf16, 0 = fp32.
 hipError_t launch_sscan(int dtype, int N, const SScanParams &p, hipStream_t stream);
 
-// Gradients of the scan (64-token chunks).  The caller has filled `states`
-// with the state entering every chunk; launch_bwd computes the rest.
+// Gradients of the scan (64-token chunks); launch_bwd runs every kernel.
 struct BwdParams {
   const void *x;        // [b, L, H, P] input dtype
   const float *dt;      // [b, L, H] raw
@@ -125,11 +124,10 @@ struct BwdParams {
   const float *D;       // [H] or null
   const void *dy;       // [b, L, H, P] input dtype: gradient at the output
   const float *dfinal;  // [b, H, P, N] or null: gradient at the final state
-  const float *states;  // scratch [b, H, nc, P, N]: state entering each chunk
-  float *adj;           // scratch [b, H, nc, P, N]: slot nc-1-c ends as the
-                        // gradient at chunk c's last state
-  float *rdecay;        // scratch [b, H, nc]: log2 decays in reversed chunk order
-  float *dec0;          // scratch [b, H]: log2 decay of chunk 0
+  const float *states_init; // [b, H, P, N] or null: the initial state
+  float *states;        // scratch [b, H, nc, P, N]: state entering each chunk
+  float *adj;           // scratch [b, H, nc, P, N]: gradient at each chunk's
+                        // last state
   float *part;          // scratch [b, H, nc, 3]: partial dA, dD, d dt_bias
   float *dx;            // [b, L, H, P]
   float *ddt;           // [b, L, H]
