@@ -98,12 +98,16 @@ __device__ __forceinline__ float wave_sum(float v) { return sum_lg(sum16(v)); }
 struct ChunkDecay {
   float delta, cum2, e_in, e_out, sig, cum2_last;
 };
-__device__ __forceinline__ ChunkDecay chunk_decay(const float *dt, const float *dt_bias, const float *A, int b_, int L,
-                                                  int H, int h, int t0, int lane) {
-  ChunkDecay d;
+// dt of token t0 + lane of head h (0 past the end of the sequence)
+__device__ __forceinline__ float load_dt(const float *dt, int b_, int L, int H, int h, int t0, int lane) {
   const int t = t0 + lane;
-  const bool valid = t < L;
-  const float z = valid ? dt[((int64_t)b_ * L + t) * H + h] + (dt_bias ? dt_bias[h] : 0.f) : 0.f;
+  return t < L ? dt[((int64_t)b_ * L + t) * H + h] : 0.f;
+}
+__device__ __forceinline__ ChunkDecay chunk_decay_v(float dtv, const float *dt_bias, const float *A, int L, int h,
+                                                    int t0, int lane) {
+  ChunkDecay d;
+  const bool valid = t0 + lane < L;
+  const float z = valid ? dtv + (dt_bias ? dt_bias[h] : 0.f) : 0.f;
   d.delta = valid ? softplus_f(z) : 0.f;
   d.sig = valid ? __builtin_amdgcn_rcpf(1.f + hw_exp2(-z * kLog2e)) : 0.f;
   d.cum2 = wave_incl_scan(d.delta * A[h] * kLog2e);
@@ -111,6 +115,10 @@ __device__ __forceinline__ ChunkDecay chunk_decay(const float *dt, const float *
   d.e_in = hw_exp2(d.cum2);
   d.e_out = hw_exp2(d.cum2_last - d.cum2);
   return d;
+}
+__device__ __forceinline__ ChunkDecay chunk_decay(const float *dt, const float *dt_bias, const float *A, int b_, int L,
+                                                  int H, int h, int t0, int lane) {
+  return chunk_decay_v(load_dt(dt, b_, L, H, h, t0, lane), dt_bias, A, L, h, t0, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -128,6 +136,7 @@ __device__ __forceinline__ ChunkDecay chunk_decay(const float *dt, const float *
 // of the reverse walk is the gradient of the initial state.  The next
 // chunk's inputs are loaded into registers while the current chunk's
 // products run; the per-token weights are applied to the A fragments.
+
 template <typename T, int COLS> struct RowPrefetch {
   // one 64-row tile of COLS elements of T, 16 bytes per load, 256 threads
   static constexpr int kPerRow = COLS * (int)sizeof(T) / 16;
@@ -188,10 +197,12 @@ __global__ void __launch_bounds__(256) bwd_state_scan_kernel(const BwdParams p) 
 
   RowPrefetch<T, P> pl;
   RowPrefetch<T, N> pr;
+  float dtv = 0.f;
   auto fetch = [&](int c) {
     const int t0 = c * kQ, nv = min(kQ, L - t0);
     pl.load(lsrc + (int64_t)t0 * H * P, (int64_t)H * P, nv, tid);
     pr.load(rsrc + (int64_t)t0 * G * N, (int64_t)G * N, nv, tid);
+    if (w == 0) dtv = load_dt(p.dt, b_, L, H, h, t0, lane);
   };
   fetch(REV ? nc - 1 : 0);
   for (int step = 0; step < nc; ++step) {
@@ -206,7 +217,7 @@ __global__ void __launch_bounds__(256) bwd_state_scan_kernel(const BwdParams p) 
     pl.store(sL, LX, tid);
     pr.store(sR, LB, tid);
     if (w == 0) {
-      const ChunkDecay d = chunk_decay(p.dt, p.dt_bias, p.A, b_, L, H, h, c * kQ, lane);
+      const ChunkDecay d = chunk_decay_v(dtv, p.dt_bias, p.A, L, h, c * kQ, lane);
       sW[lane] = REV ? d.e_in : d.e_out * d.delta;
       if (lane == 0) sTot[0] = hw_exp2(d.cum2_last);
     }
@@ -592,6 +603,106 @@ __device__ __forceinline__ float stage_state_split(__bf16 *hi, __bf16 *lo, int l
   return dot;
 }
 
+// The same walk for bf16 inputs on the bf16 matrix cores: the weighted
+// input w_j x_j (fp32) is kept as a bf16 high part plus a bf16 remainder,
+// B or C are exact in bf16, and each product is two 16x16x32 MFMAs.
+template <int P, int N, bool REV>
+__global__ void __launch_bounds__(256) bwd_state_scan_bf16_kernel(const BwdParams p) {
+  constexpr int LX = tr_ld(P, 2), LB = tr_ld(N, 2), PT = P / 16, NT = N / 16, TILES = PT * NT / 4;
+  __shared__ __attribute__((aligned(16))) __bf16 sLh[kQ * LX];
+  __shared__ __attribute__((aligned(16))) __bf16 sLl[kQ * LX];
+  __shared__ __attribute__((aligned(16))) __bf16 sR[kQ * LB];
+  __shared__ float sW[kQ];
+  __shared__ float sTot[1];
+  const int nc = p.nc, H = p.H, G = p.G, L = p.L;
+  const int bh = blockIdx.x, b_ = bh / H, h = bh % H, g = (int)(((int64_t)h * G) / H);
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+  const int PN = P * N;
+  const __bf16 *lsrc = reinterpret_cast<const __bf16 *>(REV ? p.dy : p.x) + ((int64_t)b_ * L * H + h) * P;
+  const __bf16 *rsrc = reinterpret_cast<const __bf16 *>(REV ? p.C : p.B) + ((int64_t)b_ * L * G + g) * N;
+  const float *s0 = REV ? p.dfinal : p.states_init;
+  float *out = (REV ? p.adj : p.states) + (int64_t)bh * nc * PN;
+
+  f32x4 S[TILES];
+#pragma unroll
+  for (int k = 0; k < TILES; ++k) {
+    const int tile = w + 4 * k, pt = tile % PT, nt = tile / PT;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      S[k][r] = s0 ? s0[(int64_t)bh * PN + (pt * 16 + 4 * lg + r) * N + nt * 16 + li] : 0.f;
+  }
+
+  RowPrefetch<__bf16, P> pl;
+  RowPrefetch<__bf16, N> pr;
+  float dtv = 0.f;
+  auto fetch = [&](int c) {
+    const int t0 = c * kQ, nv = min(kQ, L - t0);
+    pl.load(lsrc + (int64_t)t0 * H * P, (int64_t)H * P, nv, tid);
+    pr.load(rsrc + (int64_t)t0 * G * N, (int64_t)G * N, nv, tid);
+    if (w == 0) dtv = load_dt(p.dt, b_, L, H, h, t0, lane);
+  };
+  fetch(REV ? nc - 1 : 0);
+  for (int step = 0; step < nc; ++step) {
+    const int c = REV ? nc - 1 - step : step;
+#pragma unroll
+    for (int k = 0; k < TILES; ++k) {
+      const int tile = w + 4 * k, pt = tile % PT, nt = tile / PT;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) out[(int64_t)c * PN + (pt * 16 + 4 * lg + r) * N + nt * 16 + li] = S[k][r];
+    }
+    if (w == 0) {
+      const ChunkDecay d = chunk_decay_v(dtv, p.dt_bias, p.A, L, h, c * kQ, lane);
+      sW[lane] = REV ? d.e_in : d.e_out * d.delta;
+      if (lane == 0) sTot[0] = hw_exp2(d.cum2_last);
+    }
+    __syncthreads();
+    // stage: weighted input split into hi/lo planes, B or C copied
+    {
+      constexpr int KP = RowPrefetch<__bf16, P>::kPerRow;
+#pragma unroll
+      for (int k = 0; k < RowPrefetch<__bf16, P>::kLoads; ++k) {
+        const int idx = tid + 256 * k, r = idx / KP, cc = idx % KP;
+        if (idx >= kQ * KP) continue;
+        const __bf16 *e = reinterpret_cast<const __bf16 *>(&pl.v[k]);
+        const float wr = sW[r];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) put_split(sLh, sLl, r * LX + cc * 8 + q, wr * (float)e[q]);
+      }
+      constexpr int KN = RowPrefetch<__bf16, N>::kPerRow;
+#pragma unroll
+      for (int k = 0; k < RowPrefetch<__bf16, N>::kLoads; ++k) {
+        const int idx = tid + 256 * k, r = idx / KN, cc = idx % KN;
+        if (idx >= kQ * KN) continue;
+        *reinterpret_cast<uint4 *>(sR + r * LB + cc * 8) = pr.v[k];
+      }
+    }
+    const float tot = sTot[0];
+    __syncthreads();
+    if (step + 1 < nc) fetch(REV ? c - 1 : c + 1);
+#pragma unroll
+    for (int k = 0; k < TILES; ++k) {
+      const int tile = w + 4 * k, pt = tile % PT, nt = tile / PT;
+      f32x4 acc = S[k] * tot;
+#pragma unroll
+      for (int k0 = 0; k0 < kQ; k0 += 32) {
+        const FragBF bb = trfrag(sR, LB, k0, nt * 16, li, lg);
+        acc = mma(trfrag(sLh, LX, k0, pt * 16, li, lg), bb, acc);
+        acc = mma(trfrag(sLl, LX, k0, pt * 16, li, lg), bb, acc);
+      }
+      S[k] = acc;
+    }
+    __syncthreads();
+  }
+  if (REV && p.dinit) {
+#pragma unroll
+    for (int k = 0; k < TILES; ++k) {
+      const int tile = w + 4 * k, pt = tile % PT, nt = tile / PT;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p.dinit[(int64_t)bh * PN + (pt * 16 + 4 * lg + r) * N + nt * 16 + li] = S[k][r];
+    }
+  }
+}
+
 template <int P, int N>
 __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) {
   constexpr int LB = tr_ld(N, 2), LX = tr_ld(P, 2), LQ = tr_ld(kQ, 2), LS = tr_ld(N, 2);
@@ -923,10 +1034,16 @@ __global__ void __launch_bounds__(256) bwd_param_kernel(const float *__restrict_
 
 template <typename T, int P, int N> hipError_t launch_bwd_t(const BwdParams &p, hipStream_t st) {
   const dim3 grid_bh((unsigned)(p.b * p.H));
-  hipLaunchKernelGGL((bwd_state_scan_kernel<T, P, N, false>), grid_bh, dim3(256), 0, st, p);
+  if constexpr (sizeof(T) == 2)
+    hipLaunchKernelGGL((bwd_state_scan_bf16_kernel<P, N, false>), grid_bh, dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((bwd_state_scan_kernel<T, P, N, false>), grid_bh, dim3(256), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_state_scan_kernel<T, P, N, true>), grid_bh, dim3(256), 0, st, p);
+  if constexpr (sizeof(T) == 2)
+    hipLaunchKernelGGL((bwd_state_scan_bf16_kernel<P, N, true>), grid_bh, dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((bwd_state_scan_kernel<T, P, N, true>), grid_bh, dim3(256), 0, st, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (sizeof(T) == 2)
