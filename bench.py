@@ -146,7 +146,8 @@ def bench_sscan(ssd, staging, inputs, torch, dev):
             "hbm_GBs": nbytes / (ms * 1e-3) / 1e9, "bytes_per_launch": nbytes}
 
 
-MFMA_F32 = 157.3e12  # MI355X dense fp32 matrix peak, FLOP/s
+MFMA_F32 = 157.3e12   # MI355X dense fp32 matrix peak, FLOP/s
+MFMA_BF16 = 2.5e15    # MI355X dense bf16 matrix peak, FLOP/s
 
 
 def bwd_flops(b, L, H, P, G, N, Q=64):
@@ -184,10 +185,14 @@ def bench_bwd(ssd, staging, inputs, torch, dev):
     fl = bwd_flops(b, L, H, P, G, N)
     el = ELEM[si.dtype]
     nbytes = b * L * H * P * (2 * el + 4) + b * L * H * 8 + 2 * b * L * G * N * (el + 4) + 3 * b * H * P * N * 4
+    # the contraction runs in bf16 for bf16 inputs (fp32 operands carried as
+    # two bf16 parts), in fp32 for fp32 inputs: the peak of that dtype
+    peak = MFMA_BF16 if si.dtype == inputs.BF16 else MFMA_F32
     return {"workload": WORKLOAD, "ms_per_step": ms, "tokens_per_s": b * L / (ms * 1e-3),
-            "roofline": {"bound": "mfma", "achieved": fl / (ms * 1e-3) / 1e12, "peak": MFMA_F32 / 1e12,
-                         "unit": "TFLOP/s", "frac": fl / (ms * 1e-3) / MFMA_F32, "flops_per_launch": fl,
-                         "dtype": "f32"},
+            "roofline": {"bound": "mfma", "achieved": fl / (ms * 1e-3) / 1e12, "peak": peak / 1e12,
+                         "unit": "TFLOP/s", "frac": fl / (ms * 1e-3) / peak, "flops_per_launch": fl,
+                         "dtype": "bf16" if si.dtype == inputs.BF16 else "f32",
+                         "of_fp32_peak": fl / (ms * 1e-3) / MFMA_F32},
             "hbm_GBs": nbytes / (ms * 1e-3) / 1e9, "bytes_per_launch": nbytes}
 
 
