@@ -395,3 +395,68 @@ def test_last_error_is_per_thread(ssd):
         t.join()
     assert not errs, errs[:3]
     assert len(msgs) == 8
+
+
+# --- gradients (ssd_scan_bwd): host-side validation, no device call -------
+
+def _bwd_args(b=1, L=100, H=4, P=32, G=2, N=32, dtype=torch.bfloat16):
+    a = _scan_args(b, L, H, P, G, N, dtype)
+    del a["out"], a["final_state"]
+    a.update(dout=torch.zeros(b, L, H, P, dtype=dtype), dfinal_state=torch.zeros(b, H, P, N),
+             dx=torch.zeros(b, L, H, P), ddt=torch.zeros(b, L, H), ddt_bias=torch.zeros(H),
+             dA=torch.zeros(H), dB=torch.zeros(b, L, G, N), dC=torch.zeros(b, L, G, N),
+             dD=torch.zeros(H), dinit_state=torch.zeros(b, H, P, N))
+    return a
+
+
+BWD_ORDER = ["x", "dt", "dt_bias", "A", "B", "C", "D", "init_state", "dout", "dfinal_state",
+             "dx", "ddt", "ddt_bias", "dA", "dB", "dC", "dD", "dinit_state"]
+
+
+def _call_bwd(ssd, a):
+    d = ssd.describe
+    st = ssd.lib().ssd_scan_bwd(*[d(a[k]) for k in BWD_ORDER], None)
+    return st, ssd.ssd_last_error()
+
+
+BWD_CASES = [
+    ("dout_none", lambda a: a.update(dout=None), 1),
+    ("dx_none", lambda a: a.update(dx=None), 1),
+    ("dA_none", lambda a: a.update(dA=None), 1),
+    ("dB_none", lambda a: a.update(dB=None), 1),
+    ("ddt_none", lambda a: a.update(ddt=None), 1),
+    ("dout_dtype", lambda a: a.update(dout=torch.zeros(1, 100, 4, 32)), 3),
+    ("dx_bf16", lambda a: a.update(dx=torch.zeros(1, 100, 4, 32, dtype=torch.bfloat16)), 3),
+    ("dC_shape", lambda a: a.update(dC=torch.zeros(1, 100, 2, 16)), 2),
+    ("ddt_shape", lambda a: a.update(ddt=torch.zeros(1, 100, 3)), 2),
+    ("dinit_shape", lambda a: a.update(dinit_state=torch.zeros(1, 4, 32, 16)), 2),
+    ("dfinal_shape", lambda a: a.update(dfinal_state=torch.zeros(1, 4, 16, 32)), 2),
+    ("dx_strided", lambda a: a.update(dx=torch.zeros(1, 100, 4, 64)[..., ::2]), 4),
+    ("dx_aliases_x", lambda a: a.update(dx=a["x"]), 3),
+    ("dB_aliases_dC", lambda a: a.update(dB=a["dC"]), 6),
+    ("ddt_aliases_dt", lambda a: a.update(ddt=a["dt"]), 6),
+    ("dinit_aliases_init", lambda a: a.update(dinit_state=a["init_state"]), 6),
+]
+
+
+@pytest.mark.parametrize("name,mutate,status", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_bwd_rejects(ssd, name, mutate, status):
+    a = _bwd_args()
+    mutate(a)
+    st, msg = _call_bwd(ssd, a)
+    assert st == status, (st, msg)
+    assert msg
+
+
+@pytest.mark.parametrize("P,N", [(16, 32), (128, 32), (64, 16)])
+def test_bwd_rejects_unsupported_sizes(ssd, P, N):
+    a = _bwd_args(P=P, N=N)
+    st, msg = _call_bwd(ssd, a)
+    assert st == 5 and "backward" in msg, (st, msg)
+
+
+def test_bwd_host_memory_refused(ssd):
+    # valid shapes in pageable host memory: refused before any launch
+    # (with no device present the refusal names the missing device instead)
+    st, msg = _call_bwd(ssd, _bwd_args())
+    assert st == 4 and msg, (st, msg)

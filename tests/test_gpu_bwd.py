@@ -132,3 +132,25 @@ def test_bwd_workload_2p7b_sampled_heads():
     check(got["dinit"][:, heads], ref["dinit"], 2e-2, "dinit")
     for k in ("dA", "dD", "ddt_bias"):
         check(got[k][heads], ref[k], 2e-2, k)
+
+
+@pytest.mark.parametrize("kind", ["frozen", "no_decay", "zero_x"])
+def test_bwd_degenerate(kind):
+    # frozen: Delta ~ 1e-13 (decays ~1, inputs barely enter, softplus' ~ Delta);
+    # no_decay: A = 0 (every decay is 1); zero_x: x = 0 (only the initial state
+    # reaches y, yet dx, dB, dDelta are nonzero)
+    si = inputs.make_scan(2, 300, 4, 64, 2, 64, dtype=inputs.F32, seed=101, init_std=0.5)
+    if kind == "frozen":
+        si.dt[...] = -30.0
+        si.dt_bias[...] = 0.0
+    elif kind == "no_decay":
+        si.A[...] = 0.0
+        si.dt[...] = -3.0
+    else:
+        si.x[...] = 0
+    dy, df = make_grads_in(si, 102)
+    say("bwd degenerate", kind)
+    got = run(si, dy, df)
+    ref = ref_grads(si, dy, df)
+    for k in NAMES:
+        check(got[k], ref[k], 1e-4, "%s %s" % (kind, k))
