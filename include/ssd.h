@@ -285,8 +285,8 @@ int ssd_selective_scan_fwd(const ssd_tensor *x, const ssd_tensor *dt,
  *   ddt_bias [H], dD [H], dinit_state [b,H,P,N]: each may be NULL (not
  *                         computed).
  *
- * Supported: P in {32, 64}, N in {32, 64, 128}, either input dtype, the
- * size limits of ssd_scan_fwd.  No output may overlap an input or another
+ * Supported: P in {16, 32, 64}, N in {16, 32, 64, 128}, either input dtype,
+ * the size limits of ssd_scan_fwd.  No output may overlap an input or another
  * output (SSD_ERR_ALIAS).  Arithmetic in fp32 (matrix products on the
  * matrix cores from fp32 operands).  Sums over heads, chunks and batch run
  * in a fixed order, so the result does not vary from run to run.  Scratch:

@@ -783,10 +783,8 @@ int ssd_scan_bwd(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt
   g_last_error.clear();
   ScanShape s;
   SSD_CHECK(validate_scan(x, dt, dt_bias, A, B, C, D, init_state, dout, nullptr, 64, &s, "dout", false));
-  if (s.P != 32 && s.P != 64)
-    return fail(SSD_ERR_UNSUPPORTED, "backward: P=%lld not in {32,64}", (long long)s.P);
-  if (s.N != 32 && s.N != 64 && s.N != 128)
-    return fail(SSD_ERR_UNSUPPORTED, "backward: N=%lld not in {32,64,128}", (long long)s.N);
+  if (s.P > 64)
+    return fail(SSD_ERR_UNSUPPORTED, "backward: P=%lld not in {16,32,64}", (long long)s.P);
   const int64_t sx[4] = {s.b, s.L, s.H, s.P}, sdt[3] = {s.b, s.L, s.H}, sh[1] = {s.H},
                 sbc[4] = {s.b, s.L, s.G, s.N}, sst[4] = {s.b, s.H, s.P, s.N};
   if (dfinal_state) SSD_CHECK(check_tensor(dfinal_state, "dfinal_state", SSD_F32, 4, sst));

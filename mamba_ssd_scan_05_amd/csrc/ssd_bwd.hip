@@ -172,7 +172,7 @@ template <typename T, int COLS> struct RowPrefetch {
 
 template <typename T, int P, int N, bool REV>
 __global__ void __launch_bounds__(256) bwd_state_scan_kernel(const BwdParams p) {
-  constexpr int LX = P + 4, LB = N + 4, PT = P / 16, NT = N / 16, TILES = PT * NT / 4;
+  constexpr int LX = P + 4, LB = N + 4, PT = P / 16, NT = N / 16, TILES = (PT * NT + 3) / 4;
   __shared__ __attribute__((aligned(16))) float sL[kQ * LX]; // x (forward) or dy (reverse), [token][p]
   __shared__ __attribute__((aligned(16))) float sR[kQ * LB]; // B (forward) or C (reverse), [token][n]
   __shared__ float sW[kQ];
@@ -190,6 +190,7 @@ __global__ void __launch_bounds__(256) bwd_state_scan_kernel(const BwdParams p) 
 #pragma unroll
   for (int k = 0; k < TILES; ++k) {
     const int tile = w + 4 * k, pt = tile % PT, nt = tile / PT;
+      if (tile >= PT * NT) break;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       S[k][r] = s0 ? s0[(int64_t)bh * PN + (pt * 16 + 4 * lg + r) * N + nt * 16 + li] : 0.f;
@@ -211,6 +212,7 @@ __global__ void __launch_bounds__(256) bwd_state_scan_kernel(const BwdParams p) 
 #pragma unroll
     for (int k = 0; k < TILES; ++k) {
       const int tile = w + 4 * k, pt = tile % PT, nt = tile / PT;
+      if (tile >= PT * NT) break;
 #pragma unroll
       for (int r = 0; r < 4; ++r) out[(int64_t)c * PN + (pt * 16 + 4 * lg + r) * N + nt * 16 + li] = S[k][r];
     }
@@ -235,6 +237,7 @@ __global__ void __launch_bounds__(256) bwd_state_scan_kernel(const BwdParams p) 
 #pragma unroll
     for (int k = 0; k < TILES; ++k) {
       const int tile = w + 4 * k, pt = tile % PT, nt = tile / PT;
+      if (tile >= PT * NT) break;
       f32x4 acc = S[k] * tot;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
@@ -251,6 +254,7 @@ __global__ void __launch_bounds__(256) bwd_state_scan_kernel(const BwdParams p) 
 #pragma unroll
     for (int k = 0; k < TILES; ++k) {
       const int tile = w + 4 * k, pt = tile % PT, nt = tile / PT;
+      if (tile >= PT * NT) break;
 #pragma unroll
       for (int r = 0; r < 4; ++r) p.dinit[(int64_t)bh * PN + (pt * 16 + 4 * lg + r) * N + nt * 16 + li] = S[k][r];
     }
@@ -264,14 +268,16 @@ __global__ void __launch_bounds__(256) bwd_state_scan_kernel(const BwdParams p) 
 // tiles w/4, w/4 + 2, ...
 template <typename T, int P, int N>
 __global__ void __launch_bounds__(512) bwd_chunk_kernel(const BwdParams p) {
-  constexpr int LB = N + 4, LX = P + 4, LQ = kQ + 4, LS = N + 4;
-  constexpr int PT = P / 16, NT = N / 16;
+  // P or N below 32 run padded to 32 (zero columns/rows in LDS)
+  constexpr int PP = P < 32 ? 32 : P, NP = N < 32 ? 32 : N;
+  constexpr int LB = NP + 4, LX = PP + 4, LQ = kQ + 4, LS = NP + 4;
+  constexpr int PT = PP / 16, NT = NP / 16;
   __shared__ __attribute__((aligned(16))) float sB[kQ * LB];
   __shared__ __attribute__((aligned(16))) float sC[kQ * LB];
   __shared__ __attribute__((aligned(16))) float sX[kQ * LX];
   __shared__ __attribute__((aligned(16))) float sDY[kQ * LX];
   __shared__ __attribute__((aligned(16))) float sM[kQ * LQ];
-  __shared__ __attribute__((aligned(16))) float sSt[P * LS];
+  __shared__ __attribute__((aligned(16))) float sSt[PP * LS];
   __shared__ float sCum[kQ], sDel[kQ], sEin[kQ], sEout[kQ], sSig[kQ];
   __shared__ float rowW[2][kQ], colW[4][kQ], uP[2][kQ], vP[2][kQ], dinP[2][kQ], sDiag[kQ];
   __shared__ float sRed[9]; // [0]: log2 decay of the chunk; [1 + w]: wave w's share of <G, H>
@@ -286,6 +292,13 @@ __global__ void __launch_bounds__(512) bwd_chunk_kernel(const BwdParams p) {
   const int t0 = c * kQ, nv = min(kQ, L - t0);
   const int PN = P * N;
 
+  if constexpr (PP != P || NP != N) {
+    for (int e = tid; e < kQ * LX; e += 512) sX[e] = sDY[e] = 0.f;
+    for (int e = tid; e < PP * LS; e += 512) sSt[e] = 0.f;
+    for (int e = tid; e < kQ * LB; e += 512) sB[e] = sC[e] = 0.f;
+    __syncthreads();
+  }
+
   // B and C of the group's chunk, and S = C B^T (two 16x16 tiles per wave)
   const T *Bg = reinterpret_cast<const T *>(p.B) + (((int64_t)b_ * L + t0) * G + g) * N;
   const T *Cg = reinterpret_cast<const T *>(p.C) + (((int64_t)b_ * L + t0) * G + g) * N;
@@ -298,7 +311,7 @@ __global__ void __launch_bounds__(512) bwd_chunk_kernel(const BwdParams p) {
     const int ct = ct0 + 2 * k;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k0 = 0; k0 < N; k0 += 32)
+    for (int k0 = 0; k0 < NP; k0 += 32)
       acc = mma(frag_k_contig(sC, LB, rt * 16 + li, k0, lg), frag_k_contig(sB, LB, ct * 16 + li, k0, lg), acc);
     S[k] = acc;
   }
@@ -343,7 +356,7 @@ __global__ void __launch_bounds__(512) bwd_chunk_kernel(const BwdParams p) {
       const int ct = ct0 + 2 * k;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k0 = 0; k0 < P; k0 += 32)
+      for (int k0 = 0; k0 < PP; k0 += 32)
         acc = mma(frag_k_contig(sDY, LX, rt * 16 + li, k0, lg), frag_k_contig(sX, LX, ct * 16 + li, k0, lg), acc);
       const int j = ct * 16 + li;
       const float cj = sCum[j], dj = sDel[j];
@@ -377,7 +390,7 @@ __global__ void __launch_bounds__(512) bwd_chunk_kernel(const BwdParams p) {
         const int ct = ct0 + 2 * k;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k0 = 0; k0 < P; k0 += 32)
+        for (int k0 = 0; k0 < PP; k0 += 32)
           acc = mma(frag_k_contig(sDY, LX, rt * 16 + li, k0, lg), trfrag(sSt, LS, k0, ct * 16, li, lg), acc);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -422,14 +435,14 @@ __global__ void __launch_bounds__(512) bwd_chunk_kernel(const BwdParams p) {
         for (int k0 = 0; k0 < kQ; k0 += 32)
           a3 = mma(trfrag(sM, LQ, k0, rt * 16, li, lg), trfrag(sDY, LX, k0, ct * 16, li, lg), a3);
 #pragma unroll
-        for (int k0 = 0; k0 < N; k0 += 32)
+        for (int k0 = 0; k0 < NP; k0 += 32)
           b3 = mma(frag_k_contig(sB, LB, rt * 16 + li, k0, lg), frag_k_contig(sSt, LS, ct * 16 + li, k0, lg), b3);
         const int pc = ct * 16 + li;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = rt * 16 + 4 * lg + r;
           const float br = a3[r] + sEout[t] * b3[r];
-          if (t < nv)
+          if (t < nv && pc < P)
             p.dx[(((int64_t)b_ * L + t0 + t) * H + h) * P + pc] = Dh * sDY[t * LX + pc] + sDel[t] * br;
           dp[r] += sX[t * LX + pc] * br;
         }
@@ -450,7 +463,7 @@ __global__ void __launch_bounds__(512) bwd_chunk_kernel(const BwdParams p) {
         const int ct = ct0 + 2 * k;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k0 = 0; k0 < P; k0 += 32)
+        for (int k0 = 0; k0 < PP; k0 += 32)
           acc = mma(frag_k_contig(sX, LX, rt * 16 + li, k0, lg), trfrag(sSt, LS, k0, ct * 16, li, lg), acc);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -543,7 +556,7 @@ __global__ void __launch_bounds__(512) bwd_chunk_kernel(const BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = rt * 16 + 4 * lg + r;
-      if (t < nv) {
+      if (t < nv && n < N) {
         const int64_t o = (((int64_t)b_ * L + t0 + t) * G + g) * N + n;
         p.dB[o] = dBacc[k][r];
         p.dC[o] = dCacc[k][r];
@@ -608,7 +621,7 @@ __device__ __forceinline__ float stage_state_split(__bf16 *hi, __bf16 *lo, int l
 // B or C are exact in bf16, and each product is two 16x16x32 MFMAs.
 template <int P, int N, bool REV>
 __global__ void __launch_bounds__(256) bwd_state_scan_bf16_kernel(const BwdParams p) {
-  constexpr int LX = tr_ld(P, 2), LB = tr_ld(N, 2), PT = P / 16, NT = N / 16, TILES = PT * NT / 4;
+  constexpr int LX = tr_ld(P, 2), LB = tr_ld(N, 2), PT = P / 16, NT = N / 16, TILES = (PT * NT + 3) / 4;
   __shared__ __attribute__((aligned(16))) __bf16 sLh[kQ * LX];
   __shared__ __attribute__((aligned(16))) __bf16 sLl[kQ * LX];
   __shared__ __attribute__((aligned(16))) __bf16 sR[kQ * LB];
@@ -627,6 +640,7 @@ __global__ void __launch_bounds__(256) bwd_state_scan_bf16_kernel(const BwdParam
 #pragma unroll
   for (int k = 0; k < TILES; ++k) {
     const int tile = w + 4 * k, pt = tile % PT, nt = tile / PT;
+      if (tile >= PT * NT) break;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       S[k][r] = s0 ? s0[(int64_t)bh * PN + (pt * 16 + 4 * lg + r) * N + nt * 16 + li] : 0.f;
@@ -647,6 +661,7 @@ __global__ void __launch_bounds__(256) bwd_state_scan_bf16_kernel(const BwdParam
 #pragma unroll
     for (int k = 0; k < TILES; ++k) {
       const int tile = w + 4 * k, pt = tile % PT, nt = tile / PT;
+      if (tile >= PT * NT) break;
 #pragma unroll
       for (int r = 0; r < 4; ++r) out[(int64_t)c * PN + (pt * 16 + 4 * lg + r) * N + nt * 16 + li] = S[k][r];
     }
@@ -682,6 +697,7 @@ __global__ void __launch_bounds__(256) bwd_state_scan_bf16_kernel(const BwdParam
 #pragma unroll
     for (int k = 0; k < TILES; ++k) {
       const int tile = w + 4 * k, pt = tile % PT, nt = tile / PT;
+      if (tile >= PT * NT) break;
       f32x4 acc = S[k] * tot;
 #pragma unroll
       for (int k0 = 0; k0 < kQ; k0 += 32) {
@@ -697,6 +713,7 @@ __global__ void __launch_bounds__(256) bwd_state_scan_bf16_kernel(const BwdParam
 #pragma unroll
     for (int k = 0; k < TILES; ++k) {
       const int tile = w + 4 * k, pt = tile % PT, nt = tile / PT;
+      if (tile >= PT * NT) break;
 #pragma unroll
       for (int r = 0; r < 4; ++r) p.dinit[(int64_t)bh * PN + (pt * 16 + 4 * lg + r) * N + nt * 16 + li] = S[k][r];
     }
@@ -705,16 +722,18 @@ __global__ void __launch_bounds__(256) bwd_state_scan_bf16_kernel(const BwdParam
 
 template <int P, int N>
 __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) {
-  constexpr int LB = tr_ld(N, 2), LX = tr_ld(P, 2), LQ = tr_ld(kQ, 2), LS = tr_ld(N, 2);
-  constexpr int PT = P / 16, NT = N / 16;
+  // P or N below 32 run padded to 32 (zero columns/rows in LDS)
+  constexpr int PP = P < 32 ? 32 : P, NP = N < 32 ? 32 : N;
+  constexpr int LB = tr_ld(NP, 2), LX = tr_ld(PP, 2), LQ = tr_ld(kQ, 2), LS = tr_ld(NP, 2);
+  constexpr int PT = PP / 16, NT = NP / 16;
   __shared__ __attribute__((aligned(16))) __bf16 sB[kQ * LB];
   __shared__ __attribute__((aligned(16))) __bf16 sC[kQ * LB];
   __shared__ __attribute__((aligned(16))) __bf16 sX[kQ * LX];
   __shared__ __attribute__((aligned(16))) __bf16 sDY[kQ * LX];
   __shared__ __attribute__((aligned(16))) __bf16 sMh[kQ * LQ];
   __shared__ __attribute__((aligned(16))) __bf16 sMl[kQ * LQ];
-  __shared__ __attribute__((aligned(16))) __bf16 sSh[P * LS];
-  __shared__ __attribute__((aligned(16))) __bf16 sSl[P * LS];
+  __shared__ __attribute__((aligned(16))) __bf16 sSh[PP * LS];
+  __shared__ __attribute__((aligned(16))) __bf16 sSl[PP * LS];
   __shared__ float sCum[kQ], sDel[kQ], sEin[kQ], sEout[kQ], sSig[kQ];
   __shared__ float rowW[2][kQ], colW[4][kQ], uP[2][kQ], vP[2][kQ], dinP[2][kQ], sDiag[kQ];
   __shared__ float sRed[9]; // [0]: log2 decay of the chunk; [1 + w]: wave w's share of <G, H>
@@ -729,6 +748,13 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
   const int t0 = c * kQ, nv = min(kQ, L - t0);
   const int PN = P * N;
 
+  if constexpr (PP != P || NP != N) {
+    for (int e = tid; e < kQ * LX; e += 512) sX[e] = sDY[e] = (__bf16)0.f;
+    for (int e = tid; e < PP * LS; e += 512) sSh[e] = sSl[e] = (__bf16)0.f;
+    for (int e = tid; e < kQ * LB; e += 512) sB[e] = sC[e] = (__bf16)0.f;
+    __syncthreads();
+  }
+
   const __bf16 *Bg = reinterpret_cast<const __bf16 *>(p.B) + (((int64_t)b_ * L + t0) * G + g) * N;
   const __bf16 *Cg = reinterpret_cast<const __bf16 *>(p.C) + (((int64_t)b_ * L + t0) * G + g) * N;
   stage_bf16(sB, LB, Bg, (int64_t)G * N, kQ, nv, N, tid, 512);
@@ -740,7 +766,7 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
     const int ct = ct0 + 2 * k;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k0 = 0; k0 < N; k0 += 32)
+    for (int k0 = 0; k0 < NP; k0 += 32)
       acc = mma(kc16(sC, LB, rt * 16 + li, k0, lg), kc16(sB, LB, ct * 16 + li, k0, lg), acc);
     S[k] = acc;
   }
@@ -782,7 +808,7 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
       const int ct = ct0 + 2 * k;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k0 = 0; k0 < P; k0 += 32)
+      for (int k0 = 0; k0 < PP; k0 += 32)
         acc = mma(kc16(sDY, LX, rt * 16 + li, k0, lg), kc16(sX, LX, ct * 16 + li, k0, lg), acc);
       const int j = ct * 16 + li;
       const float cj = sCum[j], dj = sDel[j];
@@ -816,7 +842,7 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
         const int ct = ct0 + 2 * k;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k0 = 0; k0 < P; k0 += 32) {
+        for (int k0 = 0; k0 < PP; k0 += 32) {
           const FragBF a = kc16(sDY, LX, rt * 16 + li, k0, lg);
           acc = mma(a, trfrag(sSh, LS, k0, ct * 16, li, lg), acc);
           acc = mma(a, trfrag(sSl, LS, k0, ct * 16, li, lg), acc);
@@ -858,7 +884,7 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
           a3 = mma(trfrag(sMl, LQ, k0, rt * 16, li, lg), bb, a3);
         }
 #pragma unroll
-        for (int k0 = 0; k0 < N; k0 += 32) {
+        for (int k0 = 0; k0 < NP; k0 += 32) {
           const FragBF a = kc16(sB, LB, rt * 16 + li, k0, lg);
           b3 = mma(a, kc16(sSh, LS, ct * 16 + li, k0, lg), b3);
           b3 = mma(a, kc16(sSl, LS, ct * 16 + li, k0, lg), b3);
@@ -868,7 +894,7 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
         for (int r = 0; r < 4; ++r) {
           const int t = rt * 16 + 4 * lg + r;
           const float br = a3[r] + sEout[t] * b3[r];
-          if (t < nv)
+          if (t < nv && pc < P)
             p.dx[(((int64_t)b_ * L + t0 + t) * H + h) * P + pc] = Dh * (float)sDY[t * LX + pc] + sDel[t] * br;
           dp[r] += (float)sX[t * LX + pc] * br;
         }
@@ -889,7 +915,7 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
         const int ct = ct0 + 2 * k;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k0 = 0; k0 < P; k0 += 32) {
+        for (int k0 = 0; k0 < PP; k0 += 32) {
           const FragBF a = kc16(sX, LX, rt * 16 + li, k0, lg);
           acc = mma(a, trfrag(sSh, LS, k0, ct * 16, li, lg), acc);
           acc = mma(a, trfrag(sSl, LS, k0, ct * 16, li, lg), acc);
@@ -991,7 +1017,7 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = rt * 16 + 4 * lg + r;
-      if (t < nv) {
+      if (t < nv && n < N) {
         const int64_t o = (((int64_t)b_ * L + t0 + t) * G + g) * N + n;
         p.dB[o] = dBacc[k][r];
         p.dC[o] = dCacc[k][r];
@@ -1059,6 +1085,7 @@ template <typename T, int P, int N> hipError_t launch_bwd_t(const BwdParams &p, 
 
 template <typename T, int P> hipError_t launch_bwd_n(int N, const BwdParams &p, hipStream_t st) {
   switch (N) {
+  case 16: return launch_bwd_t<T, P, 16>(p, st);
   case 32: return launch_bwd_t<T, P, 32>(p, st);
   case 64: return launch_bwd_t<T, P, 64>(p, st);
   case 128: return launch_bwd_t<T, P, 128>(p, st);
@@ -1067,6 +1094,7 @@ template <typename T, int P> hipError_t launch_bwd_n(int N, const BwdParams &p, 
 }
 template <typename T> hipError_t launch_bwd_p(int P, int N, const BwdParams &p, hipStream_t st) {
   switch (P) {
+  case 16: return launch_bwd_n<T, 16>(N, p, st);
   case 32: return launch_bwd_n<T, 32>(N, p, st);
   case 64: return launch_bwd_n<T, 64>(N, p, st);
   }

@@ -137,6 +137,6 @@ struct BwdParams {
   float *dinit;         // [b, H, P, N] or null
   int b, L, H, G, nc;
 };
-// P in {32, 64}, N in {32, 64, 128}; dtype 1 = bf16, 0 = fp32.
+// P in {16, 32, 64}, N in {16, 32, 64, 128}; dtype 1 = bf16, 0 = fp32.
 hipError_t launch_bwd(int dtype, int P, int N, const BwdParams &p, hipStream_t stream);
 } // namespace ssd

@@ -448,8 +448,9 @@ def test_bwd_rejects(ssd, name, mutate, status):
     assert msg
 
 
-@pytest.mark.parametrize("P,N", [(16, 32), (128, 32), (64, 16)])
+@pytest.mark.parametrize("P,N", [(128, 32), (128, 128)])
 def test_bwd_rejects_unsupported_sizes(ssd, P, N):
+    # P = 128 (bf16 forward only) is not supported by the backward
     a = _bwd_args(P=P, N=N)
     st, msg = _call_bwd(ssd, a)
     assert st == 5 and "backward" in msg, (st, msg)

@@ -71,6 +71,11 @@ CASES = [
     (2, 200, 4, 64, 1, 128, inputs.BF16),
     (1, 257, 4, 32, 2, 128, inputs.BF16),
     (1, 1, 2, 32, 1, 64, inputs.F32),
+    # P or N of 16 (run padded to 32 inside the chunk step)
+    (1, 200, 4, 16, 1, 16, inputs.F32),
+    (2, 130, 2, 16, 2, 64, inputs.BF16),
+    (1, 100, 2, 32, 1, 16, inputs.BF16),
+    (1, 257, 4, 64, 2, 16, inputs.F32),
 ]
 
 
