@@ -14,6 +14,7 @@ with gcc, loads it with ctypes and marshals numpy arrays:
 * ``gate(y, z)`` -> ``y * silu(z)``
 * ``step(state, x, delta, A, B, C, D)`` -> ``(y, new_state)``
 * ``scan_bwd(x, dt, dt_bias, A, B, C, D, init, dy, dfinal)`` -> dict of gradients
+* ``scan_bwd_gated(x, dt, dt_bias, A, B, C, z, D, init, dout, dfinal)`` -> the same plus dz
 
 Every array argument is converted to contiguous float64 first; callers pass
 the values exactly as the device sees them (bf16 inputs upcast exactly).
@@ -65,6 +66,8 @@ class Oracle:
         lib.oracle_sscan_f64.restype = None
         lib.oracle_scan_bwd_f64.argtypes = [i64] * 6 + [vp] * 18
         lib.oracle_scan_bwd_f64.restype = None
+        lib.oracle_gate_bwd_f64.argtypes = [i64] + [vp] * 5
+        lib.oracle_gate_bwd_f64.restype = None
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
         self.lib = lib
@@ -89,6 +92,9 @@ class Oracle:
 
     def scan_bwd(self, *args, **kwargs):
         return _scan_bwd(self.lib, *args, **kwargs)
+
+    def scan_bwd_gated(self, *args, **kwargs):
+        return _scan_bwd_gated(self, *args, **kwargs)
 
 
 def default() -> Oracle:
@@ -120,6 +126,10 @@ def _ptr(a):
 
 def scan_bwd(x, dt, dt_bias, A, B, C, D, init, dy, dfinal=None):
     return default().scan_bwd(x, dt, dt_bias, A, B, C, D, init, dy, dfinal)
+
+
+def scan_bwd_gated(x, dt, dt_bias, A, B, C, z, D, init, dout, dfinal=None):
+    return default().scan_bwd_gated(x, dt, dt_bias, A, B, C, z, D, init, dout, dfinal)
 
 
 def scan(x, dt, dt_bias, A, B, C, D=None, init=None, want_final=True):
@@ -248,3 +258,19 @@ def _scan_bwd(lib, x, dt, dt_bias, A, B, C, D, init, dy, dfinal=None):
                             _ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["ddt_bias"]), _ptr(out["dA"]),
                             _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dinit"]))
     return out
+
+
+def _scan_bwd_gated(o, x, dt, dt_bias, A, B, C, z, D, init, dout, dfinal=None):
+    """Gradients of the gated scan out = y * silu(z) (y the scan output with
+    the D term): the scan's own y, then the gate's derivative
+    (oracle_gate_bwd_f64: dy = dout * silu(z), dz = dout * y * silu'(z)), then
+    the scan's gradients for dy.  Returns scan_bwd's dict plus dz."""
+    y, _ = o.scan(x, dt, dt_bias, A, B, C, D, init, want_final=False)
+    z, dout = _f64(z), _f64(dout)
+    assert z.shape == y.shape and dout.shape == y.shape
+    dy = np.empty_like(y)
+    dz = np.empty_like(y)
+    o.lib.oracle_gate_bwd_f64(y.size, _ptr(y), _ptr(z), _ptr(dout), _ptr(dy), _ptr(dz))
+    g = o.scan_bwd(x, dt, dt_bias, A, B, C, D, init, dy, dfinal)
+    g["dz"] = dz
+    return g

@@ -153,6 +153,18 @@ void oracle_gate_f64(int64_t n, const double *y, const double *z, double *out) {
     for (int64_t i = 0; i < n; ++i) out[i] = y[i] * (z[i] / (1.0 + exp(-z[i])));
 }
 
+/* Gradient through the output gate out = y * silu(z) (oracle_gate_f64):
+ * dy = dout * silu(z) and dz = dout * y * silu'(z), where
+ * silu'(z) = s + z s (1 - s) with s = 1 / (1 + e^{-z}) the logistic. */
+void oracle_gate_bwd_f64(int64_t n, const double *y, const double *z, const double *dout,
+                         double *dy, double *dz) {
+    for (int64_t i = 0; i < n; ++i) {
+        double sg = 1.0 / (1.0 + exp(-z[i]));
+        dy[i] = dout[i] * z[i] * sg;
+        dz[i] = dout[i] * y[i] * (sg + z[i] * sg * (1.0 - sg));
+    }
+}
+
 /* Selective scan with a per-channel step size and a diagonal A per
  * (channel, state index): the Mamba-1 selective SSM (Mamba paper-reading
  * notes, sxlin0.github.io, the selective-mechanism section: B, C and Delta

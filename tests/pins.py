@@ -36,6 +36,8 @@ fixed independently of the oracle's own loop:
 * ``pin_bwd_transpose`` dx, dinit, dD exactly as transposes of the explicit
                       L x L operator (the forward is linear in x and h0)
 * ``pin_bwd_hand``    a one-token gradient example worked by hand
+* ``pin_bwd_gated_finite_difference`` gradients of the gated scan (and dz)
+                      against central differences of the gated forward
 
 Softplus here is ``numpy.logaddexp(0, z)`` (a library routine).
 """
@@ -506,8 +508,37 @@ def pin_bwd_hand(o):
         _close(g[k].ravel(), np.array([v]), 1e-12, "hand " + k)
 
 
+def pin_bwd_gated_finite_difference(o, seed=27):
+    """Gradients of the gated scan (scan_bwd_gated, with dz) against central
+    differences of the (separately pinned) gated forward along random
+    directions, every input and z."""
+    rng = np.random.default_rng(seed)
+    b, L, H, P, G, N = 2, 7, 4, 3, 2, 4
+    case = rand_case(rng, b, L, H, P, G, N)
+    z = 1.5 * rng.standard_normal((b, L, H, P))
+    dout = rng.standard_normal((b, L, H, P))
+    dfinal = rng.standard_normal((b, H, P, N))
+    g = o.scan_bwd_gated(case["x"], case["dt"], case["dt_bias"], case["A"], case["B"], case["C"], z,
+                         case["D"], case["init"], dout, dfinal)
+
+    def obj(c, zz):
+        y = o.gate(o.scan(**c, want_final=False)[0], zz)
+        return float(np.sum(dout * y) + np.sum(dfinal * o.scan(**c)[1]))
+    eps = 1e-5
+    for k in BWD_KEYS + ["z"]:
+        v = rng.standard_normal(z.shape if k == "z" else case[k].shape)
+        if k == "z":
+            fd = (obj(case, z + eps * v) - obj(case, z - eps * v)) / (2 * eps)
+            an = float(np.sum(g["dz"] * v))
+        else:
+            fd = (obj(dict(case, **{k: case[k] + eps * v}), z) - obj(dict(case, **{k: case[k] - eps * v}), z)) / (2 * eps)
+            an = float(np.sum(g[GRAD_OF[k]] * v))
+        assert abs(fd - an) <= 1e-6 * (1.0 + abs(fd)), (k, fd, an)
+
+
 ALL_PINS = [pin_golden, pin_quadratic, pin_no_decay, pin_scalar_state, pin_split,
             pin_lti, pin_step_scan, pin_exact_int, pin_linearity, pin_groups,
             pin_head_perm, pin_decay_bound, pin_gate_closed_forms, pin_gate_expit,
             pin_sscan_closed_form, pin_sscan_reduces_to_ssd, pin_sscan_hand,
-            pin_bwd_finite_difference, pin_bwd_transpose, pin_bwd_hand]
+            pin_bwd_finite_difference, pin_bwd_transpose, pin_bwd_hand,
+            pin_bwd_gated_finite_difference]

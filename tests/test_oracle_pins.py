@@ -88,6 +88,9 @@ MUTATIONS = [
     ("decay_dot += adj[p * N + n] * hp[p * N + n];", "decay_dot += adj[p * N + n] * hv[p * N + n] + 0.0 * hp[0];",
      "backward: decay term with the current state"),
     ("xg += xv[p] * adj[p * N + n];", "xg += dyv[p] * adj[p * N + n] + 0.0 * xv[0];", "backward: dB from dy"),
+    ("dz[i] = dout[i] * y[i] * (sg + z[i] * sg * (1.0 - sg));", "dz[i] = dout[i] * y[i] * sg;",
+     "gate backward: silu' taken as the logistic"),
+    ("dy[i] = dout[i] * z[i] * sg;", "dy[i] = dout[i] * sg;", "gate backward: dy through the logistic"),
 ]
 
 
