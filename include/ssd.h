@@ -303,6 +303,29 @@ int ssd_scan_bwd(const ssd_tensor *x, const ssd_tensor *dt,
                  ssd_tensor *dinit_state, void *stream);
 
 /*
+ * ssd_scan_bwd_gated -- gradients of ssd_scan_fwd_gated (out = y * silu(z),
+ * y the scan output including the D term) for the objective
+ * <dout, out> + <dfinal_state, h_last>.
+ *
+ * The gated output is the Mamba block's gate before its output projection
+ * (Mamba paper-reading notes, sxlin0.github.io, the simplified-block section).
+ * Arguments are as for ssd_scan_bwd, plus z [b,L,H,P] (dtype of x, an input)
+ * and dz [b,L,H,P] f32 (an output, required).  The call recomputes y with the
+ * forward scan, forms dy = dout * silu(z) (rounded to x's dtype) and
+ * dz = dout * y * silu'(z), then runs ssd_scan_bwd on dy.  Scratch: two
+ * tensors the size of x, plus what the forward scan and ssd_scan_bwd use.
+ */
+int ssd_scan_bwd_gated(const ssd_tensor *x, const ssd_tensor *dt,
+                       const ssd_tensor *dt_bias, const ssd_tensor *A,
+                       const ssd_tensor *B, const ssd_tensor *C,
+                       const ssd_tensor *D, const ssd_tensor *z,
+                       const ssd_tensor *init_state, const ssd_tensor *dout,
+                       const ssd_tensor *dfinal_state, ssd_tensor *dx,
+                       ssd_tensor *ddt, ssd_tensor *ddt_bias, ssd_tensor *dA,
+                       ssd_tensor *dB, ssd_tensor *dC, ssd_tensor *dD,
+                       ssd_tensor *dz, ssd_tensor *dinit_state, void *stream);
+
+/*
  * ssd_scan_plan -- the plan SSD_ALGO_AUTO uses for a shape on a device with
  * `cus` compute units for inputs of element type `dtype` (SSD_BF16 or
  * SSD_F32), host only, no HIP call: *algo is SSD_ALGO_FUSED,

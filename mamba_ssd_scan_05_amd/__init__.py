@@ -9,4 +9,4 @@ from .ssd import (SSD_ALGO_AUTO, SSD_ALGO_CHUNKED, SSD_ALGO_FUSED, SSD_ALGO_ROWS
                   SsdError, ssd_last_error, ssd_scan_fwd, ssd_scan_fwd_gated, ssd_scan_fwd_rows, ssd_selective_scan_fwd,
                   ssd_scan_plan,
                   ssd_status_string, ssd_step, ssd_version,
-                  ssd_release_scratch, ssd_scan_bwd)
+                  ssd_release_scratch, ssd_scan_bwd, ssd_scan_bwd_gated)

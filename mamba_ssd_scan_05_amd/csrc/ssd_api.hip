@@ -188,13 +188,16 @@ constexpr size_t kScratchGranule = (size_t)1 << 20;
 struct ScratchSlot {
   int dev;
   hipStream_t st;
+  int tag;
   void *p;
   size_t cap;
   hipEvent_t done;
   bool pending; // done has been recorded after the last use
 };
 
-std::mutex g_scratch_mu;
+// Recursive: a call may hold one buffer (tag 1) while the calls it makes take
+// another (tag 0) on the same stream.
+std::recursive_mutex g_scratch_mu;
 std::vector<ScratchSlot> g_scratch;
 
 // One call's scratch.  get() returns the buffer; the lock on the kept
@@ -203,7 +206,7 @@ std::vector<ScratchSlot> g_scratch;
 // buffer.
 class Scratch {
 public:
-  explicit Scratch(hipStream_t st) : st_(st) {}
+  explicit Scratch(hipStream_t st, int tag = 0) : st_(st), tag_(tag) {}
   Scratch(const Scratch &) = delete;
   Scratch &operator=(const Scratch &) = delete;
   ~Scratch() { (void)finish(); }
@@ -223,14 +226,16 @@ public:
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "scratch: current device");
-    lock_ = std::unique_lock<std::mutex>(g_scratch_mu);
+    lock_ = std::unique_lock<std::recursive_mutex>(g_scratch_mu);
     size_t i = 0;
-    while (i < g_scratch.size() && !(g_scratch[i].dev == dev && g_scratch[i].st == st_)) ++i;
+    while (i < g_scratch.size() &&
+           !(g_scratch[i].dev == dev && g_scratch[i].st == st_ && g_scratch[i].tag == tag_))
+      ++i;
     if (i == g_scratch.size()) {
       hipEvent_t ev = nullptr;
       e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
       if (e != hipSuccess) return hip_fail(e, "scratch: event");
-      g_scratch.push_back(ScratchSlot{dev, st_, nullptr, 0, ev, false});
+      g_scratch.push_back(ScratchSlot{dev, st_, tag_, nullptr, 0, ev, false});
     }
     ScratchSlot &s = g_scratch[i];
     if (s.pending) {
@@ -279,7 +284,8 @@ public:
 
 private:
   hipStream_t st_;
-  std::unique_lock<std::mutex> lock_;
+  int tag_;
+  std::unique_lock<std::recursive_mutex> lock_;
   int slot_ = -1;
   void *own_ = nullptr;
 };
@@ -562,6 +568,89 @@ int validate_gate(const ssd_tensor *z, const ssd_tensor *x, const ssd_tensor *ou
   return SSD_OK;
 }
 
+// Checks of ssd_scan_bwd's arguments (and, for the gated call, z and dz);
+// every check runs on the host before any HIP call.
+int validate_bwd(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bias,
+                 const ssd_tensor *A, const ssd_tensor *B, const ssd_tensor *C,
+                 const ssd_tensor *D, const ssd_tensor *init_state, const ssd_tensor *dout,
+                 const ssd_tensor *dfinal_state, const ssd_tensor *dx, const ssd_tensor *ddt,
+                 const ssd_tensor *ddt_bias, const ssd_tensor *dA, const ssd_tensor *dB,
+                 const ssd_tensor *dC, const ssd_tensor *dD, const ssd_tensor *dinit_state,
+                 const ssd_tensor *z, const ssd_tensor *dz, ScanShape &s) {
+  SSD_CHECK(validate_scan(x, dt, dt_bias, A, B, C, D, init_state, dout, nullptr, 64, &s, "dout", false));
+  if (s.P > 64)
+    return fail(SSD_ERR_UNSUPPORTED, "backward: P=%lld not in {16,32,64}", (long long)s.P);
+  const int64_t sx[4] = {s.b, s.L, s.H, s.P}, sdt[3] = {s.b, s.L, s.H}, sh[1] = {s.H},
+                sbc[4] = {s.b, s.L, s.G, s.N}, sst[4] = {s.b, s.H, s.P, s.N};
+  if (dfinal_state) SSD_CHECK(check_tensor(dfinal_state, "dfinal_state", SSD_F32, 4, sst));
+  SSD_CHECK(check_tensor(dx, "dx", SSD_F32, 4, sx));
+  SSD_CHECK(check_tensor(ddt, "ddt", SSD_F32, 3, sdt));
+  if (ddt_bias) SSD_CHECK(check_tensor(ddt_bias, "ddt_bias", SSD_F32, 1, sh));
+  SSD_CHECK(check_tensor(dA, "dA", SSD_F32, 1, sh));
+  SSD_CHECK(check_tensor(dB, "dB", SSD_F32, 4, sbc));
+  SSD_CHECK(check_tensor(dC, "dC", SSD_F32, 4, sbc));
+  if (dD) SSD_CHECK(check_tensor(dD, "dD", SSD_F32, 1, sh));
+  if (dinit_state) SSD_CHECK(check_tensor(dinit_state, "dinit_state", SSD_F32, 4, sst));
+  if (z) {
+    SSD_CHECK(check_tensor(z, "z", x->dtype, 4, sx));
+    if (!dz) return fail(SSD_ERR_NULL, "dz: descriptor is NULL");
+    SSD_CHECK(check_tensor(dz, "dz", SSD_F32, 4, sx));
+  }
+  // inputs 0..10, outputs 11..19 (z and dz only for the gated call)
+  const ssd_tensor *ts[] = {x, dt, dt_bias, A, B, C, D, init_state, dout, dfinal_state, z,
+                            dx, ddt, ddt_bias, dA, dB, dC, dD, dinit_state, dz};
+  const char *nm[] = {"x", "dt", "dt_bias", "A", "B", "C", "D", "init_state", "dout", "dfinal_state", "z",
+                      "dx", "ddt", "ddt_bias", "dA", "dB", "dC", "dD", "dinit_state", "dz"};
+  // no output may overlap an input or another output
+  for (int i = 11; i < 20; ++i) {
+    const Range ri = range_of(ts[i]);
+    for (int j = 0; j < 20; ++j)
+      if (j != i && overlap(ri, range_of(ts[j])))
+        return fail(SSD_ERR_ALIAS, "%s overlaps %s", nm[i], nm[j]);
+  }
+  SSD_CHECK(check_addressable(ts, nm, 20));
+  return SSD_OK;
+}
+
+
+// The backward after validation: dout is the gradient at the scan output y.
+int run_bwd(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bias,
+            const ssd_tensor *A, const ssd_tensor *B, const ssd_tensor *C, const ssd_tensor *D,
+            const ssd_tensor *init_state, const void *dout, const ssd_tensor *dfinal_state,
+            ssd_tensor *dx, ssd_tensor *ddt, ssd_tensor *ddt_bias, ssd_tensor *dA, ssd_tensor *dB,
+            ssd_tensor *dC, ssd_tensor *dD, ssd_tensor *dinit_state, const ScanShape &s,
+            hipStream_t st) {
+  const int64_t nc = (s.L + 63) / 64, PN = s.P * s.N, nbh = s.b * s.H;
+  auto al = [](size_t v) { return (v + 255) / 256 * 256; };
+  const size_t o_adj = al((size_t)(nbh * nc * PN) * 4);
+  const size_t o_part = o_adj + al((size_t)(nbh * nc * PN) * 4);
+  const size_t total = o_part + al((size_t)(nbh * nc * 3) * 4);
+  Scratch scratch(st);
+  void *ws = nullptr;
+  SSD_CHECK(scratch.get(total, &ws));
+  char *base = (char *)ws;
+  ssd::BwdParams bp{};
+  bp.x = x->data; bp.dt = (const float *)dt->data;
+  bp.dt_bias = dt_bias ? (const float *)dt_bias->data : nullptr;
+  bp.A = (const float *)A->data; bp.B = B->data; bp.C = C->data;
+  bp.D = D ? (const float *)D->data : nullptr;
+  bp.dy = dout; bp.dfinal = dfinal_state ? (const float *)dfinal_state->data : nullptr;
+  bp.states_init = init_state ? (const float *)init_state->data : nullptr;
+  bp.states = (float *)base; bp.adj = (float *)(base + o_adj); bp.part = (float *)(base + o_part);
+  bp.dx = (float *)dx->data; bp.ddt = (float *)ddt->data; bp.dB = (float *)dB->data;
+  bp.dC = (float *)dC->data; bp.dA = (float *)dA->data;
+  bp.dD = dD ? (float *)dD->data : nullptr;
+  bp.ddt_bias = ddt_bias ? (float *)ddt_bias->data : nullptr;
+  bp.dinit = dinit_state ? (float *)dinit_state->data : nullptr;
+  bp.b = (int)s.b; bp.L = (int)s.L; bp.H = (int)s.H; bp.G = (int)s.G; bp.nc = (int)nc;
+  int status = SSD_OK;
+  const hipError_t e = ssd::launch_bwd(x->dtype, (int)s.P, (int)s.N, bp, st);
+  if (e != hipSuccess) status = hip_fail(e, "backward launch");
+  const int fs = scratch.finish();
+  return status != SSD_OK ? status : fs;
+}
+
+
 } // namespace
 
 extern "C" {
@@ -782,61 +871,45 @@ int ssd_scan_bwd(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt
                  ssd_tensor *dD, ssd_tensor *dinit_state, void *stream) {
   g_last_error.clear();
   ScanShape s;
-  SSD_CHECK(validate_scan(x, dt, dt_bias, A, B, C, D, init_state, dout, nullptr, 64, &s, "dout", false));
-  if (s.P > 64)
-    return fail(SSD_ERR_UNSUPPORTED, "backward: P=%lld not in {16,32,64}", (long long)s.P);
-  const int64_t sx[4] = {s.b, s.L, s.H, s.P}, sdt[3] = {s.b, s.L, s.H}, sh[1] = {s.H},
-                sbc[4] = {s.b, s.L, s.G, s.N}, sst[4] = {s.b, s.H, s.P, s.N};
-  if (dfinal_state) SSD_CHECK(check_tensor(dfinal_state, "dfinal_state", SSD_F32, 4, sst));
-  SSD_CHECK(check_tensor(dx, "dx", SSD_F32, 4, sx));
-  SSD_CHECK(check_tensor(ddt, "ddt", SSD_F32, 3, sdt));
-  if (ddt_bias) SSD_CHECK(check_tensor(ddt_bias, "ddt_bias", SSD_F32, 1, sh));
-  SSD_CHECK(check_tensor(dA, "dA", SSD_F32, 1, sh));
-  SSD_CHECK(check_tensor(dB, "dB", SSD_F32, 4, sbc));
-  SSD_CHECK(check_tensor(dC, "dC", SSD_F32, 4, sbc));
-  if (dD) SSD_CHECK(check_tensor(dD, "dD", SSD_F32, 1, sh));
-  if (dinit_state) SSD_CHECK(check_tensor(dinit_state, "dinit_state", SSD_F32, 4, sst));
-  const ssd_tensor *ts[] = {x, dt, dt_bias, A, B, C, D, init_state, dout, dfinal_state,
-                            dx, ddt, ddt_bias, dA, dB, dC, dD, dinit_state};
-  const char *nm[] = {"x", "dt", "dt_bias", "A", "B", "C", "D", "init_state", "dout", "dfinal_state",
-                      "dx", "ddt", "ddt_bias", "dA", "dB", "dC", "dD", "dinit_state"};
-  // no output may overlap an input or another output
-  for (int i = 10; i < 18; ++i) {
-    const Range ri = range_of(ts[i]);
-    for (int j = 0; j < 18; ++j)
-      if (j != i && overlap(ri, range_of(ts[j])))
-        return fail(SSD_ERR_ALIAS, "%s overlaps %s", nm[i], nm[j]);
-  }
-  SSD_CHECK(check_addressable(ts, nm, 18));
+  SSD_CHECK(validate_bwd(x, dt, dt_bias, A, B, C, D, init_state, dout, dfinal_state, dx, ddt, ddt_bias,
+                         dA, dB, dC, dD, dinit_state, nullptr, nullptr, s));
+  return run_bwd(x, dt, dt_bias, A, B, C, D, init_state, dout->data, dfinal_state, dx, ddt, ddt_bias, dA,
+                 dB, dC, dD, dinit_state, s, (hipStream_t)stream);
+}
 
-  const int64_t nc = (s.L + 63) / 64, PN = s.P * s.N, nbh = s.b * s.H;
-  auto al = [](size_t v) { return (v + 255) / 256 * 256; };
-  const size_t o_adj = al((size_t)(nbh * nc * PN) * 4);
-  const size_t o_part = o_adj + al((size_t)(nbh * nc * PN) * 4);
-  const size_t total = o_part + al((size_t)(nbh * nc * 3) * 4);
+int ssd_scan_bwd_gated(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bias,
+                       const ssd_tensor *A, const ssd_tensor *B, const ssd_tensor *C,
+                       const ssd_tensor *D, const ssd_tensor *z, const ssd_tensor *init_state,
+                       const ssd_tensor *dout, const ssd_tensor *dfinal_state, ssd_tensor *dx,
+                       ssd_tensor *ddt, ssd_tensor *ddt_bias, ssd_tensor *dA, ssd_tensor *dB,
+                       ssd_tensor *dC, ssd_tensor *dD, ssd_tensor *dz, ssd_tensor *dinit_state,
+                       void *stream) {
+  g_last_error.clear();
+  if (!z) return fail(SSD_ERR_NULL, "z: descriptor is NULL");
+  ScanShape s;
+  SSD_CHECK(validate_bwd(x, dt, dt_bias, A, B, C, D, init_state, dout, dfinal_state, dx, ddt, ddt_bias,
+                         dA, dB, dC, dD, dinit_state, z, dz, s));
   hipStream_t st = (hipStream_t)stream;
-  Scratch scratch(st);
+  // y (the scan output before the gate) and the gradient at it, in x's dtype
+  const size_t n = (size_t)(s.b * s.L * s.H * s.P), es = (size_t)elem_size(x->dtype);
+  const size_t half = (n * es + 255) / 256 * 256;
+  Scratch keep(st, 1);
   void *ws = nullptr;
-  SSD_CHECK(scratch.get(total, &ws));
-  char *base = (char *)ws;
-  ssd::BwdParams bp{};
-  bp.x = x->data; bp.dt = (const float *)dt->data;
-  bp.dt_bias = dt_bias ? (const float *)dt_bias->data : nullptr;
-  bp.A = (const float *)A->data; bp.B = B->data; bp.C = C->data;
-  bp.D = D ? (const float *)D->data : nullptr;
-  bp.dy = dout->data; bp.dfinal = dfinal_state ? (const float *)dfinal_state->data : nullptr;
-  bp.states_init = init_state ? (const float *)init_state->data : nullptr;
-  bp.states = (float *)base; bp.adj = (float *)(base + o_adj); bp.part = (float *)(base + o_part);
-  bp.dx = (float *)dx->data; bp.ddt = (float *)ddt->data; bp.dB = (float *)dB->data;
-  bp.dC = (float *)dC->data; bp.dA = (float *)dA->data;
-  bp.dD = dD ? (float *)dD->data : nullptr;
-  bp.ddt_bias = ddt_bias ? (float *)ddt_bias->data : nullptr;
-  bp.dinit = dinit_state ? (float *)dinit_state->data : nullptr;
-  bp.b = (int)s.b; bp.L = (int)s.L; bp.H = (int)s.H; bp.G = (int)s.G; bp.nc = (int)nc;
-  int status = SSD_OK;
-  const hipError_t e = ssd::launch_bwd(x->dtype, (int)s.P, (int)s.N, bp, st);
-  if (e != hipSuccess) status = hip_fail(e, "backward launch");
-  const int fs = scratch.finish();
+  SSD_CHECK(keep.get(2 * half, &ws));
+  ssd_tensor yt = *x;
+  yt.data = ws;
+  int status = scan_dispatch(x, dt, dt_bias, A, B, C, D, nullptr, init_state, &yt, nullptr, s, 256,
+                             SSD_ALGO_AUTO, stream);
+  void *dyg = (char *)ws + half;
+  if (status == SSD_OK) {
+    const hipError_t e = ssd::launch_gate_bwd(x->dtype, ws, z->data, dout->data, dyg, (float *)dz->data,
+                                              (int64_t)n, st);
+    if (e != hipSuccess) status = hip_fail(e, "gate backward launch");
+  }
+  if (status == SSD_OK)
+    status = run_bwd(x, dt, dt_bias, A, B, C, D, init_state, dyg, dfinal_state, dx, ddt, ddt_bias, dA, dB,
+                     dC, dD, dinit_state, s, st);
+  const int fs = keep.finish();
   return status != SSD_OK ? status : fs;
 }
 
@@ -876,7 +949,7 @@ int ssd_version(void) { return SSD_VERSION; }
 
 int ssd_release_scratch(void) {
   g_last_error.clear();
-  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  std::lock_guard<std::recursive_mutex> lock(g_scratch_mu);
   if (g_scratch.empty()) return SSD_OK;
   int cur = 0;
   hipError_t e = hipGetDevice(&cur);

@@ -1026,6 +1026,39 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
   }
 }
 
+// Gradient through the output gate out = y * silu(z): dy = dout * silu(z)
+// (stored in the input dtype, the backward's dout) and
+// dz = dout * y * silu'(z) with silu'(z) = s + z s (1 - s), s the logistic.
+// Four elements per thread (the element count is a multiple of 16).
+template <typename T> __device__ __forceinline__ void ld4(const T *p, float *v);
+template <> __device__ __forceinline__ void ld4<__bf16>(const __bf16 *p, float *v) {
+  const bf16x4 a = *reinterpret_cast<const bf16x4 *>(p);
+  v[0] = (float)a[0]; v[1] = (float)a[1]; v[2] = (float)a[2]; v[3] = (float)a[3];
+}
+template <> __device__ __forceinline__ void ld4<float>(const float *p, float *v) {
+  const float4 a = *reinterpret_cast<const float4 *>(p);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+}
+template <typename T>
+__global__ void __launch_bounds__(256) gate_bwd_kernel(const T *__restrict__ y, const T *__restrict__ z,
+                                                       const T *__restrict__ dout, T *__restrict__ dy,
+                                                       float *__restrict__ dz, int64_t n4) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  float yv[4], zv[4], gv[4], a[4], b[4];
+  ld4<T>(y + 4 * i, yv);
+  ld4<T>(z + 4 * i, zv);
+  ld4<T>(dout + 4 * i, gv);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float sg = __builtin_amdgcn_rcpf(1.f + hw_exp2(-zv[k] * kLog2e));
+    a[k] = gv[k] * zv[k] * sg;
+    b[k] = gv[k] * yv[k] * (sg + zv[k] * sg * (1.f - sg));
+  }
+  st4<T>(dy + 4 * i, a[0], a[1], a[2], a[3]);
+  *reinterpret_cast<float4 *>(dz + 4 * i) = make_float4(b[0], b[1], b[2], b[3]);
+}
+
 // dA, dD, d dt_bias per head: one workgroup per head sums the (batch, chunk)
 // partials, each thread a fixed strided subset, then a fixed shuffle tree and
 // a fixed order over the four waves, so the result is the same every run.
@@ -1102,6 +1135,19 @@ template <typename T> hipError_t launch_bwd_p(int P, int N, const BwdParams &p, 
 }
 
 } // namespace
+
+hipError_t launch_gate_bwd(int dtype, const void *y, const void *z, const void *dout, void *dy, float *dz,
+                           int64_t n, hipStream_t st) {
+  const int64_t n4 = n / 4;
+  const dim3 grid((unsigned)((n4 + 255) / 256));
+  if (dtype == 1)
+    hipLaunchKernelGGL(gate_bwd_kernel<__bf16>, grid, dim3(256), 0, st, (const __bf16 *)y, (const __bf16 *)z,
+                       (const __bf16 *)dout, (__bf16 *)dy, dz, n4);
+  else
+    hipLaunchKernelGGL(gate_bwd_kernel<float>, grid, dim3(256), 0, st, (const float *)y, (const float *)z,
+                       (const float *)dout, (float *)dy, dz, n4);
+  return hipGetLastError();
+}
 
 hipError_t launch_bwd(int dtype, int P, int N, const BwdParams &p, hipStream_t st) {
   return dtype == 1 ? launch_bwd_p<__bf16>(P, N, p, st) : launch_bwd_p<float>(P, N, p, st);

@@ -139,4 +139,8 @@ struct BwdParams {
 };
 // P in {16, 32, 64}, N in {16, 32, 64, 128}; dtype 1 = bf16, 0 = fp32.
 hipError_t launch_bwd(int dtype, int P, int N, const BwdParams &p, hipStream_t stream);
+// Gradient through the output gate: dy = dout * silu(z) in the input dtype,
+// dz = dout * y * silu'(z) in fp32; n elements, a multiple of 4.
+hipError_t launch_gate_bwd(int dtype, const void *y, const void *z, const void *dout, void *dy, float *dz,
+                           int64_t n, hipStream_t stream);
 } // namespace ssd

@@ -61,6 +61,8 @@ def lib():
         L.ssd_step.argtypes = [P] * 8 + [ctypes.c_void_p]
         L.ssd_scan_bwd.argtypes = [P] * 18 + [ctypes.c_void_p]
         L.ssd_scan_bwd.restype = ctypes.c_int
+        L.ssd_scan_bwd_gated.argtypes = [P] * 20 + [ctypes.c_void_p]
+        L.ssd_scan_bwd_gated.restype = ctypes.c_int
         L.ssd_step.restype = ctypes.c_int
         L.ssd_status_string.argtypes = [ctypes.c_int]
         L.ssd_status_string.restype = ctypes.c_char_p
@@ -167,6 +169,35 @@ def ssd_scan_bwd(x, dt, dt_bias, A, B, C, D, init_state, dout, dfinal_state=None
             describe(D), describe(init_state), describe(dout), describe(dfinal_state),
             describe(g["dx"]), describe(g["ddt"]), describe(g["ddt_bias"]), describe(g["dA"]),
             describe(g["dB"]), describe(g["dC"]), describe(g["dD"]), describe(g["dinit"]), st)
+    _check(status)
+    return g
+
+
+def ssd_scan_bwd_gated(x, dt, dt_bias, A, B, C, z, D, init_state, dout, dfinal_state=None, *,
+                       want_dt_bias: bool = True, want_D: bool = True, want_init: bool = True,
+                       out: dict = None, stream=None):
+    """Gradients of ssd_scan_fwd_gated (out = y * silu(z)); the dict of
+    ssd_scan_bwd plus dz (fp32)."""
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    dev = x.device
+    shapes = dict(dx=(b, L, H, P), ddt=(b, L, H), dA=(H,), dB=(b, L, G, N), dC=(b, L, G, N),
+                  ddt_bias=(H,) if want_dt_bias else None, dD=(H,) if want_D else None,
+                  dinit=(b, H, P, N) if want_init else None, dz=(b, L, H, P))
+    g = dict(out or {})
+    for k, shp in shapes.items():
+        if shp is not None and g.get(k) is None:
+            g[k] = torch.empty(shp, dtype=torch.float32, device=dev)
+        elif shp is None:
+            g[k] = None
+    with _on_device(x):
+        st = _stream(stream, x)
+        status = lib().ssd_scan_bwd_gated(
+            describe(x), describe(dt), describe(dt_bias), describe(A), describe(B), describe(C),
+            describe(D), describe(z), describe(init_state), describe(dout), describe(dfinal_state),
+            describe(g["dx"]), describe(g["ddt"]), describe(g["ddt_bias"]), describe(g["dA"]),
+            describe(g["dB"]), describe(g["dC"]), describe(g["dD"]), describe(g["dz"]),
+            describe(g["dinit"]), st)
     _check(status)
     return g
 

@@ -461,3 +461,48 @@ def test_bwd_host_memory_refused(ssd):
     # (with no device present the refusal names the missing device instead)
     st, msg = _call_bwd(ssd, _bwd_args())
     assert st == 4 and msg, (st, msg)
+
+
+GATED_ORDER = ["x", "dt", "dt_bias", "A", "B", "C", "D", "z", "init_state", "dout", "dfinal_state",
+               "dx", "ddt", "ddt_bias", "dA", "dB", "dC", "dD", "dz", "dinit_state"]
+
+
+def _gated_bwd_args():
+    a = _bwd_args()
+    a.update(z=torch.zeros(1, 100, 4, 32, dtype=torch.bfloat16), dz=torch.zeros(1, 100, 4, 32))
+    return a
+
+
+def _call_gated_bwd(ssd, a):
+    d = ssd.describe
+    st = ssd.lib().ssd_scan_bwd_gated(*[d(a[k]) for k in GATED_ORDER], None)
+    return st, ssd.ssd_last_error()
+
+
+GATED_BWD_CASES = [
+    ("z_none", lambda a: a.update(z=None), 1),
+    ("dz_none", lambda a: a.update(dz=None), 1),
+    ("z_dtype", lambda a: a.update(z=torch.zeros(1, 100, 4, 32)), 3),
+    ("dz_bf16", lambda a: a.update(dz=torch.zeros(1, 100, 4, 32, dtype=torch.bfloat16)), 3),
+    ("dz_shape", lambda a: a.update(dz=torch.zeros(1, 100, 4, 16)), 2),
+    ("dz_aliases_dx", lambda a: a.update(dz=a["dx"]), 6),
+    ("dx_aliases_z_storage", lambda a: a.update(dx=torch.zeros(1, 100, 4, 32), z=None), 1),
+]
+
+
+@pytest.mark.parametrize("name,mutate,status", GATED_BWD_CASES, ids=[c[0] for c in GATED_BWD_CASES])
+def test_gated_bwd_rejects(ssd, name, mutate, status):
+    a = _gated_bwd_args()
+    mutate(a)
+    st, msg = _call_gated_bwd(ssd, a)
+    assert st == status, (st, msg)
+    assert msg
+
+
+def test_gated_bwd_output_overlapping_z(ssd):
+    a = _gated_bwd_args()
+    buf = torch.zeros(2 * 100 * 4 * 32)
+    a["dz"] = buf[: 100 * 4 * 32].view(1, 100, 4, 32)
+    a["z"] = torch.zeros(1, 100, 4, 32, dtype=torch.bfloat16)
+    a["dx"] = buf[100 * 4 * 32 - 64: 2 * 100 * 4 * 32 - 64].view(1, 100, 4, 32)  # overlaps dz
+    assert _call_gated_bwd(ssd, a)[0] == 6

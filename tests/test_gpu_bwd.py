@@ -159,3 +159,28 @@ def test_bwd_degenerate(kind):
     ref = ref_grads(si, dy, df)
     for k in NAMES:
         check(got[k], ref[k], 1e-4, "%s %s" % (kind, k))
+
+
+GATED_CASES = [
+    (2, 150, 4, 32, 2, 64, inputs.F32),
+    (2, 300, 4, 64, 1, 128, inputs.BF16),
+    (1, 70, 2, 16, 1, 16, inputs.BF16),
+]
+
+
+@pytest.mark.parametrize("b,L,H,P,G,N,dtype", GATED_CASES, ids=["b%dL%dH%dP%dG%dN%d%s" % c for c in GATED_CASES])
+def test_bwd_gated(b, L, H, P, G, N, dtype):
+    say("bwd gated", b, L, H, P, G, N, dtype)
+    si = inputs.make_scan(b, L, H, P, G, N, dtype=dtype, seed=110 + L, init_std=0.3)
+    z = inputs.make_gate(si, seed=111)
+    dy, df = make_grads_in(si, 112)
+    t = staging.scan_tensors(si, DEV)
+    zt = staging.tensor(z, si.dtype, DEV)
+    g = ssd.ssd_scan_bwd_gated(**t, z=zt, dout=dy.to(DEV), dfinal_state=df.to(DEV))
+    torch.cuda.synchronize()
+    got = {k: v.double().cpu().numpy() for k, v in g.items() if v is not None}
+    a = si.f64()
+    ref = oracle.scan_bwd_gated(a["x"], a["dt"], a["dt_bias"], a["A"], a["B"], a["C"], inputs.to_f64(z, si.dtype),
+                                a["D"], a["init"], dy.double().numpy(), df.double().numpy())
+    for k in NAMES + ["dz"]:
+        check(got[k], ref[k], TOL[dtype], "gated " + k)
