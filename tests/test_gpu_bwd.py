@@ -184,3 +184,14 @@ def test_bwd_gated(b, L, H, P, G, N, dtype):
                                 a["D"], a["init"], dy.double().numpy(), df.double().numpy())
     for k in NAMES + ["dz"]:
         check(got[k], ref[k], TOL[dtype], "gated " + k)
+
+
+def test_bwd_long_sequence():
+    # L = 2^18: 4096 chunks through both state walks
+    si = inputs.make_scan(1, 1 << 18, 2, 32, 1, 32, dtype=inputs.BF16, seed=120, init_std=0.3)
+    dy, df = make_grads_in(si, 121)
+    say("bwd long sequence, L = 2^18")
+    got = run(si, dy, df)
+    ref = ref_grads(si, dy, df)
+    for k in NAMES:
+        check(got[k], ref[k], 2e-2, "long " + k)
