@@ -92,3 +92,38 @@ def test_release_between_calls():
         check(staging.to_f64(out), ref[0], "y")
         check(staging.to_f64(fin), ref[1], "final")
     ssd.ssd_release_scratch()           # nothing kept: no-op
+
+
+def test_two_host_threads():
+    # two host threads, each queueing scans on its own stream at the same time
+    # (the C calls run without the interpreter lock): every result matches
+    import threading
+    cases = [scan_case(2000 + 300 * k, 130 + k) for k in range(2)]
+    torch.cuda.synchronize()
+    results = [[], []]
+    errors = []
+
+    def worker(k):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for rep in range(6):
+                    algo = ssd.SSD_ALGO_ROWS if rep % 2 == 0 else ssd.SSD_ALGO_CHUNKED
+                    results[k].append(ssd.ssd_scan_fwd(**cases[k][1], algo=algo, chunk=256))
+            s.synchronize()
+        except Exception as e:  # reported below
+            errors.append(e)
+
+    say("two host threads")
+    th = [threading.Thread(target=worker, args=(k,)) for k in range(2)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for k in range(2):
+        assert len(results[k]) == 6
+        for out, fin in results[k]:
+            check(staging.to_f64(out), cases[k][2][0], "thread %d y" % k)
+            check(staging.to_f64(fin), cases[k][2][1], "thread %d final" % k)
