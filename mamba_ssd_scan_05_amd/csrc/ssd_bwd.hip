@@ -4,8 +4,8 @@
 // inputs.  The Mamba paper-reading notes (sxlin0.github.io, the section on
 // the hardware-aware selective scan) describe the backward pass as
 // recomputing the states it needs instead of keeping them from the forward
-// pass; here the states at 64-token chunk boundaries are recomputed by the
-// forward chunk walk, and everything inside a chunk is rebuilt on chip.
+// pass; here the states at 64-token chunk boundaries are recomputed by a
+// walk over the chunks, and everything inside a chunk is rebuilt on chip.
 //
 // Notation per (batch, head), chunk of Q = 64 tokens starting at t0, local
 // index i: a_i = Delta_i A (log decay), cum_i = a_0 + ... + a_i,
@@ -36,17 +36,19 @@
 // G_{c-1} = exp(cum_last^(c)) G_c + sum_i e_in_i dy_i C_i^T; the gradient of
 // the initial state is the last of these, G_{-1}.
 //
-// Kernels: bwd_state_scan_kernel (both recursions, one workgroup per
-// (batch, head) walking the chunks with the state in matrix-core
-// accumulators), bwd_chunk_kernel (one workgroup per (batch, group, chunk),
-// all heads of the group in turn: dB and dC stay in registers across heads,
-// so no atomics and a fixed summation order), bwd_param_kernel (sums of the
-// per-(batch, head, chunk) partials of dA, dD and d dt_bias).
+// Kernels: bwd_state_scan_kernel / _bf16 (both recursions, one workgroup
+// per (batch, head) walking the chunks with the state in matrix-core
+// accumulators), bwd_chunk_kernel / bwd_chunk_bf16_kernel (one workgroup per
+// (batch, group, chunk), all heads of the group in turn: dB and dC stay in
+// registers across heads, so no atomics and a fixed summation order),
+// bwd_param_kernel (sums of the per-(batch, head, chunk) partials of dA, dD
+// and d dt_bias), gate_bwd_kernel (the output gate's derivative, for the
+// gated call).
 //
 // Matrix products run on the matrix cores: for fp32 inputs in fp32 (16x16x4
 // MFMA) from fp32 LDS tiles; for bf16 inputs in bf16 (16x16x32 MFMA), with
-// every fp32 operand carried as a bf16 high part plus a bf16 remainder
-// (bwd_chunk_bf16_kernel).
+// every fp32 operand carried as a bf16 high part plus a bf16 remainder (the
+// _bf16 kernels).
 #include "ssd_device.h"
 #include "ssd_internal.h"
 
@@ -170,15 +172,18 @@ template <typename T, int COLS> struct RowPrefetch {
   }
 };
 
+template <typename T, int P, int N> struct StateScanLds {
+  float sL[kQ * (P + 4)]; // x (forward) or dy (reverse), [token][p]
+  float sR[kQ * (N + 4)]; // B (forward) or C (reverse), [token][n]
+  float sW[kQ];
+  float sTot[1];
+};
 template <typename T, int P, int N, bool REV>
-__global__ void __launch_bounds__(256) bwd_state_scan_kernel(const BwdParams p) {
+__device__ __forceinline__ void state_scan_body(const BwdParams &p, int bh, StateScanLds<T, P, N> &lds) {
   constexpr int LX = P + 4, LB = N + 4, PT = P / 16, NT = N / 16, TILES = (PT * NT + 3) / 4;
-  __shared__ __attribute__((aligned(16))) float sL[kQ * LX]; // x (forward) or dy (reverse), [token][p]
-  __shared__ __attribute__((aligned(16))) float sR[kQ * LB]; // B (forward) or C (reverse), [token][n]
-  __shared__ float sW[kQ];
-  __shared__ float sTot[1];
+  float *sL = lds.sL, *sR = lds.sR, *sW = lds.sW, *sTot = lds.sTot;
   const int nc = p.nc, H = p.H, G = p.G, L = p.L;
-  const int bh = blockIdx.x, b_ = bh / H, h = bh % H, g = (int)(((int64_t)h * G) / H);
+  const int b_ = bh / H, h = bh % H, g = (int)(((int64_t)h * G) / H);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
   const int PN = P * N;
   const T *lsrc = reinterpret_cast<const T *>(REV ? p.dy : p.x) + ((int64_t)b_ * L * H + h) * P;
@@ -259,6 +264,17 @@ __global__ void __launch_bounds__(256) bwd_state_scan_kernel(const BwdParams p) 
       for (int r = 0; r < 4; ++r) p.dinit[(int64_t)bh * PN + (pt * 16 + 4 * lg + r) * N + nt * 16 + li] = S[k][r];
     }
   }
+}
+
+// Both walks in one launch: blocks [0, b*H) walk forward, [b*H, 2*b*H) backward.
+template <typename T, int P, int N>
+__global__ void __launch_bounds__(256) bwd_state_scan_kernel(const BwdParams p) {
+  __shared__ __attribute__((aligned(16))) StateScanLds<T, P, N> lds;
+  const int nbh = p.b * p.H;
+  if ((int)blockIdx.x < nbh)
+    state_scan_body<T, P, N, false>(p, blockIdx.x, lds);
+  else
+    state_scan_body<T, P, N, true>(p, blockIdx.x - nbh, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -619,16 +635,20 @@ __device__ __forceinline__ float stage_state_split(__bf16 *hi, __bf16 *lo, int l
 // The same walk for bf16 inputs on the bf16 matrix cores: the weighted
 // input w_j x_j (fp32) is kept as a bf16 high part plus a bf16 remainder,
 // B or C are exact in bf16, and each product is two 16x16x32 MFMAs.
+template <int P, int N> struct StateScanBf16Lds {
+  __bf16 sLh[kQ * tr_ld(P, 2)];
+  __bf16 sLl[kQ * tr_ld(P, 2)];
+  __bf16 sR[kQ * tr_ld(N, 2)];
+  float sW[kQ];
+  float sTot[1];
+};
 template <int P, int N, bool REV>
-__global__ void __launch_bounds__(256) bwd_state_scan_bf16_kernel(const BwdParams p) {
+__device__ __forceinline__ void state_scan_bf16_body(const BwdParams &p, int bh, StateScanBf16Lds<P, N> &lds) {
   constexpr int LX = tr_ld(P, 2), LB = tr_ld(N, 2), PT = P / 16, NT = N / 16, TILES = (PT * NT + 3) / 4;
-  __shared__ __attribute__((aligned(16))) __bf16 sLh[kQ * LX];
-  __shared__ __attribute__((aligned(16))) __bf16 sLl[kQ * LX];
-  __shared__ __attribute__((aligned(16))) __bf16 sR[kQ * LB];
-  __shared__ float sW[kQ];
-  __shared__ float sTot[1];
+  __bf16 *sLh = lds.sLh, *sLl = lds.sLl, *sR = lds.sR;
+  float *sW = lds.sW, *sTot = lds.sTot;
   const int nc = p.nc, H = p.H, G = p.G, L = p.L;
-  const int bh = blockIdx.x, b_ = bh / H, h = bh % H, g = (int)(((int64_t)h * G) / H);
+  const int b_ = bh / H, h = bh % H, g = (int)(((int64_t)h * G) / H);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
   const int PN = P * N;
   const __bf16 *lsrc = reinterpret_cast<const __bf16 *>(REV ? p.dy : p.x) + ((int64_t)b_ * L * H + h) * P;
@@ -718,6 +738,16 @@ __global__ void __launch_bounds__(256) bwd_state_scan_bf16_kernel(const BwdParam
       for (int r = 0; r < 4; ++r) p.dinit[(int64_t)bh * PN + (pt * 16 + 4 * lg + r) * N + nt * 16 + li] = S[k][r];
     }
   }
+}
+
+template <int P, int N>
+__global__ void __launch_bounds__(256) bwd_state_scan_bf16_kernel(const BwdParams p) {
+  __shared__ __attribute__((aligned(16))) StateScanBf16Lds<P, N> lds;
+  const int nbh = p.b * p.H;
+  if ((int)blockIdx.x < nbh)
+    state_scan_bf16_body<P, N, false>(p, blockIdx.x, lds);
+  else
+    state_scan_bf16_body<P, N, true>(p, blockIdx.x - nbh, lds);
 }
 
 template <int P, int N>
@@ -1092,18 +1122,13 @@ __global__ void __launch_bounds__(256) bwd_param_kernel(const float *__restrict_
 }
 
 template <typename T, int P, int N> hipError_t launch_bwd_t(const BwdParams &p, hipStream_t st) {
-  const dim3 grid_bh((unsigned)(p.b * p.H));
+  // the forward and the backward state walks, together in one launch
+  const dim3 grid_bh((unsigned)(2 * p.b * p.H));
   if constexpr (sizeof(T) == 2)
-    hipLaunchKernelGGL((bwd_state_scan_bf16_kernel<P, N, false>), grid_bh, dim3(256), 0, st, p);
+    hipLaunchKernelGGL((bwd_state_scan_bf16_kernel<P, N>), grid_bh, dim3(256), 0, st, p);
   else
-    hipLaunchKernelGGL((bwd_state_scan_kernel<T, P, N, false>), grid_bh, dim3(256), 0, st, p);
+    hipLaunchKernelGGL((bwd_state_scan_kernel<T, P, N>), grid_bh, dim3(256), 0, st, p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if constexpr (sizeof(T) == 2)
-    hipLaunchKernelGGL((bwd_state_scan_bf16_kernel<P, N, true>), grid_bh, dim3(256), 0, st, p);
-  else
-    hipLaunchKernelGGL((bwd_state_scan_kernel<T, P, N, true>), grid_bh, dim3(256), 0, st, p);
-  e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (sizeof(T) == 2)
     hipLaunchKernelGGL((bwd_chunk_bf16_kernel<P, N>), dim3((unsigned)(p.b * p.G * p.nc)), dim3(512), 0, st, p);
