@@ -614,9 +614,9 @@ __device__ __forceinline__ void stage_bf16(__bf16 *dst, int ld, const __bf16 *sr
 // of <state, other> when `other` is given (exact fp32 values from global)
 template <int N>
 __device__ __forceinline__ float stage_state_split(__bf16 *hi, __bf16 *lo, int ld, const float *src,
-                                                   const float *other, int PN, int tid) {
+                                                   const float *other, int PN, int tid, int nthreads) {
   float dot = 0.f;
-  for (int idx = tid; idx < PN / 4; idx += 512) {
+  for (int idx = tid; idx < PN / 4; idx += nthreads) {
     const int r = (idx * 4) / N, col = (idx * 4) % N;
     const float4 v = reinterpret_cast<const float4 *>(src)[idx];
     if (other) {
@@ -764,9 +764,12 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
   __shared__ __attribute__((aligned(16))) __bf16 sMl[kQ * LQ];
   __shared__ __attribute__((aligned(16))) __bf16 sSh[PP * LS];
   __shared__ __attribute__((aligned(16))) __bf16 sSl[PP * LS];
-  __shared__ float sCum[kQ], sDel[kQ], sEin[kQ], sEout[kQ], sSig[kQ];
+  // per-token decay quantities, double-buffered: the next head's are formed
+  // while the current head finishes
+  __shared__ float sCumB[2][kQ], sDelB[2][kQ], sEinB[2][kQ], sEoutB[2][kQ], sSigB[2][kQ];
   __shared__ float rowW[2][kQ], colW[4][kQ], uP[2][kQ], vP[2][kQ], dinP[2][kQ], sDiag[kQ];
-  __shared__ float sRed[9]; // [0]: log2 decay of the chunk; [1 + w]: wave w's share of <G, H>
+  __shared__ float sRed[9]; // [1 + w]: wave w's share of <G, H>
+  __shared__ float sLast[2]; // log2 decay of the chunk, per decay buffer
 
   const int nc = p.nc, G = p.G, H = p.H, L = p.L;
   const int c = blockIdx.x % nc;
@@ -808,27 +811,37 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
     dCacc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  // decays of head hh into buffer q (one wave), and x, dy, the entering state
+  // of head hh into LDS (threads [t_lo, t_lo + nt))
+  auto decay_of = [&](int hh, int q) {
+    const ChunkDecay d = chunk_decay(p.dt, p.dt_bias, p.A, b_, L, H, hh, t0, lane);
+    sCumB[q][lane] = d.cum2;
+    sDelB[q][lane] = d.delta;
+    sEinB[q][lane] = d.e_in;
+    sEoutB[q][lane] = d.e_out;
+    sSigB[q][lane] = d.sig;
+    if (lane == 0) sLast[q] = d.cum2_last;
+  };
+  auto stage_head = [&](int hh, int t_lo, int nt) {
+    const __bf16 *xh = reinterpret_cast<const __bf16 *>(p.x) + (((int64_t)b_ * L + t0) * H + hh) * P;
+    const __bf16 *dyh = reinterpret_cast<const __bf16 *>(p.dy) + (((int64_t)b_ * L + t0) * H + hh) * P;
+    stage_bf16(sX, LX, xh, (int64_t)H * P, kQ, nv, P, tid - t_lo, nt);
+    stage_bf16(sDY, LX, dyh, (int64_t)H * P, kQ, nv, P, tid - t_lo, nt);
+    stage_state_split<N>(sSh, sSl, LS, p.states + (((int64_t)b_ * H + hh) * nc + c) * PN, nullptr, PN,
+                         tid - t_lo, nt);
+  };
+  if (w == 0) decay_of(g * hpg, 0);
+  stage_head(g * hpg, 0, 512);
+  __syncthreads();
+
   for (int h = g * hpg; h < (g + 1) * hpg; ++h) {
     const int64_t bh = (int64_t)b_ * H + h;
     const float Ah = p.A[h], Dh = p.D ? p.D[h] : 0.f;
-    if (w == 0) {
-      const ChunkDecay d = chunk_decay(p.dt, p.dt_bias, p.A, b_, L, H, h, t0, lane);
-      sCum[lane] = d.cum2;
-      sDel[lane] = d.delta;
-      sEin[lane] = d.e_in;
-      sEout[lane] = d.e_out;
-      sSig[lane] = d.sig;
-      if (lane == 0) sRed[0] = d.cum2_last;
-    }
-    const __bf16 *xh = reinterpret_cast<const __bf16 *>(p.x) + (((int64_t)b_ * L + t0) * H + h) * P;
-    const __bf16 *dyh = reinterpret_cast<const __bf16 *>(p.dy) + (((int64_t)b_ * L + t0) * H + h) * P;
-    stage_bf16(sX, LX, xh, (int64_t)H * P, kQ, nv, P, tid, 512);
-    stage_bf16(sDY, LX, dyh, (int64_t)H * P, kQ, nv, P, tid, 512);
+    const int cur = (h - g * hpg) & 1;
+    float *sCum = sCumB[cur], *sDel = sDelB[cur], *sEin = sEinB[cur], *sEout = sEoutB[cur], *sSig = sSigB[cur];
     const float *Hs = p.states + (bh * nc + c) * PN;
     const float *Gs = p.adj + (bh * nc + c) * PN;
-    stage_state_split<N>(sSh, sSl, LS, Hs, nullptr, PN, tid);
-    __syncthreads();
-    const float cum_last2 = sRed[0];
+    const float cum_last2 = sLast[cur];
 
     // --- DX = dY X^T, M = S o E (split to LDS), P2 = DX o E, W sums, diag(DX)
     f32x4 P2[2];
@@ -895,7 +908,7 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
 
     // --- replace H by G; <G, H> from the fp32 values in global memory
     {
-      const float gh = wave_sum(stage_state_split<N>(sSh, sSl, LS, Gs, Hs, PN, tid));
+      const float gh = wave_sum(stage_state_split<N>(sSh, sSl, LS, Gs, Hs, PN, tid, 512));
       if (lane == 0) sRed[1 + w] = gh;
     }
     __syncthreads();
@@ -1008,8 +1021,14 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
       dCacc[k] = acc;
     }
 
-    // --- da, ddt and the head's partial sums (wave 0, lane k = token)
-    if (w == 0) {
+    // --- da, ddt and the head's partial sums (wave 0, lane k = token); wave 1
+    //     forms the next head's decays, waves 2..7 stage its x, dy and state
+    if (w != 0) {
+      if (h + 1 < (g + 1) * hpg) {
+        if (w == 1) decay_of(h + 1, cur ^ 1);
+        else stage_head(h + 1, 128, 384);
+      }
+    } else {
       const int k = lane;
       const float colsum = colW[0][k] + colW[1][k] + colW[2][k] + colW[3][k];
       const float rowsum = rowW[0][k] + rowW[1][k];
