@@ -764,6 +764,9 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
   __shared__ __attribute__((aligned(16))) __bf16 sMl[kQ * LQ];
   __shared__ __attribute__((aligned(16))) __bf16 sSh[PP * LS];
   __shared__ __attribute__((aligned(16))) __bf16 sSl[PP * LS];
+  // G of the coming head, fp32 [P][N], copied straight from global memory to
+  // LDS (buffer loads to LDS, 1 KiB per wave instruction) ahead of its use
+  __shared__ __attribute__((aligned(16))) float sGst[P * N];
   // per-token decay quantities, double-buffered: the next head's are formed
   // while the current head finishes
   __shared__ float sCumB[2][kQ], sDelB[2][kQ], sEinB[2][kQ], sEoutB[2][kQ], sSigB[2][kQ];
@@ -830,8 +833,17 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
     stage_state_split<N>(sSh, sSl, LS, p.states + (((int64_t)b_ * H + hh) * nc + c) * PN, nullptr, PN,
                          tid - t_lo, nt);
   };
+  // G of head hh into sGst: 1 KiB pieces q = w - w_lo, w - w_lo + nw, ...
+  auto fetch_g = [&](int hh, int w_lo, int nw) {
+    const float *Gn = p.adj + (((int64_t)b_ * H + hh) * nc + c) * PN;
+    const auto rs = make_rsrc(Gn, (uint32_t)PN * 4u);
+    for (int q = w - w_lo; q < PN / 256; q += nw)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(sGst + q * 256), 16,
+                                               q * 1024 + lane * 16, 0, 0, 0);
+  };
   if (w == 0) decay_of(g * hpg, 0);
   stage_head(g * hpg, 0, 512);
+  fetch_g(g * hpg, 0, 8);
   __syncthreads();
 
   for (int h = g * hpg; h < (g + 1) * hpg; ++h) {
@@ -839,8 +851,6 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
     const float Ah = p.A[h], Dh = p.D ? p.D[h] : 0.f;
     const int cur = (h - g * hpg) & 1;
     float *sCum = sCumB[cur], *sDel = sDelB[cur], *sEin = sEinB[cur], *sEout = sEoutB[cur], *sSig = sSigB[cur];
-    const float *Hs = p.states + (bh * nc + c) * PN;
-    const float *Gs = p.adj + (bh * nc + c) * PN;
     const float cum_last2 = sLast[cur];
 
     // --- DX = dY X^T, M = S o E (split to LDS), P2 = DX o E, W sums, diag(DX)
@@ -906,9 +916,22 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
     }
     __syncthreads();
 
-    // --- replace H by G; <G, H> from the fp32 values in global memory
+    // --- replace H by G (already in LDS); <G, H> with H from its two planes
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
     {
-      const float gh = wave_sum(stage_state_split<N>(sSh, sSl, LS, Gs, Hs, PN, tid, 512));
+      float gh = 0.f;
+      for (int idx = tid; idx < PN / 4; idx += 512) {
+        const int r = (idx * 4) / N, col = (idx * 4) % N, off = r * LS + col;
+        const float4 gv = *reinterpret_cast<const float4 *>(sGst + 4 * idx);
+        const float gq[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          gh += gq[q] * ((float)sSh[off + q] + (float)sSl[off + q]);
+          put_split(sSh, sSl, off + q, gq[q]);
+        }
+      }
+      gh = wave_sum(gh);
       if (lane == 0) sRed[1 + w] = gh;
     }
     __syncthreads();
@@ -1025,8 +1048,12 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
     //     forms the next head's decays, waves 2..7 stage its x, dy and state
     if (w != 0) {
       if (h + 1 < (g + 1) * hpg) {
-        if (w == 1) decay_of(h + 1, cur ^ 1);
-        else stage_head(h + 1, 128, 384);
+        if (w == 1) {
+          decay_of(h + 1, cur ^ 1);
+        } else {
+          stage_head(h + 1, 128, 384);
+          fetch_g(h + 1, 2, 6);
+        }
       }
     } else {
       const int k = lane;
