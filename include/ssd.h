@@ -290,8 +290,9 @@ int ssd_selective_scan_fwd(const ssd_tensor *x, const ssd_tensor *dt,
  * output (SSD_ERR_ALIAS).  Arithmetic in fp32 (matrix products on the
  * matrix cores from fp32 operands).  Sums over heads, chunks and batch run
  * in a fixed order, so the result does not vary from run to run.  Scratch:
- * b*H*(L + 2*ceil(L/64)*P*N) floats and a little more (see Scratch above;
- * above 256 MiB it is allocated per call).
+ * b*H*ceil(L/64)*(2*P*N + 3) floats (the states entering each 64-token chunk,
+ * the gradients at each chunk's end, per-chunk partial sums; see Scratch
+ * above: above 256 MiB it is allocated per call).
  */
 int ssd_scan_bwd(const ssd_tensor *x, const ssd_tensor *dt,
                  const ssd_tensor *dt_bias, const ssd_tensor *A,
