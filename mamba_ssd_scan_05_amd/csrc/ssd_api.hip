@@ -621,10 +621,18 @@ int run_bwd(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bias
             ssd_tensor *dC, ssd_tensor *dD, ssd_tensor *dinit_state, const ScanShape &s,
             hipStream_t st) {
   const int64_t nc = (s.L + 63) / 64, PN = s.P * s.N, nbh = s.b * s.H;
+  // the two state walks run as 2*b*H*nseg workgroups: cut the sequence into
+  // segments when b*H alone would leave the GPU short of work
+  const int64_t seg_chunks = (nc + std::min<int64_t>(nc, std::max<int64_t>(1, (256 + nbh - 1) / nbh)) - 1) /
+                             std::min<int64_t>(nc, std::max<int64_t>(1, (256 + nbh - 1) / nbh));
+  const int64_t nseg = (nc + seg_chunks - 1) / seg_chunks;
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
   const size_t o_adj = al((size_t)(nbh * nc * PN) * 4);
   const size_t o_part = o_adj + al((size_t)(nbh * nc * PN) * 4);
-  const size_t total = o_part + al((size_t)(nbh * nc * 3) * 4);
+  const size_t o_pre = o_part + al((size_t)(nbh * nc * 3) * 4);
+  const size_t o_seg = o_pre + 2 * al((size_t)(nbh * nc) * 4);
+  const size_t o_sdec = o_seg + 2 * al((size_t)(nbh * nseg * PN) * 4);
+  const size_t total = o_sdec + 2 * al((size_t)(nbh * nseg) * 4) + al((size_t)nbh * 4);
   Scratch scratch(st);
   void *ws = nullptr;
   SSD_CHECK(scratch.get(total, &ws));
@@ -637,6 +645,11 @@ int run_bwd(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bias
   bp.dy = dout; bp.dfinal = dfinal_state ? (const float *)dfinal_state->data : nullptr;
   bp.states_init = init_state ? (const float *)init_state->data : nullptr;
   bp.states = (float *)base; bp.adj = (float *)(base + o_adj); bp.part = (float *)(base + o_part);
+  bp.nseg = (int)nseg; bp.seg_chunks = (int)seg_chunks;
+  bp.fpre = (float *)(base + o_pre); bp.rpre = (float *)(base + o_pre + al((size_t)(nbh * nc) * 4));
+  bp.segend_f = (float *)(base + o_seg); bp.segend_r = (float *)(base + o_seg + al((size_t)(nbh * nseg * PN) * 4));
+  bp.segdec_f = (float *)(base + o_sdec); bp.segdec_r = (float *)(base + o_sdec + al((size_t)(nbh * nseg) * 4));
+  bp.rdec0 = (float *)(base + o_sdec + 2 * al((size_t)(nbh * nseg) * 4));
   bp.dx = (float *)dx->data; bp.ddt = (float *)ddt->data; bp.dB = (float *)dB->data;
   bp.dC = (float *)dC->data; bp.dA = (float *)dA->data;
   bp.dD = dD ? (float *)dD->data : nullptr;

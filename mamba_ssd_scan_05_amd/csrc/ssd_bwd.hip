@@ -179,7 +179,7 @@ template <typename T, int P, int N> struct StateScanLds {
   float sTot[1];
 };
 template <typename T, int P, int N, bool REV>
-__device__ __forceinline__ void state_scan_body(const BwdParams &p, int bh, StateScanLds<T, P, N> &lds) {
+__device__ __forceinline__ void state_scan_body(const BwdParams &p, int bh, int sg, StateScanLds<T, P, N> &lds) {
   constexpr int LX = P + 4, LB = N + 4, PT = P / 16, NT = N / 16, TILES = (PT * NT + 3) / 4;
   float *sL = lds.sL, *sR = lds.sR, *sW = lds.sW, *sTot = lds.sTot;
   const int nc = p.nc, H = p.H, G = p.G, L = p.L;
@@ -190,6 +190,13 @@ __device__ __forceinline__ void state_scan_body(const BwdParams &p, int bh, Stat
   const T *rsrc = reinterpret_cast<const T *>(REV ? p.C : p.B) + ((int64_t)b_ * L * G + g) * N;
   const float *s0 = REV ? p.dfinal : p.states_init;
   float *out = (REV ? p.adj : p.states) + (int64_t)bh * nc * PN;
+  // this workgroup's segment of chunks [c_lo, c_hi).  One segment starts
+  // from init (forward) / dfinal (reverse); with several, every segment
+  // starts from zero and the fold over segments carries init / dfinal in
+  const int nseg = p.nseg, c_lo = sg * p.seg_chunks, c_hi = min(nc, c_lo + p.seg_chunks);
+  const int nsteps = c_hi - c_lo;
+  const bool from_s0 = nseg == 1;
+  float acc_dec = 0.f; // log2 decay walked so far in the segment (wave 0, lane 0)
 
   f32x4 S[TILES];
 #pragma unroll
@@ -198,7 +205,7 @@ __device__ __forceinline__ void state_scan_body(const BwdParams &p, int bh, Stat
       if (tile >= PT * NT) break;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      S[k][r] = s0 ? s0[(int64_t)bh * PN + (pt * 16 + 4 * lg + r) * N + nt * 16 + li] : 0.f;
+      S[k][r] = (s0 && from_s0) ? s0[(int64_t)bh * PN + (pt * 16 + 4 * lg + r) * N + nt * 16 + li] : 0.f;
   }
 
   RowPrefetch<T, P> pl;
@@ -210,9 +217,9 @@ __device__ __forceinline__ void state_scan_body(const BwdParams &p, int bh, Stat
     pr.load(rsrc + (int64_t)t0 * G * N, (int64_t)G * N, nv, tid);
     if (w == 0) dtv = load_dt(p.dt, b_, L, H, h, t0, lane);
   };
-  fetch(REV ? nc - 1 : 0);
-  for (int step = 0; step < nc; ++step) {
-    const int c = REV ? nc - 1 - step : step;
+  fetch(REV ? c_hi - 1 : c_lo);
+  for (int step = 0; step < nsteps; ++step) {
+    const int c = REV ? c_hi - 1 - step : c_lo + step;
     // the state at this chunk boundary
 #pragma unroll
     for (int k = 0; k < TILES; ++k) {
@@ -227,9 +234,13 @@ __device__ __forceinline__ void state_scan_body(const BwdParams &p, int bh, Stat
       const ChunkDecay d = chunk_decay_v(dtv, p.dt_bias, p.A, L, h, c * kQ, lane);
       sW[lane] = REV ? d.e_in : d.e_out * d.delta;
       if (lane == 0) sTot[0] = hw_exp2(d.cum2_last);
+      if (lane == 0 && nseg > 1) {
+        (REV ? p.rpre : p.fpre)[(int64_t)bh * nc + c] = acc_dec;
+        acc_dec += d.cum2_last;
+      }
     }
     __syncthreads();
-    if (step + 1 < nc) fetch(REV ? c - 1 : c + 1);
+    if (step + 1 < nsteps) fetch(REV ? c - 1 : c + 1);
     const float tot = sTot[0];
     float wk[2][8];
 #pragma unroll
@@ -255,26 +266,45 @@ __device__ __forceinline__ void state_scan_body(const BwdParams &p, int bh, Stat
     }
     __syncthreads();
   }
-  if (REV && p.dinit) {
+  // the state left at the end of the walk: with one segment, the reverse one
+  // is the initial-state gradient; with several, every segment's goes to the
+  // fold (reverse segments in reversed order), with the segment's log2 decay,
+  // and segment 0's reverse one also to dinit (the fold's carry is added later)
+  float *dst0 = nullptr, *dst1 = nullptr;
+  if (nseg > 1) {
+    const int slot = REV ? nseg - 1 - sg : sg;
+    dst0 = (REV ? p.segend_r : p.segend_f) + ((int64_t)bh * nseg + slot) * PN;
+    if (w == 0 && lane == 0) {
+      (REV ? p.segdec_r : p.segdec_f)[(int64_t)bh * nseg + slot] = acc_dec;
+      if (REV && sg == 0) p.rdec0[bh] = acc_dec;
+    }
+    if (REV && sg == 0 && p.dinit) dst1 = p.dinit + (int64_t)bh * PN;
+  } else if (REV && p.dinit) {
+    dst0 = p.dinit + (int64_t)bh * PN;
+  }
 #pragma unroll
-    for (int k = 0; k < TILES; ++k) {
-      const int tile = w + 4 * k, pt = tile % PT, nt = tile / PT;
-      if (tile >= PT * NT) break;
+  for (int k = 0; k < TILES; ++k) {
+    const int tile = w + 4 * k, pt = tile % PT, nt = tile / PT;
+    if (tile >= PT * NT) break;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) p.dinit[(int64_t)bh * PN + (pt * 16 + 4 * lg + r) * N + nt * 16 + li] = S[k][r];
+    for (int r = 0; r < 4; ++r) {
+      const int e = (pt * 16 + 4 * lg + r) * N + nt * 16 + li;
+      if (dst0) dst0[e] = S[k][r];
+      if (dst1) dst1[e] = S[k][r];
     }
   }
 }
 
-// Both walks in one launch: blocks [0, b*H) walk forward, [b*H, 2*b*H) backward.
+// Both walks in one launch: blocks [0, b*H*nseg) walk forward, the rest
+// backward; block (b*H index) * nseg + segment within each half.
 template <typename T, int P, int N>
 __global__ void __launch_bounds__(256) bwd_state_scan_kernel(const BwdParams p) {
   __shared__ __attribute__((aligned(16))) StateScanLds<T, P, N> lds;
-  const int nbh = p.b * p.H;
-  if ((int)blockIdx.x < nbh)
-    state_scan_body<T, P, N, false>(p, blockIdx.x, lds);
+  const int per = p.b * p.H * p.nseg, rem = (int)blockIdx.x % per;
+  if ((int)blockIdx.x < per)
+    state_scan_body<T, P, N, false>(p, rem / p.nseg, rem % p.nseg, lds);
   else
-    state_scan_body<T, P, N, true>(p, blockIdx.x - nbh, lds);
+    state_scan_body<T, P, N, true>(p, rem / p.nseg, rem % p.nseg, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -643,7 +673,7 @@ template <int P, int N> struct StateScanBf16Lds {
   float sTot[1];
 };
 template <int P, int N, bool REV>
-__device__ __forceinline__ void state_scan_bf16_body(const BwdParams &p, int bh, StateScanBf16Lds<P, N> &lds) {
+__device__ __forceinline__ void state_scan_bf16_body(const BwdParams &p, int bh, int sg, StateScanBf16Lds<P, N> &lds) {
   constexpr int LX = tr_ld(P, 2), LB = tr_ld(N, 2), PT = P / 16, NT = N / 16, TILES = (PT * NT + 3) / 4;
   __bf16 *sLh = lds.sLh, *sLl = lds.sLl, *sR = lds.sR;
   float *sW = lds.sW, *sTot = lds.sTot;
@@ -655,6 +685,13 @@ __device__ __forceinline__ void state_scan_bf16_body(const BwdParams &p, int bh,
   const __bf16 *rsrc = reinterpret_cast<const __bf16 *>(REV ? p.C : p.B) + ((int64_t)b_ * L * G + g) * N;
   const float *s0 = REV ? p.dfinal : p.states_init;
   float *out = (REV ? p.adj : p.states) + (int64_t)bh * nc * PN;
+  // this workgroup's segment of chunks [c_lo, c_hi).  One segment starts
+  // from init (forward) / dfinal (reverse); with several, every segment
+  // starts from zero and the fold over segments carries init / dfinal in
+  const int nseg = p.nseg, c_lo = sg * p.seg_chunks, c_hi = min(nc, c_lo + p.seg_chunks);
+  const int nsteps = c_hi - c_lo;
+  const bool from_s0 = nseg == 1;
+  float acc_dec = 0.f; // log2 decay walked so far in the segment (wave 0, lane 0)
 
   f32x4 S[TILES];
 #pragma unroll
@@ -663,7 +700,7 @@ __device__ __forceinline__ void state_scan_bf16_body(const BwdParams &p, int bh,
       if (tile >= PT * NT) break;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      S[k][r] = s0 ? s0[(int64_t)bh * PN + (pt * 16 + 4 * lg + r) * N + nt * 16 + li] : 0.f;
+      S[k][r] = (s0 && from_s0) ? s0[(int64_t)bh * PN + (pt * 16 + 4 * lg + r) * N + nt * 16 + li] : 0.f;
   }
 
   RowPrefetch<__bf16, P> pl;
@@ -675,9 +712,9 @@ __device__ __forceinline__ void state_scan_bf16_body(const BwdParams &p, int bh,
     pr.load(rsrc + (int64_t)t0 * G * N, (int64_t)G * N, nv, tid);
     if (w == 0) dtv = load_dt(p.dt, b_, L, H, h, t0, lane);
   };
-  fetch(REV ? nc - 1 : 0);
-  for (int step = 0; step < nc; ++step) {
-    const int c = REV ? nc - 1 - step : step;
+  fetch(REV ? c_hi - 1 : c_lo);
+  for (int step = 0; step < nsteps; ++step) {
+    const int c = REV ? c_hi - 1 - step : c_lo + step;
 #pragma unroll
     for (int k = 0; k < TILES; ++k) {
       const int tile = w + 4 * k, pt = tile % PT, nt = tile / PT;
@@ -689,6 +726,10 @@ __device__ __forceinline__ void state_scan_bf16_body(const BwdParams &p, int bh,
       const ChunkDecay d = chunk_decay_v(dtv, p.dt_bias, p.A, L, h, c * kQ, lane);
       sW[lane] = REV ? d.e_in : d.e_out * d.delta;
       if (lane == 0) sTot[0] = hw_exp2(d.cum2_last);
+      if (lane == 0 && nseg > 1) {
+        (REV ? p.rpre : p.fpre)[(int64_t)bh * nc + c] = acc_dec;
+        acc_dec += d.cum2_last;
+      }
     }
     __syncthreads();
     // stage: weighted input split into hi/lo planes, B or C copied
@@ -713,7 +754,7 @@ __device__ __forceinline__ void state_scan_bf16_body(const BwdParams &p, int bh,
     }
     const float tot = sTot[0];
     __syncthreads();
-    if (step + 1 < nc) fetch(REV ? c - 1 : c + 1);
+    if (step + 1 < nsteps) fetch(REV ? c - 1 : c + 1);
 #pragma unroll
     for (int k = 0; k < TILES; ++k) {
       const int tile = w + 4 * k, pt = tile % PT, nt = tile / PT;
@@ -729,13 +770,31 @@ __device__ __forceinline__ void state_scan_bf16_body(const BwdParams &p, int bh,
     }
     __syncthreads();
   }
-  if (REV && p.dinit) {
+  // the state left at the end of the walk: with one segment, the reverse one
+  // is the initial-state gradient; with several, every segment's goes to the
+  // fold (reverse segments in reversed order), with the segment's log2 decay,
+  // and segment 0's reverse one also to dinit (the fold's carry is added later)
+  float *dst0 = nullptr, *dst1 = nullptr;
+  if (nseg > 1) {
+    const int slot = REV ? nseg - 1 - sg : sg;
+    dst0 = (REV ? p.segend_r : p.segend_f) + ((int64_t)bh * nseg + slot) * PN;
+    if (w == 0 && lane == 0) {
+      (REV ? p.segdec_r : p.segdec_f)[(int64_t)bh * nseg + slot] = acc_dec;
+      if (REV && sg == 0) p.rdec0[bh] = acc_dec;
+    }
+    if (REV && sg == 0 && p.dinit) dst1 = p.dinit + (int64_t)bh * PN;
+  } else if (REV && p.dinit) {
+    dst0 = p.dinit + (int64_t)bh * PN;
+  }
 #pragma unroll
-    for (int k = 0; k < TILES; ++k) {
-      const int tile = w + 4 * k, pt = tile % PT, nt = tile / PT;
-      if (tile >= PT * NT) break;
+  for (int k = 0; k < TILES; ++k) {
+    const int tile = w + 4 * k, pt = tile % PT, nt = tile / PT;
+    if (tile >= PT * NT) break;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) p.dinit[(int64_t)bh * PN + (pt * 16 + 4 * lg + r) * N + nt * 16 + li] = S[k][r];
+    for (int r = 0; r < 4; ++r) {
+      const int e = (pt * 16 + 4 * lg + r) * N + nt * 16 + li;
+      if (dst0) dst0[e] = S[k][r];
+      if (dst1) dst1[e] = S[k][r];
     }
   }
 }
@@ -743,11 +802,11 @@ __device__ __forceinline__ void state_scan_bf16_body(const BwdParams &p, int bh,
 template <int P, int N>
 __global__ void __launch_bounds__(256) bwd_state_scan_bf16_kernel(const BwdParams p) {
   __shared__ __attribute__((aligned(16))) StateScanBf16Lds<P, N> lds;
-  const int nbh = p.b * p.H;
-  if ((int)blockIdx.x < nbh)
-    state_scan_bf16_body<P, N, false>(p, blockIdx.x, lds);
+  const int per = p.b * p.H * p.nseg, rem = (int)blockIdx.x % per;
+  if ((int)blockIdx.x < per)
+    state_scan_bf16_body<P, N, false>(p, rem / p.nseg, rem % p.nseg, lds);
   else
-    state_scan_bf16_body<P, N, true>(p, blockIdx.x - nbh, lds);
+    state_scan_bf16_body<P, N, true>(p, rem / p.nseg, rem % p.nseg, lds);
 }
 
 template <int P, int N>
@@ -1135,6 +1194,40 @@ __global__ void __launch_bounds__(256) gate_bwd_kernel(const T *__restrict__ y, 
   *reinterpret_cast<float4 *>(dz + 4 * i) = make_float4(b[0], b[1], b[2], b[3]);
 }
 
+// With several segments per walk (each walked from zero): add the carried-in
+// state of each chunk's segment (after the fold over segments, which starts
+// from init / dfinal), decayed to the chunk boundary: states[c] += 2^fpre[c]
+// C_s, adj[c] += 2^rpre[c] C'_s (C'_s in fold slot nseg-1-s), and the
+// gradient of the initial state dinit += 2^rdec0 C'_0.  One float4 per thread.
+__global__ void __launch_bounds__(256) bwd_fixup_kernel(const BwdParams p, int PN) {
+  const int64_t nbh = (int64_t)p.b * p.H, per = (int64_t)p.nc * (PN / 4);
+  const int64_t n1 = nbh * per, id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int nseg = p.nseg, cps = p.seg_chunks, PN4 = PN / 4;
+  if (id < 2 * n1) {
+    const bool rev = id >= n1;
+    const int64_t j = rev ? id - n1 : id;
+    const int64_t bh = j / per;
+    const int c = (int)((j % per) / PN4), e4 = (int)(j % PN4);
+    const int sgm = c / cps;
+    const int slot = rev ? nseg - 1 - sgm : sgm;
+    const float f = hw_exp2((rev ? p.rpre : p.fpre)[bh * p.nc + c]);
+    const float4 cv = reinterpret_cast<const float4 *>((rev ? p.segend_r : p.segend_f) + (bh * nseg + slot) * PN)[e4];
+    float4 *d = reinterpret_cast<float4 *>((rev ? p.adj : p.states) + (bh * p.nc + c) * PN) + e4;
+    float4 v = *d;
+    v.x += f * cv.x; v.y += f * cv.y; v.z += f * cv.z; v.w += f * cv.w;
+    *d = v;
+  } else if (p.dinit && id < 2 * n1 + nbh * PN4) {
+    const int64_t j = id - 2 * n1, bh = j / PN4;
+    const int e4 = (int)(j % PN4);
+    const float f = hw_exp2(p.rdec0[bh]);
+    const float4 cv = reinterpret_cast<const float4 *>(p.segend_r + (bh * nseg + nseg - 1) * PN)[e4];
+    float4 *d = reinterpret_cast<float4 *>(p.dinit + bh * PN) + e4;
+    float4 v = *d;
+    v.x += f * cv.x; v.y += f * cv.y; v.z += f * cv.z; v.w += f * cv.w;
+    *d = v;
+  }
+}
+
 // dA, dD, d dt_bias per head: one workgroup per head sums the (batch, chunk)
 // partials, each thread a fixed strided subset, then a fixed shuffle tree and
 // a fixed order over the four waves, so the result is the same every run.
@@ -1168,14 +1261,26 @@ __global__ void __launch_bounds__(256) bwd_param_kernel(const float *__restrict_
 }
 
 template <typename T, int P, int N> hipError_t launch_bwd_t(const BwdParams &p, hipStream_t st) {
-  // the forward and the backward state walks, together in one launch
-  const dim3 grid_bh((unsigned)(2 * p.b * p.H));
+  // the forward and the backward state walks (and their segments), together in one launch
+  const dim3 grid_bh((unsigned)(2 * p.b * p.H * p.nseg));
   if constexpr (sizeof(T) == 2)
     hipLaunchKernelGGL((bwd_state_scan_bf16_kernel<P, N>), grid_bh, dim3(256), 0, st, p);
   else
     hipLaunchKernelGGL((bwd_state_scan_kernel<T, P, N>), grid_bh, dim3(256), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (p.nseg > 1) {
+    // fold the segment end states in order (reverse ones stored reversed),
+    // then add each segment's carried-in state into its chunks
+    e = launch_state_pass(p.segend_f, p.segdec_f, p.states_init, p.b, p.H, P * N, p.nseg, st);
+    if (e != hipSuccess) return e;
+    e = launch_state_pass(p.segend_r, p.segdec_r, p.dfinal, p.b, p.H, P * N, p.nseg, st);
+    if (e != hipSuccess) return e;
+    const int64_t n = 2 * (int64_t)p.b * p.H * p.nc * (P * N / 4) + (int64_t)p.b * p.H * (P * N / 4);
+    hipLaunchKernelGGL(bwd_fixup_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, P * N);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if constexpr (sizeof(T) == 2)
     hipLaunchKernelGGL((bwd_chunk_bf16_kernel<P, N>), dim3((unsigned)(p.b * p.G * p.nc)), dim3(512), 0, st, p);
   else

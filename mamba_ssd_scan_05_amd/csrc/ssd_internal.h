@@ -129,13 +129,21 @@ struct BwdParams {
   float *adj;           // scratch [b, H, nc, P, N]: gradient at each chunk's
                         // last state
   float *part;          // scratch [b, H, nc, 3]: partial dA, dD, d dt_bias
+  // the state walks cut into nseg segments of seg_chunks chunks (nseg = 1:
+  // one walk over the whole sequence, the arrays below unused)
+  float *fpre, *rpre;   // scratch [b, H, nc]: log2 decay from the segment's
+                        // start to the chunk (forward) / chunk end to the
+                        // segment's end (reverse)
+  float *segend_f, *segend_r; // scratch [b, H, nseg, P, N]: segment end states
+  float *segdec_f, *segdec_r; // scratch [b, H, nseg]: segment log2 decays
+  float *rdec0;         // scratch [b, H]: log2 decay of segment 0
   float *dx;            // [b, L, H, P]
   float *ddt;           // [b, L, H]
   float *dB, *dC;       // [b, L, G, N]
   float *dA;            // [H]
   float *dD, *ddt_bias; // [H] or null
   float *dinit;         // [b, H, P, N] or null
-  int b, L, H, G, nc;
+  int b, L, H, G, nc, nseg, seg_chunks;
 };
 // P in {16, 32, 64}, N in {16, 32, 64, 128}; dtype 1 = bf16, 0 = fp32.
 hipError_t launch_bwd(int dtype, int P, int N, const BwdParams &p, hipStream_t stream);
