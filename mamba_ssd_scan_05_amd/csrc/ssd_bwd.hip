@@ -37,8 +37,11 @@
 // the initial state is the last of these, G_{-1}.
 //
 // Kernels: bwd_state_scan_kernel / _bf16 (both recursions, one workgroup
-// per (batch, head) walking the chunks with the state in matrix-core
-// accumulators), bwd_chunk_kernel / bwd_chunk_bf16_kernel (one workgroup per
+// per (batch, head) -- or per (batch, head, segment of chunks) when b*H is
+// small -- walking the chunks with the state in matrix-core accumulators),
+// bwd_fixup_kernel (with segments: adds each segment's carried-in state,
+// folded over segments by the state-pass kernel, into its chunks),
+// bwd_chunk_kernel / bwd_chunk_bf16_kernel (one workgroup per
 // (batch, group, chunk), all heads of the group in turn: dB and dC stay in
 // registers across heads, so no atomics and a fixed summation order),
 // bwd_param_kernel (sums of the per-(batch, head, chunk) partials of dA, dD
