@@ -195,3 +195,29 @@ def test_bwd_long_sequence():
     ref = ref_grads(si, dy, df)
     for k in NAMES:
         check(got[k], ref[k], 2e-2, "long " + k)
+
+
+def test_bwd_workload_long_gva_sampled_heads():
+    # long GVA (b=1, L=65536, H=32, G=8): the state walks run in 8 segments.
+    # Two heads of different groups, with their groups' B and C, are cut out
+    # for the oracle (their dx, ddt, dA, dD, d dt_bias, dinit depend on
+    # nothing else)
+    name = "long_gva_b1_L65536_H32_G8_P64_N128"
+    si = inputs.make_workload(name)
+    if si.init is None:
+        si.init = (0.3 * np.random.default_rng(122).standard_normal((1, 32, 64, 128))).astype(np.float32)
+    dy, df = make_grads_in(si, 123)
+    say("bwd workload", name)
+    got = run(si, dy, df)
+    heads = [3, 29]
+    H, G = si.x.shape[2], si.B.shape[2]
+    groups = [h * G // H for h in heads]
+    a = si.f64()
+    ref = oracle.scan_bwd(a["x"][:, :, heads], a["dt"][:, :, heads], a["dt_bias"][heads], a["A"][heads],
+                          a["B"][:, :, groups], a["C"][:, :, groups], a["D"][heads], a["init"][:, heads],
+                          dy.double().numpy()[:, :, heads], df.double().numpy()[:, heads])
+    check(got["dx"][:, :, heads], ref["dx"], 2e-2, "dx")
+    check(got["ddt"][:, :, heads], ref["ddt"], 2e-2, "ddt")
+    check(got["dinit"][:, heads], ref["dinit"], 2e-2, "dinit")
+    for k in ("dA", "dD", "ddt_bias"):
+        check(got[k][heads], ref[k], 2e-2, k)
