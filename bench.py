@@ -103,7 +103,7 @@ def cpu_baseline(si, reps):
         times.append(time.perf_counter() - t0)
     best = min(times)
     return {"value": b * L / best, "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu_info(),
             "sample": "whole workload (b=4, L=4096, H=80, P=64, N=128, fp64), best of %d runs, "
                       "%.2f s each" % (reps, best)}
 
@@ -144,6 +144,121 @@ def bench_sscan(ssd, staging, inputs, torch, dev):
                          "peak": VALU_LANE_OPS / 1e9, "unit": "G lane-op/s",
                          "frac": ops / (ms * 1e-3) / VALU_LANE_OPS, "ops_per_launch": ops},
             "hbm_GBs": nbytes / (ms * 1e-3) / 1e9, "bytes_per_launch": nbytes}
+
+
+EVICT_BYTES = 512 << 20   # written between cold reps: more than the 256 MB MALL plus L2
+COLD_REPS = 30
+
+
+def percentiles(ms):
+    return {"median_ms": float(np.median(ms)), "p10_ms": float(np.percentile(ms, 10)),
+            "p90_ms": float(np.percentile(ms, 90)), "mean_ms": float(np.mean(ms)), "reps": len(ms)}
+
+
+def time_cold(fn, torch, evict, reps=COLD_REPS):
+    """Each rep: a 512 MiB device write on the same stream (outside the events)
+    evicts L2 and the MALL, then HIP events bracket one call."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for k in range(reps):
+        evict.fill_(k & 0x7f)
+        ev[k][0].record()
+        fn()
+        ev[k][1].record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def time_warm(fn, torch, reps=COLD_REPS):
+    """Back-to-back calls, HIP events between consecutive calls."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for k in range(reps):
+        fn()
+        ev[k + 1].record()
+    torch.cuda.synchronize()
+    return [ev[k].elapsed_time(ev[k + 1]) for k in range(reps)]
+
+
+def state_bytes(b, L, H, P, N, Q):
+    """One write and one read of the fp32 inter-chunk states of the chunked
+    method (chunk Q): the traffic the secondary roofline fraction counts."""
+    nc = (L + Q - 1) // Q
+    return 2 * b * H * nc * P * N * 4
+
+
+def bench_scan_config(name, ssd, staging, inputs, torch, dev, evict):
+    """One named scan workload under the automatic plan: cold-cache median
+    (p10/p90) of 30 reps and warm back-to-back mean, tokens/s and roofline
+    fractions (strict: algorithmic bytes and FLOPs; secondary: plus the
+    inter-chunk states of the chunked method)."""
+    si = inputs.make_workload(name)
+    shp = si.shape
+    b, L, H, P, G, N = (shp[k] for k in ("b", "L", "H", "P", "G", "N"))
+    Q = si.chunk
+    t = staging.scan_tensors(si, dev)
+    out = torch.empty_like(t["x"])
+    fin = torch.empty((b, H, P, N), dtype=torch.float32, device=dev)
+
+    def fn():
+        ssd.ssd_scan_fwd(**t, out=out, final_state=fin, chunk=Q)
+    for _ in range(5):
+        fn()
+    torch.cuda.synchronize()
+    cold = percentiles(time_cold(fn, torch, evict))
+    warm = percentiles(time_warm(fn, torch))
+    nbytes = scan_bytes(b, L, H, P, G, N, si.dtype, si.init is not None, True)
+    flops = scan_flops(b, L, H, P, G, N, Q)
+    peak_flops = (MFMA_BF16_PEAK_TFLOPS * 1e12) if si.dtype == inputs.BF16 else MFMA_F32
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / peak_flops
+    t_roof = max(t_hbm, t_mfma)
+    sec = nbytes + state_bytes(b, L, H, P, N, Q)
+    a, seg = ssd.ssd_scan_plan(b, L, H, P, G, N, t["x"].dtype,
+                               torch.cuda.get_device_properties(0).multi_processor_count)
+    med = cold["median_ms"] * 1e-3
+    res = {"workload": name, "dtype": si.dtype, "plan": {"algo": a, "segment": seg},
+           "cold": cold, "warm": warm, "tokens_per_s": b * L / med,
+           "algorithmic_bytes": nbytes, "counted_flops": flops,
+           "bound": "hbm" if t_hbm >= t_mfma else "mfma",
+           "roofline_us": t_roof * 1e6, "roofline_tokens_per_s": b * L / t_roof,
+           "frac": t_roof / med, "frac_warm": t_roof / (warm["mean_ms"] * 1e-3),
+           "achieved_GBs": nbytes / med / 1e9,
+           "secondary_bytes": sec, "secondary_frac": (sec / (HBM_PEAK_GBS * 1e9)) / med}
+    del t, out, fin
+    return res
+
+
+def cpu_info():
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"model": model, "logical_cpus": os.cpu_count()}
+
+
+def cpu_single_thread(names, inputs):
+    """The fp64 oracle on one host thread over each named workload (once)."""
+    import oracle
+    n0 = oracle.num_threads()
+    res = {}
+    try:
+        oracle.set_num_threads(1)
+        for name in names:
+            si = inputs.make_workload(name)
+            f = si.f64()
+            b, L = si.x.shape[0], si.x.shape[1]
+            t0 = time.perf_counter()
+            oracle.scan(**f)
+            dt = time.perf_counter() - t0
+            res[name] = {"seconds": dt, "tokens_per_s": b * L / dt, "threads": 1}
+    finally:
+        oracle.set_num_threads(n0)
+    return res
 
 
 MFMA_F32 = 157.3e12   # MI355X dense fp32 matrix peak, FLOP/s
@@ -212,12 +327,15 @@ def bench_decode(ssd, staging, inputs, torch, dev):
     torch.cuda.synchronize()
     per = [ev[k].elapsed_time(ev[k + 1]) for k in range(T)]
     avg_ms = float(np.mean(per))
+    stats = percentiles(per)
     b, H, P, N = sp.state.shape
     G = sp.B.shape[2]
     nbytes = step_bytes(b, H, P, G, N, sp.dtype)
     return {"workload": DECODE, "tokens_per_s": b / (avg_ms * 1e-3), "ms_per_step": avg_ms,
             "achieved_GBs": nbytes / (avg_ms * 1e-3) / 1e9, "peak_GBs": HBM_PEAK_GBS,
-            "frac": nbytes / (avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes_per_step": nbytes}
+            "frac": nbytes / (avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes_per_step": nbytes,
+            "per_step": stats,
+            "frac_median": nbytes / (stats["median_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
 def main():
@@ -235,6 +353,8 @@ def main():
     ap.add_argument("--no-gated", action="store_true",
                     help="skip the timing of the gated scan (out = y * silu(z))")
     ap.add_argument("--no-alt", action="store_true", help="skip timing the other algorithm")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload table (all scan workloads, cold-cache protocol)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 1 GiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -314,7 +434,24 @@ def main():
                 "roofline_tokens_per_s": tokens / max(t_hbm, t_mfma),
                 "mfma_frac": flops / (kern_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
 
-    extra = {"p10_ms": float(np.percentile(per_ms, 10)), "p90_ms": float(np.percentile(per_ms, 90))}
+    extra = {"p10_ms": float(np.percentile(per_ms, 10)), "p90_ms": float(np.percentile(per_ms, 90)),
+             "median_ms": float(np.median(per_ms))}
+    # cold-cache protocol: 30 reps, each after a 512 MiB eviction write on the
+    # same stream outside the events; median with p10/p90
+    evict = torch.empty(EVICT_BYTES, dtype=torch.uint8, device=dev)
+    cold = percentiles(time_cold(one, torch, evict))
+    roofline["cold"] = cold
+    roofline["frac_cold_median"] = nbytes / (cold["median_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS
+    roofline["secondary_frac_cold_median"] = (
+        (nbytes + state_bytes(b, L, H, P, N, Q)) / (cold["median_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS)
+    if not args.no_configs:
+        # every scan workload under the automatic plan, the same protocol
+        extra["configs"] = {}
+        for name in inputs.WORKLOAD_ORDER:
+            if inputs.WORKLOADS[name]["kind"] != "scan":
+                continue
+            print("bench: config %s" % name, file=sys.stderr, flush=True)
+            extra["configs"][name] = bench_scan_config(name, ssd, staging, inputs, torch, dev, evict)
     if not args.no_alt:
         alts = {}
         for name_a, a, q in (("rows", ssd.SSD_ALGO_ROWS, Q), ("fused", ssd.SSD_ALGO_FUSED, Q),
@@ -384,6 +521,9 @@ def main():
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
         cpu = cpu_baseline(si, reps=2)
+        print("bench: cpu baseline, one thread", file=sys.stderr, flush=True)
+        cpu["single_thread"] = cpu_single_thread(
+            ["tiny_fp32_b1_L256_H4_P16_N16", WORKLOAD], inputs)
 
     line = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,

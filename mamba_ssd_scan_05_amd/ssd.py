@@ -132,12 +132,15 @@ def ssd_scan_fwd(x, dt, dt_bias, A, B, C, D=None, init_state=None, out=None,
     if final_state is None and return_final_state:
         final_state = torch.empty((x.shape[0], x.shape[2], x.shape[3], B.shape[3]),
                                   dtype=torch.float32, device=x.device)
+    args = (describe(x), describe(dt), describe(dt_bias), describe(A), describe(B), describe(C),
+            describe(D), describe(init_state), describe(out), describe(final_state), int(chunk))
     with _on_device(x):
         st = _stream(stream, x)
-        status = lib().ssd_scan_fwd_algo(
-            describe(x), describe(dt), describe(dt_bias), describe(A), describe(B), describe(C),
-            describe(D), describe(init_state), describe(out), describe(final_state),
-            int(chunk), int(algo), st)
+        if algo == SSD_ALGO_AUTO:
+            # the library's own plan: the plain entry point
+            status = lib().ssd_scan_fwd(*args, st)
+        else:
+            status = lib().ssd_scan_fwd_algo(*args, int(algo), st)
     _check(status)
     return out, final_state
 

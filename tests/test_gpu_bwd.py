@@ -117,26 +117,31 @@ def test_bwd_deterministic():
         assert np.array_equal(a[k], b[k]), k
 
 
-def test_bwd_workload_2p7b_sampled_heads():
-    # the 2.7B layer shape (b=4, L=4096, H=80, P=64, N=128, bf16): the GPU
-    # computes every gradient; the oracle recomputes the gradients that belong
-    # to two heads alone (dx, ddt, dA, dD, d dt_bias, dinit of head h depend
-    # only on head h's inputs and on B, C) on the problem cut to those heads
+def test_bwd_many_heads_one_group():
+    # 80 heads share one B/C group: the chunk step accumulates dB and dC over
+    # all 80 heads of the group in turn; every gradient against the full oracle
+    si = inputs.make_scan(1, 1024, 80, 64, 1, 128, dtype=inputs.BF16, seed=131, init_std=0.1)
+    dy, df = make_grads_in(si, 132)
+    say("bwd b1 L1024 H80 G1 (80 heads per group), all gradients")
+    got = run(si, dy, df)
+    ref = ref_grads(si, dy, df)
+    for k in NAMES:
+        say("  %s %.3e" % (k, check(got[k], ref[k], 2e-2, k)))
+
+
+def test_bwd_workload_2p7b_full():
+    # the 2.7B layer shape (b=4, L=4096, H=80, P=64, G=1, N=128, bf16): every
+    # gradient, dB and dC (sums over all 80 heads) included, against the full
+    # fp64 oracle
     name = "mamba2_2p7b_b4_L4096_H80_P64_N128"
     si = inputs.make_workload(name)
     dy, df = make_grads_in(si, 99)
     say("bwd workload", name)
     got = run(si, dy, df)
-    heads = [3, 61]
-    a = si.f64()
-    ref = oracle.scan_bwd(a["x"][:, :, heads], a["dt"][:, :, heads], a["dt_bias"][heads], a["A"][heads],
-                          a["B"], a["C"], a["D"][heads], a["init"][:, heads],
-                          dy.double().numpy()[:, :, heads], df.double().numpy()[:, heads])
-    check(got["dx"][:, :, heads], ref["dx"], 2e-2, "dx")
-    check(got["ddt"][:, :, heads], ref["ddt"], 2e-2, "ddt")
-    check(got["dinit"][:, heads], ref["dinit"], 2e-2, "dinit")
-    for k in ("dA", "dD", "ddt_bias"):
-        check(got[k][heads], ref[k], 2e-2, k)
+    say("  oracle backward (full)")
+    ref = ref_grads(si, dy, df)
+    for k in NAMES:
+        say("  %s %.3e" % (k, check(got[k], ref[k], 2e-2, k)))
 
 
 @pytest.mark.parametrize("kind", ["frozen", "no_decay", "zero_x"])
@@ -197,11 +202,11 @@ def test_bwd_long_sequence():
         check(got[k], ref[k], 2e-2, "long " + k)
 
 
-def test_bwd_workload_long_gva_sampled_heads():
+def test_bwd_workload_long_gva_whole_group():
     # long GVA (b=1, L=65536, H=32, G=8): the state walks run in 8 segments.
-    # Two heads of different groups, with their groups' B and C, are cut out
-    # for the oracle (their dx, ddt, dA, dD, d dt_bias, dinit depend on
-    # nothing else)
+    # One whole group (heads 0-3 with B/C group 0) and one head of another
+    # group are cut out for the oracle: the gradients of a group's heads and
+    # that group's dB, dC depend on nothing else
     name = "long_gva_b1_L65536_H32_G8_P64_N128"
     si = inputs.make_workload(name)
     if si.init is None:
@@ -209,15 +214,18 @@ def test_bwd_workload_long_gva_sampled_heads():
     dy, df = make_grads_in(si, 123)
     say("bwd workload", name)
     got = run(si, dy, df)
-    heads = [3, 29]
     H, G = si.x.shape[2], si.B.shape[2]
-    groups = [h * G // H for h in heads]
     a = si.f64()
-    ref = oracle.scan_bwd(a["x"][:, :, heads], a["dt"][:, :, heads], a["dt_bias"][heads], a["A"][heads],
-                          a["B"][:, :, groups], a["C"][:, :, groups], a["D"][heads], a["init"][:, heads],
-                          dy.double().numpy()[:, :, heads], df.double().numpy()[:, heads])
-    check(got["dx"][:, :, heads], ref["dx"], 2e-2, "dx")
-    check(got["ddt"][:, :, heads], ref["ddt"], 2e-2, "ddt")
-    check(got["dinit"][:, heads], ref["dinit"], 2e-2, "dinit")
-    for k in ("dA", "dD", "ddt_bias"):
-        check(got[k][heads], ref[k], 2e-2, k)
+    for heads in ([0, 1, 2, 3], [29]):
+        groups = sorted({h * G // H for h in heads})
+        ref = oracle.scan_bwd(a["x"][:, :, heads], a["dt"][:, :, heads], a["dt_bias"][heads], a["A"][heads],
+                              a["B"][:, :, groups], a["C"][:, :, groups], a["D"][heads], a["init"][:, heads],
+                              dy.double().numpy()[:, :, heads], df.double().numpy()[:, heads])
+        check(got["dx"][:, :, heads], ref["dx"], 2e-2, "dx")
+        check(got["ddt"][:, :, heads], ref["ddt"], 2e-2, "ddt")
+        check(got["dinit"][:, heads], ref["dinit"], 2e-2, "dinit")
+        for k in ("dA", "dD", "ddt_bias"):
+            check(got[k][heads], ref[k], 2e-2, k)
+        if len(heads) == H // G:  # a whole group: its dB, dC are complete
+            check(got["dB"][:, :, groups], ref["dB"], 2e-2, "dB group %s" % groups)
+            check(got["dC"][:, :, groups], ref["dC"], 2e-2, "dC group %s" % groups)

@@ -182,6 +182,8 @@ def test_workload_decode_steps():
     t = staging.step_tensors(sp, DEV)
     ref = sp.state.astype(np.float64)
     T = sp.x.shape[0]
+    sb_idx = torch.as_tensor(SAMPLE_B, device=DEV)
+    sh_idx = torch.as_tensor(SAMPLE_H, device=DEV)
     worst = 0.0
     for k in range(T):
         y = ssd.ssd_step(t["state"], t["x"][k], t["dt"][k], t["A"], t["B"][k], t["C"][k], t["D"])
@@ -189,9 +191,50 @@ def test_workload_decode_steps():
                               inputs.to_f64(sp.B[k], sp.dtype), inputs.to_f64(sp.C[k], sp.dtype),
                               sp.D)
         worst = max(worst, check(staging.to_f64(y), yr, 2e-2, "decode y step %d" % k))
+        # the state after this step on a fixed sample of (batch, head) slices
+        got_s = t["state"][sb_idx, sh_idx].cpu().numpy().astype(np.float64)
+        worst = max(worst, check(got_s, ref[SAMPLE_B, SAMPLE_H], 2e-2, "decode state step %d" % k))
     torch.cuda.synchronize()
     worst = max(worst, check(staging.to_f64(t["state"]), ref, 2e-2, "decode state"))
     say("  max rel err %.3e" % worst)
+
+
+# (batch, head) slices of the decode state compared after every step: the
+# first and last batch rows and heads plus a spread of others
+SAMPLE_B = np.array([0, 255, 1, 37, 128, 200, 77, 254, 3, 160, 99, 31])
+SAMPLE_H = np.array([0, 79, 40, 1, 63, 17, 78, 5, 33, 50, 71, 12])
+
+
+def test_exported_scan_fwd_symbol():
+    """ssd_scan_fwd itself (not the algorithm-selecting variant), called through
+    ctypes with hand-built descriptors and the raw stream handle."""
+    import ctypes
+    si = inputs.make_scan(2, 300, 8, 64, 2, 128, dtype=inputs.BF16, seed=31, init_std=0.1)
+    t = staging.scan_tensors(si, DEV)
+    b, L, H, P = si.x.shape
+    N = si.B.shape[3]
+    out = torch.empty_like(t["x"])
+    fin = torch.full((b, H, P, N), float("nan"), dtype=torch.float32, device=DEV)
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    say("ssd_scan_fwd symbol")
+    lib = ssd.lib()
+    fn = lib.ssd_scan_fwd
+    assert fn.argtypes[-2] is ctypes.c_int and len(fn.argtypes) == 12
+    status = fn(ssd.describe(t["x"]), ssd.describe(t["dt"]), ssd.describe(t["dt_bias"]),
+                ssd.describe(t["A"]), ssd.describe(t["B"]), ssd.describe(t["C"]), ssd.describe(t["D"]),
+                ssd.describe(t["init_state"]), ssd.describe(out), ssd.describe(fin), 256,
+                ctypes.c_void_p(stream.cuda_stream))
+    assert status == 0, lib.ssd_last_error().decode()
+    stream.synchronize()
+    yr, fr = oracle_scan(si)
+    check(staging.to_f64(out), yr, 2e-2, "ssd_scan_fwd y")
+    check(staging.to_f64(fin), fr, 2e-2, "ssd_scan_fwd final")
+    # a rejected call returns its status before any launch
+    bad = fn(ssd.describe(t["x"]), ssd.describe(t["dt"]), None, ssd.describe(t["A"]),
+             ssd.describe(t["B"]), ssd.describe(t["C"]), None, None, ssd.describe(out), None, 100,
+             ctypes.c_void_p(stream.cuda_stream))
+    assert bad == 5 and b"chunk" in lib.ssd_last_error()
 
 
 # ---------------------------------------------------------------------------
