@@ -36,10 +36,14 @@
  * that stream in stream order and grown stream-ordered on `stream` when a
  * call needs more (an event recorded after each call orders the next use if
  * a handle is reused for another stream).  A request above 256 MiB is
- * allocated and freed stream-ordered on `stream` for that call alone.  Kept
- * buffers live until ssd_release_scratch() or the end of the process.
- * Allocating scratch per call would make the host wait for the stream's
- * earlier work; keeping it lets back-to-back calls queue ahead of the GPU.
+ * allocated and freed stream-ordered on `stream` for that call alone.  At
+ * most 16 buffers of at most 1 GiB in total are kept: a call that needs a
+ * new buffer first frees the least recently used ones (after waiting for
+ * their last use) until both limits hold.  Kept buffers live until
+ * ssd_release_scratch(), eviction, or the end of the process.  Allocating
+ * scratch per call would make the host wait for the stream's earlier work;
+ * keeping it lets back-to-back calls queue ahead of the GPU.  Calls that take
+ * scratch are serialised on the host while they queue their launches.
  *
  * Errors: every argument is validated on the host before any work is
  * queued; a failed validation returns a nonzero status and queues nothing.  A failed
@@ -287,8 +291,13 @@ int ssd_selective_scan_fwd(const ssd_tensor *x, const ssd_tensor *dt,
  *
  * Supported: P in {16, 32, 64}, N in {16, 32, 64, 128}, either input dtype,
  * the size limits of ssd_scan_fwd.  No output may overlap an input or another
- * output (SSD_ERR_ALIAS).  Arithmetic in fp32 (matrix products on the
- * matrix cores from fp32 operands).  Sums over heads, chunks and batch run
+ * output (SSD_ERR_ALIAS).  Arithmetic: fp32 inputs use fp32 matrix-core
+ * products throughout.  bf16 inputs use bf16 matrix-core products with fp32
+ * accumulation; where a product pairs a bf16 input with an fp32 quantity
+ * (decayed scores, states, adjoints, weighted x or dout), the fp32 operand is
+ * carried as a bf16 high part plus a bf16 remainder, so each such product is
+ * two bf16 MFMAs with a relative error near 2^-17.  The state walks keep
+ * their states in fp32.  Sums over heads, chunks and batch run
  * in a fixed order, so the result does not vary from run to run.  Scratch:
  * b*H*ceil(L/64)*(2*P*N + 3) floats (the states entering each 64-token chunk,
  * the gradients at each chunk's end, per-chunk partial sums; see Scratch
@@ -355,6 +364,11 @@ int ssd_version(void);
  * SSD_ERR_HIP if a HIP call failed (the buffers are forgotten either way).
  * Makes no HIP call when no buffer is kept. */
 int ssd_release_scratch(void);
+
+/* Number of scratch buffers the library currently keeps and their total
+ * bytes (see Scratch above).  Host only; returns SSD_ERR_NULL for a NULL
+ * argument. */
+int ssd_scratch_stats(int64_t *buffers, int64_t *bytes);
 
 #ifdef __cplusplus
 }

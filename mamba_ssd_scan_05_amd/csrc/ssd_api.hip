@@ -181,9 +181,14 @@ int hip_fail(hipError_t e, const char *what) {
 // when one handle names several streams, as the per-thread default stream
 // does).  A buffer grows, stream-ordered, to the largest request up to
 // kScratchKeepMax; a larger request is allocated and freed on the stream for
-// that call alone.  ssd_release_scratch() frees every kept buffer.
+// that call alone.  At most kScratchSlots buffers holding at most
+// kScratchTotal bytes are kept: a call that needs a new one first frees the
+// least recently used idle buffers (after waiting for their last use) until
+// both limits hold.  ssd_release_scratch() frees every kept buffer.
 constexpr size_t kScratchKeepMax = (size_t)256 << 20;
 constexpr size_t kScratchGranule = (size_t)1 << 20;
+constexpr size_t kScratchSlots = 16;
+constexpr size_t kScratchTotal = (size_t)1 << 30;
 
 struct ScratchSlot {
   int dev;
@@ -192,13 +197,52 @@ struct ScratchSlot {
   void *p;
   size_t cap;
   hipEvent_t done;
-  bool pending; // done has been recorded after the last use
+  bool pending;       // done has been recorded after the last use
+  bool busy;          // held by a call in progress (this thread, an outer call)
+  uint64_t last_use;  // for least-recently-used eviction
 };
 
 // Recursive: a call may hold one buffer (tag 1) while the calls it makes take
 // another (tag 0) on the same stream.
 std::recursive_mutex g_scratch_mu;
 std::vector<ScratchSlot> g_scratch;
+uint64_t g_scratch_clock = 0;
+
+// Frees slot i (waiting for its last use first) and removes it.  Called with
+// the lock held.
+int drop_slot(size_t i) {
+  ScratchSlot s = g_scratch[i];
+  g_scratch.erase(g_scratch.begin() + (ptrdiff_t)i);
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_fail(e, "scratch eviction: current device");
+  int status = SSD_OK;
+  e = hipSetDevice(s.dev);
+  if (e == hipSuccess && s.pending) e = hipEventSynchronize(s.done);
+  if (e == hipSuccess && s.p) e = hipFree(s.p);
+  if (e == hipSuccess) e = hipEventDestroy(s.done);
+  if (e != hipSuccess) status = hip_fail(e, "scratch eviction");
+  e = hipSetDevice(cur);
+  if (e != hipSuccess && status == SSD_OK) status = hip_fail(e, "scratch eviction: restore device");
+  return status;
+}
+
+// Evicts idle slots, least recently used first, until `more_slots` more
+// slots and `more_bytes` more bytes fit both limits.  Called with the lock
+// held.
+int make_room(size_t more_slots, size_t more_bytes) {
+  for (;;) {
+    size_t total = more_bytes;
+    for (const ScratchSlot &s : g_scratch) total += s.cap;
+    if (g_scratch.size() + more_slots <= kScratchSlots && total <= kScratchTotal) return SSD_OK;
+    size_t victim = g_scratch.size();
+    for (size_t i = 0; i < g_scratch.size(); ++i)
+      if (!g_scratch[i].busy && (victim == g_scratch.size() || g_scratch[i].last_use < g_scratch[victim].last_use))
+        victim = i;
+    if (victim == g_scratch.size()) return SSD_OK; // every kept buffer is in use by this thread
+    SSD_CHECK(drop_slot(victim));
+  }
+}
 
 // One call's scratch.  get() returns the buffer; the lock on the kept
 // buffers is held from get() until finish() (or destruction), so the event
@@ -227,15 +271,28 @@ public:
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "scratch: current device");
     lock_ = std::unique_lock<std::recursive_mutex>(g_scratch_mu);
+    const size_t want = (bytes + kScratchGranule - 1) / kScratchGranule * kScratchGranule;
     size_t i = 0;
     while (i < g_scratch.size() &&
            !(g_scratch[i].dev == dev && g_scratch[i].st == st_ && g_scratch[i].tag == tag_))
       ++i;
     if (i == g_scratch.size()) {
+      SSD_CHECK(make_room(1, want));
       hipEvent_t ev = nullptr;
       e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
       if (e != hipSuccess) return hip_fail(e, "scratch: event");
-      g_scratch.push_back(ScratchSlot{dev, st_, tag_, nullptr, 0, ev, false});
+      g_scratch.push_back(ScratchSlot{dev, st_, tag_, nullptr, 0, ev, false, false, 0});
+      i = g_scratch.size() - 1;
+    } else if (g_scratch[i].cap < bytes) {
+      // growing: keep the other buffers within the byte limit
+      g_scratch[i].busy = true;
+      int st = make_room(0, want - g_scratch[i].cap);
+      g_scratch[i].busy = false;
+      SSD_CHECK(st);
+      while (i < g_scratch.size() &&
+             !(g_scratch[i].dev == dev && g_scratch[i].st == st_ && g_scratch[i].tag == tag_))
+        ++i;
+      if (i == g_scratch.size()) return fail(SSD_ERR_NOMEM, "scratch: slot lost while growing");
     }
     ScratchSlot &s = g_scratch[i];
     if (s.pending) {
@@ -249,7 +306,6 @@ public:
         s.cap = 0;
         if (e != hipSuccess) return hip_fail(e, "scratch: free to grow");
       }
-      const size_t want = (bytes + kScratchGranule - 1) / kScratchGranule * kScratchGranule;
       e = hipMallocAsync(&s.p, want, st_);
       if (e != hipSuccess || !s.p) {
         (void)hipGetLastError();
@@ -258,7 +314,11 @@ public:
       }
       s.cap = want;
     }
-    slot_ = (int)i;
+    s.busy = true;
+    s.last_use = ++g_scratch_clock;
+    slot_dev_ = dev;
+    slot_st_ = st_;
+    slot_ = 1;
     *out = s.p;
     return SSD_OK;
   }
@@ -272,11 +332,17 @@ public:
       if (e != hipSuccess) status = hip_fail(e, "scratch free");
     }
     if (slot_ >= 0) {
-      ScratchSlot &s = g_scratch[slot_];
-      const hipError_t e = hipEventRecord(s.done, st_);
-      s.pending = true;
+      // find the slot again: a nested call may have evicted others meanwhile
+      for (ScratchSlot &s : g_scratch) {
+        if (s.dev == slot_dev_ && s.st == slot_st_ && s.tag == tag_) {
+          const hipError_t e = hipEventRecord(s.done, st_);
+          s.pending = true;
+          s.busy = false;
+          if (e != hipSuccess) status = hip_fail(e, "scratch: record its use");
+          break;
+        }
+      }
       slot_ = -1;
-      if (e != hipSuccess) status = hip_fail(e, "scratch: record its use");
     }
     if (lock_.owns_lock()) lock_.unlock();
     return status;
@@ -287,8 +353,19 @@ private:
   int tag_;
   std::unique_lock<std::recursive_mutex> lock_;
   int slot_ = -1;
+  int slot_dev_ = 0;
+  hipStream_t slot_st_ = nullptr;
   void *own_ = nullptr;
 };
+
+// Number of buffers kept and their total bytes (tests).
+void scratch_usage(size_t *slots, size_t *bytes) {
+  std::lock_guard<std::recursive_mutex> lock(g_scratch_mu);
+  *slots = g_scratch.size();
+  size_t t = 0;
+  for (const ScratchSlot &s : g_scratch) t += s.cap;
+  *bytes = t;
+}
 
 // Every tensor must be memory the current device can address: device memory
 // of the current device, managed memory, or pinned host memory.  Pageable
@@ -346,9 +423,9 @@ int run_chunked(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_
   const size_t off_dec = n_tok * sizeof(float);
   const size_t off_states = off_dec + ((n_seg * sizeof(float) + 255) / 256) * 256;
   const size_t total = off_states + n_seg * (size_t)PN * sizeof(float);
-  Scratch scratch(st);
+  Scratch sc(st);
   void *ws = nullptr;
-  SSD_CHECK(scratch.get(total, &ws));
+  SSD_CHECK(sc.get(total, &ws));
   hipError_t e;
   float *delta = (float *)ws;
   float *seg_decay = (float *)((char *)ws + off_dec);
@@ -386,7 +463,7 @@ int run_chunked(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_
     e = ssd::launch_walk(x->dtype, (int)s.P, (int)s.N, ssd::kWalkChunkOut, p, st);
     if (e != hipSuccess) { status = hip_fail(e, "chunk-output launch"); break; }
   } while (0);
-  const int fs = scratch.finish();
+  const int fs = sc.finish();
   return status != SSD_OK ? status : fs;
 }
 
@@ -419,9 +496,9 @@ int run_rows(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bia
              const ScanShape &s, int W, hipStream_t st) {
   const int64_t nsub = (s.L + 63) / 64;
   const size_t bytes = (size_t)(s.b * s.G * nsub) * 64 * 64 * 2;
-  Scratch scratch(st);
+  Scratch sc(st);
   void *ws = nullptr;
-  SSD_CHECK(scratch.get(bytes, &ws));
+  SSD_CHECK(sc.get(bytes, &ws));
   int status = SSD_OK;
   hipError_t e;
   do {
@@ -443,7 +520,7 @@ int run_rows(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bia
     e = ssd::launch_rwalk((int)s.N, W, p, st);
     if (e != hipSuccess) { status = hip_fail(e, "row walk launch"); break; }
   } while (0);
-  const int fs = scratch.finish();
+  const int fs = sc.finish();
   return status != SSD_OK ? status : fs;
 }
 
@@ -633,9 +710,9 @@ int run_bwd(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bias
   const size_t o_seg = o_pre + 2 * al((size_t)(nbh * nc) * 4);
   const size_t o_sdec = o_seg + 2 * al((size_t)(nbh * nseg * PN) * 4);
   const size_t total = o_sdec + 2 * al((size_t)(nbh * nseg) * 4) + al((size_t)nbh * 4);
-  Scratch scratch(st);
+  Scratch sc(st);
   void *ws = nullptr;
-  SSD_CHECK(scratch.get(total, &ws));
+  SSD_CHECK(sc.get(total, &ws));
   char *base = (char *)ws;
   ssd::BwdParams bp{};
   bp.x = x->data; bp.dt = (const float *)dt->data;
@@ -659,7 +736,7 @@ int run_bwd(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bias
   int status = SSD_OK;
   const hipError_t e = ssd::launch_bwd(x->dtype, (int)s.P, (int)s.N, bp, st);
   if (e != hipSuccess) status = hip_fail(e, "backward launch");
-  const int fs = scratch.finish();
+  const int fs = sc.finish();
   return status != SSD_OK ? status : fs;
 }
 
@@ -697,6 +774,16 @@ int ssd_scan_fwd(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt
                  ssd_tensor *final_state, int chunk, void *stream) {
   return ssd_scan_fwd_algo(x, dt, dt_bias, A, B, C, D, init_state, out, final_state, chunk,
                            SSD_ALGO_AUTO, stream);
+}
+
+int ssd_scratch_stats(int64_t *buffers, int64_t *bytes) {
+  g_last_error.clear();
+  if (!buffers || !bytes) return fail(SSD_ERR_NULL, "buffers/bytes: NULL");
+  size_t n = 0, t = 0;
+  scratch_usage(&n, &t);
+  *buffers = (int64_t)n;
+  *bytes = (int64_t)t;
+  return SSD_OK;
 }
 
 int ssd_scan_fwd_rows(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bias,
@@ -856,7 +943,7 @@ int ssd_selective_scan_fwd(const ssd_tensor *x, const ssd_tensor *dt, const ssd_
   p.out = out->data; p.final_state = final_state ? (float *)final_state->data : nullptr;
   p.b = (int)b; p.L = (int)L; p.Dc = (int)Dc; p.G = (int)G; p.seg_len = (int)seg_len; p.nseg = (int)nseg;
   hipStream_t st = (hipStream_t)stream;
-  Scratch scratch(st);
+  Scratch sc(st);
   void *ws = nullptr;
   if (nseg > 1) {
     // scratch: segment end states [b,nseg,D,N] | segment Delta sums [b,nseg,D] | staged init [b,D,N]
@@ -864,7 +951,7 @@ int ssd_selective_scan_fwd(const ssd_tensor *x, const ssd_tensor *dt, const ssd_
     const size_t off_sd = ((n_end * N * sizeof(float) + 255) / 256) * 256;
     const size_t off_hc = off_sd + ((n_end * sizeof(float) + 255) / 256) * 256;
     const size_t total = off_hc + (size_t)(b * Dc * N) * sizeof(float);
-    SSD_CHECK(scratch.get(total, &ws));
+    SSD_CHECK(sc.get(total, &ws));
     p.hend = (float *)ws;
     p.sdelta = (float *)((char *)ws + off_sd);
     p.hcopy = (float *)((char *)ws + off_hc);
@@ -872,7 +959,7 @@ int ssd_selective_scan_fwd(const ssd_tensor *x, const ssd_tensor *dt, const ssd_
   int status = SSD_OK;
   hipError_t e = ssd::launch_sscan(xd, (int)N, p, st);
   if (e != hipSuccess) status = hip_fail(e, "selective scan launch");
-  const int fs = scratch.finish();
+  const int fs = sc.finish();
   return status != SSD_OK ? status : fs;
 }
 

@@ -70,6 +70,8 @@ def lib():
         L.ssd_version.restype = ctypes.c_int
         L.ssd_release_scratch.restype = ctypes.c_int
         L.ssd_release_scratch.argtypes = []
+        L.ssd_scratch_stats.argtypes = [ctypes.POINTER(ctypes.c_int64)] * 2
+        L.ssd_scratch_stats.restype = ctypes.c_int
         L.ssd_scan_plan.argtypes = [ctypes.c_int64] * 6 + [ctypes.c_int, ctypes.c_int,
                                                             ctypes.POINTER(ctypes.c_int),
                                                             ctypes.POINTER(ctypes.c_int)]
@@ -143,6 +145,13 @@ def ssd_scan_fwd(x, dt, dt_bias, A, B, C, D=None, init_state=None, out=None,
             status = lib().ssd_scan_fwd_algo(*args, int(algo), st)
     _check(status)
     return out, final_state
+
+
+def ssd_scratch_stats():
+    """(number of kept scratch buffers, their total bytes)."""
+    n, t = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().ssd_scratch_stats(ctypes.byref(n), ctypes.byref(t)))
+    return n.value, t.value
 
 
 def ssd_scan_bwd(x, dt, dt_bias, A, B, C, D, init_state, dout, dfinal_state=None, *,

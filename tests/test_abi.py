@@ -45,6 +45,12 @@ def test_release_scratch_with_nothing_kept(ssd):
     ssd.ssd_release_scratch()
 
 
+def test_scratch_stats_host_only(ssd):
+    # nothing kept in this process: zero buffers, zero bytes; NULL refused
+    assert ssd.ssd_scratch_stats() == (0, 0)
+    assert ssd.lib().ssd_scratch_stats(None, None) == 1
+
+
 def test_version_and_strings(ssd):
     assert ssd.ssd_version() == 100
     assert ssd.ssd_status_string(0) == "ok"

@@ -127,3 +127,28 @@ def test_two_host_threads():
         for out, fin in results[k]:
             check(staging.to_f64(out), cases[k][2][0], "thread %d y" % k)
             check(staging.to_f64(fin), cases[k][2][1], "thread %d final" % k)
+
+
+def test_kept_buffers_capped_over_many_streams():
+    # 20 streams, one scan each: the library keeps at most 16 buffers (1 GiB
+    # in total), freeing the least recently used idle ones; every result is
+    # still correct
+    ssd.ssd_release_scratch()
+    si, t, ref = scan_case(500, 86)
+    streams = [torch.cuda.Stream() for _ in range(20)]
+    torch.cuda.synchronize()
+    outs = []
+    for k, s in enumerate(streams):
+        with torch.cuda.stream(s):
+            outs.append(ssd.ssd_scan_fwd(**t, chunk=256, algo=ssd.SSD_ALGO_ROWS))
+        n, nbytes = ssd.ssd_scratch_stats()
+        say("stream", k, "kept", n, "buffers,", nbytes, "bytes")
+        assert 1 <= n <= 16 and nbytes <= (1 << 30)
+    torch.cuda.synchronize()
+    n, nbytes = ssd.ssd_scratch_stats()
+    assert n == 16, n
+    for out, fin in outs:
+        check(staging.to_f64(out), ref[0], "y")
+        check(staging.to_f64(fin), ref[1], "final")
+    ssd.ssd_release_scratch()
+    assert ssd.ssd_scratch_stats() == (0, 0)
