@@ -153,6 +153,31 @@ int ssd_scan_fwd_algo(const ssd_tensor *x, const ssd_tensor *dt,
                       int algo, void *stream);
 
 /*
+ * ssd_scan_fwd_noalloc -- ssd_scan_fwd for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid allocation.  Same arguments, validation, plan
+ * (SSD_ALGO_AUTO) and results as ssd_scan_fwd; the call makes no hipMalloc,
+ * hipFree or other allocation.  Its scratch is a fixed array of
+ * ssd_fixed_scratch_bytes() bytes (64 MiB) in the library's device memory,
+ * one copy per device, held until the process ends; a call whose plan needs
+ * more scratch than that returns SSD_ERR_NOMEM before queuing anything
+ * (every scratch user writes its scratch before reading it, so nothing
+ * needs clearing between calls).  Every ssd_scan_fwd_noalloc call on one
+ * device shares that device's array: calls that overlap in time on one
+ * device (on different streams, or from several host threads) race on it
+ * and must be ordered by the caller.
+ */
+int ssd_scan_fwd_noalloc(const ssd_tensor *x, const ssd_tensor *dt,
+                         const ssd_tensor *dt_bias, const ssd_tensor *A,
+                         const ssd_tensor *B, const ssd_tensor *C,
+                         const ssd_tensor *D, const ssd_tensor *init_state,
+                         ssd_tensor *out, ssd_tensor *final_state, int chunk,
+                         void *stream);
+
+/* Size in bytes of the fixed scratch array of ssd_scan_fwd_noalloc. */
+int64_t ssd_fixed_scratch_bytes(void);
+
+/*
  * ssd_scan_fwd_gated -- the scan with the block's output gate fused into its
  * output step.  The Mamba block follows the selective SSM with a gate before
  * the output projection (Mamba paper-reading notes, sxlin0.github.io, the

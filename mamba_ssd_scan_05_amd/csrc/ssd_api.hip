@@ -20,6 +20,14 @@
 #include "ssd.h"
 #include "ssd_internal.h"
 
+// Scratch of the allocation-free entry point ssd_scan_fwd_noalloc: a fixed
+// array in the code object's device memory, one copy per device, kept until
+// the process ends.  Host code never passes the array's name to a kernel (in
+// host code it is a stand-in, not a device address): it takes the device
+// address with hipGetSymbolAddress once per device (fixed_scratch_ptr).
+#define SSD_FIXED_SCRATCH_BYTES ((size_t)64 << 20)
+static __device__ __align__(256) unsigned char scratch[SSD_FIXED_SCRATCH_BYTES];
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -208,6 +216,14 @@ std::recursive_mutex g_scratch_mu;
 std::vector<ScratchSlot> g_scratch;
 uint64_t g_scratch_clock = 0;
 
+// The allocation-free entry point points every call it makes at the fixed
+// device array instead (set for the duration of that call on this thread).
+struct FixedScratch {
+  void *p = nullptr;
+  size_t cap = 0;
+};
+thread_local FixedScratch g_fixed;
+
 // Frees slot i (waiting for its last use first) and removes it.  Called with
 // the lock held.
 int drop_slot(size_t i) {
@@ -257,6 +273,15 @@ public:
 
   int get(size_t bytes, void **out) {
     *out = nullptr;
+    if (g_fixed.p) {
+      // allocation-free call: the fixed array, shared by every such call on
+      // this device
+      if (bytes > g_fixed.cap)
+        return fail(SSD_ERR_NOMEM, "this call needs %zu bytes of scratch; the fixed scratch array holds %zu",
+                    bytes, g_fixed.cap);
+      *out = g_fixed.p;
+      return SSD_OK;
+    }
     if (bytes > kScratchKeepMax) {
       const hipError_t e = hipMallocAsync(&own_, bytes, st_);
       if (e != hipSuccess || !own_) {
@@ -356,6 +381,37 @@ private:
   int slot_dev_ = 0;
   hipStream_t slot_st_ = nullptr;
   void *own_ = nullptr;
+};
+
+// Device address of this device's copy of the fixed scratch array, looked up
+// once per device (with that device current) and kept.
+std::mutex g_fixed_mu;
+void *g_fixed_ptr[64] = {};
+
+int fixed_scratch_ptr(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "fixed scratch: current device");
+  if (dev < 0 || dev >= 64) return fail(SSD_ERR_UNSUPPORTED, "device %d: at most 64 devices", dev);
+  std::lock_guard<std::mutex> lock(g_fixed_mu);
+  if (!g_fixed_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return fail(SSD_ERR_HIP, "fixed scratch: hipGetSymbolAddress: %s", hipGetErrorString(e));
+    }
+    g_fixed_ptr[dev] = p;
+  }
+  *out = g_fixed_ptr[dev];
+  return SSD_OK;
+}
+
+// Points this thread's scratch requests at the fixed array for one call.
+class FixedScratchScope {
+public:
+  FixedScratchScope(void *p, size_t cap) { g_fixed = FixedScratch{p, cap}; }
+  ~FixedScratchScope() { g_fixed = FixedScratch{}; }
 };
 
 // Number of buffers kept and their total bytes (tests).
@@ -775,6 +831,22 @@ int ssd_scan_fwd(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt
   return ssd_scan_fwd_algo(x, dt, dt_bias, A, B, C, D, init_state, out, final_state, chunk,
                            SSD_ALGO_AUTO, stream);
 }
+
+int ssd_scan_fwd_noalloc(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bias,
+                         const ssd_tensor *A, const ssd_tensor *B, const ssd_tensor *C,
+                         const ssd_tensor *D, const ssd_tensor *init_state, ssd_tensor *out,
+                         ssd_tensor *final_state, int chunk, void *stream) {
+  g_last_error.clear();
+  ScanShape s;
+  SSD_CHECK(validate_scan(x, dt, dt_bias, A, B, C, D, init_state, out, final_state, chunk, &s));
+  void *p = nullptr;
+  SSD_CHECK(fixed_scratch_ptr(&p));
+  FixedScratchScope scope(p, SSD_FIXED_SCRATCH_BYTES);
+  return scan_dispatch(x, dt, dt_bias, A, B, C, D, nullptr, init_state, out, final_state, s, chunk,
+                       SSD_ALGO_AUTO, stream);
+}
+
+int64_t ssd_fixed_scratch_bytes(void) { return (int64_t)SSD_FIXED_SCRATCH_BYTES; }
 
 int ssd_scratch_stats(int64_t *buffers, int64_t *bytes) {
   g_last_error.clear();

@@ -72,6 +72,10 @@ def lib():
         L.ssd_release_scratch.argtypes = []
         L.ssd_scratch_stats.argtypes = [ctypes.POINTER(ctypes.c_int64)] * 2
         L.ssd_scratch_stats.restype = ctypes.c_int
+        L.ssd_scan_fwd_noalloc.argtypes = [P] * 10 + [ctypes.c_int, ctypes.c_void_p]
+        L.ssd_scan_fwd_noalloc.restype = ctypes.c_int
+        L.ssd_fixed_scratch_bytes.argtypes = []
+        L.ssd_fixed_scratch_bytes.restype = ctypes.c_int64
         L.ssd_scan_plan.argtypes = [ctypes.c_int64] * 6 + [ctypes.c_int, ctypes.c_int,
                                                             ctypes.POINTER(ctypes.c_int),
                                                             ctypes.POINTER(ctypes.c_int)]
@@ -145,6 +149,26 @@ def ssd_scan_fwd(x, dt, dt_bias, A, B, C, D=None, init_state=None, out=None,
             status = lib().ssd_scan_fwd_algo(*args, int(algo), st)
     _check(status)
     return out, final_state
+
+
+def ssd_scan_fwd_noalloc(x, dt, dt_bias, A, B, C, D=None, init_state=None, out=None,
+                         final_state=None, chunk: int = 256, stream=None):
+    """ssd_scan_fwd through the allocation-free entry point (scratch in the
+    library's fixed device array).  out (and final_state, if wanted) should
+    be passed in by callers that cannot allocate; returns (out, final_state)."""
+    if out is None:
+        out = torch.empty_like(x)
+    with _on_device(x):
+        st = _stream(stream, x)
+        status = lib().ssd_scan_fwd_noalloc(
+            describe(x), describe(dt), describe(dt_bias), describe(A), describe(B), describe(C),
+            describe(D), describe(init_state), describe(out), describe(final_state), int(chunk), st)
+    _check(status)
+    return out, final_state
+
+
+def ssd_fixed_scratch_bytes() -> int:
+    return int(lib().ssd_fixed_scratch_bytes())
 
 
 def ssd_scratch_stats():

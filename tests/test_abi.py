@@ -49,6 +49,7 @@ def test_scratch_stats_host_only(ssd):
     # nothing kept in this process: zero buffers, zero bytes; NULL refused
     assert ssd.ssd_scratch_stats() == (0, 0)
     assert ssd.lib().ssd_scratch_stats(None, None) == 1
+    assert ssd.ssd_fixed_scratch_bytes() == 64 << 20
 
 
 def test_version_and_strings(ssd):
