@@ -89,9 +89,10 @@ enum {
                            sequence in order with the state in registers      */
   SSD_ALGO_CHUNKED = 2, /* chunk-parallel: log-decay cumsum, chunk states,
                            inter-chunk state passing, fused intra+output      */
-  SSD_ALGO_ROWS = 3     /* bf16, N in {32, 64, 128}: the causal C B^T scores
-                           of each (batch, group, 64-token block) computed
-                           once and shared by the heads of the group; each
+  SSD_ALGO_ROWS = 3     /* bf16, N in {32, 64, 128}: C, B and the causal
+                           C B^T scores of each (batch, group, 64-token
+                           block) laid out once in matrix-core fragment
+                           order and shared by the heads of the group; each
                            wave walks 16 state rows of one head            */
 };
 
@@ -144,7 +145,7 @@ int ssd_scan_fwd(const ssd_tensor *x, const ssd_tensor *dt,
  * SSD_ALGO_CHUNKED uses `chunk` as its segment length; SSD_ALGO_ROWS
  * returns SSD_ERR_UNSUPPORTED for fp32 inputs or N outside {32, 64, 128}.
  * SSD_ALGO_ROWS and SSD_ALGO_CHUNKED use scratch (see Scratch above; ROWS:
- * b*G*ceil(L/64)*8 KiB). */
+ * b*G*ceil(L/64)*(N/4 + 6) KiB, 38 KiB per block at N = 128). */
 int ssd_scan_fwd_algo(const ssd_tensor *x, const ssd_tensor *dt,
                       const ssd_tensor *dt_bias, const ssd_tensor *A,
                       const ssd_tensor *B, const ssd_tensor *C,

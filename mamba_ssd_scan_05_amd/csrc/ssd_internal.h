@@ -57,7 +57,8 @@ struct RWalkParams {
   const void *B;        // [b, L, G, N] bf16
   const void *C;        // [b, L, G, N] bf16
   const float *D;       // [H] or null
-  const void *scores;   // [b, G, ceil(L/64), 64, 64] bf16 from launch_scores
+  const void *rec;      // [b, G, ceil(L/64), prep_record_blocks(N), 512] bf16
+                        // operand records from launch_prep
   const float *init;    // [b, H, P, N] or null
   void *out;            // [b, L, H, P] bf16
   const void *z;        // [b, L, H, P] bf16 gate input (out = y * silu(z)) or null
@@ -65,10 +66,12 @@ struct RWalkParams {
   int b, L, H, G, P, rows_per_bg, wg_per_bg;
 };
 
-// Causal score tiles C_t . B_t' of every (batch, group, 64-token sub-block),
-// bf16, columns in the fragment order the row-sliced walk reads.
-hipError_t launch_scores(const void *B, const void *C, void *scores, int b, int L, int G,
-                         int N, hipStream_t stream);
+// Operand records of every (batch, group, 64-token sub-block) for the
+// row-sliced walk: C, B and causal C_t . B_t' score fragments in matrix-core
+// lane order (ssd_prep.hip); prep_record_blocks(N) 1 KiB blocks each.
+int prep_record_blocks(int N);
+hipError_t launch_prep(const void *B, const void *C, void *rec, int b, int L, int G, int N,
+                       hipStream_t stream);
 
 // Row-sliced walk with W waves per workgroup (1..8); N in {32, 64, 128}.
 hipError_t launch_rwalk(int N, int W, const RWalkParams &p, hipStream_t stream);

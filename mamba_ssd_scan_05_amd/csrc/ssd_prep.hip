@@ -1,0 +1,138 @@
+// ssd_prep.hip -- per (batch, group, 64-token sub-block) operand records for
+// the row-sliced walk (ssd_rwalk.hip).
+//
+// The method ("Mamba-3 deep dive ch. 2, SSM foundations", 171host.com,
+// section 2.1.2 recurrence and section 2.2.1 matrix form Y = (L o C B^T) X;
+// "Transformers are SSMs" summary, gongshangzheng.github.io, section 1.2:
+// quadratic form inside a block, the N-dimensional state across blocks).
+// Inside a 64-token sub-block every product the walk takes has one operand
+// that depends on the (batch, group) alone: C for the state term S C_t,
+// B for the state update sum_t xs_t B_t^T and the raw scores C_t . B_t' for
+// the intra-block term.  This kernel writes them once per (batch, group,
+// sub-block), already in the per-lane order of the matrix-core fragments
+// the walk feeds, so that the walk copies a record into LDS linearly and
+// reads every fragment as one 16-byte, bank-conflict-free LDS read.
+//
+// Fragment order (v_mfma_f32_16x16x32_bf16, one 1 KiB block per fragment):
+// lane l = li + 16 lg of a block holds eight bf16 K-values for row/column li
+// of the fragment; the K-values of lane group lg are the positions
+// {4lg .. 4lg+3, 16+4lg .. 16+4lg+3} of the 32-wide K-step (the order the
+// state registers and the transposed x reads produce).
+//
+//   C blocks  (ks, u), ks < N/32, u < 4:   C[16u + li][32ks + K(lg)]
+//   B blocks  (ks, kk), ks < 2, kk < N/16: B[32ks + K(lg)][16kk + li]
+//   S blocks  (u, ks) in (0,0) (1,0) (2,0) (2,1) (3,0) (3,1):
+//             S[16u + li][32ks + K(lg)], S[t][t'] = C_t . B_t' for t' <= t,
+//             zero above the diagonal
+//
+// Tokens past the sequence end read as zero.  Record of sub-block k of
+// (batch ib, group g): blocks [C | B | S] at rec + ((ib*G + g)*nsub + k) *
+// rec_blocks(N) * 512 bf16.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ssd_device.h"
+#include "ssd_internal.h"
+
+namespace ssd {
+namespace {
+
+template <int N>
+__global__ void __launch_bounds__(256) prep_kernel(const __bf16 *__restrict__ B, const __bf16 *__restrict__ C,
+                                                   __bf16 *__restrict__ rec, int L, int G, int nsub) {
+  constexpr int NCB = 4 * (N / 32);     // C blocks
+  constexpr int NBB = 2 * (N / 16);     // B blocks
+  constexpr int NRB = NCB + NBB + 6;    // blocks per record
+  constexpr int LDB = tr_ld(N, 2);      // B tile: transposed reads
+  constexpr int LDC = N + 8;            // C tile: row reads
+  constexpr int RW = N / 8;             // 16-byte pieces per row
+  __shared__ __attribute__((aligned(16))) __bf16 sB[64 * LDB];
+  __shared__ __attribute__((aligned(16))) __bf16 sC[64 * LDC];
+
+  const int wg = blockIdx.x;
+  const int k = wg % nsub, bg = wg / nsub;
+  const int g = bg % G, ib = bg / G;
+  const int tid = threadIdx.x, u = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
+  const int t0 = 64 * k, nv = min(64, L - t0);
+  const int64_t rowB = (int64_t)G * N;
+  const int64_t base = ((int64_t)ib * L + t0) * rowB + (int64_t)g * N;
+  const uint32_t bytes = (uint32_t)(((int64_t)(nv - 1) * rowB + N) * 2);
+  const auto rsB = make_rsrc(B + base, bytes);
+  const auto rsC = make_rsrc(C + base, bytes);
+  for (int q = tid; q < 64 * RW; q += 256) {
+    const int j = q / RW, n0 = (q % RW) * 8;
+    const uint32_t off = (uint32_t)((j * rowB + n0) * 2);
+    *reinterpret_cast<float4 *>(&sB[j * LDB + n0]) = bload16(rsB, off);
+    *reinterpret_cast<float4 *>(&sC[j * LDC + n0]) = bload16(rsC, off);
+  }
+  __syncthreads();
+
+  __bf16 *out = rec + ((int64_t)bg * nsub + k) * (NRB * 512);
+  // C blocks: wave u writes the blocks of token tile u
+#pragma unroll
+  for (int ks = 0; ks < N / 32; ++ks) {
+    const FragBF f = ld4x2(&sC[(16 * u + li) * LDC + 32 * ks + 4 * lg], &sC[(16 * u + li) * LDC + 32 * ks + 16 + 4 * lg]);
+    *reinterpret_cast<bf16x8 *>(out + (ks * 4 + u) * 512 + 8 * l) = f.v;
+  }
+  // B blocks: transposed reads of the B tile, blocks split over the waves
+  for (int blk = u; blk < NBB; blk += 4) {
+    const int ks = blk / (N / 16), kk = blk % (N / 16);
+    const FragBF f = trfrag(sB, LDB, 32 * ks, 16 * kk, li, lg);
+    *reinterpret_cast<bf16x8 *>(out + (NCB + blk) * 512 + 8 * l) = f.v;
+  }
+  // Scores of query tile u: A operand = C rows of the queries (K = n),
+  // B operand = B rows of the keys; D[t][t'] in the accumulator layout
+  // (rows 4lg + r = t' within the key tile, column li = t within tile u).
+  FragBF cq[N / 32];
+#pragma unroll
+  for (int ks = 0; ks < N / 32; ++ks) cq[ks] = ld8(&sC[(16 * u + li) * LDC + 32 * ks + 8 * lg]);
+  // key tiles 0..u; a key tile jt supplies K-values of the score fragment
+  // (u, jt / 2): positions 4lg + r (jt even) or 16 + 4lg + r (jt odd)
+  float sv[2][8];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sv[a][e] = 0.f;
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt) {
+    if (jt > u) break;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < N / 32; ++ks)
+      acc = mma(ld8(&sB[(16 * jt + li) * LDB + 32 * ks + 8 * lg]), cq[ks], acc);
+    // acc[r] = B_{16jt + 4lg + r} . C_{16u + li} = S[16u + li][16jt + 4lg + r]
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool keep = 16 * jt + 4 * lg + r <= 16 * u + li;
+      sv[jt / 2][4 * (jt % 2) + r] = keep ? acc[r] : 0.f;
+    }
+  }
+  // score blocks of tile u: (u, 0) and, for u >= 2, (u, 1)
+  const int sb0 = u < 2 ? u : 2 + 2 * (u - 2);
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    if (a == 1 && u < 2) break;
+    *reinterpret_cast<bf16x8 *>(out + (NCB + NBB + sb0 + a) * 512 + 8 * l) = pack8<__bf16>(sv[a]).v;
+  }
+}
+
+} // namespace
+
+int prep_record_blocks(int N) { return 4 * (N / 32) + 2 * (N / 16) + 6; }
+
+hipError_t launch_prep(const void *B, const void *C, void *rec, int b, int L, int G, int N, hipStream_t stream) {
+  const int nsub = (L + 63) / 64;
+  const dim3 grid((unsigned)(b * G * nsub));
+  const __bf16 *Bp = reinterpret_cast<const __bf16 *>(B);
+  const __bf16 *Cp = reinterpret_cast<const __bf16 *>(C);
+  __bf16 *r = reinterpret_cast<__bf16 *>(rec);
+  switch (N) {
+  case 32: hipLaunchKernelGGL(prep_kernel<32>, grid, dim3(256), 0, stream, Bp, Cp, r, L, G, nsub); break;
+  case 64: hipLaunchKernelGGL(prep_kernel<64>, grid, dim3(256), 0, stream, Bp, Cp, r, L, G, nsub); break;
+  case 128: hipLaunchKernelGGL(prep_kernel<128>, grid, dim3(256), 0, stream, Bp, Cp, r, L, G, nsub); break;
+  default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+} // namespace ssd

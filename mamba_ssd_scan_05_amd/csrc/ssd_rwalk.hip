@@ -1,5 +1,4 @@
-// ssd_rwalk.hip -- the row-sliced walk for bf16 inputs and the per-group
-// score precompute it reads.
+// ssd_rwalk.hip -- the row-sliced walk for bf16 inputs.
 //
 // The method ("Mamba-3 deep dive ch. 2, SSM foundations", 171host.com,
 // section 2.1.2 recurrence, section 2.2.1 matrix form Y = (L o C B^T) X;
@@ -14,8 +13,10 @@
 // Two observations shape this kernel:
 //
 // 1. The raw scores C_t . B_t' do not depend on the head, only on its B/C
-//    group.  scores_kernel computes them once per (batch, group, sub-block)
-//    as a causal 64x64 bf16 tile; every head of the group reads that tile.
+//    group.  prep_kernel (ssd_prep.hip) computes them once per (batch,
+//    group, sub-block) as a causal 64x64 bf16 tile, next to the C and B
+//    tiles, all in matrix-core fragment order (the sub-block's record);
+//    every head of the group reads that record.
 //
 // 2. The decay weight is separable: 2^{c_t - q_t'} = 2^{c_t + e} 2^{-q_t' - e}
 //    for any reference e.  The kernel keeps the state as S = 2^e hs, where
@@ -33,10 +34,11 @@
 // Work split: a workgroup of W waves owns 16W consecutive state rows of one
 // (batch, group) -- rows are (head, p) pairs of the heads in the group, 16
 // rows per wave, all in one head -- and walks the sequence in 64-token
-// sub-blocks.  The B and C tiles of a sub-block are staged once in LDS and
-// read by every wave; each wave holds its 16 x N state in MFMA accumulator
-// registers, stages its own 16 columns of x in a private LDS tile and loads
-// the score fragments straight from global memory (L2).  Two schedules of
+// sub-blocks.  The B and C fragments of a sub-block's record are copied
+// once into LDS and read by every wave (one 16-byte read per fragment);
+// each wave holds its 16 x N state in MFMA accumulator registers, stages
+// its own 16 columns of x in a private LDS tile and loads the score
+// fragments of the record straight from global memory (L2).  Two schedules of
 // the same arithmetic (bitwise the same results): with at most four waves
 // every wave has a SIMD to itself and the plain order is fastest; with more,
 // the decay factors of the next sub-block are computed next to the products
@@ -67,54 +69,6 @@ constexpr float kExpLim = 90.f;
 __host__ __device__ constexpr int kperm(int g, int j) { return j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4); }
 
 // ---------------------------------------------------------------------------
-// Scores: Sc[b][g][k][t][32ks + 8lg + j] = C_t . B_{t'} for t' = 32ks +
-// kperm(lg, j) <= t, 0 above the diagonal; t, t' are tokens of sub-block k.
-// One workgroup per (batch, group, sub-block); wave u computes query rows
-// [16u, 16u+16).  Tokens past L read as zero.
-template <int N>
-__global__ void __launch_bounds__(256) scores_kernel(const __bf16 *__restrict__ B, const __bf16 *__restrict__ C,
-                                                     __bf16 *__restrict__ Sc, int L, int G, int nsub) {
-  constexpr int KN = N / 32;
-  const int wg = blockIdx.x;
-  const int k = wg % nsub, bg = wg / nsub;
-  const int g = bg % G, ib = bg / G;
-  const int u = threadIdx.x >> 6, l = threadIdx.x & 63, li = l & 15, lg = l >> 4;
-  const int t0 = 64 * k, nv = min(64, L - t0);
-  const int64_t rowB = (int64_t)G * N;
-  const int64_t base = ((int64_t)ib * L + t0) * rowB + (int64_t)g * N;
-  const uint32_t bytes = (uint32_t)(((int64_t)(nv - 1) * rowB + N) * 2);
-  const auto rsB = make_rsrc(B + base, bytes);
-  const auto rsC = make_rsrc(C + base, bytes);
-
-  // B operand: C rows of the queries t = 16u + li, K = n.
-  FragBF cf[KN];
-#pragma unroll
-  for (int ks = 0; ks < KN; ++ks)
-    cf[ks].v = __builtin_bit_cast(bf16x8, bload16(rsC, (uint32_t)(((16 * u + li) * rowB + 32 * ks + 8 * lg) * 2)));
-  __bf16 *dst = Sc + ((int64_t)wg * 64 + 16 * u + li) * 64;
-#pragma unroll
-  for (int jt = 0; jt < 4; ++jt) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (jt <= u) {
-      // A operand: B rows of the keys t' = 16jt + li; D[t'][t].
-#pragma unroll
-      for (int ks = 0; ks < KN; ++ks) {
-        FragBF bf;
-        bf.v = __builtin_bit_cast(bf16x8, bload16(rsB, (uint32_t)(((16 * jt + li) * rowB + 32 * ks + 8 * lg) * 2)));
-        acc = mma(bf, cf[ks], acc);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (16 * jt + 4 * lg + r > 16 * u + li) acc[r] = 0.f;
-    }
-    bf16x4 v;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) v[r] = (__bf16)acc[r];
-    *reinterpret_cast<bf16x4 *>(dst + 32 * (jt / 2) + 8 * lg + 4 * (jt % 2)) = v;
-  }
-}
-
-// ---------------------------------------------------------------------------
 // The row-sliced walk.
 // This file is built with MFMA accumulators in ordinary VGPRs: with
 // accumulator registers the compiler parks the state tile there and copies
@@ -125,15 +79,16 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
   constexpr int NTH = W * 64;
   constexpr int NT = N / 16;            // n-tiles of the state
   constexpr int KN = N / 32;            // K-steps over n
-  constexpr int LDB = tr_ld(N, 2);      // B tile: transposed reads
-  constexpr int LDC = N + 8;            // C tile: row reads
-  constexpr int RW = N / 8;             // 16-byte pieces per B/C row
-  constexpr int PIECES = 64 * RW;       // per tile
+  constexpr int NCB = 4 * KN;           // C fragment blocks of a record
+  constexpr int NBB = 2 * NT;           // B fragment blocks of a record
+  constexpr int NRB = NCB + NBB + 6;    // blocks per record (C, B, scores)
+  constexpr int PIECES = (NCB + NBB) * 64; // 16-byte pieces staged per sub-block
   constexpr int PPT = (PIECES + NTH - 1) / NTH;
   constexpr int NSF = 6;                // score fragments per lane and sub-block
 
-  __shared__ __attribute__((aligned(16))) __bf16 sB[2][64 * LDB];
-  __shared__ __attribute__((aligned(16))) __bf16 sC[2][64 * LDC];
+  // C and B fragment blocks of a sub-block's record, double-buffered: a
+  // fragment is the 16 bytes of its lane, one conflict-free LDS read
+  __shared__ __attribute__((aligned(16))) __bf16 sRec[2][(NCB + NBB) * 512];
   __shared__ __attribute__((aligned(16))) __bf16 sX[W][64 * 16]; // x[token][16 columns]
   // per-wave token factors, double-buffered: scan() fills the other slot
   __shared__ __attribute__((aligned(16))) float sF0[2][W][64];   // xs scale (fast) / w (slow)
@@ -178,37 +133,22 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
     for (int k = 0; k < NT; ++k) hs[k] = *reinterpret_cast<const f32x4 *>(prm.init + srow + 16 * k + 4 * lg);
   }
 
-  const int64_t rowB = (int64_t)G * N, rowX = (int64_t)H * P;
-  const __bf16 *Bbase = reinterpret_cast<const __bf16 *>(prm.B) + ((int64_t)ib * L * G + g) * N;
-  const __bf16 *Cbase = reinterpret_cast<const __bf16 *>(prm.C) + ((int64_t)ib * L * G + g) * N;
+  const int64_t rowX = (int64_t)H * P;
   const __bf16 *Xbase = reinterpret_cast<const __bf16 *>(prm.x) + (int64_t)ib * L * rowX + (int64_t)h * P + p0;
   const float *dtbase = prm.dt + (int64_t)ib * L * H + h;
   const int nsub = (L + 63) / 64;
-  const __bf16 *Sbase = reinterpret_cast<const __bf16 *>(prm.scores) + (int64_t)bg * nsub * 4096;
+  // records of this (batch, group), one per sub-block
+  const __bf16 *Rbase = reinterpret_cast<const __bf16 *>(prm.rec) + (int64_t)bg * nsub * (NRB * 512);
 
-  // The C tile is stored with the columns of each 32-column group permuted
-  // (column 32ks + 8g + j holds n = 32ks + kperm(g, j)), so that a state-term
-  // fragment is one 16-byte read.  A piece of 8 consecutive n, the m-th of
-  // its 32-column group, splits into two 4-column halves stored 8 columns
-  // apart, the first at column 16m (m < 2) or 16(m - 2) + 4 (m >= 2).
-  //
   // Loop-invariant offsets.  Every wave issues the same sequence of memory
   // operations on every path through the loop (threads without a piece of
   // their own repeat the last piece; fetches past the end use empty ranges
   // and read zeros; stores of idle waves fall outside an empty range), so
   // the compiler can wait for exactly the loads each step needs while
   // later loads and the y stores stay in flight.
-  uint32_t offBC[PPT];
-  int ldsB[PPT], ldsC[PPT];
+  uint32_t offR[PPT];
 #pragma unroll
-  for (int i = 0; i < PPT; ++i) {
-    const int q = min(tid + i * NTH, PIECES - 1);
-    const int j = q / RW, n0 = (q % RW) * 8;
-    const int mq = (n0 % 32) / 8;
-    offBC[i] = (uint32_t)((j * rowB + n0) * 2);
-    ldsB[i] = j * LDB + n0;
-    ldsC[i] = j * LDC + (n0 / 32) * 32 + (mq < 2 ? 16 * mq : 16 * (mq - 2) + 4);
-  }
+  for (int i = 0; i < PPT; ++i) offR[i] = (uint32_t)min(tid + i * NTH, PIECES - 1) * 16u;
   // x pieces of this wave: piece l + 64e = (token, half) -> 8 columns.
   uint32_t offX[2];
   int ldsX[2];
@@ -218,16 +158,7 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
     offX[e] = (uint32_t)((tok * rowX + 8 * half) * 2);
     ldsX[e] = tok * 16 + 8 * half;
   }
-  // score fragments: (u, ks) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
-  uint32_t offS[NSF];
-#pragma unroll
-  for (int f = 0; f < NSF; ++f) {
-    const int u = f < 2 ? f : 2 + (f - 2) / 2, ks = f < 2 ? 0 : (f - 2) % 2;
-    offS[f] = (uint32_t)(((16 * u + li) * 64 + 32 * ks + 8 * lg) * 2);
-  }
-  const auto rsS = make_rsrc(Sbase, (uint32_t)nsub * 4096u * 2u);
-
-  float4 rB[PPT], rC[PPT], rX[2];
+  float4 rR[PPT], rX[2];
   // B, C and x of sub-block k (loads past the end read zeros).  With more
   // than four waves the byte counts are formed before the select, which
   // makes the choice a scalar select and keeps the loop body one scheduling
@@ -235,20 +166,10 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
   // measured; the gated walk keeps the branch form as well).
   auto fetch_bcx = [&](int k) {
     const int t0 = 64 * k, nv = min(64, L - t0);
-    uint32_t bcb;
-    if constexpr (W > 4 && !GATED) {
-      const uint32_t bcb0 = (uint32_t)(((int64_t)(nv - 1) * rowB + N) * 2);
-      bcb = nv > 0 ? bcb0 : 0u;
-    } else {
-      bcb = nv > 0 ? (uint32_t)(((int64_t)(nv - 1) * rowB + N) * 2) : 0u;
-    }
-    const auto rsB = make_rsrc(Bbase + (int64_t)t0 * rowB, bcb);
-    const auto rsC = make_rsrc(Cbase + (int64_t)t0 * rowB, bcb);
+    const uint32_t bcb = nv > 0 ? (uint32_t)PIECES * 16u : 0u;
+    const auto rsR = make_rsrc(Rbase + (int64_t)min(k, nsub - 1) * (NRB * 512), bcb);
 #pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      rB[i] = bload16(rsB, offBC[i]);
-      rC[i] = bload16(rsC, offBC[i]);
-    }
+    for (int i = 0; i < PPT; ++i) rR[i] = bload16(rsR, offR[i]);
     uint32_t nbX;
     if constexpr (W > 4 && !GATED) {
       const uint32_t nbX0 = (uint32_t)(((int64_t)(nv - 1) * rowX + 16) * 2);
@@ -270,17 +191,13 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
   // sub-block's intra-block product has consumed the registers.
   FragBF sf[NSF];
   auto fetch_scores = [&](int k) {
+    const auto rsS = make_rsrc(Rbase + (int64_t)k * (NRB * 512) + (NCB + NBB) * 512, NSF * 1024u);
 #pragma unroll
-    for (int f = 0; f < NSF; ++f)
-      sf[f].v = __builtin_bit_cast(bf16x8, bload16(rsS, (uint32_t)k * 8192u + offS[f]));
+    for (int f = 0; f < NSF; ++f) sf[f].v = __builtin_bit_cast(bf16x8, bload16(rsS, (uint32_t)(f * 1024 + 16 * l)));
   };
   auto stage = [&](int slot) {
 #pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      *reinterpret_cast<float4 *>(&sB[slot][ldsB[i]]) = rB[i];
-      *reinterpret_cast<float2 *>(&sC[slot][ldsC[i]]) = make_float2(rC[i].x, rC[i].y);
-      *reinterpret_cast<float2 *>(&sC[slot][ldsC[i] + 8]) = make_float2(rC[i].z, rC[i].w);
-    }
+    for (int i = 0; i < PPT; ++i) *reinterpret_cast<float4 *>(&sRec[slot][offR[i] / 2]) = rR[i];
     *reinterpret_cast<float4 *>(&sX[w][ldsX[0]]) = rX[0];
     *reinterpret_cast<float4 *>(&sX[w][ldsX[1]]) = rX[1];
   };
@@ -376,7 +293,7 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
     for (int ks = 0; ks < KN; ++ks) {
       FragBF cf[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) cf[u] = ld8(&sC[slot][(16 * u + li) * LDC + 8 * lg + 32 * ks]);
+      for (int u = 0; u < 4; ++u) cf[u] = ld8(&sRec[slot][(ks * 4 + u) * 512 + 8 * l]);
 #pragma unroll
       for (int u = 0; u < 4; ++u) yacc[u] = mma(hf[ks], cf[u], yacc[u]);
     }
@@ -386,7 +303,7 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int kk = 0; kk < NT; ++kk) hs[kk] = mma(trfrag(sB[slot], LDB, 32 * ks, 16 * kk, li, lg), xs[ks], hs[kk]);
+      for (int kk = 0; kk < NT; ++kk) hs[kk] = mma(ld8(&sRec[slot][(NCB + ks * NT + kk) * 512 + 8 * l]), xs[ks], hs[kk]);
   };
   // Per-element path: decay the state by 2^{c_last} before its update (its xs
   // holds 2^{c_last - q - e} x).
@@ -646,22 +563,6 @@ hipError_t launch_rwalk_n(int W, const RWalkParams &p, int nwg, hipStream_t st) 
 }
 
 } // namespace
-
-hipError_t launch_scores(const void *B, const void *C, void *scores_v, int b, int L, int G, int N,
-                         hipStream_t stream) {
-  const int nsub = (L + 63) / 64;
-  __bf16 *scores = reinterpret_cast<__bf16 *>(scores_v);
-  const dim3 grid((unsigned)(b * G * nsub));
-  const __bf16 *Bp = reinterpret_cast<const __bf16 *>(B);
-  const __bf16 *Cp = reinterpret_cast<const __bf16 *>(C);
-  switch (N) {
-  case 32: hipLaunchKernelGGL(scores_kernel<32>, grid, dim3(256), 0, stream, Bp, Cp, scores, L, G, nsub); break;
-  case 64: hipLaunchKernelGGL(scores_kernel<64>, grid, dim3(256), 0, stream, Bp, Cp, scores, L, G, nsub); break;
-  case 128: hipLaunchKernelGGL(scores_kernel<128>, grid, dim3(256), 0, stream, Bp, Cp, scores, L, G, nsub); break;
-  default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
 
 hipError_t launch_rwalk(int N, int W, const RWalkParams &p, hipStream_t stream) {
   const int nwg = p.b * p.G * p.wg_per_bg;
