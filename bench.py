@@ -8,12 +8,25 @@ workload (b=4, L=4096, H=80, P=64, G=1, N=128, chunk 256, bf16 inputs,
 fp32 initial and final state), inputs resident in HBM.  W untimed steps,
 then exactly K timed steps between two device synchronisations; value =
 b*L*K / elapsed.  Each step is also bracketed by HIP events on the stream
-the library launches on, giving the kernel's average duration for the
-roofline figure.  Rank 0 prints one JSON line.
+the library launches on, giving the call's average duration for the
+roofline figure (every launch of the call: the operand records and the
+walk under the automatic plan).  Rank 0 prints one JSON line.
 
-Also reported (context, not the metric): the recurrent-step workload
-(b=256, H=80, P=64, N=128, 64 steps) and the fp64 oracle timed on the host
-cores (cpu_baseline).
+Cold-cache protocol (roofline.cold and extra.configs): 30 repetitions,
+each after a 512 MiB device write on the same stream (outside the events)
+that evicts L2 and the 256 MB MALL; median with p10/p90.  The warm figure
+is the mean of back-to-back calls.
+
+Also reported (context, not the metric): every scan workload under the
+automatic plan, the other algorithms, the gated scan, the backward, the
+selective scan, the recurrent-step workload (b=256, H=80, P=64, N=128, 64
+steps) and the fp64 oracle timed on the host cores (cpu_baseline, all
+threads and one thread).
+
+Counter runs (rocprofv3 --pmc) use the same entry with a short leg mix,
+e.g. --steps 3 --warmup 1 --no-cpu-baseline --no-configs --copy-probe;
+--copy-probe adds a 1 GiB device copy whose FETCH_SIZE / WRITE_SIZE
+calibrate the byte counters.
 """
 from __future__ import annotations
 
@@ -67,28 +80,41 @@ def step_bytes(b, H, P, G, N, dtype):
     return 2 * b * H * P * N * 4 + 2 * b * H * P * e + 2 * b * G * N * e + b * H * 4 + 2 * H * 4
 
 
-def kernel_sha():
-    """Hash of every kernel source: counter-derived traffic is used only for
-    the exact sources it was measured on."""
+# Sources each plan's kernels are built from (the launch plan itself is
+# fixed by the shape): counter-derived traffic is used only while these
+# files are unchanged since the counters were taken.
+PLAN_SOURCES = {
+    "rows": ["ssd_rwalk.hip", "ssd_prep.hip", "ssd_device.h", "ssd_internal.h"],
+    "chunked": ["ssd_kernels.hip", "ssd_device.h", "ssd_internal.h"],
+    "fused": ["ssd_kernels.hip", "ssd_device.h", "ssd_internal.h"],
+    "step": ["ssd_kernels.hip", "ssd_device.h", "ssd_internal.h"],
+    "bwd": ["ssd_bwd.hip", "ssd_device.h", "ssd_internal.h"],
+    "sscan": ["ssd_sscan.hip", "ssd_device.h", "ssd_internal.h"],
+}
+
+
+def kernel_sha(files):
+    """Hash of the named kernel sources (sha256, first 16 hex digits)."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".h")):
-            h.update(name.encode())
-            h.update(open(os.path.join(CSRC, name), "rb").read())
+    for name in sorted(files):
+        h.update(name.encode())
+        h.update(open(os.path.join(CSRC, name), "rb").read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel, workload):
-    """HBM bytes per launch from committed counter runs, if the kernel source
-    is unchanged since they were taken; else None."""
+def load_traffic(plan, workload):
+    """HBM bytes per call of a plan from committed counter runs (the sum
+    over the call's launches), if its kernel sources are unchanged since
+    they were taken; else None."""
     try:
         t = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    rec = t.get(kernel, {}).get(workload)
-    if not rec or rec.get("kernel_source_sha") != kernel_sha():
+    rec = t.get(plan, {}).get(workload)
+    base = plan.split("_seg")[0]
+    if not rec or base not in PLAN_SOURCES or rec.get("kernel_source_sha") != kernel_sha(PLAN_SOURCES[base]):
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec.get("hbm_bytes_per_call")
 
 
 def cpu_baseline(si, reps):
@@ -418,8 +444,8 @@ def main():
         dominant = "walk_kernel (fused walk, one launch)"
         seg_len = L
     elif used_algo == "rows":
-        dominant = ("rwalk_kernel (row-sliced walk) with its scores_kernel precompute: the "
-                    "timed duration is the whole call, both launches")
+        dominant = ("rwalk_kernel (row-sliced walk) with its prep_kernel operand records: "
+                    "the timed duration is the whole call, both launches")
         seg_len = L
     else:
         dominant = ("ssd_scan_fwd chunked path, segment %d: cumsum + chunk-state walk + "
