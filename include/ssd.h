@@ -89,11 +89,17 @@ enum {
                            sequence in order with the state in registers      */
   SSD_ALGO_CHUNKED = 2, /* chunk-parallel: log-decay cumsum, chunk states,
                            inter-chunk state passing, fused intra+output      */
-  SSD_ALGO_ROWS = 3     /* bf16, N in {32, 64, 128}: C, B and the causal
+  SSD_ALGO_ROWS = 3,    /* bf16, N in {32, 64, 128}: C, B and the causal
                            C B^T scores of each (batch, group, 64-token
                            block) laid out once in matrix-core fragment
                            order and shared by the heads of the group; each
                            wave walks 16 state rows of one head            */
+  SSD_ALGO_QUAD = 4     /* L <= 256: the whole-sequence quadratic form
+                           Y = (L o C B^T) X (+ D x, + the decayed initial
+                           state) with no state carried between blocks: one
+                           workgroup per (batch, head, 64-token query
+                           block), its key blocks spread over its waves;
+                           P in {16,32,64} (128 for bf16)                   */
 };
 
 /* Dense tensor descriptor.  shape/strides beyond ndim are ignored; strides

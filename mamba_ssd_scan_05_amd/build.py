@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libssd.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-SOURCES = ["ssd_api.hip", "ssd_kernels.hip", "ssd_prep.hip", "ssd_rwalk.hip", "ssd_sscan.hip", "ssd_bwd.hip"]
+SOURCES = ["ssd_api.hip", "ssd_kernels.hip", "ssd_prep.hip", "ssd_quad.hip", "ssd_rwalk.hip", "ssd_sscan.hip", "ssd_bwd.hip"]
 # Per-source flags.  The row walk keeps its MFMA accumulators (the state
 # tile) in ordinary VGPRs; otherwise the compiler places them in accumulator
 # registers and copies them to VGPRs and back on every sub-block.

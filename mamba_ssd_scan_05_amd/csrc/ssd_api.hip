@@ -467,6 +467,31 @@ int run_fused(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bi
   return e == hipSuccess ? SSD_OK : hip_fail(e, "fused walk launch");
 }
 
+// The quadratic path takes L <= 256 and every P the fused walk takes
+// except 128 with fp32 inputs.
+bool quad_supported(int dtype, const ScanShape &s) {
+  return s.L <= ssd::kQuadMaxL && (s.P <= 64 || dtype == SSD_BF16);
+}
+
+int run_quad(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bias,
+             const ssd_tensor *A, const ssd_tensor *B, const ssd_tensor *C,
+             const ssd_tensor *D, const ssd_tensor *z, const ssd_tensor *init, ssd_tensor *out,
+             ssd_tensor *fin, const ScanShape &s, hipStream_t st) {
+  ssd::WalkParams p{};
+  p.x = x->data; p.dt = (const float *)dt->data;
+  p.dt_bias = dt_bias ? (const float *)dt_bias->data : nullptr;
+  p.A = (const float *)A->data; p.B = B->data; p.C = C->data;
+  p.D = D ? (const float *)D->data : nullptr;
+  p.init = init ? (const float *)init->data : nullptr;
+  p.out = out->data;
+  p.z = z ? z->data : nullptr;
+  p.final_state = fin ? (float *)fin->data : nullptr;
+  p.b = (int)s.b; p.L = (int)s.L; p.H = (int)s.H; p.G = (int)s.G;
+  p.seg_len = (int)s.L; p.nseg = 1;
+  hipError_t e = ssd::launch_quad(x->dtype, (int)s.P, (int)s.N, p, st);
+  return e == hipSuccess ? SSD_OK : hip_fail(e, "quadratic path launch");
+}
+
 int run_chunked(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bias,
                 const ssd_tensor *A, const ssd_tensor *B, const ssd_tensor *C,
                 const ssd_tensor *D, const ssd_tensor *z, const ssd_tensor *init, ssd_tensor *out,
@@ -643,6 +668,15 @@ Plan choose_plan(const ScanShape &s, int dtype, int cus) {
       best.algo = SSD_ALGO_ROWS;
     }
   }
+  // Quadratic path (L <= 256): one workgroup per (batch, head, query block)
+  // with no chain of blocks; taken when those workgroups fit one pass over
+  // the units and there is a chain to avoid (two or more blocks).  Measured
+  // kernel times: fp32 b=1, L=256, H=4, P=N=16 12.0 us against 19.6 us for
+  // one walk per head; bf16 b=1, L=256, H=80 (320 workgroups, two passes)
+  // 15.4 us against 16.6 us, and b=8, L=256, H=32 (1024 workgroups) 33.5
+  // us against 18.6 us.
+  if (quad_supported(dtype, s) && nsub >= 2 && s.b * s.H * nsub <= cus)
+    return Plan{SSD_ALGO_QUAD, (int)s.L};
   double best_t = 0.9 * single_t;
   for (int seg = 65536; seg >= 256; seg /= 2) {
     const int64_t S = (s.L + seg - 1) / seg;
@@ -666,10 +700,13 @@ int scan_dispatch(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *d
                   ssd_tensor *out, ssd_tensor *final_state, const ScanShape &s, int chunk, int algo,
                   void *stream) {
   if (algo != SSD_ALGO_AUTO && algo != SSD_ALGO_FUSED && algo != SSD_ALGO_CHUNKED &&
-      algo != SSD_ALGO_ROWS)
+      algo != SSD_ALGO_ROWS && algo != SSD_ALGO_QUAD)
     return fail(SSD_ERR_UNSUPPORTED, "unknown algorithm %d", algo);
   if (algo == SSD_ALGO_ROWS && !rows_supported(x->dtype, s.N))
     return fail(SSD_ERR_UNSUPPORTED, "row-sliced walk needs bf16 inputs and N in {32,64,128}");
+  if (algo == SSD_ALGO_QUAD && !quad_supported(x->dtype, s))
+    return fail(SSD_ERR_UNSUPPORTED, "quadratic path needs L <= %d (L=%lld) and P <= 64 with fp32 inputs",
+                ssd::kQuadMaxL, (long long)s.L);
   {
     const ssd_tensor *ts[] = {x, dt, dt_bias, A, B, C, D, z, init_state, out, final_state};
     const char *nm[] = {"x", "dt", "dt_bias", "A", "B", "C", "D", "z", "init_state", "out", "final_state"};
@@ -686,6 +723,8 @@ int scan_dispatch(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *d
     return run_rows(x, dt, dt_bias, A, B, C, D, z, init_state, out, final_state, s, rows_waves(s, cus), st);
   if (algo == SSD_ALGO_FUSED)
     return run_fused(x, dt, dt_bias, A, B, C, D, z, init_state, out, final_state, s, st);
+  if (algo == SSD_ALGO_QUAD)
+    return run_quad(x, dt, dt_bias, A, B, C, D, z, init_state, out, final_state, s, st);
   return run_chunked(x, dt, dt_bias, A, B, C, D, z, init_state, out, final_state, s, chunk, st);
 }
 

@@ -45,6 +45,14 @@ enum WalkMode {
 hipError_t launch_walk(int dtype, int P, int N, WalkMode mode,
                        const WalkParams &p, hipStream_t stream);
 
+// Whole-sequence quadratic form for L <= kQuadMaxL (ssd_quad.hip): one
+// workgroup per (batch, head, 64-token query block); reads x, dt (raw),
+// dt_bias, A, B, C, D, init, z and writes out and final_state of p
+// (seg_len, nseg, state_out and seg_decay unused).  P in {16, 32, 64} (and
+// 128 for bf16), N in {16, 32, 64, 128}.
+constexpr int kQuadMaxL = 256;
+hipError_t launch_quad(int dtype, int P, int N, const WalkParams &p, hipStream_t stream);
+
 // Parameters of the row-sliced walk (bf16 inputs).  A workgroup of W waves
 // owns 16W consecutive state rows -- (head, p) pairs of the heads of one
 // group -- of one (batch, group); rows_per_bg = (H/G)*P, wg_per_bg =

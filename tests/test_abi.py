@@ -243,6 +243,14 @@ def test_plan(ssd):
         st = lib.ssd_scan_plan(b, L, H, P, G, N, dtype, cus, ct.byref(algo), ct.byref(seg))
         assert st == 0
         return algo.value, seg.value
+    # short sequences whose (batch, head, 64-token block) workgroups fit one
+    # pass over the units: the quadratic path (the tiny fp32 workload: 12.0
+    # us kernel time against 19.6 us for one walk per head)
+    assert plan(1, 256, 4, P=16, N=16, dtype=0) == (ssd.SSD_ALGO_QUAD, 256)
+    assert plan(1, 200, 16, dtype=1) == (ssd.SSD_ALGO_QUAD, 200)
+    assert plan(1, 64, 4, dtype=0)[0] != ssd.SSD_ALGO_QUAD     # one block: no chain to avoid
+    assert plan(8, 256, 32)[0] != ssd.SSD_ALGO_QUAD           # 1024 workgroups: 33.5 against 18.6 us
+    assert plan(1, 257, 4, dtype=0)[0] != ssd.SSD_ALGO_QUAD   # above 256 tokens
     assert plan(8, 2048, 32) == (ssd.SSD_ALGO_ROWS, 2048)    # 370M layer
     assert plan(4, 4096, 80) == (ssd.SSD_ALGO_ROWS, 4096)    # 2.7B layer
     assert plan(4, 4096, 80, dtype=0) == (ssd.SSD_ALGO_CHUNKED, 1024)
@@ -254,7 +262,7 @@ def test_plan(ssd):
     a, s = plan(1, 4096, 16, dtype=0)                 # 16 walks on 256 units
     assert a == ssd.SSD_ALGO_CHUNKED
     a, s = plan(1, 100, 2)
-    assert a in (1, 2, 3) and s >= 64
+    assert a == ssd.SSD_ALGO_QUAD and s == 100
     assert lib.ssd_scan_plan(0, 10, 2, 64, 1, 128, 1, 256, ct.byref(algo), ct.byref(seg)) == 2
     assert lib.ssd_scan_plan(1, 10, 2, 64, 1, 128, 7, 256, ct.byref(algo), ct.byref(seg)) == 3
 
@@ -277,7 +285,21 @@ def test_rows_rejections(ssd):
     a["x"] = torch.zeros(1, 99, 4, 16, dtype=torch.bfloat16)   # L disagrees with dt
     assert call(a, 1) == 2
     assert _call_scan(ssd, _scan_args(dtype=torch.float32), algo=3)[0] == 5
-    assert _call_scan(ssd, _scan_args(), algo=4)[0] == 5
+    assert _call_scan(ssd, _scan_args(), algo=5)[0] == 5
+
+
+def test_quad_rejections(ssd):
+    """The quadratic path (SSD_ALGO_QUAD) takes L <= 256 only and, for fp32
+    inputs, P <= 64 (fp32 P = 128 is refused by every algorithm); the check
+    comes before any device call."""
+    st, msg = _call_scan(ssd, _scan_args(L=257), algo=4)
+    assert st == 5 and "quadratic" in msg, (st, msg)
+    st, msg = _call_scan(ssd, _scan_args(L=257, dtype=torch.float32), algo=4)
+    assert st == 5 and "quadratic" in msg, (st, msg)
+    # L = 256 passes the quadratic-path check and stops at the device check
+    # (no GPU here; host memory on a GPU box)
+    st, msg = _call_scan(ssd, _scan_args(L=256), algo=4)
+    assert st == 4 and "quadratic" not in msg, (st, msg)
 
 
 def test_gated_rejections(ssd):
@@ -295,7 +317,7 @@ def test_gated_rejections(ssd):
     assert call(a, torch.zeros(1, 100, 4, 16)) == 3
     assert call(a, torch.zeros(1, 4, 100, 16, dtype=torch.bfloat16).transpose(1, 2)) == 4
     assert call(a, a["out"]) == 6
-    assert call(a, torch.zeros(1, 100, 4, 16, dtype=torch.bfloat16), algo=4) == 5
+    assert call(a, torch.zeros(1, 100, 4, 16, dtype=torch.bfloat16), algo=5) == 5
     b = _scan_args()
     b["x"] = None
     assert call(b, torch.zeros(1, 100, 4, 16, dtype=torch.bfloat16)) == 1
