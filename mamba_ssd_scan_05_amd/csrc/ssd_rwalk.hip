@@ -34,15 +34,13 @@
 // Work split: a workgroup of W waves owns 16W consecutive state rows of one
 // (batch, group) -- rows are (head, p) pairs of the heads in the group, 16
 // rows per wave, all in one head -- and walks the sequence in 64-token
-// sub-blocks.  The B and C fragments of a sub-block's record are copied
-// once into LDS and read by every wave (one 16-byte read per fragment);
-// each wave holds its 16 x N state in MFMA accumulator registers, stages
-// its own 16 columns of x in a private LDS tile and loads the score
-// fragments of the record straight from global memory (L2).  Two schedules of
-// the same arithmetic (bitwise the same results): with at most four waves
-// every wave has a SIMD to itself and the plain order is fastest; with more,
-// the decay factors of the next sub-block are computed next to the products
-// of the current one.
+// sub-blocks.  A sub-block's whole record (C, B and score fragments) is
+// copied once into LDS and read by every wave (one 16-byte read per
+// fragment); each wave holds its 16 x N state in MFMA accumulator
+// registers and has its own 16 columns of x copied into a private LDS tile.
+// The copies go straight from global memory to LDS (buffer loads to LDS),
+// one sub-block ahead, so they hold no registers; the decay factors of the
+// next sub-block are formed next to the current sub-block's state update.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -76,35 +74,35 @@ __host__ __device__ constexpr int kperm(int g, int j) { return j < 4 ? 4 * g + j
 // GATED: out = y * silu(z) with z read next to y.
 template <int N, int W, bool GATED>
 __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
-  constexpr int NTH = W * 64;
-  constexpr int NT = N / 16;            // n-tiles of the state
-  constexpr int KN = N / 32;            // K-steps over n
-  constexpr int NCB = 4 * KN;           // C fragment blocks of a record
-  constexpr int NBB = 2 * NT;           // B fragment blocks of a record
-  constexpr int NRB = NCB + NBB + 6;    // blocks per record (C, B, scores)
-  constexpr int PIECES = (NCB + NBB) * 64; // 16-byte pieces staged per sub-block
-  constexpr int PPT = (PIECES + NTH - 1) / NTH;
-  constexpr int NSF = 6;                // score fragments per lane and sub-block
+  constexpr int NT = N / 16;             // n-tiles of the state
+  constexpr int KN = N / 32;             // K-steps over n
+  constexpr int NCB = 4 * KN;            // C fragment blocks of a record
+  constexpr int NBB = 2 * NT;            // B fragment blocks of a record
+  constexpr int NRB = NCB + NBB + 6;     // blocks per record (C, B, scores)
+  constexpr int NSF = 6;                 // score fragments per sub-block
+  constexpr int CPW = (NRB + W - 1) / W; // record blocks each wave copies
 
-  // C and B fragment blocks of a sub-block's record, double-buffered: a
-  // fragment is the 16 bytes of its lane, one conflict-free LDS read
-  __shared__ __attribute__((aligned(16))) __bf16 sRec[2][(NCB + NBB) * 512];
-  __shared__ __attribute__((aligned(16))) __bf16 sX[W][64 * 16]; // x[token][16 columns]
-  // per-wave token factors, double-buffered: scan() fills the other slot
-  __shared__ __attribute__((aligned(16))) float sF0[2][W][64];   // xs scale (fast) / w (slow)
-  __shared__ __attribute__((aligned(16))) float sF1[2][W][64];   // y scale 2^{c + e}
-  __shared__ __attribute__((aligned(16))) float2 sQC[2][W][64];  // (q, c) for the slow path
-  // With more than four waves: y of a sub-block for all rows of the
-  // workgroup, [token][row], written by each wave and stored after the next
-  // barrier as whole row runs.
-  constexpr int YLD = 16 * W + 8;
-  __shared__ __attribute__((aligned(16))) __bf16 sY[2][(W > 4 ? 64 : 1) * YLD];
+  // A sub-block's record and each wave's x tile are copied from global
+  // memory straight into LDS (buffer loads to LDS: no registers, no LDS
+  // writes), double-buffered.  The two buffers are distinct arrays and the
+  // loop is unrolled by two, so every LDS address is static: the compiler
+  // can tell the buffer being read from the one being filled and adds no
+  // wait for the copy in flight.
+  __shared__ __attribute__((aligned(16))) __bf16 sRecA[NRB * 512];
+  __shared__ __attribute__((aligned(16))) __bf16 sRecB[NRB * 512];
+  __shared__ __attribute__((aligned(16))) __bf16 sXA[W][64 * 16]; // x[token][16 columns]
+  __shared__ __attribute__((aligned(16))) __bf16 sXB[W][64 * 16];
+  // per-wave token factors, two sub-blocks: those of sub-block k + 1 are
+  // formed at the end of sub-block k, next to its state update
+  __shared__ __attribute__((aligned(16))) float sF0[2][W][64];  // xs scale (fast) / w (slow)
+  __shared__ __attribute__((aligned(16))) float sF1[2][W][64];  // y scale 2^{c + e}
+  __shared__ __attribute__((aligned(16))) float2 sQC[2][W][64]; // (q, c) for the slow path
 
   const int H = prm.H, G = prm.G, L = prm.L, P = prm.P;
   const int nwg = gridDim.x, bid = blockIdx.x;
   // XCD-aware order: consecutive ids go round-robin to the 8 XCDs; give
   // each XCD a contiguous range of logical ids so that the workgroups of one
-  // (batch, group) share its B/C/score tiles through one L2.
+  // (batch, group) share its records through one L2.
   const int logical = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;
   const int bg = logical / prm.wg_per_bg, wi = logical % prm.wg_per_bg;
   const int g = bg % G, ib = bg / G;
@@ -140,66 +138,38 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
   // records of this (batch, group), one per sub-block
   const __bf16 *Rbase = reinterpret_cast<const __bf16 *>(prm.rec) + (int64_t)bg * nsub * (NRB * 512);
 
-  // Loop-invariant offsets.  Every wave issues the same sequence of memory
-  // operations on every path through the loop (threads without a piece of
-  // their own repeat the last piece; fetches past the end use empty ranges
-  // and read zeros; stores of idle waves fall outside an empty range), so
-  // the compiler can wait for exactly the loads each step needs while
-  // later loads and the y stores stay in flight.
-  uint32_t offR[PPT];
-#pragma unroll
-  for (int i = 0; i < PPT; ++i) offR[i] = (uint32_t)min(tid + i * NTH, PIECES - 1) * 16u;
-  // x pieces of this wave: piece l + 64e = (token, half) -> 8 columns.
+  // x pieces of this wave: piece l + 64e = (token, half) -> 8 columns, which
+  // lands at byte 16 (l + 64e) of the wave's x tile (one 1 KiB copy per e).
   uint32_t offX[2];
-  int ldsX[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const int pc = l + 64 * e, tok = pc >> 1, half = pc & 1;
     offX[e] = (uint32_t)((tok * rowX + 8 * half) * 2);
-    ldsX[e] = tok * 16 + 8 * half;
   }
-  float4 rR[PPT], rX[2];
-  // B, C and x of sub-block k (loads past the end read zeros).  With more
-  // than four waves the byte counts are formed before the select, which
-  // makes the choice a scalar select and keeps the loop body one scheduling
-  // region; with one wave per SIMD the branch form schedules better (both
-  // measured; the gated walk keeps the branch form as well).
-  auto fetch_bcx = [&](int k) {
+  // Copy the record and this wave's x of sub-block k into (rec, xt).  Wave w
+  // copies record blocks w, w + W, ... (the last block again where it has
+  // none of its own, so every wave issues the same number of copies); copies
+  // past the end of the sequence use empty ranges and write zeros.
+  auto copy_in = [&](int k, __bf16 *rec, __bf16 (*xt)[1024]) {
     const int t0 = 64 * k, nv = min(64, L - t0);
-    const uint32_t bcb = nv > 0 ? (uint32_t)PIECES * 16u : 0u;
-    const auto rsR = make_rsrc(Rbase + (int64_t)min(k, nsub - 1) * (NRB * 512), bcb);
+    const auto rsR = make_rsrc(Rbase + (int64_t)min(k, nsub - 1) * (NRB * 512), nv > 0 ? (uint32_t)NRB * 1024u : 0u);
 #pragma unroll
-    for (int i = 0; i < PPT; ++i) rR[i] = bload16(rsR, offR[i]);
-    uint32_t nbX;
-    if constexpr (W > 4 && !GATED) {
-      const uint32_t nbX0 = (uint32_t)(((int64_t)(nv - 1) * rowX + 16) * 2);
-      nbX = nv > 0 ? nbX0 : 0u;
-    } else {
-      nbX = nv > 0 ? (uint32_t)(((int64_t)(nv - 1) * rowX + 16) * 2) : 0u;
+    for (int i = 0; i < CPW; ++i) {
+      const int c = min(w + i * W, NRB - 1);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsR, (__attribute__((address_space(3))) void *)&rec[c * 512], 16,
+                                               l * 16, c * 1024, 0, 0);
     }
-    const auto rsX = make_rsrc(Xbase + (int64_t)t0 * rowX, nbX);
-    rX[0] = bload16(rsX, offX[0]);
-    rX[1] = bload16(rsX, offX[1]);
+    const auto rsX = make_rsrc(Xbase + (int64_t)t0 * rowX, nv > 0 ? (uint32_t)(((int64_t)(nv - 1) * rowX + 16) * 2) : 0u);
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsX, (__attribute__((address_space(3))) void *)&xt[w][512 * e], 16,
+                                               offX[e], 0, 0, 0);
   };
   // Raw step size of token l of sub-block k (zero past the end).
   auto fetch_dt = [&](int k) {
     const int t0 = 64 * k, nv = min(64, L - t0);
     const auto rsD = make_rsrc(dtbase + (int64_t)t0 * H, nv > 0 ? (uint32_t)(((int64_t)(nv - 1) * H + 1) * 4) : 0u);
     return bload4(rsD, (uint32_t)(l * H * 4));
-  };
-  // Score fragments of sub-block k, issued right after the previous
-  // sub-block's intra-block product has consumed the registers.
-  FragBF sf[NSF];
-  auto fetch_scores = [&](int k) {
-    const auto rsS = make_rsrc(Rbase + (int64_t)k * (NRB * 512) + (NCB + NBB) * 512, NSF * 1024u);
-#pragma unroll
-    for (int f = 0; f < NSF; ++f) sf[f].v = __builtin_bit_cast(bf16x8, bload16(rsS, (uint32_t)(f * 1024 + 16 * l)));
-  };
-  auto stage = [&](int slot) {
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) *reinterpret_cast<float4 *>(&sRec[slot][offR[i] / 2]) = rR[i];
-    *reinterpret_cast<float4 *>(&sX[w][ldsX[0]]) = rX[0];
-    *reinterpret_cast<float4 *>(&sX[w][ldsX[1]]) = rX[1];
   };
 
   // ---- decay factors of one sub-block (lane = token) ------------------------
@@ -215,11 +185,11 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
   // e to within half an octave of 0 and uses
   //   y_t = 2^{c_t + e_k} hs C_t + sum_t' Score[t][t'] 2^{c_t - q_t'} x_t' + D x_t,
   //   hs' = 2^{c_last} hs + sum_t 2^{c_last - q_t - e_k} x_t B_t^T,  e_{k+1} = e_k.
-  // scan() writes the per-token factors of sub-block k to slot `sl` and sets
-  // the next_* scalars.
+  // scan() writes the per-token factors of sub-block k and sets the next_*
+  // scalars.
   int next_fast = 1, next_shift = 0;
   float next_clast = 0.f, next_eout = 0.f;
-  auto scan = [&](int k, float rdt, float e_in, int sl) {
+  auto scan = [&](int k, float rdt, float e_in, int fs) {
     const int nv = min(64, L - 64 * k);
     float dl = softplus_f(rdt + bias);
     dl = (l < nv) ? dl : 0.f;
@@ -227,29 +197,18 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
     float clast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, c), 63));
     // Keep the (wave-uniform) decisions below in vector registers: as
     // per-lane selects they stay inside one basic block with the products
-    // they are scheduled against, instead of becoming scalar branches; every
-    // arm is computed before the choice so that none becomes a branch.
+    // they are scheduled against, instead of becoming scalar branches.
     float e_v = e_in;
-    if constexpr (GATED)
-      __asm__ volatile("" : "+v"(clast), "+v"(e_v));
-    else
-      __asm__("" : "+v"(clast), "+v"(e_v));
+    __asm__("" : "+v"(clast), "+v"(e_v));
     const float q = c - hw_log2(dl); // +inf where Delta = 0
     const bool fast = fabsf(clast) <= kSpanMax;
     const bool keep = e_v >= -clast - kExpLim && e_v <= kExpLim;
-    float n; // octaves
-    if constexpr (GATED) {
-      // (the gated walk holds the gate inputs as well; with every arm
-      // computed up front it spills)
-      n = fast ? (keep ? 0.f : floorf(kExpLim - e_v)) : -rintf(e_v);
-    } else {
-      const float n_up = floorf(kExpLim - e_v), n_fast = keep ? 0.f : n_up, n_slow = -rintf(e_v);
-      n = fast ? n_fast : n_slow;
-    }
+    const float n_up = floorf(kExpLim - e_v), n_fast = keep ? 0.f : n_up, n_slow = -rintf(e_v);
+    const float n = fast ? n_fast : n_slow; // octaves
     const float ek = e_v + n;
-    sF0[sl][w][l] = hw_exp2((fast ? 0.f : clast) - q - ek);
-    sF1[sl][w][l] = hw_exp2(c + ek);
-    sQC[sl][w][l] = make_float2(q, c);
+    sF0[fs][w][l] = hw_exp2((fast ? 0.f : clast) - q - ek);
+    sF1[fs][w][l] = hw_exp2(c + ek);
+    sQC[fs][w][l] = make_float2(q, c);
     next_fast = __builtin_amdgcn_readfirstlane((int)fast);
     next_shift = __builtin_amdgcn_readfirstlane((int)n);
     next_clast = clast;
@@ -257,26 +216,25 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
   };
 
   // ---- the phases of one sub-block -------------------------------------------
-  // x^T fragments (row p0 + li, K = tokens), raw and scaled by the token
-  // factors of slot `slot`.
-  FragBF xr[2], xs[2];
-  auto scale_x = [&](int slot) {
+  // x^T fragments (row p0 + li, K = tokens) scaled by the token factors.
+  FragBF xs[2];
+  auto scale_x = [&](const __bf16 (*xt)[1024], int fs) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      xr[ks] = trfrag(sX[w], 16, 32 * ks, 0, li, lg);
-      const float4 fa = *reinterpret_cast<const float4 *>(&sF0[slot][w][32 * ks + 4 * lg]);
-      const float4 fb = *reinterpret_cast<const float4 *>(&sF0[slot][w][32 * ks + 16 + 4 * lg]);
-      const float v[8] = {elem(xr[ks], 0) * fa.x, elem(xr[ks], 1) * fa.y, elem(xr[ks], 2) * fa.z,
-                          elem(xr[ks], 3) * fa.w, elem(xr[ks], 4) * fb.x, elem(xr[ks], 5) * fb.y,
-                          elem(xr[ks], 6) * fb.z, elem(xr[ks], 7) * fb.w};
+      const FragBF xr = trfrag(xt[w], 16, 32 * ks, 0, li, lg);
+      const float4 fa = *reinterpret_cast<const float4 *>(&sF0[fs][w][32 * ks + 4 * lg]);
+      const float4 fb = *reinterpret_cast<const float4 *>(&sF0[fs][w][32 * ks + 16 + 4 * lg]);
+      const float v[8] = {elem(xr, 0) * fa.x, elem(xr, 1) * fa.y, elem(xr, 2) * fa.z, elem(xr, 3) * fa.w,
+                          elem(xr, 4) * fb.x, elem(xr, 5) * fb.y, elem(xr, 6) * fb.z, elem(xr, 7) * fb.w};
       xs[ks] = pack8<__bf16>(v);
     }
   };
   // State term Y[p][t] = sum_n hs[p][n] C[t][n]; K-step outer, the four
-  // token tiles of a step are independent MFMAs read together.
+  // token tiles of a step are independent MFMAs.
   f32x4 yacc[4];
-  auto state_term = [&](int slot) {
-    FragBF hf[KN];
+  auto state_term = [&](const __bf16 *rec) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) yacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KN; ++ks) {
       float v[8];
@@ -285,76 +243,54 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
         v[r] = hs[2 * ks][r];
         v[4 + r] = hs[2 * ks + 1][r];
       }
-      hf[ks] = pack8<__bf16>(v);
-    }
+      const FragBF hf = pack8<__bf16>(v);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) yacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KN; ++ks) {
-      FragBF cf[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) cf[u] = ld8(&sRec[slot][(ks * 4 + u) * 512 + 8 * l]);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) yacc[u] = mma(hf[ks], cf[u], yacc[u]);
+      for (int u = 0; u < 4; ++u) yacc[u] = mma(hf, ld8(&rec[(ks * 4 + u) * 512 + 8 * l]), yacc[u]);
     }
   };
   // State update hs += B^T xs (after the state term has read hs).
-  auto update = [&](int slot) {
+  auto update = [&](const __bf16 *rec) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int kk = 0; kk < NT; ++kk) hs[kk] = mma(ld8(&sRec[slot][(NCB + ks * NT + kk) * 512 + 8 * l]), xs[ks], hs[kk]);
-  };
-  // Per-element path: decay the state by 2^{c_last} before its update (its xs
-  // holds 2^{c_last - q - e} x).
-  auto decay_state = [&](float clast) {
-    const float mid = hw_exp2(clast);
-#pragma unroll
-    for (int kk = 0; kk < NT; ++kk) hs[kk] *= mid;
-  };
-  // Exact renormalisation hs *= 2^{-n}.
-  auto shift_state = [&](int n) {
-#pragma unroll
-    for (int kk = 0; kk < NT; ++kk)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) hs[kk][r] = __builtin_amdgcn_ldexpf(hs[kk][r], -n);
+      for (int kk = 0; kk < NT; ++kk) hs[kk] = mma(ld8(&rec[(NCB + ks * NT + kk) * 512 + 8 * l]), xs[ks], hs[kk]);
   };
   // Intra-block term added to the state term, and the token factor of y.
-  auto intra = [&](int slot, auto fast_tag) {
+  auto intra = [&](const __bf16 *rec, const __bf16 (*xt)[1024], int fs, auto fast_tag) {
     if constexpr (decltype(fast_tag)::value) {
       // on the shared scores; y = 2^{c + e} (state + intra)
 #pragma unroll
       for (int f = 0; f < NSF; ++f) {
         const int u = f < 2 ? f : 2 + (f - 2) / 2, ks = f < 2 ? 0 : (f - 2) % 2;
-        yacc[u] = mma(xs[ks], sf[f], yacc[u]);
+        yacc[u] = mma(xs[ks], ld8(&rec[(NCB + NBB + f) * 512 + 8 * l]), yacc[u]);
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) yacc[u] *= sF1[slot][w][16 * u + li];
+      for (int u = 0; u < 4; ++u) yacc[u] *= sF1[fs][w][16 * u + li];
     } else {
       // per-element decay M[t][t'] = Score[t][t'] 2^{c_t - q_t'} on raw x; the
       // state term is scaled by 2^{c_t + e} first
 #pragma unroll
-      for (int u = 0; u < 4; ++u) yacc[u] *= sF1[slot][w][16 * u + li];
+      for (int u = 0; u < 4; ++u) yacc[u] *= sF1[fs][w][16 * u + li];
 #pragma unroll
       for (int f = 0; f < NSF; ++f) {
         const int u = f < 2 ? f : 2 + (f - 2) / 2, ks = f < 2 ? 0 : (f - 2) % 2;
         const int t = 16 * u + li;
-        const float ct = sQC[slot][w][t].y;
+        const float ct = sQC[fs][w][t].y;
+        const FragBF sfr = ld8(&rec[(NCB + NBB + f) * 512 + 8 * l]);
         float v[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int tp = 32 * ks + kperm(lg, j);
-          v[j] = (tp <= t) ? elem(sf[f], j) * hw_exp2(ct - sQC[slot][w][tp].x) : 0.f;
+          v[j] = (tp <= t) ? elem(sfr, j) * hw_exp2(ct - sQC[fs][w][tp].x) : 0.f;
         }
-        yacc[u] = mma(xr[ks], pack8<__bf16>(v), yacc[u]);
+        yacc[u] = mma(trfrag(xt[w], 16, 32 * ks, 0, li, lg), pack8<__bf16>(v), yacc[u]);
       }
     }
   };
-  // y = acc + D x stored directly; rows past the end (and idle waves) are
-  // dropped.
+  // y = acc + D x stored directly (times silu(z) when gated); rows past the
+  // end (and idle waves) are dropped by the range check.
   const uint32_t offY = (uint32_t)((li * rowX + 4 * lg) * 2);
   __bf16 *Ybase = reinterpret_cast<__bf16 *>(prm.out) + (int64_t)ib * L * rowX + (int64_t)h * P + p0;
-  // Gate input of this wave's y values of a sub-block (same positions).
   const __bf16 *Zbase = GATED ? reinterpret_cast<const __bf16 *>(prm.z) + (int64_t)ib * L * rowX + (int64_t)h * P + p0
                               : nullptr;
   float4 zq[4];
@@ -364,13 +300,13 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) zq[u] = bload4x<__bf16>(rsZ, offY + (uint32_t)(16 * u * rowX * 2));
   };
-  auto store_y = [&](int k) {
+  auto store_y = [&](int k, const __bf16 (*xt)[1024]) {
     const int t0 = 64 * k, nv = min(64, L - t0);
     const auto rsY = make_rsrc(Ybase + (int64_t)t0 * rowX,
                                active ? (uint32_t)(((int64_t)(nv - 1) * rowX + 16) * 2) : 0u);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(&sX[w][(16 * u + li) * 16 + 4 * lg]);
+      const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(&xt[w][(16 * u + li) * 16 + 4 * lg]);
       float v[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) v[r] = yacc[u][r] + d_h * (float)xv[r];
@@ -383,156 +319,68 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
       bstore4<__bf16>(rsY, offY + (uint32_t)(16 * u * rowX * 2), v[0], v[1], v[2], v[3]);
     }
   };
-  // With more than four waves: y = acc + D x of this wave's rows into the
-  // workgroup tile of slot `slot`.
-  auto put_y = [&](int slot) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int t = 16 * u + li;
-      const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(&sX[w][t * 16 + 4 * lg]);
-      bf16x4 v;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = (__bf16)(yacc[u][r] + d_h * (float)xv[r]);
-      *reinterpret_cast<bf16x4 *>(&sY[slot][t * YLD + 16 * w + 4 * lg]) = v;
-    }
-  };
-  // Store the tile of sub-block k (after a barrier).  For one token the
-  // workgroup's rows are one contiguous run of y (rows are (head, p) pairs,
-  // head-major, and y is [.., token, head, p]), so the tile goes out as
-  // aligned 16-byte pieces, two per thread; pieces of rows past the group's
-  // last row are dropped, as are tokens past L.  k < 0 stores nothing.
-  const int rows_valid = min(16 * W, prm.rows_per_bg - wi * 16 * W);
-  __bf16 *Ywg = reinterpret_cast<__bf16 *>(prm.out) + (int64_t)ib * L * rowX + (int64_t)g * (H / G) * P + wi * 16 * W;
-  // Gate input pieces matching the pieces flush_y stores for sub-block k
-  // (zeros for k < 0).
-  const __bf16 *Zwg = GATED ? reinterpret_cast<const __bf16 *>(prm.z) + (int64_t)ib * L * rowX +
-                                  (int64_t)g * (H / G) * P + wi * 16 * W
-                            : nullptr;
-  float4 zpc[2];
-  auto fetch_zpieces = [&](int k) {
-    const int t0 = 64 * k, nv = min(64, L - t0);
-    const auto rs = make_rsrc(Zwg + (int64_t)max(t0, 0) * rowX,
-                              k >= 0 ? (uint32_t)(((int64_t)(nv - 1) * rowX + rows_valid) * 2) : 0u);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int q = tid + i * NTH, t = q / (2 * W), j = q % (2 * W);
-      zpc[i] = bload16(rs, 8 * j < rows_valid ? (uint32_t)((t * rowX + 8 * j) * 2) : 0xfffffff0u);
-    }
-  };
-  auto flush_y = [&](int k) {
-    const int t0 = 64 * k, nv = min(64, L - t0);
-    // byte count before the select: a scalar select, not a branch (the gated
-    // walk keeps the branch form, which schedules better there)
-    uint32_t nbY;
-    if constexpr (GATED) {
-      nbY = k >= 0 ? (uint32_t)(((int64_t)(nv - 1) * rowX + rows_valid) * 2) : 0u;
-    } else {
-      const uint32_t nbY0 = (uint32_t)(((int64_t)(nv - 1) * rowX + rows_valid) * 2);
-      nbY = k >= 0 ? nbY0 : 0u;
-    }
-    const auto rs = make_rsrc(Ywg + (int64_t)max(t0, 0) * rowX, nbY);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int q = tid + i * NTH, t = q / (2 * W), j = q % (2 * W);
-      float4 v = *reinterpret_cast<const float4 *>(&sY[k & 1][t * YLD + 8 * j]);
-      if constexpr (GATED) {
-        const bf16x8 yb = __builtin_bit_cast(bf16x8, v), zb = __builtin_bit_cast(bf16x8, zpc[i]);
-        bf16x8 ob;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ob[e] = (__bf16)((float)yb[e] * silu_f((float)zb[e]));
-        v = __builtin_bit_cast(float4, ob);
-      }
-      const uint32_t off = 8 * j < rows_valid ? (uint32_t)((t * rowX + 8 * j) * 2) : 0xfffffff0u;
-      bstore16(rs, off, v);
-    }
-  };
 
-  float e_final = 0.f;
-  if constexpr (W <= 4) {
-    // ---- one wave per SIMD: the wave's own latency sets the pace.  The
-    //      factors of sub-block k are computed at its start; the state term
-    //      runs first, the update last, and the renormalisation is applied
-    //      unconditionally (a shift by 0 is exact) so that the block has no
-    //      branch before the intra-block term.
-    float rdt = fetch_dt(0);
-    fetch_bcx(0);
-    fetch_scores(0);
-    stage(0);
-    float e = 0.f;
-    for (int k = 0; k < nsub; ++k) {
-      const int slot = k & 1;
-      lds_barrier(); // B/C/x of sub-block k staged; slot ^ 1 no longer read
-      scan(k, rdt, e, slot);
-      const int fast = next_fast;
-      rdt = fetch_dt(k + 1);
-      fetch_bcx(k + 1);
-      if constexpr (GATED) fetch_z(k);
-      shift_state(next_shift);
-      state_term(slot);
-      scale_x(slot);
-      if (fast) {
-        intra(slot, std::true_type{});
-      } else {
-        intra(slot, std::false_type{});
-        decay_state(next_clast);
-      }
-      fetch_scores(min(k + 1, nsub - 1));
-      store_y(k);
-      update(slot);
-      stage(slot ^ 1);
-      e = next_eout;
+  // ---- the walk ------------------------------------------------------------
+  // Per sub-block k: barrier (the copies of k have landed, every wave is done
+  // with the other buffer), the copies of k + 1 into the other buffer, the
+  // state term, the intra term, y, the state update, and the factors of
+  // sub-block k + 1 (their step sizes were fetched one sub-block earlier), so
+  // that their scan chain runs next to the update's products.  The four y
+  // stores are the last memory operations of a sub-block (loads cannot move
+  // past them); the barrier waits for everything older (vmcnt(4)).
+  float rdt = fetch_dt(0);
+  copy_in(0, sRecA, sXA);
+  __builtin_amdgcn_s_waitcnt(0x70); // vmcnt(0) expcnt(7) lgkmcnt(0)
+  scan(0, rdt, 0.f, 0);
+  rdt = fetch_dt(1);
+  int cur_fast = next_fast, cur_shift = next_shift;
+  float cur_clast = next_clast, e = next_eout;
+  auto step = [&](int k, const __bf16 *rec, __bf16 (*xt)[1024], __bf16 *recN, __bf16 (*xtN)[1024]) {
+    const int fs = k & 1;
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x74); // vmcnt(4) expcnt(7) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    copy_in(k + 1, recN, xtN);
+    const float rdt_next = fetch_dt(k + 2);
+    if constexpr (GATED) fetch_z(k);
+    if (cur_shift != 0) {
+#pragma unroll
+      for (int kk = 0; kk < NT; ++kk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hs[kk][r] = __builtin_amdgcn_ldexpf(hs[kk][r], -cur_shift);
     }
-    e_final = e;
-  } else {
-    // ---- two waves on some SIMD: the factors of sub-block k + 1 are computed
-    //      during sub-block k, next to its products, the step sizes are
-    //      fetched two sub-blocks ahead, and each path (separable or
-    //      per-element) is one straight block.
-    float rdt_next = 0.f, rdt_next2 = 0.f;
-    float cur_clast = 0.f, cur_eout = 0.f;
-    auto body = [&](int k, auto fast_tag) {
-      constexpr bool FAST = decltype(fast_tag)::value;
-      const int slot = k & 1;
-      scale_x(slot);
-      state_term(slot);
-      if constexpr (!FAST) decay_state(cur_clast);
-      update(slot);
-      flush_y(k - 1);
-      scan(k + 1, rdt_next, cur_eout, slot ^ 1);
-      intra(slot, fast_tag);
-      fetch_scores(min(k + 1, nsub - 1));
-      put_y(slot);
-      stage(slot ^ 1);
-    };
-    fetch_bcx(0);
-    const float rdt0 = fetch_dt(0);
-    rdt_next = fetch_dt(1);
-    fetch_scores(0);
-    stage(0);
-    scan(0, rdt0, 0.f, 0);
-    for (int k = 0; k < nsub; ++k) {
-      lds_barrier(); // B/C/x of sub-block k staged; slot ^ 1 no longer read
-      fetch_bcx(k + 1);
-      rdt_next2 = fetch_dt(k + 2);
-      if constexpr (GATED) fetch_zpieces(k - 1);
-      const int fast = next_fast;
-      cur_clast = next_clast;
-      cur_eout = next_eout;
-      if (__builtin_expect(next_shift != 0, 0)) shift_state(next_shift);
-      if (fast)
-        body(k, std::true_type{});
-      else
-        body(k, std::false_type{});
-      rdt_next = rdt_next2;
+    state_term(rec);
+    scale_x(xt, fs);
+    if (cur_fast) {
+      intra(rec, xt, fs, std::true_type{});
+    } else {
+      intra(rec, xt, fs, std::false_type{});
+      const float mid = hw_exp2(cur_clast);
+#pragma unroll
+      for (int kk = 0; kk < NT; ++kk) hs[kk] *= mid;
     }
-    if constexpr (GATED) fetch_zpieces(nsub - 1);
-    lds_barrier(); // y tile of the last sub-block complete
-    flush_y(nsub - 1);
-    e_final = cur_eout;
+    store_y(k, xt);
+    update(rec);
+    // the factors of sub-block k + 1 (rdt holds its step sizes)
+    scan(k + 1, rdt, e, fs ^ 1);
+    cur_fast = next_fast;
+    cur_shift = next_shift;
+    cur_clast = next_clast;
+    e = next_eout;
+    rdt = rdt_next;
+  };
+  for (int k = 0; k < nsub; k += 2) {
+    step(k, sRecA, sXA, sRecB, sXB);
+    if (k + 1 < nsub) step(k + 1, sRecB, sXB, sRecA, sXA);
   }
+  // e now holds the exponent after the last sub-block: scan(nsub) of an empty
+  // sub-block (Delta = 0, no decay) keeps it unless it renormalises; undo that
+  // renormalisation's shift, which hs never received
+  e -= (float)cur_shift;
 
   if (prm.final_state != nullptr && active) {
-    const float sc = hw_exp2(e_final);
+    const float sc = hw_exp2(e);
 #pragma unroll
     for (int k = 0; k < NT; ++k) *reinterpret_cast<f32x4 *>(prm.final_state + srow + 16 * k + 4 * lg) = hs[k] * sc;
   }
