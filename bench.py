@@ -5,8 +5,10 @@
 
 One step is one ssd_scan_fwd call over the Mamba-2 2.7B layer-shape
 workload (b=4, L=4096, H=80, P=64, G=1, N=128, chunk 256, bf16 inputs,
-fp32 initial and final state), inputs resident in HBM.  W untimed steps,
-then exactly K timed steps between two device synchronisations; value =
+fp32 initial and final state), inputs resident in HBM.  W untimed steps
+(default 200: back-to-back calls reach the sustained clock after about 150
+to 200 calls), then exactly K timed steps (default 100) between two device
+synchronisations; value =
 b*L*K / elapsed.  Each step is also bracketed by HIP events on the stream
 the library launches on, giving the call's average duration for the
 roofline figure (every launch of the call: the operand records and the
@@ -228,7 +230,7 @@ def bench_scan_config(name, ssd, staging, inputs, torch, dev, evict):
 
     def fn():
         ssd.ssd_scan_fwd(**t, out=out, final_state=fin, chunk=Q)
-    for _ in range(5):
+    for _ in range(100):  # to the sustained clock
         fn()
     torch.cuda.synchronize()
     cold = percentiles(time_cold(fn, torch, evict))
@@ -367,8 +369,10 @@ def bench_decode(ssd, staging, inputs, torch, dev):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    # back-to-back calls settle only after ~150-200 calls (the clock ramps
+    # up under sustained load): 200 untimed steps, about 35 ms
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--algo", choices=["auto", "fused", "chunked", "rows"], default="auto")
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
