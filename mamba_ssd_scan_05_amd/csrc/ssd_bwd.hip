@@ -903,6 +903,20 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(sGst + q * 256), 16,
                                                q * 1024 + lane * 16, 0, 0, 0);
   };
+  // the entering state of head hh into sGst (fp32, 1 KiB pieces as fetch_g)
+  auto fetch_h = [&](int hh, int w_lo, int nw) {
+    const float *Hn = p.states + (((int64_t)b_ * H + hh) * nc + c) * PN;
+    const auto rs = make_rsrc(Hn, (uint32_t)PN * 4u);
+    for (int q = w - w_lo; q < PN / 256; q += nw)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(sGst + q * 256), 16,
+                                               q * 1024 + lane * 16, 0, 0, 0);
+  };
+  // this thread's 16-byte piece of the next head's x and dy (tokens past the
+  // end read zero): loaded into registers during the dB / dC products,
+  // written to LDS in the tail
+  constexpr int XPC = P / 8; // pieces per token row
+  const bool has_piece = tid < kQ * XPC;
+  const int xr_row = tid / XPC, xr_col = (tid % XPC) * 8;
   if (w == 0) decay_of(g * hpg, 0);
   stage_head(g * hpg, 0, 512);
   fetch_g(g * hpg, 0, 8);
@@ -997,6 +1011,9 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
       if (lane == 0) sRed[1 + w] = gh;
     }
     __syncthreads();
+    // sGst is free until the tail: copy the next head's entering state into it
+    const bool has_next = h + 1 < (g + 1) * hpg;
+    if (has_next && w >= 2) fetch_h(h + 1, 2, 6);
 
     // --- bracket = M^T dY + e_out o (B G^T); dx; x . bracket
     {
@@ -1062,6 +1079,12 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
       }
     }
     __syncthreads();
+    uint4 nx = make_uint4(0u, 0u, 0u, 0u), ndy = nx;
+    if (has_next && has_piece && xr_row < nv) {
+      const int64_t off = (((int64_t)b_ * L + t0 + xr_row) * H + h + 1) * P + xr_col;
+      nx = *reinterpret_cast<const uint4 *>(reinterpret_cast<const __bf16 *>(p.x) + off);
+      ndy = *reinterpret_cast<const uint4 *>(reinterpret_cast<const __bf16 *>(p.dy) + off);
+    }
 
     // --- P2 = DX o E (split) to LDS; dB += Delta o (e_out o XG + P2^T C)
 #pragma unroll
@@ -1107,14 +1130,34 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
     }
 
     // --- da, ddt and the head's partial sums (wave 0, lane k = token); wave 1
-    //     forms the next head's decays, waves 2..7 stage its x, dy and state
+    //     forms the next head's decays, waves 2..7 split its entering state
+    //     (in sGst) into the two planes and copy its G into sGst, piece by
+    //     piece (each wave splits the pieces it then overwrites); every
+    //     thread stores its x and dy piece of the next head
+    if (has_next && has_piece) {
+      *reinterpret_cast<uint4 *>(&sX[xr_row * LX + xr_col]) = nx;
+      *reinterpret_cast<uint4 *>(&sDY[xr_row * LX + xr_col]) = ndy;
+    }
     if (w != 0) {
-      if (h + 1 < (g + 1) * hpg) {
+      if (has_next) {
         if (w == 1) {
           decay_of(h + 1, cur ^ 1);
         } else {
-          stage_head(h + 1, 128, 384);
-          fetch_g(h + 1, 2, 6);
+          __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          const float *Gsrc = p.adj + (((int64_t)b_ * H + h + 1) * nc + c) * PN;
+          const auto rsg = make_rsrc(Gsrc, (uint32_t)PN * 4u);
+          for (int q = w - 2; q < PN / 256; q += 6) {
+            const int idx = q * 64 + lane; // float4 index
+            const int r = (idx * 4) / N, col = (idx * 4) % N, off = r * LS + col;
+            const float4 hv = *reinterpret_cast<const float4 *>(sGst + 4 * idx);
+            put_split(sSh, sSl, off, hv.x);
+            put_split(sSh, sSl, off + 1, hv.y);
+            put_split(sSh, sSl, off + 2, hv.z);
+            put_split(sSh, sSl, off + 3, hv.w);
+            __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsg, (__attribute__((address_space(3))) void *)(sGst + q * 256), 16,
+                                                     q * 1024 + lane * 16, 0, 0, 0);
+          }
         }
       }
     } else {
