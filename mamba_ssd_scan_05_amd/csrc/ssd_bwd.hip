@@ -83,12 +83,18 @@ __device__ __forceinline__ FragF32 frag_k_contig(const float *tile, int ld, int 
   return ld4x2(p, p + 16);
 }
 
-__device__ __forceinline__ float sum16(float v) { // over the 16 lanes of a lane group
-  v += __shfl_xor(v, 1, 64);
-  v += __shfl_xor(v, 2, 64);
-  v += __shfl_xor(v, 4, 64);
-  v += __shfl_xor(v, 8, 64);
-  return v;
+// Sum over the 16 lanes of a lane group in registers (DPP, no LDS round
+// trip): swap neighbours, swap pairs, mirror within each half row, mirror
+// the row.  Every lane of the group ends with the same value (each step adds
+// two values in either order).
+template <int CTRL> __device__ __forceinline__ float dpp_add(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float sum16(float v) {
+  v = dpp_add<0xB1>(v);     // quad_perm [1,0,3,2]
+  v = dpp_add<0x4E>(v);     // quad_perm [2,3,0,1]
+  v = dpp_add<0x141>(v);    // row_half_mirror
+  return dpp_add<0x140>(v); // row_mirror
 }
 __device__ __forceinline__ float sum_lg(float v) { // over the 4 lane groups
   v += __shfl_xor(v, 16, 64);
@@ -96,6 +102,10 @@ __device__ __forceinline__ float sum_lg(float v) { // over the 4 lane groups
   return v;
 }
 __device__ __forceinline__ float wave_sum(float v) { return sum_lg(sum16(v)); }
+// lane 63's value in every lane (the readlane builtin moves 32-bit integers)
+__device__ __forceinline__ float lane63(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
 
 // Per-chunk decay quantities for one (batch, head), computed by one wave:
 // lane k holds token t0 + k.  Returns Delta; writes cum (log2 units), e_in,
@@ -116,7 +126,7 @@ __device__ __forceinline__ ChunkDecay chunk_decay_v(float dtv, const float *dt_b
   d.delta = valid ? softplus_f(z) : 0.f;
   d.sig = valid ? __builtin_amdgcn_rcpf(1.f + hw_exp2(-z * kLog2e)) : 0.f;
   d.cum2 = wave_incl_scan(d.delta * A[h] * kLog2e);
-  d.cum2_last = __shfl(d.cum2, 63, 64);
+  d.cum2_last = lane63(d.cum2);
   d.e_in = hw_exp2(d.cum2);
   d.e_out = hw_exp2(d.cum2_last - d.cum2);
   return d;
@@ -574,7 +584,7 @@ __global__ void __launch_bounds__(512) bwd_chunk_kernel(const BwdParams p) {
       const float R = wave_incl_scan(dlt) - dlt;           // sum over m < k
       const float u = uP[0][k] + uP[1][k];
       const float u_incl = wave_incl_scan(u);
-      const float U = __shfl(u_incl, 63, 64) - u_incl + u;  // sum over i >= k
+      const float U = lane63(u_incl) - u_incl + u;  // sum over i >= k
       const float v = sEout[k] * sDel[k] * (vP[0][k] + vP[1][k]);
       const float V = wave_incl_scan(v) - v;               // sum over j < k
       float gh = 0.f;
@@ -1168,7 +1178,7 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
       const float R = wave_incl_scan(dlt) - dlt;
       const float u = uP[0][k] + uP[1][k];
       const float u_incl = wave_incl_scan(u);
-      const float U = __shfl(u_incl, 63, 64) - u_incl + u;
+      const float U = lane63(u_incl) - u_incl + u;
       const float v = sEout[k] * sDel[k] * (vP[0][k] + vP[1][k]);
       const float V = wave_incl_scan(v) - v;
       float gh = 0.f;
