@@ -102,6 +102,18 @@ __device__ __forceinline__ float sum_lg(float v) { // over the 4 lane groups
   return v;
 }
 __device__ __forceinline__ float wave_sum(float v) { return sum_lg(sum16(v)); }
+// Workgroup barrier that orders LDS accesses only: the wave's own LDS
+// reads and writes complete before it arrives (lgkmcnt(0)); its global loads
+// and stores and its buffer loads into LDS may stay in flight (HIP's
+// __syncthreads waits for those too).  A wave whose copy into LDS the others
+// read waits for it (vmcnt(0)) before the barrier.  The empty asm statements
+// keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void bar_lds() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0); vmcnt, expcnt not waited on
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
 // lane 63's value in every lane (the readlane builtin moves 32-bit integers)
 __device__ __forceinline__ float lane63(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
@@ -860,14 +872,14 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
     for (int e = tid; e < kQ * LX; e += 512) sX[e] = sDY[e] = (__bf16)0.f;
     for (int e = tid; e < PP * LS; e += 512) sSh[e] = sSl[e] = (__bf16)0.f;
     for (int e = tid; e < kQ * LB; e += 512) sB[e] = sC[e] = (__bf16)0.f;
-    __syncthreads();
+    bar_lds();
   }
 
   const __bf16 *Bg = reinterpret_cast<const __bf16 *>(p.B) + (((int64_t)b_ * L + t0) * G + g) * N;
   const __bf16 *Cg = reinterpret_cast<const __bf16 *>(p.C) + (((int64_t)b_ * L + t0) * G + g) * N;
   stage_bf16(sB, LB, Bg, (int64_t)G * N, kQ, nv, N, tid, 512);
   stage_bf16(sC, LB, Cg, (int64_t)G * N, kQ, nv, N, tid, 512);
-  __syncthreads();
+  bar_lds();
   f32x4 S[2];
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
@@ -930,7 +942,7 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
   if (w == 0) decay_of(g * hpg, 0);
   stage_head(g * hpg, 0, 512);
   fetch_g(g * hpg, 0, 8);
-  __syncthreads();
+  bar_lds();
 
   for (int h = g * hpg; h < (g + 1) * hpg; ++h) {
     const int64_t bh = (int64_t)b_ * H + h;
@@ -1000,11 +1012,11 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
         if (li == 0) uP[ct0][rt * 16 + 4 * lg + r] = v;
       }
     }
-    __syncthreads();
+    bar_lds();
 
     // --- replace H by G (already in LDS); <G, H> with H from its two planes
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    bar_lds();
     {
       float gh = 0.f;
       for (int idx = tid; idx < PN / 4; idx += 512) {
@@ -1020,7 +1032,7 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
       gh = wave_sum(gh);
       if (lane == 0) sRed[1 + w] = gh;
     }
-    __syncthreads();
+    bar_lds();
     // sGst is free until the tail: copy the next head's entering state into it
     const bool has_next = h + 1 < (g + 1) * hpg;
     if (has_next && w >= 2) fetch_h(h + 1, 2, 6);
@@ -1088,7 +1100,7 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
         if (li == 0) vP[ct0][rt * 16 + 4 * lg + r] = v;
       }
     }
-    __syncthreads();
+    bar_lds();
     uint4 nx = make_uint4(0u, 0u, 0u, 0u), ndy = nx;
     if (has_next && has_piece && xr_row < nv) {
       const int64_t off = (((int64_t)b_ * L + t0 + xr_row) * H + h + 1) * P + xr_col;
@@ -1102,7 +1114,7 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         put_split(sMh, sMl, (rt * 16 + 4 * lg + r) * LQ + (ct0 + 2 * k) * 16 + li, P2[k][r]);
-    __syncthreads();
+    bar_lds();
 #pragma unroll
     for (int k = 0; k < NT / 2; ++k) {
       const int ct = ct0 + 2 * k;
@@ -1116,7 +1128,7 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
 #pragma unroll
       for (int r = 0; r < 4; ++r) dBacc[k][r] += sDel[rt * 16 + 4 * lg + r] * acc[r];
     }
-    __syncthreads();
+    bar_lds();
 
     // --- P1 = P2 diag(Delta) (split) to LDS; dC += P1 B
 #pragma unroll
@@ -1125,7 +1137,7 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
 #pragma unroll
       for (int r = 0; r < 4; ++r) put_split(sMh, sMl, (rt * 16 + 4 * lg + r) * LQ + j, P2[k][r] * sDel[j]);
     }
-    __syncthreads();
+    bar_lds();
 #pragma unroll
     for (int k = 0; k < NT / 2; ++k) {
       const int ct = ct0 + 2 * k;
@@ -1199,7 +1211,7 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
         q[2] = pb;
       }
     }
-    __syncthreads();
+    bar_lds();
   }
 
 #pragma unroll
