@@ -83,37 +83,13 @@ __device__ __forceinline__ FragF32 frag_k_contig(const float *tile, int ld, int 
   return ld4x2(p, p + 16);
 }
 
-// Sum over the 16 lanes of a lane group in registers (DPP, no LDS round
-// trip): swap neighbours, swap pairs, mirror within each half row, mirror
-// the row.  Every lane of the group ends with the same value (each step adds
-// two values in either order).
-template <int CTRL> __device__ __forceinline__ float dpp_add(float v) {
-  return v + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
-}
-__device__ __forceinline__ float sum16(float v) {
-  v = dpp_add<0xB1>(v);     // quad_perm [1,0,3,2]
-  v = dpp_add<0x4E>(v);     // quad_perm [2,3,0,1]
-  v = dpp_add<0x141>(v);    // row_half_mirror
-  return dpp_add<0x140>(v); // row_mirror
-}
+__device__ __forceinline__ float sum16(float v) { return lane_group_sum<16>(v); } // over a lane group
 __device__ __forceinline__ float sum_lg(float v) { // over the 4 lane groups
   v += __shfl_xor(v, 16, 64);
   v += __shfl_xor(v, 32, 64);
   return v;
 }
 __device__ __forceinline__ float wave_sum(float v) { return sum_lg(sum16(v)); }
-// Workgroup barrier that orders LDS accesses only: the wave's own LDS
-// reads and writes complete before it arrives (lgkmcnt(0)); its global loads
-// and stores and its buffer loads into LDS may stay in flight (HIP's
-// __syncthreads waits for those too).  A wave whose copy into LDS the others
-// read waits for it (vmcnt(0)) before the barrier.  The empty asm statements
-// keep the compiler from moving memory accesses across.
-__device__ __forceinline__ void bar_lds() {
-  __asm__ volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0); vmcnt, expcnt not waited on
-  __builtin_amdgcn_s_barrier();
-  __asm__ volatile("" ::: "memory");
-}
 // lane 63's value in every lane (the readlane builtin moves 32-bit integers)
 __device__ __forceinline__ float lane63(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
@@ -872,14 +848,14 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
     for (int e = tid; e < kQ * LX; e += 512) sX[e] = sDY[e] = (__bf16)0.f;
     for (int e = tid; e < PP * LS; e += 512) sSh[e] = sSl[e] = (__bf16)0.f;
     for (int e = tid; e < kQ * LB; e += 512) sB[e] = sC[e] = (__bf16)0.f;
-    bar_lds();
+    lds_barrier();
   }
 
   const __bf16 *Bg = reinterpret_cast<const __bf16 *>(p.B) + (((int64_t)b_ * L + t0) * G + g) * N;
   const __bf16 *Cg = reinterpret_cast<const __bf16 *>(p.C) + (((int64_t)b_ * L + t0) * G + g) * N;
   stage_bf16(sB, LB, Bg, (int64_t)G * N, kQ, nv, N, tid, 512);
   stage_bf16(sC, LB, Cg, (int64_t)G * N, kQ, nv, N, tid, 512);
-  bar_lds();
+  lds_barrier();
   f32x4 S[2];
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
@@ -942,7 +918,7 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
   if (w == 0) decay_of(g * hpg, 0);
   stage_head(g * hpg, 0, 512);
   fetch_g(g * hpg, 0, 8);
-  bar_lds();
+  lds_barrier();
 
   for (int h = g * hpg; h < (g + 1) * hpg; ++h) {
     const int64_t bh = (int64_t)b_ * H + h;
@@ -1012,11 +988,11 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
         if (li == 0) uP[ct0][rt * 16 + 4 * lg + r] = v;
       }
     }
-    bar_lds();
+    lds_barrier();
 
     // --- replace H by G (already in LDS); <G, H> with H from its two planes
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    bar_lds();
+    lds_barrier();
     {
       float gh = 0.f;
       for (int idx = tid; idx < PN / 4; idx += 512) {
@@ -1032,7 +1008,7 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
       gh = wave_sum(gh);
       if (lane == 0) sRed[1 + w] = gh;
     }
-    bar_lds();
+    lds_barrier();
     // sGst is free until the tail: copy the next head's entering state into it
     const bool has_next = h + 1 < (g + 1) * hpg;
     if (has_next && w >= 2) fetch_h(h + 1, 2, 6);
@@ -1100,7 +1076,7 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
         if (li == 0) vP[ct0][rt * 16 + 4 * lg + r] = v;
       }
     }
-    bar_lds();
+    lds_barrier();
     uint4 nx = make_uint4(0u, 0u, 0u, 0u), ndy = nx;
     if (has_next && has_piece && xr_row < nv) {
       const int64_t off = (((int64_t)b_ * L + t0 + xr_row) * H + h + 1) * P + xr_col;
@@ -1114,7 +1090,7 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         put_split(sMh, sMl, (rt * 16 + 4 * lg + r) * LQ + (ct0 + 2 * k) * 16 + li, P2[k][r]);
-    bar_lds();
+    lds_barrier();
 #pragma unroll
     for (int k = 0; k < NT / 2; ++k) {
       const int ct = ct0 + 2 * k;
@@ -1128,7 +1104,7 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
 #pragma unroll
       for (int r = 0; r < 4; ++r) dBacc[k][r] += sDel[rt * 16 + 4 * lg + r] * acc[r];
     }
-    bar_lds();
+    lds_barrier();
 
     // --- P1 = P2 diag(Delta) (split) to LDS; dC += P1 B
 #pragma unroll
@@ -1137,7 +1113,7 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
 #pragma unroll
       for (int r = 0; r < 4; ++r) put_split(sMh, sMl, (rt * 16 + 4 * lg + r) * LQ + j, P2[k][r] * sDel[j]);
     }
-    bar_lds();
+    lds_barrier();
 #pragma unroll
     for (int k = 0; k < NT / 2; ++k) {
       const int ct = ct0 + 2 * k;
@@ -1211,7 +1187,7 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
         q[2] = pb;
       }
     }
-    bar_lds();
+    lds_barrier();
   }
 
 #pragma unroll

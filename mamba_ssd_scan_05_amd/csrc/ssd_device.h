@@ -221,11 +221,34 @@ __device__ __forceinline__ float wave_incl_scan(float v) {
   return v;
 }
 
-// Workgroup barrier that orders LDS only: waits for this wave's LDS
-// operations, then s_barrier.  Global loads and stores stay in flight (the
-// "memory" clobber keeps the compiler from moving memory accesses across it).
+// Workgroup barrier that orders LDS accesses only: the wave's own LDS reads
+// and writes complete before it arrives (lgkmcnt(0)); its global loads and
+// stores and its buffer loads into LDS may stay in flight (HIP's
+// __syncthreads waits for those too where a copy into LDS is pending).  A
+// wave whose copy into LDS the others read waits for it (vmcnt(0)) before
+// the barrier.  The empty asm statements keep the compiler from moving memory
+// accesses across it.
 __device__ __forceinline__ void lds_barrier() {
-  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0); vmcnt, expcnt not waited on
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+// Sum over aligned groups of NL lanes (4, 8 or 16) in registers, with DPP
+// inside a 16-lane row (no LDS round trip): swap neighbours, swap pairs,
+// mirror within each half row, mirror the row.  Every lane of a group ends
+// with the same value (each step adds two values in either order).
+template <int CTRL> __device__ __forceinline__ float dpp_add(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+template <int NL> __device__ __forceinline__ float lane_group_sum(float v) {
+  static_assert(NL == 4 || NL == 8 || NL == 16, "groups of 4, 8 or 16 lanes");
+  v = dpp_add<0xB1>(v); // quad_perm [1,0,3,2]
+  v = dpp_add<0x4E>(v); // quad_perm [2,3,0,1]
+  if constexpr (NL >= 8) v = dpp_add<0x141>(v); // row_half_mirror
+  if constexpr (NL >= 16) v = dpp_add<0x140>(v); // row_mirror
+  return v;
 }
 
 } // namespace

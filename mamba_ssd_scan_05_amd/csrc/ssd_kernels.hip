@@ -492,11 +492,12 @@ state_pass_kernel(float *__restrict__ states, const float *__restrict__ seg_deca
 // ---------------------------------------------------------------------------
 // Recurrent step ("From Transformer to Mamba", section 2.1, single-step
 // update): one workgroup per (batch, head); N/4 threads per state row, each
-// owning four consecutive entries; the readout sum over n is a shuffle
-// reduction inside those N/4 lanes.  State and x go through range-checked
-// buffer accesses (rows past P read zeros, their stores are dropped), so a
-// batch of rows is loaded without branches and all its loads are in flight
-// together; the state, read once and written once, streams non-temporally.
+// owning four consecutive entries; the readout sum over n is a DPP sum
+// inside each 16-lane row, then shuffles across rows (N >= 128).  State and
+// x go through range-checked buffer accesses (rows past P read zeros, their
+// stores are dropped), so a batch of rows is loaded without branches and all
+// its loads are in flight together; the state, read once and written once,
+// streams non-temporally.
 template <typename T> __device__ __forceinline__ float bload_elem(__amdgpu_buffer_rsrc_t r, uint32_t off);
 template <> __device__ __forceinline__ float bload_elem<__bf16>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return (float)__builtin_bit_cast(__bf16, (unsigned short)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0));
@@ -556,8 +557,13 @@ step_kernel(float *__restrict__ state, const T *__restrict__ x,
       s[u].z = alpha * s[u].z + in * bv[2];
       s[u].w = alpha * s[u].w + in * bv[3];
       float acc = s[u].x * cv[0] + s[u].y * cv[1] + s[u].z * cv[2] + s[u].w * cv[3];
+      if constexpr (TPR <= 16) {
+        acc = lane_group_sum<TPR>(acc);
+      } else {
+        acc = lane_group_sum<16>(acc);
 #pragma unroll
-      for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+        for (int off = 16; off < TPR; off <<= 1) acc += __shfl_xor(acc, off, 64);
+      }
       bstore16_nt(rsS, (uint32_t)(p * TPR + c4) * 16u, s[u]);
       // one lane per row writes y; the others aim past the range
       bstore_elem<T>(rsO, c4 == 0 ? (uint32_t)p * (uint32_t)sizeof(T) : 0xfffffff0u, acc + d_h * xv[u]);
