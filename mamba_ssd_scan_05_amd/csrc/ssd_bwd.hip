@@ -810,12 +810,23 @@ __global__ void __launch_bounds__(256) bwd_state_scan_bf16_kernel(const BwdParam
     state_scan_bf16_body<P, N, true>(p, rem / p.nseg, rem % p.nseg, lds);
 }
 
-template <int P, int N>
-__global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) {
+// Chunk step body for NW waves.  A wave owns U = 8 / NW of the four 16-token
+// row tiles (rt0 .. rt0 + U - 1) and the column tiles ct0, ct0 + 2, ...;
+// inside each product the loop over its row tiles is innermost, so a
+// fragment along the other operand is read once for all of them.  The
+// kernel runs NW = 8 (two waves per SIMD, 256 VGPRs each); NW = 4 (one wave
+// per SIMD, up to 512 registers with the accumulators in AGPRs, two row
+// tiles per wave) gives the same results and measured 1.73 ms against
+// 1.36 ms for the whole backward at the 2.7B layer shape: one wave per
+// SIMD leaves the LDS and memory latency exposed.
+template <int P, int N, int NW>
+__device__ __forceinline__ void chunk_bf16_body(const BwdParams &p) {
   // P or N below 32 run padded to 32 (zero columns/rows in LDS)
   constexpr int PP = P < 32 ? 32 : P, NP = N < 32 ? 32 : N;
   constexpr int LB = tr_ld(NP, 2), LX = tr_ld(PP, 2), LQ = tr_ld(kQ, 2), LS = tr_ld(NP, 2);
   constexpr int PT = PP / 16, NT = NP / 16;
+  constexpr int NTH = NW * 64, U = 8 / NW, RG = 4 / U;
+  static_assert(NW == 8 || NW == 4, "8 or 4 waves");
   __shared__ __attribute__((aligned(16))) __bf16 sB[kQ * LB];
   __shared__ __attribute__((aligned(16))) __bf16 sC[kQ * LB];
   __shared__ __attribute__((aligned(16))) __bf16 sX[kQ * LX];
@@ -831,8 +842,8 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
   // while the current head finishes
   __shared__ float sCumB[2][kQ], sDelB[2][kQ], sEinB[2][kQ], sEoutB[2][kQ], sSigB[2][kQ];
   __shared__ float rowW[2][kQ], colW[4][kQ], uP[2][kQ], vP[2][kQ], dinP[2][kQ], sDiag[kQ];
-  __shared__ float sRed[9]; // [1 + w]: wave w's share of <G, H>
-  __shared__ float sLast[2]; // log2 decay of the chunk, per decay buffer
+  __shared__ float sRed[1 + NW]; // [1 + w]: wave w's share of <G, H>
+  __shared__ float sLast[2];     // log2 decay of the chunk, per decay buffer
 
   const int nc = p.nc, G = p.G, H = p.H, L = p.L;
   const int c = blockIdx.x % nc;
@@ -840,39 +851,44 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
   const int b_ = bg / G, g = bg % G;
   const int hpg = H / G;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
-  const int rt = w & 3, ct0 = w >> 2;
+  const int rt0 = (w % RG) * U, ct0 = w / RG;
   const int t0 = c * kQ, nv = min(kQ, L - t0);
   const int PN = P * N;
 
   if constexpr (PP != P || NP != N) {
-    for (int e = tid; e < kQ * LX; e += 512) sX[e] = sDY[e] = (__bf16)0.f;
-    for (int e = tid; e < PP * LS; e += 512) sSh[e] = sSl[e] = (__bf16)0.f;
-    for (int e = tid; e < kQ * LB; e += 512) sB[e] = sC[e] = (__bf16)0.f;
+    for (int e = tid; e < kQ * LX; e += NTH) sX[e] = sDY[e] = (__bf16)0.f;
+    for (int e = tid; e < PP * LS; e += NTH) sSh[e] = sSl[e] = (__bf16)0.f;
+    for (int e = tid; e < kQ * LB; e += NTH) sB[e] = sC[e] = (__bf16)0.f;
     lds_barrier();
   }
 
   const __bf16 *Bg = reinterpret_cast<const __bf16 *>(p.B) + (((int64_t)b_ * L + t0) * G + g) * N;
   const __bf16 *Cg = reinterpret_cast<const __bf16 *>(p.C) + (((int64_t)b_ * L + t0) * G + g) * N;
-  stage_bf16(sB, LB, Bg, (int64_t)G * N, kQ, nv, N, tid, 512);
-  stage_bf16(sC, LB, Cg, (int64_t)G * N, kQ, nv, N, tid, 512);
+  stage_bf16(sB, LB, Bg, (int64_t)G * N, kQ, nv, N, tid, NTH);
+  stage_bf16(sC, LB, Cg, (int64_t)G * N, kQ, nv, N, tid, NTH);
   lds_barrier();
-  f32x4 S[2];
+  f32x4 S[U][2];
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int ct = ct0 + 2 * k;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k0 = 0; k0 < NP; k0 += 32)
-      acc = mma(kc16(sC, LB, rt * 16 + li, k0, lg), kc16(sB, LB, ct * 16 + li, k0, lg), acc);
-    S[k] = acc;
+    for (int u = 0; u < U; ++u) S[u][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k0 = 0; k0 < NP; k0 += 32) {
+      const FragBF bb = kc16(sB, LB, ct * 16 + li, k0, lg);
+#pragma unroll
+      for (int u = 0; u < U; ++u) S[u][k] = mma(kc16(sC, LB, (rt0 + u) * 16 + li, k0, lg), bb, S[u][k]);
+    }
   }
 
-  f32x4 dBacc[NT / 2], dCacc[NT / 2];
+  f32x4 dBacc[U][NT / 2], dCacc[U][NT / 2];
 #pragma unroll
-  for (int k = 0; k < NT / 2; ++k) {
-    dBacc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-    dCacc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int k = 0; k < NT / 2; ++k) {
+      dBacc[u][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dCacc[u][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
   // decays of head hh into buffer q (one wave), and x, dy, the entering state
   // of head hh into LDS (threads [t_lo, t_lo + nt))
@@ -909,15 +925,13 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(sGst + q * 256), 16,
                                                q * 1024 + lane * 16, 0, 0, 0);
   };
-  // this thread's 16-byte piece of the next head's x and dy (tokens past the
-  // end read zero): loaded into registers during the dB / dC products,
-  // written to LDS in the tail
-  constexpr int XPC = P / 8; // pieces per token row
-  const bool has_piece = tid < kQ * XPC;
-  const int xr_row = tid / XPC, xr_col = (tid % XPC) * 8;
+  // this thread's 16-byte pieces (tid, tid + NTH, ...) of the next head's x
+  // and dy (tokens past the end read zero): loaded into registers during the
+  // dB / dC products, written to LDS in the tail
+  constexpr int XPC = P / 8, NXP = kQ * XPC, NPC = (NXP + NTH - 1) / NTH;
   if (w == 0) decay_of(g * hpg, 0);
-  stage_head(g * hpg, 0, 512);
-  fetch_g(g * hpg, 0, 8);
+  stage_head(g * hpg, 0, NTH);
+  fetch_g(g * hpg, 0, NW);
   lds_barrier();
 
   for (int h = g * hpg; h < (g + 1) * hpg; ++h) {
@@ -928,65 +942,94 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
     const float cum_last2 = sLast[cur];
 
     // --- DX = dY X^T, M = S o E (split to LDS), P2 = DX o E, W sums, diag(DX)
-    f32x4 P2[2];
-    float rsum[4] = {0.f, 0.f, 0.f, 0.f};
+    f32x4 P2[U][2];
+    float rsum[U][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) rsum[u][r] = 0.f;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int ct = ct0 + 2 * k;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      f32x4 acc[U];
 #pragma unroll
-      for (int k0 = 0; k0 < PP; k0 += 32)
-        acc = mma(kc16(sDY, LX, rt * 16 + li, k0, lg), kc16(sX, LX, ct * 16 + li, k0, lg), acc);
+      for (int u = 0; u < U; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k0 = 0; k0 < PP; k0 += 32) {
+        const FragBF bx = kc16(sX, LX, ct * 16 + li, k0, lg);
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc[u] = mma(kc16(sDY, LX, (rt0 + u) * 16 + li, k0, lg), bx, acc[u]);
+      }
       const int j = ct * 16 + li;
       const float cj = sCum[j], dj = sDel[j];
-      float csum = 0.f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = rt * 16 + 4 * lg + r;
-        const float e = (i >= j) ? hw_exp2(sCum[i] - cj) : 0.f;
-        const float m = S[k][r] * e;
-        put_split(sMh, sMl, i * LQ + j, m);
-        P2[k][r] = acc[r] * e;
-        const float wv = (i > j) ? m * acc[r] * dj : 0.f;
-        rsum[r] += wv;
-        csum += wv;
-        if (i == j) sDiag[i] = acc[r];
-      }
-      csum = sum_lg(csum);
-      if (lg == 0) colW[rt][j] = csum;
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float v = sum16(rsum[r]);
-      if (li == 0) rowW[ct0][rt * 16 + 4 * lg + r] = v;
-    }
-
-    // --- dY H: dC += e_in o (dY H); u_i = e_in_i sum_n C_in (dY H)_in
-    {
-      float up[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k = 0; k < NT / 2; ++k) {
-        const int ct = ct0 + 2 * k;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int k0 = 0; k0 < PP; k0 += 32) {
-          const FragBF a = kc16(sDY, LX, rt * 16 + li, k0, lg);
-          acc = mma(a, trfrag(sSh, LS, k0, ct * 16, li, lg), acc);
-          acc = mma(a, trfrag(sSl, LS, k0, ct * 16, li, lg), acc);
-        }
+      for (int u = 0; u < U; ++u) {
+        const int rt = rt0 + u;
+        float csum = 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = rt * 16 + 4 * lg + r;
-          const float v = sEin[i] * acc[r];
-          dCacc[k][r] += v;
-          up[r] += (float)sC[i * LB + ct * 16 + li] * v;
+          const float e = (i >= j) ? hw_exp2(sCum[i] - cj) : 0.f;
+          const float m = S[u][k][r] * e;
+          put_split(sMh, sMl, i * LQ + j, m);
+          P2[u][k][r] = acc[u][r] * e;
+          const float wv = (i > j) ? m * acc[u][r] * dj : 0.f;
+          rsum[u][r] += wv;
+          csum += wv;
+          if (i == j) sDiag[i] = acc[u][r];
         }
+        csum = sum_lg(csum);
+        if (lg == 0) colW[rt][j] = csum;
       }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float v = sum16(up[r]);
-        if (li == 0) uP[ct0][rt * 16 + 4 * lg + r] = v;
+        const float v = sum16(rsum[u][r]);
+        if (li == 0) rowW[ct0][(rt0 + u) * 16 + 4 * lg + r] = v;
       }
+
+    // --- dY H: dC += e_in o (dY H); u_i = e_in_i sum_n C_in (dY H)_in
+    {
+      float up[U][4];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) up[u][r] = 0.f;
+#pragma unroll
+      for (int k = 0; k < NT / 2; ++k) {
+        const int ct = ct0 + 2 * k;
+        f32x4 acc[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k0 = 0; k0 < PP; k0 += 32) {
+          const FragBF bh = trfrag(sSh, LS, k0, ct * 16, li, lg), bl = trfrag(sSl, LS, k0, ct * 16, li, lg);
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const FragBF a = kc16(sDY, LX, (rt0 + u) * 16 + li, k0, lg);
+            acc[u] = mma(a, bh, acc[u]);
+            acc[u] = mma(a, bl, acc[u]);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = (rt0 + u) * 16 + 4 * lg + r;
+            const float v = sEin[i] * acc[u][r];
+            dCacc[u][k][r] += v;
+            up[u][r] += (float)sC[i * LB + ct * 16 + li] * v;
+          }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float v = sum16(up[u][r]);
+          if (li == 0) uP[ct0][(rt0 + u) * 16 + 4 * lg + r] = v;
+        }
     }
     lds_barrier();
 
@@ -995,7 +1038,7 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
     lds_barrier();
     {
       float gh = 0.f;
-      for (int idx = tid; idx < PN / 4; idx += 512) {
+      for (int idx = tid; idx < PN / 4; idx += NTH) {
         const int r = (idx * 4) / N, col = (idx * 4) % N, off = r * LS + col;
         const float4 gv = *reinterpret_cast<const float4 *>(sGst + 4 * idx);
         const float gq[4] = {gv.x, gv.y, gv.z, gv.w};
@@ -1011,98 +1054,143 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
     lds_barrier();
     // sGst is free until the tail: copy the next head's entering state into it
     const bool has_next = h + 1 < (g + 1) * hpg;
-    if (has_next && w >= 2) fetch_h(h + 1, 2, 6);
+    if (has_next && w >= 2) fetch_h(h + 1, 2, NW - 2);
 
     // --- bracket = M^T dY + e_out o (B G^T); dx; x . bracket
     {
-      float dp[4] = {0.f, 0.f, 0.f, 0.f};
+      float dp[U][4];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dp[u][r] = 0.f;
 #pragma unroll
       for (int k = 0; k < PT / 2; ++k) {
         const int ct = ct0 + 2 * k;
-        f32x4 a3 = {0.f, 0.f, 0.f, 0.f}, b3 = {0.f, 0.f, 0.f, 0.f};
+        f32x4 a3[U], b3[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) a3[u] = b3[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k0 = 0; k0 < kQ; k0 += 32) {
           const FragBF bb = trfrag(sDY, LX, k0, ct * 16, li, lg);
-          a3 = mma(trfrag(sMh, LQ, k0, rt * 16, li, lg), bb, a3);
-          a3 = mma(trfrag(sMl, LQ, k0, rt * 16, li, lg), bb, a3);
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            a3[u] = mma(trfrag(sMh, LQ, k0, (rt0 + u) * 16, li, lg), bb, a3[u]);
+            a3[u] = mma(trfrag(sMl, LQ, k0, (rt0 + u) * 16, li, lg), bb, a3[u]);
+          }
         }
 #pragma unroll
         for (int k0 = 0; k0 < NP; k0 += 32) {
-          const FragBF a = kc16(sB, LB, rt * 16 + li, k0, lg);
-          b3 = mma(a, kc16(sSh, LS, ct * 16 + li, k0, lg), b3);
-          b3 = mma(a, kc16(sSl, LS, ct * 16 + li, k0, lg), b3);
+          const FragBF gh = kc16(sSh, LS, ct * 16 + li, k0, lg), gl = kc16(sSl, LS, ct * 16 + li, k0, lg);
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const FragBF a = kc16(sB, LB, (rt0 + u) * 16 + li, k0, lg);
+            b3[u] = mma(a, gh, b3[u]);
+            b3[u] = mma(a, gl, b3[u]);
+          }
         }
         const int pc = ct * 16 + li;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = rt * 16 + 4 * lg + r;
-          const float br = a3[r] + sEout[t] * b3[r];
-          if (t < nv && pc < P)
-            p.dx[(((int64_t)b_ * L + t0 + t) * H + h) * P + pc] = Dh * (float)sDY[t * LX + pc] + sDel[t] * br;
-          dp[r] += (float)sX[t * LX + pc] * br;
-        }
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = (rt0 + u) * 16 + 4 * lg + r;
+            const float br = a3[u][r] + sEout[t] * b3[u][r];
+            if (t < nv && pc < P)
+              p.dx[(((int64_t)b_ * L + t0 + t) * H + h) * P + pc] = Dh * (float)sDY[t * LX + pc] + sDel[t] * br;
+            dp[u][r] += (float)sX[t * LX + pc] * br;
+          }
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float v = sum16(dp[r]);
-        if (li == 0) dinP[ct0][rt * 16 + 4 * lg + r] = v;
-      }
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float v = sum16(dp[u][r]);
+          if (li == 0) dinP[ct0][(rt0 + u) * 16 + 4 * lg + r] = v;
+        }
     }
 
     // --- X G: dB part e_out o (X G); v_j = e_out_j Delta_j sum_n B_jn (X G)_jn
-    f32x4 acc6[NT / 2];
+    f32x4 acc6[U][NT / 2];
     {
-      float vp[4] = {0.f, 0.f, 0.f, 0.f};
+      float vp[U][4];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vp[u][r] = 0.f;
 #pragma unroll
       for (int k = 0; k < NT / 2; ++k) {
         const int ct = ct0 + 2 * k;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        f32x4 acc[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k0 = 0; k0 < PP; k0 += 32) {
-          const FragBF a = kc16(sX, LX, rt * 16 + li, k0, lg);
-          acc = mma(a, trfrag(sSh, LS, k0, ct * 16, li, lg), acc);
-          acc = mma(a, trfrag(sSl, LS, k0, ct * 16, li, lg), acc);
+          const FragBF th = trfrag(sSh, LS, k0, ct * 16, li, lg), tl = trfrag(sSl, LS, k0, ct * 16, li, lg);
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const FragBF a = kc16(sX, LX, (rt0 + u) * 16 + li, k0, lg);
+            acc[u] = mma(a, th, acc[u]);
+            acc[u] = mma(a, tl, acc[u]);
+          }
         }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = (rt0 + u) * 16 + 4 * lg + r;
+            vp[u][r] += (float)sB[t * LB + ct * 16 + li] * acc[u][r];
+            acc6[u][k][r] = sEout[t] * acc[u][r];
+          }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int t = rt * 16 + 4 * lg + r;
-          vp[r] += (float)sB[t * LB + ct * 16 + li] * acc[r];
-          acc6[k][r] = sEout[t] * acc[r];
+          const float v = sum16(vp[u][r]);
+          if (li == 0) vP[ct0][(rt0 + u) * 16 + 4 * lg + r] = v;
         }
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float v = sum16(vp[r]);
-        if (li == 0) vP[ct0][rt * 16 + 4 * lg + r] = v;
-      }
     }
     lds_barrier();
-    uint4 nx = make_uint4(0u, 0u, 0u, 0u), ndy = nx;
-    if (has_next && has_piece && xr_row < nv) {
-      const int64_t off = (((int64_t)b_ * L + t0 + xr_row) * H + h + 1) * P + xr_col;
-      nx = *reinterpret_cast<const uint4 *>(reinterpret_cast<const __bf16 *>(p.x) + off);
-      ndy = *reinterpret_cast<const uint4 *>(reinterpret_cast<const __bf16 *>(p.dy) + off);
+    uint4 nx[NPC], ndy[NPC];
+#pragma unroll
+    for (int i = 0; i < NPC; ++i) {
+      const int piece = tid + i * NTH, xr_row = piece / XPC, xr_col = (piece % XPC) * 8;
+      nx[i] = ndy[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (has_next && piece < NXP && xr_row < nv) {
+        const int64_t off = (((int64_t)b_ * L + t0 + xr_row) * H + h + 1) * P + xr_col;
+        nx[i] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const __bf16 *>(p.x) + off);
+        ndy[i] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const __bf16 *>(p.dy) + off);
+      }
     }
 
     // --- P2 = DX o E (split) to LDS; dB += Delta o (e_out o XG + P2^T C)
 #pragma unroll
-    for (int k = 0; k < 2; ++k)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        put_split(sMh, sMl, (rt * 16 + 4 * lg + r) * LQ + (ct0 + 2 * k) * 16 + li, P2[k][r]);
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          put_split(sMh, sMl, ((rt0 + u) * 16 + 4 * lg + r) * LQ + (ct0 + 2 * k) * 16 + li, P2[u][k][r]);
     lds_barrier();
 #pragma unroll
     for (int k = 0; k < NT / 2; ++k) {
       const int ct = ct0 + 2 * k;
-      f32x4 acc = acc6[k];
+      f32x4 acc[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc[u] = acc6[u][k];
 #pragma unroll
       for (int k0 = 0; k0 < kQ; k0 += 32) {
         const FragBF bb = trfrag(sC, LB, k0, ct * 16, li, lg);
-        acc = mma(trfrag(sMh, LQ, k0, rt * 16, li, lg), bb, acc);
-        acc = mma(trfrag(sMl, LQ, k0, rt * 16, li, lg), bb, acc);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          acc[u] = mma(trfrag(sMh, LQ, k0, (rt0 + u) * 16, li, lg), bb, acc[u]);
+          acc[u] = mma(trfrag(sMl, LQ, k0, (rt0 + u) * 16, li, lg), bb, acc[u]);
+        }
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dBacc[k][r] += sDel[rt * 16 + 4 * lg + r] * acc[r];
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dBacc[u][k][r] += sDel[(rt0 + u) * 16 + 4 * lg + r] * acc[u][r];
     }
     lds_barrier();
 
@@ -1111,30 +1199,38 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
     for (int k = 0; k < 2; ++k) {
       const int j = (ct0 + 2 * k) * 16 + li;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) put_split(sMh, sMl, (rt * 16 + 4 * lg + r) * LQ + j, P2[k][r] * sDel[j]);
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          put_split(sMh, sMl, ((rt0 + u) * 16 + 4 * lg + r) * LQ + j, P2[u][k][r] * sDel[j]);
     }
     lds_barrier();
 #pragma unroll
     for (int k = 0; k < NT / 2; ++k) {
       const int ct = ct0 + 2 * k;
-      f32x4 acc = dCacc[k];
 #pragma unroll
       for (int k0 = 0; k0 < kQ; k0 += 32) {
         const FragBF bb = trfrag(sB, LB, k0, ct * 16, li, lg);
-        acc = mma(kc16(sMh, LQ, rt * 16 + li, k0, lg), bb, acc);
-        acc = mma(kc16(sMl, LQ, rt * 16 + li, k0, lg), bb, acc);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          dCacc[u][k] = mma(kc16(sMh, LQ, (rt0 + u) * 16 + li, k0, lg), bb, dCacc[u][k]);
+          dCacc[u][k] = mma(kc16(sMl, LQ, (rt0 + u) * 16 + li, k0, lg), bb, dCacc[u][k]);
+        }
       }
-      dCacc[k] = acc;
     }
 
     // --- da, ddt and the head's partial sums (wave 0, lane k = token); wave 1
-    //     forms the next head's decays, waves 2..7 split its entering state
+    //     forms the next head's decays, waves 2.. split its entering state
     //     (in sGst) into the two planes and copy its G into sGst, piece by
     //     piece (each wave splits the pieces it then overwrites); every
-    //     thread stores its x and dy piece of the next head
-    if (has_next && has_piece) {
-      *reinterpret_cast<uint4 *>(&sX[xr_row * LX + xr_col]) = nx;
-      *reinterpret_cast<uint4 *>(&sDY[xr_row * LX + xr_col]) = ndy;
+    //     thread stores its x and dy pieces of the next head
+#pragma unroll
+    for (int i = 0; i < NPC; ++i) {
+      const int piece = tid + i * NTH, xr_row = piece / XPC, xr_col = (piece % XPC) * 8;
+      if (has_next && piece < NXP) {
+        *reinterpret_cast<uint4 *>(&sX[xr_row * LX + xr_col]) = nx[i];
+        *reinterpret_cast<uint4 *>(&sDY[xr_row * LX + xr_col]) = ndy[i];
+      }
     }
     if (w != 0) {
       if (has_next) {
@@ -1144,7 +1240,7 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
           __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
           const float *Gsrc = p.adj + (((int64_t)b_ * H + h + 1) * nc + c) * PN;
           const auto rsg = make_rsrc(Gsrc, (uint32_t)PN * 4u);
-          for (int q = w - 2; q < PN / 256; q += 6) {
+          for (int q = w - 2; q < PN / 256; q += NW - 2) {
             const int idx = q * 64 + lane; // float4 index
             const int r = (idx * 4) / N, col = (idx * 4) % N, off = r * LS + col;
             const float4 hv = *reinterpret_cast<const float4 *>(sGst + 4 * idx);
@@ -1164,15 +1260,15 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
       const float rowsum = rowW[0][k] + rowW[1][k];
       const float dlt = colsum - rowsum;
       const float R = wave_incl_scan(dlt) - dlt;
-      const float u = uP[0][k] + uP[1][k];
-      const float u_incl = wave_incl_scan(u);
-      const float U = lane63(u_incl) - u_incl + u;
+      const float uk = uP[0][k] + uP[1][k];
+      const float u_incl = wave_incl_scan(uk);
+      const float Uf = lane63(u_incl) - u_incl + uk;
       const float v = sEout[k] * sDel[k] * (vP[0][k] + vP[1][k]);
       const float V = wave_incl_scan(v) - v;
       float gh = 0.f;
 #pragma unroll
-      for (int q = 1; q <= 8; ++q) gh += sRed[q];
-      const float da = R + U + V + hw_exp2(cum_last2) * gh;
+      for (int q = 1; q <= NW; ++q) gh += sRed[q];
+      const float da = R + Uf + V + hw_exp2(cum_last2) * gh;
       const float din = dinP[0][k] + dinP[1][k];
       const float ddt = (din + Ah * da) * sSig[k];
       const bool valid = k < nv;
@@ -1191,18 +1287,25 @@ __global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) 
   }
 
 #pragma unroll
-  for (int k = 0; k < NT / 2; ++k) {
-    const int n = (ct0 + 2 * k) * 16 + li;
+  for (int u = 0; u < U; ++u)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = rt * 16 + 4 * lg + r;
-      if (t < nv && n < N) {
-        const int64_t o = (((int64_t)b_ * L + t0 + t) * G + g) * N + n;
-        p.dB[o] = dBacc[k][r];
-        p.dC[o] = dCacc[k][r];
+    for (int k = 0; k < NT / 2; ++k) {
+      const int n = (ct0 + 2 * k) * 16 + li;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = (rt0 + u) * 16 + 4 * lg + r;
+        if (t < nv && n < N) {
+          const int64_t o = (((int64_t)b_ * L + t0 + t) * G + g) * N + n;
+          p.dB[o] = dBacc[u][k][r];
+          p.dC[o] = dCacc[u][k][r];
+        }
       }
     }
-  }
+}
+
+template <int P, int N>
+__global__ void __launch_bounds__(512) bwd_chunk_bf16_kernel(const BwdParams p) {
+  chunk_bf16_body<P, N, 8>(p);
 }
 
 // Gradient through the output gate out = y * silu(z): dy = dout * silu(z)
