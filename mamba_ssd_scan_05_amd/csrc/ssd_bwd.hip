@@ -742,8 +742,16 @@ __device__ __forceinline__ void state_scan_bf16_body(const BwdParams &p, int bh,
         if (idx >= kQ * KP) continue;
         const __bf16 *e = reinterpret_cast<const __bf16 *>(&pl.v[k]);
         const float wr = sW[r];
+        bf16x8 hv, lv;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) put_split(sLh, sLl, r * LX + cc * 8 + q, wr * (float)e[q]);
+        for (int q = 0; q < 8; ++q) {
+          const float v = wr * (float)e[q];
+          hv[q] = (__bf16)v;
+          lv[q] = (__bf16)(v - (float)hv[q]);
+        }
+        // eight consecutive values of a row: one 16-byte write per plane
+        *reinterpret_cast<bf16x8 *>(sLh + r * LX + cc * 8) = hv;
+        *reinterpret_cast<bf16x8 *>(sLl + r * LX + cc * 8) = lv;
       }
       constexpr int KN = RowPrefetch<__bf16, N>::kPerRow;
 #pragma unroll
@@ -1042,11 +1050,17 @@ __device__ __forceinline__ void chunk_bf16_body(const BwdParams &p) {
         const int r = (idx * 4) / N, col = (idx * 4) % N, off = r * LS + col;
         const float4 gv = *reinterpret_cast<const float4 *>(sGst + 4 * idx);
         const float gq[4] = {gv.x, gv.y, gv.z, gv.w};
+        // four consecutive columns: 8-byte reads and writes per plane
+        const bf16x4 oh = *reinterpret_cast<const bf16x4 *>(sSh + off), ol = *reinterpret_cast<const bf16x4 *>(sSl + off);
+        bf16x4 nh, nl;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          gh += gq[q] * ((float)sSh[off + q] + (float)sSl[off + q]);
-          put_split(sSh, sSl, off + q, gq[q]);
+          gh += gq[q] * ((float)oh[q] + (float)ol[q]);
+          nh[q] = (__bf16)gq[q];
+          nl[q] = (__bf16)(gq[q] - (float)nh[q]);
         }
+        *reinterpret_cast<bf16x4 *>(sSh + off) = nh;
+        *reinterpret_cast<bf16x4 *>(sSl + off) = nl;
       }
       gh = wave_sum(gh);
       if (lane == 0) sRed[1 + w] = gh;
@@ -1244,10 +1258,15 @@ __device__ __forceinline__ void chunk_bf16_body(const BwdParams &p) {
             const int idx = q * 64 + lane; // float4 index
             const int r = (idx * 4) / N, col = (idx * 4) % N, off = r * LS + col;
             const float4 hv = *reinterpret_cast<const float4 *>(sGst + 4 * idx);
-            put_split(sSh, sSl, off, hv.x);
-            put_split(sSh, sSl, off + 1, hv.y);
-            put_split(sSh, sSl, off + 2, hv.z);
-            put_split(sSh, sSl, off + 3, hv.w);
+            const float hq[4] = {hv.x, hv.y, hv.z, hv.w};
+            bf16x4 nh, nl;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              nh[e] = (__bf16)hq[e];
+              nl[e] = (__bf16)(hq[e] - (float)nh[e]);
+            }
+            *reinterpret_cast<bf16x4 *>(sSh + off) = nh;
+            *reinterpret_cast<bf16x4 *>(sSl + off) = nl;
             __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rsg, (__attribute__((address_space(3))) void *)(sGst + q * 256), 16,
                                                      q * 1024 + lane * 16, 0, 0, 0);
