@@ -12,6 +12,7 @@ from __future__ import annotations
 import contextlib
 import ctypes
 import os
+import struct
 from typing import Optional
 
 import torch
@@ -47,7 +48,9 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError("libssd.so is not built (python -m mamba_ssd_scan_05_amd.build)")
         L = ctypes.CDLL(LIB_PATH)
-        P = ctypes.POINTER(SsdTensor)
+        # tensor descriptors go in as addresses (ctypes pointers from
+        # describe() are accepted too)
+        P = ctypes.c_void_p
         L.ssd_scan_fwd.argtypes = [P] * 10 + [ctypes.c_int, ctypes.c_void_p]
         L.ssd_scan_fwd.restype = ctypes.c_int
         L.ssd_scan_fwd_algo.argtypes = [P] * 10 + [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
@@ -84,12 +87,11 @@ def lib():
     return _lib
 
 
+_DTYPE_CODE = {torch.float32: SSD_F32, torch.bfloat16: SSD_BF16}
+
+
 def _dtype_code(t: torch.Tensor) -> int:
-    if t.dtype == torch.float32:
-        return SSD_F32
-    if t.dtype == torch.bfloat16:
-        return SSD_BF16
-    return 99  # rejected by the library as SSD_ERR_DTYPE
+    return _DTYPE_CODE.get(t.dtype, 99)  # 99: rejected by the library as SSD_ERR_DTYPE
 
 
 def describe(t: Optional[torch.Tensor]):
@@ -108,10 +110,35 @@ def describe(t: Optional[torch.Tensor]):
     return ctypes.pointer(d)
 
 
+# ssd_tensor as packed bytes: data, dtype, ndim, shape[4], strides[4]
+_DESC = struct.Struct("<Qii4q4q")
+assert _DESC.size == ctypes.sizeof(SsdTensor)
+
+
+def _descs(*ts):
+    """Descriptors of a call's tensors in one buffer: (buffer, addresses),
+    None -> NULL.  Keep the buffer alive until the call returns."""
+    buf = ctypes.create_string_buffer(_DESC.size * len(ts))
+    base = ctypes.addressof(buf)
+    addrs = []
+    for i, t in enumerate(ts):
+        if t is None:
+            addrs.append(None)
+            continue
+        n = t.dim()
+        if n > 4:
+            raise ValueError("ssd tensors have at most 4 dimensions")
+        pad = (0,) * (4 - n)
+        _DESC.pack_into(buf, i * _DESC.size, t.data_ptr() if t.numel() else 0, _dtype_code(t), n,
+                        *t.shape, *pad, *t.stride(), *pad)
+        addrs.append(base + i * _DESC.size)
+    return buf, addrs
+
+
 def _on_device(t):
     """Make t's device current for the call (the library launches on the
     current device and refuses memory that device cannot address)."""
-    if t is not None and t.is_cuda:
+    if t is not None and t.is_cuda and t.device.index != torch.cuda.current_device():
         return torch.cuda.device(t.device)
     return contextlib.nullcontext()
 
@@ -138,15 +165,14 @@ def ssd_scan_fwd(x, dt, dt_bias, A, B, C, D=None, init_state=None, out=None,
     if final_state is None and return_final_state:
         final_state = torch.empty((x.shape[0], x.shape[2], x.shape[3], B.shape[3]),
                                   dtype=torch.float32, device=x.device)
-    args = (describe(x), describe(dt), describe(dt_bias), describe(A), describe(B), describe(C),
-            describe(D), describe(init_state), describe(out), describe(final_state), int(chunk))
+    keep, d = _descs(x, dt, dt_bias, A, B, C, D, init_state, out, final_state)
     with _on_device(x):
         st = _stream(stream, x)
         if algo == SSD_ALGO_AUTO:
             # the library's own plan: the plain entry point
-            status = lib().ssd_scan_fwd(*args, st)
+            status = lib().ssd_scan_fwd(*d, int(chunk), st)
         else:
-            status = lib().ssd_scan_fwd_algo(*args, int(algo), st)
+            status = lib().ssd_scan_fwd_algo(*d, int(chunk), int(algo), st)
     _check(status)
     return out, final_state
 
@@ -160,9 +186,8 @@ def ssd_scan_fwd_noalloc(x, dt, dt_bias, A, B, C, D=None, init_state=None, out=N
         out = torch.empty_like(x)
     with _on_device(x):
         st = _stream(stream, x)
-        status = lib().ssd_scan_fwd_noalloc(
-            describe(x), describe(dt), describe(dt_bias), describe(A), describe(B), describe(C),
-            describe(D), describe(init_state), describe(out), describe(final_state), int(chunk), st)
+        keep, d = _descs(x, dt, dt_bias, A, B, C, D, init_state, out, final_state)
+        status = lib().ssd_scan_fwd_noalloc(*d, int(chunk), st)
     _check(status)
     return out, final_state
 
@@ -200,11 +225,9 @@ def ssd_scan_bwd(x, dt, dt_bias, A, B, C, D, init_state, dout, dfinal_state=None
             g[k] = None
     with _on_device(x):
         st = _stream(stream, x)
-        status = lib().ssd_scan_bwd(
-            describe(x), describe(dt), describe(dt_bias), describe(A), describe(B), describe(C),
-            describe(D), describe(init_state), describe(dout), describe(dfinal_state),
-            describe(g["dx"]), describe(g["ddt"]), describe(g["ddt_bias"]), describe(g["dA"]),
-            describe(g["dB"]), describe(g["dC"]), describe(g["dD"]), describe(g["dinit"]), st)
+        keep, d = _descs(x, dt, dt_bias, A, B, C, D, init_state, dout, dfinal_state,
+                         g["dx"], g["ddt"], g["ddt_bias"], g["dA"], g["dB"], g["dC"], g["dD"], g["dinit"])
+        status = lib().ssd_scan_bwd(*d, st)
     _check(status)
     return g
 
@@ -228,12 +251,10 @@ def ssd_scan_bwd_gated(x, dt, dt_bias, A, B, C, z, D, init_state, dout, dfinal_s
             g[k] = None
     with _on_device(x):
         st = _stream(stream, x)
-        status = lib().ssd_scan_bwd_gated(
-            describe(x), describe(dt), describe(dt_bias), describe(A), describe(B), describe(C),
-            describe(D), describe(z), describe(init_state), describe(dout), describe(dfinal_state),
-            describe(g["dx"]), describe(g["ddt"]), describe(g["ddt_bias"]), describe(g["dA"]),
-            describe(g["dB"]), describe(g["dC"]), describe(g["dD"]), describe(g["dz"]),
-            describe(g["dinit"]), st)
+        keep, d = _descs(x, dt, dt_bias, A, B, C, D, z, init_state, dout, dfinal_state,
+                         g["dx"], g["ddt"], g["ddt_bias"], g["dA"], g["dB"], g["dC"], g["dD"], g["dz"],
+                         g["dinit"])
+        status = lib().ssd_scan_bwd_gated(*d, st)
     _check(status)
     return g
 
@@ -250,10 +271,8 @@ def ssd_scan_fwd_gated(x, dt, dt_bias, A, B, C, z, D=None, init_state=None, out=
                                   dtype=torch.float32, device=x.device)
     with _on_device(x):
         st = _stream(stream, x)
-        status = lib().ssd_scan_fwd_gated(
-            describe(x), describe(dt), describe(dt_bias), describe(A), describe(B), describe(C),
-            describe(D), describe(z), describe(init_state), describe(out), describe(final_state),
-            int(chunk), int(algo), st)
+        keep, d = _descs(x, dt, dt_bias, A, B, C, D, z, init_state, out, final_state)
+        status = lib().ssd_scan_fwd_gated(*d, int(chunk), int(algo), st)
     _check(status)
     return out, final_state
 
@@ -269,10 +288,8 @@ def ssd_scan_fwd_rows(x, dt, dt_bias, A, B, C, D=None, init_state=None, out=None
                                   dtype=torch.float32, device=x.device)
     with _on_device(x):
         st = _stream(stream, x)
-        status = lib().ssd_scan_fwd_rows(
-            describe(x), describe(dt), describe(dt_bias), describe(A), describe(B), describe(C),
-            describe(D), describe(init_state), describe(out), describe(final_state),
-            int(waves), st)
+        keep, d = _descs(x, dt, dt_bias, A, B, C, D, init_state, out, final_state)
+        status = lib().ssd_scan_fwd_rows(*d, int(waves), st)
     _check(status)
     return out, final_state
 
@@ -289,10 +306,8 @@ def ssd_selective_scan_fwd(x, dt, dt_bias, A, B, C, D=None, init_state=None, out
                                   device=x.device)
     with _on_device(x):
         st = _stream(stream, x)
-        status = lib().ssd_selective_scan_fwd(
-            describe(x), describe(dt), describe(dt_bias), describe(A), describe(B), describe(C),
-            describe(D), describe(init_state), describe(out), describe(final_state),
-            int(segments), st)
+        keep, d = _descs(x, dt, dt_bias, A, B, C, D, init_state, out, final_state)
+        status = lib().ssd_selective_scan_fwd(*d, int(segments), st)
     _check(status)
     return out, final_state
 
@@ -303,8 +318,8 @@ def ssd_step(state, x, dt, A, B, C, D=None, out=None, stream=None):
         out = torch.empty_like(x)
     with _on_device(state):
         st = _stream(stream, state)
-        status = lib().ssd_step(describe(state), describe(x), describe(dt), describe(A),
-                                describe(B), describe(C), describe(D), describe(out), st)
+        keep, d = _descs(state, x, dt, A, B, C, D, out)
+        status = lib().ssd_step(*d, st)
     _check(status)
     return out
 
