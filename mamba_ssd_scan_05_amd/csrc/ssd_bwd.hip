@@ -1039,11 +1039,12 @@ __device__ __forceinline__ void chunk_bf16_body(const BwdParams &p) {
           if (li == 0) uP[ct0][(rt0 + u) * 16 + 4 * lg + r] = v;
         }
     }
+    // every wave is done with H's planes, and its copy of G into sGst has
+    // landed (each wave waits for its own copies before the barrier)
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
 
     // --- replace H by G (already in LDS); <G, H> with H from its two planes
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    lds_barrier();
     {
       float gh = 0.f;
       for (int idx = tid; idx < PN / 4; idx += NTH) {
@@ -1206,29 +1207,38 @@ __device__ __forceinline__ void chunk_bf16_body(const BwdParams &p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) dBacc[u][k][r] += sDel[(rt0 + u) * 16 + 4 * lg + r] * acc[u][r];
     }
-    lds_barrier();
 
-    // --- P1 = P2 diag(Delta) (split) to LDS; dC += P1 B
+    // --- dC += P2 diag(Delta) B on the same planes: this wave's P2 rows
+    //     as A fragments (hi + lo), each K-value (token j) scaled by Delta_j
+    //     in registers and split again; no second pass through LDS
+    FragBF ph[U][kQ / 32], pl[U][kQ / 32];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int j = (ct0 + 2 * k) * 16 + li;
+    for (int kk = 0; kk < kQ / 32; ++kk) {
+      const float4 d0 = *reinterpret_cast<const float4 *>(&sDel[32 * kk + 4 * lg]);
+      const float4 d1 = *reinterpret_cast<const float4 *>(&sDel[32 * kk + 16 + 4 * lg]);
+      const float dj[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+      for (int u = 0; u < U; ++u) {
+        const FragBF h = kc16(sMh, LQ, (rt0 + u) * 16 + li, 32 * kk, lg);
+        const FragBF l = kc16(sMl, LQ, (rt0 + u) * 16 + li, 32 * kk, lg);
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          put_split(sMh, sMl, ((rt0 + u) * 16 + 4 * lg + r) * LQ + j, P2[u][k][r] * sDel[j]);
+        for (int e = 0; e < 8; ++e) {
+          const float v = ((float)h.v[e] + (float)l.v[e]) * dj[e];
+          ph[u][kk].v[e] = (__bf16)v;
+          pl[u][kk].v[e] = (__bf16)(v - (float)ph[u][kk].v[e]);
+        }
+      }
     }
-    lds_barrier();
 #pragma unroll
     for (int k = 0; k < NT / 2; ++k) {
       const int ct = ct0 + 2 * k;
 #pragma unroll
-      for (int k0 = 0; k0 < kQ; k0 += 32) {
-        const FragBF bb = trfrag(sB, LB, k0, ct * 16, li, lg);
+      for (int kk = 0; kk < kQ / 32; ++kk) {
+        const FragBF bb = trfrag(sB, LB, 32 * kk, ct * 16, li, lg);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          dCacc[u][k] = mma(kc16(sMh, LQ, (rt0 + u) * 16 + li, k0, lg), bb, dCacc[u][k]);
-          dCacc[u][k] = mma(kc16(sMl, LQ, (rt0 + u) * 16 + li, k0, lg), bb, dCacc[u][k]);
+          dCacc[u][k] = mma(ph[u][kk], bb, dCacc[u][k]);
+          dCacc[u][k] = mma(pl[u][kk], bb, dCacc[u][k]);
         }
       }
     }
