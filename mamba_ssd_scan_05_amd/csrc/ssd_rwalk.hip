@@ -80,7 +80,6 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
   constexpr int NBB = 2 * NT;            // B fragment blocks of a record
   constexpr int NRB = NCB + NBB + 6;     // blocks per record (C, B, scores)
   constexpr int NSF = 6;                 // score fragments per sub-block
-  constexpr int CPW = (NRB + W - 1) / W; // record blocks each wave copies
 
   // A sub-block's record and each wave's x tile are copied from global
   // memory straight into LDS (buffer loads to LDS: no registers, no LDS
@@ -146,24 +145,49 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
     const int pc = l + 64 * e, tok = pc >> 1, half = pc & 1;
     offX[e] = (uint32_t)((tok * rowX + 8 * half) * 2);
   }
-  // Copy the record and this wave's x of sub-block k into (rec, xt).  Wave w
-  // copies record blocks w, w + W, ... (the last block again where it has
-  // none of its own, so every wave issues the same number of copies); copies
-  // past the end of the sequence use empty ranges and write zeros.
+  // Copy the record and the x tiles of sub-block k into (rec, xt).  The
+  // copying waves (WC of them) take record blocks w, w + WC, ... (the last
+  // block again where a wave has none of its own, so they issue the same
+  // number of record copies); copies past the end of the sequence use empty
+  // ranges and write zeros.  With five waves the fifth shares a SIMD with
+  // the first and loses issue priority to it, so it is the last to reach
+  // each barrier: it issues no copies (each copy instruction holds its wave
+  // for a while), waves 0-3 copy the whole record and waves 1 and 2 one half
+  // each of its x tile besides their own.
+  constexpr bool kSpare4 = (W == 5);
+  constexpr int WC = kSpare4 ? 4 : W;
+  constexpr int CPW = (NRB + WC - 1) / WC; // record blocks per copying wave
+  const __bf16 *Xbase4 = nullptr;          // x columns of wave 4
+  if constexpr (kSpare4) {
+    const int R4 = (wi * W + 4) * 16, Rc4 = R4 < prm.rows_per_bg ? R4 : 0;
+    Xbase4 = reinterpret_cast<const __bf16 *>(prm.x) + (int64_t)ib * L * rowX + (int64_t)(g * (H / G) + Rc4 / P) * P +
+             Rc4 % P;
+  }
   auto copy_in = [&](int k, __bf16 *rec, __bf16 (*xt)[1024]) {
     const int t0 = 64 * k, nv = min(64, L - t0);
     const auto rsR = make_rsrc(Rbase + (int64_t)min(k, nsub - 1) * (NRB * 512), nv > 0 ? (uint32_t)NRB * 1024u : 0u);
+    const uint32_t xbytes = nv > 0 ? (uint32_t)(((int64_t)(nv - 1) * rowX + 16) * 2) : 0u;
+    if (!kSpare4 || w < 4) {
 #pragma unroll
-    for (int i = 0; i < CPW; ++i) {
-      const int c = min(w + i * W, NRB - 1);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsR, (__attribute__((address_space(3))) void *)&rec[c * 512], 16,
-                                               l * 16, c * 1024, 0, 0);
+      for (int i = 0; i < CPW; ++i) {
+        const int c = min(w + i * WC, NRB - 1);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsR, (__attribute__((address_space(3))) void *)&rec[c * 512], 16,
+                                                 l * 16, c * 1024, 0, 0);
+      }
+      const auto rsX = make_rsrc(Xbase + (int64_t)t0 * rowX, xbytes);
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsX, (__attribute__((address_space(3))) void *)&xt[w][512 * e], 16,
+                                                 offX[e], 0, 0, 0);
     }
-    const auto rsX = make_rsrc(Xbase + (int64_t)t0 * rowX, nv > 0 ? (uint32_t)(((int64_t)(nv - 1) * rowX + 16) * 2) : 0u);
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsX, (__attribute__((address_space(3))) void *)&xt[w][512 * e], 16,
-                                               offX[e], 0, 0, 0);
+    if constexpr (kSpare4) {
+      if (w == 1 || w == 2) {
+        const int e = w - 1;
+        const auto rsX4 = make_rsrc(Xbase4 + (int64_t)t0 * rowX, xbytes);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsX4, (__attribute__((address_space(3))) void *)&xt[4][512 * e], 16,
+                                                 offX[e], 0, 0, 0);
+      }
+    }
   };
   // Raw step size of token l of sub-block k (zero past the end).
   auto fetch_dt = [&](int k) {
