@@ -9,10 +9,13 @@ fp32 initial and final state), inputs resident in HBM.  W untimed steps
 (default 200: back-to-back calls reach the sustained clock after about 150
 to 200 calls), then exactly K timed steps (default 100) between two device
 synchronisations; value =
-b*L*K / elapsed.  Each step is also bracketed by HIP events on the stream
-the library launches on, giving the call's average duration for the
-roofline figure (every launch of the call: the operand records and the
-walk under the automatic plan).  Rank 0 prints one JSON line.
+b*L*K / elapsed.  Two HIP events on the stream the library launches on
+bracket the K steps, giving the call's average duration for the roofline
+figure (every launch of the call: the operand records and the walk under
+the automatic plan); no event sits between two timed steps (one would add
+about 4 us of GPU time per step).  The per-step spread (p10/p90) comes from
+a second run of K steps with an event between every two.  Rank 0 prints
+one JSON line.
 
 Cold-cache protocol (roofline.cold and extra.configs): 30 repetitions,
 each after a 512 MiB device write on the same stream (outside the events)
@@ -422,16 +425,20 @@ def main():
     for _ in range(args.warmup):
         one()
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    # The timed steps run back to back with HIP events only around the whole
+    # run (an event recorded between two calls adds ~4 us of GPU time per
+    # step); the kernel average is the event span over the steps.
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    ev[0].record()
+    e0.record()
     for k in range(args.steps):
         one()
-        ev[k + 1].record()
+    e1.record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    per_ms = [ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps)]
-    kern_ms = float(np.mean(per_ms))
+    kern_ms = e0.elapsed_time(e1) / args.steps
+    # per-step spread from a separate run with an event between every two steps
+    per_ms = time_warm(one, torch, reps=args.steps)
     ms_per_step = elapsed * 1e3 / args.steps
     tokens = b * L
     value = tokens * args.steps / elapsed
@@ -467,7 +474,9 @@ def main():
                 "mfma_frac": flops / (kern_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
 
     extra = {"p10_ms": float(np.percentile(per_ms, 10)), "p90_ms": float(np.percentile(per_ms, 90)),
-             "median_ms": float(np.median(per_ms))}
+             "median_ms": float(np.median(per_ms)),
+             "per_step_spread": "p10/p90/median from a second run of the same steps with an event "
+                                "between every two (those events add ~4 us per step)"}
     # cold-cache protocol: 30 reps, each after a 512 MiB eviction write on the
     # same stream outside the events; median with p10/p90
     evict = torch.empty(EVICT_BYTES, dtype=torch.uint8, device=dev)

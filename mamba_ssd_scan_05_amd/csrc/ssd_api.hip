@@ -304,7 +304,11 @@ public:
     if (i == g_scratch.size()) {
       SSD_CHECK(make_room(1, want));
       hipEvent_t ev = nullptr;
-      e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+      // No system-scope fence: the event orders later device work on the
+      // same device (and the host's wait before a free), so a device-scope
+      // release suffices; the system-scope one writes back the L2 at every
+      // call end (about 2 us per back-to-back 2.7B-layer call).
+      e = hipEventCreateWithFlags(&ev, hipEventDisableTiming | hipEventDisableSystemFence);
       if (e != hipSuccess) return hip_fail(e, "scratch: event");
       g_scratch.push_back(ScratchSlot{dev, st_, tag_, nullptr, 0, ev, false, false, 0});
       i = g_scratch.size() - 1;
