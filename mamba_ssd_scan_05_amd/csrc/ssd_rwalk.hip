@@ -317,12 +317,15 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
   __bf16 *Ybase = reinterpret_cast<__bf16 *>(prm.out) + (int64_t)ib * L * rowX + (int64_t)h * P + p0;
   const __bf16 *Zbase = GATED ? reinterpret_cast<const __bf16 *>(prm.z) + (int64_t)ib * L * rowX + (int64_t)h * P + p0
                               : nullptr;
-  float4 zq[4];
+  // z of the current sub-block (zq) and of the next one (zn, loaded a
+  // sub-block ahead so that its latency is hidden behind a whole sub-block)
+  bf16x4 zq[4], zn[4];
   auto fetch_z = [&](int k) {
     const int t0 = 64 * k, nv = min(64, L - t0);
-    const auto rsZ = make_rsrc(Zbase + (int64_t)t0 * rowX, (uint32_t)(((int64_t)(nv - 1) * rowX + 16) * 2));
+    const auto rsZ = make_rsrc(Zbase + (int64_t)t0 * rowX, nv > 0 ? (uint32_t)(((int64_t)(nv - 1) * rowX + 16) * 2) : 0u);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) zq[u] = bload4x<__bf16>(rsZ, offY + (uint32_t)(16 * u * rowX * 2));
+    for (int u = 0; u < 4; ++u)
+      zn[u] = __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(rsZ, (int)(offY + (uint32_t)(16 * u * rowX * 2)), 0, 0));
   };
   auto store_y = [&](int k, const __bf16 (*xt)[1024]) {
     const int t0 = 64 * k, nv = min(64, L - t0);
@@ -335,10 +338,8 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) v[r] = yacc[u][r] + d_h * (float)xv[r];
       if constexpr (GATED) {
-        v[0] *= silu_f(zq[u].x);
-        v[1] *= silu_f(zq[u].y);
-        v[2] *= silu_f(zq[u].z);
-        v[3] *= silu_f(zq[u].w);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] *= silu_f((float)zq[u][r]);
       }
       bstore4<__bf16>(rsY, offY + (uint32_t)(16 * u * rowX * 2), v[0], v[1], v[2], v[3]);
     }
@@ -354,6 +355,7 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
   // past them); the barrier waits for everything older (vmcnt(4)).
   float rdt = fetch_dt(0);
   copy_in(0, sRecA, sXA);
+  if constexpr (GATED) fetch_z(0);
   __builtin_amdgcn_s_waitcnt(0x70); // vmcnt(0) expcnt(7) lgkmcnt(0)
   scan(0, rdt, 0.f, 0);
   rdt = fetch_dt(1);
@@ -367,7 +369,11 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
     __asm__ volatile("" ::: "memory");
     copy_in(k + 1, recN, xtN);
     const float rdt_next = fetch_dt(k + 2);
-    if constexpr (GATED) fetch_z(k);
+    if constexpr (GATED) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) zq[u] = zn[u];
+      fetch_z(k + 1);
+    }
     if (cur_shift != 0) {
 #pragma unroll
       for (int kk = 0; kk < NT; ++kk)
