@@ -151,7 +151,8 @@ int ssd_scan_fwd(const ssd_tensor *x, const ssd_tensor *dt,
  * SSD_ALGO_CHUNKED uses `chunk` as its segment length; SSD_ALGO_ROWS
  * returns SSD_ERR_UNSUPPORTED for fp32 inputs or N outside {32, 64, 128}.
  * SSD_ALGO_ROWS and SSD_ALGO_CHUNKED use scratch (see Scratch above; ROWS:
- * b*G*ceil(L/64)*(N/4 + 6) KiB, 38 KiB per block at N = 128). */
+ * b*G*ceil(L/64)*(N/4 + 6) KiB of operand records, 38 KiB per block at
+ * N = 128, plus b*H*64*ceil(L/64)*4 bytes for a head-major copy of dt). */
 int ssd_scan_fwd_algo(const ssd_tensor *x, const ssd_tensor *dt,
                       const ssd_tensor *dt_bias, const ssd_tensor *A,
                       const ssd_tensor *B, const ssd_tensor *C,

@@ -580,14 +580,17 @@ int run_rows(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bia
              const ssd_tensor *z, const ssd_tensor *init, ssd_tensor *out, ssd_tensor *fin,
              const ScanShape &s, int W, hipStream_t st) {
   const int64_t nsub = (s.L + 63) / 64;
-  const size_t bytes = (size_t)(s.b * s.G * nsub) * (size_t)ssd::prep_record_blocks((int)s.N) * 1024;
+  const size_t rec_bytes = (size_t)(s.b * s.G * nsub) * (size_t)ssd::prep_record_blocks((int)s.N) * 1024;
+  const size_t bytes = rec_bytes + (size_t)(s.b * s.H * nsub * 64) * 4;
   Scratch sc(st);
   void *ws = nullptr;
   SSD_CHECK(sc.get(bytes, &ws));
+  float *dtT = reinterpret_cast<float *>(static_cast<char *>(ws) + rec_bytes);
   int status = SSD_OK;
   hipError_t e;
   do {
-    e = ssd::launch_prep(B->data, C->data, ws, (int)s.b, (int)s.L, (int)s.G, (int)s.N, st);
+    e = ssd::launch_prep(B->data, C->data, ws, (const float *)dt->data, dtT, (int)s.b, (int)s.L, (int)s.H, (int)s.G,
+                         (int)s.N, st);
     if (e != hipSuccess) { status = hip_fail(e, "operand record launch"); break; }
     ssd::RWalkParams p{};
     p.x = x->data; p.dt = (const float *)dt->data;
@@ -595,6 +598,7 @@ int run_rows(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bia
     p.A = (const float *)A->data; p.B = B->data; p.C = C->data;
     p.D = D ? (const float *)D->data : nullptr;
     p.rec = ws;
+    p.dtT = dtT;
     p.init = init ? (const float *)init->data : nullptr;
     p.out = out->data;
     p.z = z ? z->data : nullptr;

@@ -28,6 +28,11 @@
 // Tokens past the sequence end read as zero.  Record of sub-block k of
 // (batch ib, group g): blocks [C | B | S] at rec + ((ib*G + g)*nsub + k) *
 // rec_blocks(N) * 512 bf16.
+//
+// The workgroups of group 0 also copy the sub-block's raw step sizes
+// head-major, dtT[ib][h][64k + j] = dt[ib][64k + j][h] (zero past the end),
+// so that each wave of the walk reads its head's 64 step sizes as one
+// contiguous 256-byte run instead of 64 loads 4H bytes apart.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -39,7 +44,8 @@ namespace {
 
 template <int N>
 __global__ void __launch_bounds__(256) prep_kernel(const __bf16 *__restrict__ B, const __bf16 *__restrict__ C,
-                                                   __bf16 *__restrict__ rec, int L, int G, int nsub) {
+                                                   __bf16 *__restrict__ rec, const float *__restrict__ dt,
+                                                   float *__restrict__ dtT, int L, int H, int G, int nsub) {
   constexpr int NCB = 4 * (N / 32);     // C blocks
   constexpr int NBB = 2 * (N / 16);     // B blocks
   constexpr int NRB = NCB + NBB + 6;    // blocks per record
@@ -48,6 +54,8 @@ __global__ void __launch_bounds__(256) prep_kernel(const __bf16 *__restrict__ B,
   constexpr int RW = N / 8;             // 16-byte pieces per row
   __shared__ __attribute__((aligned(16))) __bf16 sB[64 * LDB];
   __shared__ __attribute__((aligned(16))) __bf16 sC[64 * LDC];
+  constexpr int HC = 128;         // heads per pass of the step-size transpose
+  __shared__ float sT[HC * 65];   // step sizes of HC heads x 64 tokens, transposed
 
   const int wg = blockIdx.x;
   const int k = wg % nsub, bg = wg / nsub;
@@ -65,6 +73,31 @@ __global__ void __launch_bounds__(256) prep_kernel(const __bf16 *__restrict__ B,
     *reinterpret_cast<float4 *>(&sB[j * LDB + n0]) = bload16(rsB, off);
     *reinterpret_cast<float4 *>(&sC[j * LDC + n0]) = bload16(rsC, off);
   }
+  // the step sizes of heads [h0, h0 + HC) of the sub-block into sT[head][token]
+  // (the workgroups of group 0 only; zero past the sequence end)
+  auto fill_dt = [&](int h0) {
+    const int hc = min(HC, H - h0);
+    if ((H & 3) == 0) {
+      // float4 pieces: lane l takes piece j of row ro of each group of rpi
+      // rows (a token row of the pass holds hc / 4 pieces)
+      const int H4 = hc >> 2, rpi = 64 / H4, ro = l / H4, j = l % H4;
+      if (ro < rpi) {
+        for (int t = u * rpi + ro; t < 64; t += 4 * rpi) {
+          const float4 v = t < nv ? *reinterpret_cast<const float4 *>(dt + ((int64_t)ib * L + t0 + t) * H + h0 + 4 * j)
+                                  : float4{0.f, 0.f, 0.f, 0.f};
+          sT[(4 * j) * 65 + t] = v.x;
+          sT[(4 * j + 1) * 65 + t] = v.y;
+          sT[(4 * j + 2) * 65 + t] = v.z;
+          sT[(4 * j + 3) * 65 + t] = v.w;
+        }
+      }
+    } else {
+      for (int t = u; t < 64; t += 4)
+        for (int hh = l; hh < hc; hh += 64)
+          sT[hh * 65 + t] = t < nv ? dt[((int64_t)ib * L + t0 + t) * H + h0 + hh] : 0.f;
+    }
+  };
+  if (g == 0) fill_dt(0);
   __syncthreads();
 
   __bf16 *out = rec + ((int64_t)bg * nsub + k) * (NRB * 512);
@@ -114,22 +147,47 @@ __global__ void __launch_bounds__(256) prep_kernel(const __bf16 *__restrict__ B,
     if (a == 1 && u < 2) break;
     *reinterpret_cast<bf16x8 *>(out + (NCB + NBB + sb0 + a) * 512 + 8 * l) = pack8<__bf16>(sv[a]).v;
   }
+
+  // Head-major copy of the raw step sizes of the sub-block (the workgroups
+  // of group 0 write it for every head): dtT[ib][h][64k + j] = dt[ib][64k + j][h],
+  // zero past the sequence end.  Each head's 64 step sizes are then one
+  // contiguous 256-byte run for the walk.
+  // The first HC heads were staged with B and C; more heads take further
+  // passes through sT.
+  if (g == 0) {
+    const int Lp = nsub * 64;
+    for (int h0 = 0; h0 < H; h0 += HC) {
+      const int hc = min(HC, H - h0);
+      if (h0 > 0) {
+        __syncthreads();
+        fill_dt(h0);
+        __syncthreads();
+      }
+      // four consecutive tokens of a head per thread (16-byte stores)
+      for (int e = tid; e < 16 * hc; e += 256) {
+        const int hh = e >> 4, t = (e & 15) * 4;
+        const float *r = &sT[hh * 65 + t];
+        *reinterpret_cast<float4 *>(dtT + ((int64_t)ib * H + h0 + hh) * Lp + t0 + t) = float4{r[0], r[1], r[2], r[3]};
+      }
+    }
+  }
 }
 
 } // namespace
 
 int prep_record_blocks(int N) { return 4 * (N / 32) + 2 * (N / 16) + 6; }
 
-hipError_t launch_prep(const void *B, const void *C, void *rec, int b, int L, int G, int N, hipStream_t stream) {
+hipError_t launch_prep(const void *B, const void *C, void *rec, const float *dt, float *dtT, int b, int L, int H, int G,
+                       int N, hipStream_t stream) {
   const int nsub = (L + 63) / 64;
   const dim3 grid((unsigned)(b * G * nsub));
   const __bf16 *Bp = reinterpret_cast<const __bf16 *>(B);
   const __bf16 *Cp = reinterpret_cast<const __bf16 *>(C);
   __bf16 *r = reinterpret_cast<__bf16 *>(rec);
   switch (N) {
-  case 32: hipLaunchKernelGGL(prep_kernel<32>, grid, dim3(256), 0, stream, Bp, Cp, r, L, G, nsub); break;
-  case 64: hipLaunchKernelGGL(prep_kernel<64>, grid, dim3(256), 0, stream, Bp, Cp, r, L, G, nsub); break;
-  case 128: hipLaunchKernelGGL(prep_kernel<128>, grid, dim3(256), 0, stream, Bp, Cp, r, L, G, nsub); break;
+  case 32: hipLaunchKernelGGL(prep_kernel<32>, grid, dim3(256), 0, stream, Bp, Cp, r, dt, dtT, L, H, G, nsub); break;
+  case 64: hipLaunchKernelGGL(prep_kernel<64>, grid, dim3(256), 0, stream, Bp, Cp, r, dt, dtT, L, H, G, nsub); break;
+  case 128: hipLaunchKernelGGL(prep_kernel<128>, grid, dim3(256), 0, stream, Bp, Cp, r, dt, dtT, L, H, G, nsub); break;
   default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

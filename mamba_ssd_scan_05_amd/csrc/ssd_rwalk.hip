@@ -132,8 +132,9 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
 
   const int64_t rowX = (int64_t)H * P;
   const __bf16 *Xbase = reinterpret_cast<const __bf16 *>(prm.x) + (int64_t)ib * L * rowX + (int64_t)h * P + p0;
-  const float *dtbase = prm.dt + (int64_t)ib * L * H + h;
   const int nsub = (L + 63) / 64;
+  // raw step sizes of this head, head-major (written by prep_kernel)
+  const float *dtbase = prm.dtT + ((int64_t)ib * H + h) * (nsub * 64);
   // records of this (batch, group), one per sub-block
   const __bf16 *Rbase = reinterpret_cast<const __bf16 *>(prm.rec) + (int64_t)bg * nsub * (NRB * 512);
 
@@ -189,11 +190,11 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
       }
     }
   };
-  // Raw step size of token l of sub-block k (zero past the end).
+  // Raw step size of token l of sub-block k (one contiguous 256-byte run per
+  // wave; nothing is read for k past the last sub-block).
   auto fetch_dt = [&](int k) {
-    const int t0 = 64 * k, nv = min(64, L - t0);
-    const auto rsD = make_rsrc(dtbase + (int64_t)t0 * H, nv > 0 ? (uint32_t)(((int64_t)(nv - 1) * H + 1) * 4) : 0u);
-    return bload4(rsD, (uint32_t)(l * H * 4));
+    const auto rsD = make_rsrc(dtbase + 64 * (int64_t)min(k, nsub - 1), k < nsub ? 256u : 0u);
+    return bload4(rsD, (uint32_t)(l * 4));
   };
 
   // ---- decay factors of one sub-block (lane = token) ------------------------
