@@ -37,6 +37,7 @@ calibrate the byte counters.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -403,6 +404,12 @@ def main():
     import torch
     from mamba_ssd_scan_05_amd import inputs, ssd, staging
 
+    # Python's cyclic garbage collector stays off while the legs run (a
+    # collection inside a timed loop stalled the host ~38 ms, long enough
+    # for the queued GPU work to drain); each leg starts after a collection.
+    gc.collect()
+    gc.disable()
+
     dev = "cuda:0"
     torch.cuda.set_device(0)
     names = {ssd.SSD_ALGO_FUSED: "fused", ssd.SSD_ALGO_CHUNKED: "chunked", ssd.SSD_ALGO_ROWS: "rows"}
@@ -492,8 +499,10 @@ def main():
             if inputs.WORKLOADS[name]["kind"] != "scan":
                 continue
             print("bench: config %s" % name, file=sys.stderr, flush=True)
+            gc.collect()
             extra["configs"][name] = bench_scan_config(name, ssd, staging, inputs, torch, dev, evict)
     if not args.no_alt:
+        gc.collect()
         alts = {}
         for name_a, a, q in (("rows", ssd.SSD_ALGO_ROWS, Q), ("fused", ssd.SSD_ALGO_FUSED, Q),
                              ("chunked_256", ssd.SSD_ALGO_CHUNKED, 256),
@@ -518,6 +527,7 @@ def main():
             alts[name_a] = e0.elapsed_time(e1) / 20
         extra["algorithms_ms"] = alts
     if not args.no_gated:
+        gc.collect()
         # the scan with the output gate fused (out = y * silu(z)): the same
         # automatic plan, z read once more (the bytes of x)
         z = staging.tensor(inputs.make_gate(si), si.dtype, dev)
@@ -550,12 +560,15 @@ def main():
         extra["copy_probe_bytes"] = 2 * (1 << 30)
     if not args.no_bwd:
         print("bench: backward", WORKLOAD, file=sys.stderr, flush=True)
+        gc.collect()
         extra["backward"] = bench_bwd(ssd, staging, inputs, torch, dev)
     if not args.no_sscan:
         print("bench: selective scan %s" % SSCAN, file=sys.stderr, flush=True)
+        gc.collect()
         extra["selective_scan"] = bench_sscan(ssd, staging, inputs, torch, dev)
     if not args.no_decode:
         print("bench: decode step workload", file=sys.stderr, flush=True)
+        gc.collect()
         extra["decode_step"] = bench_decode(ssd, staging, inputs, torch, dev)
 
     cpu = None

@@ -35,9 +35,9 @@
  * library keeps, one per (device, stream) handle, reused by every call on
  * that stream in stream order and grown stream-ordered on `stream` when a
  * call needs more (an event recorded after each call orders the next use if
- * a handle is reused for another stream).  A request above 256 MiB is
+ * a handle is reused for another stream).  A request above 4 GiB is
  * allocated and freed stream-ordered on `stream` for that call alone.  At
- * most 16 buffers of at most 1 GiB in total are kept: a call that needs a
+ * most 16 buffers of at most 8 GiB in total are kept: a call that needs a
  * new buffer first frees the least recently used ones (after waiting for
  * their last use) until both limits hold.  Kept buffers live until
  * ssd_release_scratch(), eviction, or the end of the process.  Allocating
@@ -334,7 +334,8 @@ int ssd_selective_scan_fwd(const ssd_tensor *x, const ssd_tensor *dt,
  * in a fixed order, so the result does not vary from run to run.  Scratch:
  * b*H*ceil(L/64)*(2*P*N + 3) floats (the states entering each 64-token chunk,
  * the gradients at each chunk's end, per-chunk partial sums; see Scratch
- * above: above 256 MiB it is allocated per call).
+ * above: 1.34 GB at b=4, L=4096, H=80, P=64, N=128, kept between calls
+ * like any scratch up to 4 GiB).
  */
 int ssd_scan_bwd(const ssd_tensor *x, const ssd_tensor *dt,
                  const ssd_tensor *dt_bias, const ssd_tensor *A,

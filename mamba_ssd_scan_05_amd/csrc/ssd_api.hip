@@ -193,10 +193,10 @@ int hip_fail(hipError_t e, const char *what) {
 // kScratchTotal bytes are kept: a call that needs a new one first frees the
 // least recently used idle buffers (after waiting for their last use) until
 // both limits hold.  ssd_release_scratch() frees every kept buffer.
-constexpr size_t kScratchKeepMax = (size_t)256 << 20;
+constexpr size_t kScratchKeepMax = (size_t)4 << 30;
 constexpr size_t kScratchGranule = (size_t)1 << 20;
 constexpr size_t kScratchSlots = 16;
-constexpr size_t kScratchTotal = (size_t)1 << 30;
+constexpr size_t kScratchTotal = (size_t)8 << 30;
 
 struct ScratchSlot {
   int dev;
