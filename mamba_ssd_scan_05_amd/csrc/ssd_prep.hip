@@ -29,10 +29,11 @@
 // (batch ib, group g): blocks [C | B | S] at rec + ((ib*G + g)*nsub + k) *
 // rec_blocks(N) * 512 bf16.
 //
-// The workgroups of group 0 also copy the sub-block's raw step sizes
-// head-major, dtT[ib][h][64k + j] = dt[ib][64k + j][h] (zero past the end),
-// so that each wave of the walk reads its head's 64 step sizes as one
-// contiguous 256-byte run instead of 64 loads 4H bytes apart.
+// A second set of workgroups, one per (batch, sub-block), copies the raw
+// step sizes head-major, dtT[ib][h][64k + j] = dt[ib][64k + j][h] (zero past
+// the end), so that each wave of the walk reads its head's 64 step sizes as
+// one contiguous 256-byte run instead of 64 loads 4H bytes apart; they run
+// beside the record workgroups (two workgroups fit a compute unit).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -42,41 +43,19 @@
 namespace ssd {
 namespace {
 
-template <int N>
-__global__ void __launch_bounds__(256) prep_kernel(const __bf16 *__restrict__ B, const __bf16 *__restrict__ C,
-                                                   __bf16 *__restrict__ rec, const float *__restrict__ dt,
-                                                   float *__restrict__ dtT, int L, int H, int G, int nsub) {
-  constexpr int NCB = 4 * (N / 32);     // C blocks
-  constexpr int NBB = 2 * (N / 16);     // B blocks
-  constexpr int NRB = NCB + NBB + 6;    // blocks per record
-  constexpr int LDB = tr_ld(N, 2);      // B tile: transposed reads
-  constexpr int LDC = N + 8;            // C tile: row reads
-  constexpr int RW = N / 8;             // 16-byte pieces per row
-  __shared__ __attribute__((aligned(16))) __bf16 sB[64 * LDB];
-  __shared__ __attribute__((aligned(16))) __bf16 sC[64 * LDC];
-  constexpr int HC = 128;         // heads per pass of the step-size transpose
-  __shared__ float sT[HC * 65];   // step sizes of HC heads x 64 tokens, transposed
+constexpr int kHC = 128; // heads per pass of the step-size transpose
 
-  const int wg = blockIdx.x;
-  const int k = wg % nsub, bg = wg / nsub;
-  const int g = bg % G, ib = bg / G;
-  const int tid = threadIdx.x, u = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
-  const int t0 = 64 * k, nv = min(64, L - t0);
-  const int64_t rowB = (int64_t)G * N;
-  const int64_t base = ((int64_t)ib * L + t0) * rowB + (int64_t)g * N;
-  const uint32_t bytes = (uint32_t)(((int64_t)(nv - 1) * rowB + N) * 2);
-  const auto rsB = make_rsrc(B + base, bytes);
-  const auto rsC = make_rsrc(C + base, bytes);
-  for (int q = tid; q < 64 * RW; q += 256) {
-    const int j = q / RW, n0 = (q % RW) * 8;
-    const uint32_t off = (uint32_t)((j * rowB + n0) * 2);
-    *reinterpret_cast<float4 *>(&sB[j * LDB + n0]) = bload16(rsB, off);
-    *reinterpret_cast<float4 *>(&sC[j * LDC + n0]) = bload16(rsC, off);
-  }
-  // the step sizes of heads [h0, h0 + HC) of the sub-block into sT[head][token]
-  // (the workgroups of group 0 only; zero past the sequence end)
-  auto fill_dt = [&](int h0) {
-    const int hc = min(HC, H - h0);
+// Head-major copy of the raw step sizes of sub-block k of batch ib:
+// dtT[ib][h][64k + j] = dt[ib][64k + j][h] (zero past the sequence end), in
+// passes of kHC heads through the LDS tile sT[head][token] (row stride 65).
+// Each head's 64 step sizes are then one contiguous 256-byte run for the walk.
+__device__ __forceinline__ void transpose_dt(const float *__restrict__ dt, float *__restrict__ dtT, float *sT, int ib,
+                                             int k, int L, int H, int nsub, int tid) {
+  const int u = tid >> 6, l = tid & 63;
+  const int t0 = 64 * k, nv = min(64, L - t0), Lp = nsub * 64;
+  for (int h0 = 0; h0 < H; h0 += kHC) {
+    const int hc = min(kHC, H - h0);
+    if (h0 > 0) __syncthreads();
     if ((H & 3) == 0) {
       // float4 pieces: lane l takes piece j of row ro of each group of rpi
       // rows (a token row of the pass holds hc / 4 pieces)
@@ -96,8 +75,53 @@ __global__ void __launch_bounds__(256) prep_kernel(const __bf16 *__restrict__ B,
         for (int hh = l; hh < hc; hh += 64)
           sT[hh * 65 + t] = t < nv ? dt[((int64_t)ib * L + t0 + t) * H + h0 + hh] : 0.f;
     }
-  };
-  if (g == 0) fill_dt(0);
+    __syncthreads();
+    // four consecutive tokens of a head per thread (16-byte stores)
+    for (int e = tid; e < 16 * hc; e += 256) {
+      const int hh = e >> 4, t = (e & 15) * 4;
+      const float *r = &sT[hh * 65 + t];
+      *reinterpret_cast<float4 *>(dtT + ((int64_t)ib * H + h0 + hh) * Lp + t0 + t) = float4{r[0], r[1], r[2], r[3]};
+    }
+  }
+}
+
+template <int N>
+__global__ void __launch_bounds__(256) prep_kernel(const __bf16 *__restrict__ B, const __bf16 *__restrict__ C,
+                                                   __bf16 *__restrict__ rec, const float *__restrict__ dt,
+                                                   float *__restrict__ dtT, int L, int H, int G, int nsub) {
+  constexpr int NCB = 4 * (N / 32);     // C blocks
+  constexpr int NBB = 2 * (N / 16);     // B blocks
+  constexpr int NRB = NCB + NBB + 6;    // blocks per record
+  constexpr int LDB = tr_ld(N, 2);      // B tile: transposed reads
+  constexpr int LDC = N + 8;            // C tile: row reads
+  constexpr int RW = N / 8;             // 16-byte pieces per row
+  __shared__ __attribute__((aligned(16))) __bf16 sB[64 * LDB];
+  __shared__ __attribute__((aligned(16))) __bf16 sC[64 * LDC];
+  __shared__ float sT[kHC * 65];  // step sizes of kHC heads x 64 tokens, transposed
+
+  const int tid = threadIdx.x, u = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
+  const int nrec = gridDim.x - (int)(gridDim.x / (G + 1)); // b*G*nsub record workgroups
+  if ((int)blockIdx.x >= nrec) {
+    // the step-size workgroups, one per (batch, sub-block)
+    const int wd = blockIdx.x - nrec, k = wd % nsub, ib = wd / nsub;
+    transpose_dt(dt, dtT, sT, ib, k, L, H, nsub, tid);
+    return;
+  }
+  const int wg = blockIdx.x;
+  const int k = wg % nsub, bg = wg / nsub;
+  const int g = bg % G, ib = bg / G;
+  const int t0 = 64 * k, nv = min(64, L - t0);
+  const int64_t rowB = (int64_t)G * N;
+  const int64_t base = ((int64_t)ib * L + t0) * rowB + (int64_t)g * N;
+  const uint32_t bytes = (uint32_t)(((int64_t)(nv - 1) * rowB + N) * 2);
+  const auto rsB = make_rsrc(B + base, bytes);
+  const auto rsC = make_rsrc(C + base, bytes);
+  for (int q = tid; q < 64 * RW; q += 256) {
+    const int j = q / RW, n0 = (q % RW) * 8;
+    const uint32_t off = (uint32_t)((j * rowB + n0) * 2);
+    *reinterpret_cast<float4 *>(&sB[j * LDB + n0]) = bload16(rsB, off);
+    *reinterpret_cast<float4 *>(&sC[j * LDC + n0]) = bload16(rsC, off);
+  }
   __syncthreads();
 
   __bf16 *out = rec + ((int64_t)bg * nsub + k) * (NRB * 512);
@@ -147,30 +171,6 @@ __global__ void __launch_bounds__(256) prep_kernel(const __bf16 *__restrict__ B,
     if (a == 1 && u < 2) break;
     *reinterpret_cast<bf16x8 *>(out + (NCB + NBB + sb0 + a) * 512 + 8 * l) = pack8<__bf16>(sv[a]).v;
   }
-
-  // Head-major copy of the raw step sizes of the sub-block (the workgroups
-  // of group 0 write it for every head): dtT[ib][h][64k + j] = dt[ib][64k + j][h],
-  // zero past the sequence end.  Each head's 64 step sizes are then one
-  // contiguous 256-byte run for the walk.
-  // The first HC heads were staged with B and C; more heads take further
-  // passes through sT.
-  if (g == 0) {
-    const int Lp = nsub * 64;
-    for (int h0 = 0; h0 < H; h0 += HC) {
-      const int hc = min(HC, H - h0);
-      if (h0 > 0) {
-        __syncthreads();
-        fill_dt(h0);
-        __syncthreads();
-      }
-      // four consecutive tokens of a head per thread (16-byte stores)
-      for (int e = tid; e < 16 * hc; e += 256) {
-        const int hh = e >> 4, t = (e & 15) * 4;
-        const float *r = &sT[hh * 65 + t];
-        *reinterpret_cast<float4 *>(dtT + ((int64_t)ib * H + h0 + hh) * Lp + t0 + t) = float4{r[0], r[1], r[2], r[3]};
-      }
-    }
-  }
 }
 
 } // namespace
@@ -180,7 +180,8 @@ int prep_record_blocks(int N) { return 4 * (N / 32) + 2 * (N / 16) + 6; }
 hipError_t launch_prep(const void *B, const void *C, void *rec, const float *dt, float *dtT, int b, int L, int H, int G,
                        int N, hipStream_t stream) {
   const int nsub = (L + 63) / 64;
-  const dim3 grid((unsigned)(b * G * nsub));
+  // b*G*nsub record workgroups, then b*nsub step-size workgroups
+  const dim3 grid((unsigned)(b * G * nsub + b * nsub));
   const __bf16 *Bp = reinterpret_cast<const __bf16 *>(B);
   const __bf16 *Cp = reinterpret_cast<const __bf16 *>(C);
   __bf16 *r = reinterpret_cast<__bf16 *>(rec);
