@@ -125,11 +125,23 @@ __global__ void __launch_bounds__(64) sscan_kernel(const SScanParams p, const T 
     } else {
 #pragma unroll
       for (int n = 0; n < N; ++n) h[n] = p.hend[sd * N + n];
-      for (int q = 1; q < seg; ++q) {
-        const int64_t sq = sd + (int64_t)q * Dc;
-        const float s = p.sdelta[sq];
+      // the end states of the earlier segments four at a time: the loads
+      // of a group are issued together, then folded in order
+      for (int q0 = 1; q0 < seg; q0 += 4) {
+        float hb[4][N], sb[4];
 #pragma unroll
-        for (int n = 0; n < N; ++n) h[n] = hw_exp2(a2[n] * s) * h[n] + p.hend[sq * N + n];
+        for (int j = 0; j < 4; ++j) {
+          const int64_t sq = sd + (int64_t)min(q0 + j, seg - 1) * Dc;
+          sb[j] = p.sdelta[sq];
+#pragma unroll
+          for (int n = 0; n < N; ++n) hb[j][n] = p.hend[sq * N + n];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (q0 + j >= seg) break;
+#pragma unroll
+          for (int n = 0; n < N; ++n) h[n] = hw_exp2(a2[n] * sb[j]) * h[n] + hb[j][n];
+        }
       }
     }
   }
