@@ -337,6 +337,10 @@ ROWS_SMALL = [c for c in SMALL if c[0] == inputs.BF16 and c[6] in (32, 64, 128)]
     (inputs.BF16, 2, 300, 6, 32, 2, 64, 64),
     (inputs.BF16, 1, 200, 12, 16, 3, 128, 64),
     (inputs.BF16, 3, 129, 5, 64, 5, 32, 64),
+    # more than 128 heads: the head-major step-size copy takes two passes
+    # (H a multiple of 4: 16-byte reads; H = 130: element reads)
+    (inputs.BF16, 1, 150, 136, 16, 1, 32, 64),
+    (inputs.BF16, 2, 70, 130, 16, 2, 32, 64),
 ]
 
 
