@@ -589,8 +589,11 @@ int run_rows(const ssd_tensor *x, const ssd_tensor *dt, const ssd_tensor *dt_bia
   int status = SSD_OK;
   hipError_t e;
   do {
-    e = ssd::launch_prep(B->data, C->data, ws, (const float *)dt->data, dtT, (int)s.b, (int)s.L, (int)s.H, (int)s.G,
-                         (int)s.N, st);
+    // the plain walk reads Delta, the gated walk the raw dt (its softplus in
+    // the walk measured faster there)
+    e = ssd::launch_prep(B->data, C->data, ws, (const float *)dt->data,
+                         dt_bias ? (const float *)dt_bias->data : nullptr, z ? 0 : 1, dtT, (int)s.b, (int)s.L, (int)s.H,
+                         (int)s.G, (int)s.N, st);
     if (e != hipSuccess) { status = hip_fail(e, "operand record launch"); break; }
     ssd::RWalkParams p{};
     p.x = x->data; p.dt = (const float *)dt->data;

@@ -67,7 +67,8 @@ struct RWalkParams {
   const float *D;       // [H] or null
   const void *rec;      // [b, G, ceil(L/64), prep_record_blocks(N), 512] bf16
                         // operand records from launch_prep
-  const float *dtT;     // [b, H, 64 ceil(L/64)] raw step sizes, head-major (launch_prep)
+  const float *dtT;     // [b, H, 64 ceil(L/64)] step sizes, head-major (launch_prep):
+                        // Delta for the plain walk, raw dt for the gated one
   const float *init;    // [b, H, P, N] or null
   void *out;            // [b, L, H, P] bf16
   const void *z;        // [b, L, H, P] bf16 gate input (out = y * silu(z)) or null
@@ -79,10 +80,11 @@ struct RWalkParams {
 // row-sliced walk: C, B and causal C_t . B_t' score fragments in matrix-core
 // lane order (ssd_prep.hip); prep_record_blocks(N) 1 KiB blocks each.
 int prep_record_blocks(int N);
-// Also writes the raw step sizes dt [b, L, H] head-major into dtT [b, H,
-// 64 ceil(L/64)] (zero past the end).
-hipError_t launch_prep(const void *B, const void *C, void *rec, const float *dt, float *dtT, int b, int L, int H,
-                       int G, int N, hipStream_t stream);
+// Also writes the step sizes dt [b, L, H] head-major into dtT [b, H,
+// 64 ceil(L/64)]: Delta = softplus(dt + dt_bias [H]) when `softplus` is
+// nonzero (dt_bias may be null), the raw dt otherwise.
+hipError_t launch_prep(const void *B, const void *C, void *rec, const float *dt, const float *dt_bias, int softplus,
+                       float *dtT, int b, int L, int H, int G, int N, hipStream_t stream);
 
 // Row-sliced walk with W waves per workgroup (1..8); N in {32, 64, 128}.
 hipError_t launch_rwalk(int N, int W, const RWalkParams &p, hipStream_t stream);

@@ -29,9 +29,9 @@
 // (batch ib, group g): blocks [C | B | S] at rec + ((ib*G + g)*nsub + k) *
 // rec_blocks(N) * 512 bf16.
 //
-// A second set of workgroups, one per (batch, sub-block), copies the raw
-// step sizes head-major, dtT[ib][h][64k + j] = dt[ib][64k + j][h] (zero past
-// the end), so that each wave of the walk reads its head's 64 step sizes as
+// A second set of workgroups, one per (batch, sub-block), writes the step
+// sizes Delta = softplus(dt + dt_bias) head-major, dtT[ib][h][64k + j], so
+// that each wave of the walk reads its head's 64 step sizes as
 // one contiguous 256-byte run instead of 64 loads 4H bytes apart; they run
 // beside the record workgroups (two workgroups fit a compute unit).
 #include <hip/hip_runtime.h>
@@ -45,12 +45,14 @@ namespace {
 
 constexpr int kHC = 128; // heads per pass of the step-size transpose
 
-// Head-major copy of the raw step sizes of sub-block k of batch ib:
-// dtT[ib][h][64k + j] = dt[ib][64k + j][h] (zero past the sequence end), in
+// Head-major step sizes of sub-block k of batch ib:
+// dtT[ib][h][64k + j] = softplus(dt[ib][64k + j][h] + dt_bias[h]) (the raw
+// step size read as zero past the sequence end), in
 // passes of kHC heads through the LDS tile sT[head][token] (row stride 65).
 // Each head's 64 step sizes are then one contiguous 256-byte run for the walk.
-__device__ __forceinline__ void transpose_dt(const float *__restrict__ dt, float *__restrict__ dtT, float *sT, int ib,
-                                             int k, int L, int H, int nsub, int tid) {
+__device__ __forceinline__ void transpose_dt(const float *__restrict__ dt, const float *__restrict__ dt_bias,
+                                             int softplus, float *__restrict__ dtT, float *sT, int ib, int k, int L,
+                                             int H, int nsub, int tid) {
   const int u = tid >> 6, l = tid & 63;
   const int t0 = 64 * k, nv = min(64, L - t0), Lp = nsub * 64;
   for (int h0 = 0; h0 < H; h0 += kHC) {
@@ -76,11 +78,17 @@ __device__ __forceinline__ void transpose_dt(const float *__restrict__ dt, float
           sT[hh * 65 + t] = t < nv ? dt[((int64_t)ib * L + t0 + t) * H + h0 + hh] : 0.f;
     }
     __syncthreads();
-    // four consecutive tokens of a head per thread (16-byte stores)
+    // four consecutive tokens of a head per thread (16-byte stores), as step
+    // sizes Delta = softplus(dt + dt_bias), or raw when `softplus` is 0
     for (int e = tid; e < 16 * hc; e += 256) {
       const int hh = e >> 4, t = (e & 15) * 4;
       const float *r = &sT[hh * 65 + t];
-      *reinterpret_cast<float4 *>(dtT + ((int64_t)ib * H + h0 + hh) * Lp + t0 + t) = float4{r[0], r[1], r[2], r[3]};
+      float4 v = float4{r[0], r[1], r[2], r[3]};
+      if (softplus) {
+        const float bias = dt_bias ? dt_bias[h0 + hh] : 0.f;
+        v = float4{softplus_f(v.x + bias), softplus_f(v.y + bias), softplus_f(v.z + bias), softplus_f(v.w + bias)};
+      }
+      *reinterpret_cast<float4 *>(dtT + ((int64_t)ib * H + h0 + hh) * Lp + t0 + t) = v;
     }
   }
 }
@@ -88,6 +96,7 @@ __device__ __forceinline__ void transpose_dt(const float *__restrict__ dt, float
 template <int N>
 __global__ void __launch_bounds__(256) prep_kernel(const __bf16 *__restrict__ B, const __bf16 *__restrict__ C,
                                                    __bf16 *__restrict__ rec, const float *__restrict__ dt,
+                                                   const float *__restrict__ dt_bias, int softplus,
                                                    float *__restrict__ dtT, int L, int H, int G, int nsub) {
   constexpr int NCB = 4 * (N / 32);     // C blocks
   constexpr int NBB = 2 * (N / 16);     // B blocks
@@ -104,7 +113,7 @@ __global__ void __launch_bounds__(256) prep_kernel(const __bf16 *__restrict__ B,
   if ((int)blockIdx.x >= nrec) {
     // the step-size workgroups, one per (batch, sub-block)
     const int wd = blockIdx.x - nrec, k = wd % nsub, ib = wd / nsub;
-    transpose_dt(dt, dtT, sT, ib, k, L, H, nsub, tid);
+    transpose_dt(dt, dt_bias, softplus, dtT, sT, ib, k, L, H, nsub, tid);
     return;
   }
   const int wg = blockIdx.x;
@@ -177,8 +186,8 @@ __global__ void __launch_bounds__(256) prep_kernel(const __bf16 *__restrict__ B,
 
 int prep_record_blocks(int N) { return 4 * (N / 32) + 2 * (N / 16) + 6; }
 
-hipError_t launch_prep(const void *B, const void *C, void *rec, const float *dt, float *dtT, int b, int L, int H, int G,
-                       int N, hipStream_t stream) {
+hipError_t launch_prep(const void *B, const void *C, void *rec, const float *dt, const float *dt_bias, int softplus,
+                       float *dtT, int b, int L, int H, int G, int N, hipStream_t stream) {
   const int nsub = (L + 63) / 64;
   // b*G*nsub record workgroups, then b*nsub step-size workgroups
   const dim3 grid((unsigned)(b * G * nsub + b * nsub));
@@ -186,9 +195,9 @@ hipError_t launch_prep(const void *B, const void *C, void *rec, const float *dt,
   const __bf16 *Cp = reinterpret_cast<const __bf16 *>(C);
   __bf16 *r = reinterpret_cast<__bf16 *>(rec);
   switch (N) {
-  case 32: hipLaunchKernelGGL(prep_kernel<32>, grid, dim3(256), 0, stream, Bp, Cp, r, dt, dtT, L, H, G, nsub); break;
-  case 64: hipLaunchKernelGGL(prep_kernel<64>, grid, dim3(256), 0, stream, Bp, Cp, r, dt, dtT, L, H, G, nsub); break;
-  case 128: hipLaunchKernelGGL(prep_kernel<128>, grid, dim3(256), 0, stream, Bp, Cp, r, dt, dtT, L, H, G, nsub); break;
+  case 32: hipLaunchKernelGGL(prep_kernel<32>, grid, dim3(256), 0, stream, Bp, Cp, r, dt, dt_bias, softplus, dtT, L, H, G, nsub); break;
+  case 64: hipLaunchKernelGGL(prep_kernel<64>, grid, dim3(256), 0, stream, Bp, Cp, r, dt, dt_bias, softplus, dtT, L, H, G, nsub); break;
+  case 128: hipLaunchKernelGGL(prep_kernel<128>, grid, dim3(256), 0, stream, Bp, Cp, r, dt, dt_bias, softplus, dtT, L, H, G, nsub); break;
   default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

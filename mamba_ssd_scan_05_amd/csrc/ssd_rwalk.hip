@@ -133,7 +133,9 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
   const int64_t rowX = (int64_t)H * P;
   const __bf16 *Xbase = reinterpret_cast<const __bf16 *>(prm.x) + (int64_t)ib * L * rowX + (int64_t)h * P + p0;
   const int nsub = (L + 63) / 64;
-  // raw step sizes of this head, head-major (written by prep_kernel)
+  // step sizes of this head, head-major (written by prep_kernel): Delta =
+  // softplus(dt + dt_bias) for the plain walk, the raw dt for the gated one,
+  // which applies the softplus itself (measured faster there)
   const float *dtbase = prm.dtT + ((int64_t)ib * H + h) * (nsub * 64);
   // records of this (batch, group), one per sub-block
   const __bf16 *Rbase = reinterpret_cast<const __bf16 *>(prm.rec) + (int64_t)bg * nsub * (NRB * 512);
@@ -190,8 +192,8 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
       }
     }
   };
-  // Raw step size of token l of sub-block k (one contiguous 256-byte run per
-  // wave; nothing is read for k past the last sub-block).
+  // Step size Delta of token l of sub-block k (one contiguous 256-byte run
+  // per wave; nothing is read for k past the last sub-block).
   auto fetch_dt = [&](int k) {
     const auto rsD = make_rsrc(dtbase + 64 * (int64_t)min(k, nsub - 1), k < nsub ? 256u : 0u);
     return bload4(rsD, (uint32_t)(l * 4));
@@ -216,8 +218,13 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
   float next_clast = 0.f, next_eout = 0.f;
   auto scan = [&](int k, float rdt, float e_in, int fs) {
     const int nv = min(64, L - 64 * k);
-    float dl = softplus_f(rdt + bias);
-    dl = (l < nv) ? dl : 0.f;
+    float dl;
+    if constexpr (GATED) {
+      dl = softplus_f(rdt + bias);
+      dl = (l < nv) ? dl : 0.f;
+    } else {
+      dl = (l < nv) ? rdt : 0.f;
+    }
     const float c = wave_incl_scan(dl * a2);
     float clast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, c), 63));
     // Keep the (wave-uniform) decisions below in vector registers: as
