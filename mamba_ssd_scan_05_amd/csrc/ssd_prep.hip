@@ -30,10 +30,11 @@
 // rec_blocks(N) * 512 bf16.
 //
 // A second set of workgroups, one per (batch, sub-block), writes the step
-// sizes Delta = softplus(dt + dt_bias) head-major, dtT[ib][h][64k + j], so
-// that each wave of the walk reads its head's 64 step sizes as
-// one contiguous 256-byte run instead of 64 loads 4H bytes apart; they run
-// beside the record workgroups (two workgroups fit a compute unit).
+// sizes head-major, dtT[ib][h][64k + j] (Delta = softplus(dt + dt_bias) for
+// the plain walk, the raw dt for the gated walk), so that each wave of the
+// walk reads its head's 64 step sizes as one contiguous 256-byte run instead
+// of 64 loads 4H bytes apart; they run beside the record workgroups (two
+// workgroups fit a compute unit).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -45,9 +46,9 @@ namespace {
 
 constexpr int kHC = 128; // heads per pass of the step-size transpose
 
-// Head-major step sizes of sub-block k of batch ib:
-// dtT[ib][h][64k + j] = softplus(dt[ib][64k + j][h] + dt_bias[h]) (the raw
-// step size read as zero past the sequence end), in
+// Head-major step sizes of sub-block k of batch ib: dtT[ib][h][64k + j] =
+// softplus(dt[ib][64k + j][h] + dt_bias[h]) with `softplus`, else the raw
+// dt (the raw step size read as zero past the sequence end), in
 // passes of kHC heads through the LDS tile sT[head][token] (row stride 65).
 // Each head's 64 step sizes are then one contiguous 256-byte run for the walk.
 __device__ __forceinline__ void transpose_dt(const float *__restrict__ dt, const float *__restrict__ dt_bias,

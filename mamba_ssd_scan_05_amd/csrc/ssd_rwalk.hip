@@ -192,8 +192,9 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
       }
     }
   };
-  // Step size Delta of token l of sub-block k (one contiguous 256-byte run
-  // per wave; nothing is read for k past the last sub-block).
+  // Step size of token l of sub-block k (Delta; the raw dt for the gated
+  // walk): one contiguous 256-byte run per wave, nothing read for k past the
+  // last sub-block.
   auto fetch_dt = [&](int k) {
     const auto rsD = make_rsrc(dtbase + 64 * (int64_t)min(k, nsub - 1), k < nsub ? 256u : 0u);
     return bload4(rsD, (uint32_t)(l * 4));
