@@ -173,7 +173,15 @@ __global__ void __launch_bounds__(W * 64) rwalk_kernel(const RWalkParams prm) {
     if (!kSpare4 || w < 4) {
 #pragma unroll
       for (int i = 0; i < CPW; ++i) {
-        const int c = min(w + i * WC, NRB - 1);
+        int c = min(w + i * WC, NRB - 1);
+        if constexpr (kSpare4 && !GATED) {
+          // wave 0 (sharing its SIMD with wave 4) leaves its last two blocks
+          // to waves 2 and 3, whose last slots pass the end of the record
+          // (NRB = 2 mod 4); measured slower for the gated walk, which keeps
+          // the duplicate copies
+          if (w == 0 && i >= CPW - 2) continue;
+          if (w + i * WC >= NRB) c = 4 * (CPW - 2) + 4 * (w - 2);
+        }
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsR, (__attribute__((address_space(3))) void *)&rec[c * 512], 16,
                                                  l * 16, c * 1024, 0, 0);
       }
