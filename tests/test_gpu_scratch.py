@@ -152,3 +152,30 @@ def test_kept_buffers_capped_over_many_streams():
         check(staging.to_f64(fin), ref[1], "final")
     ssd.ssd_release_scratch()
     assert ssd.ssd_scratch_stats() == (0, 0)
+
+
+def test_backward_scratch_kept_and_results_repeat():
+    # the backward's chunk states (b*H*ceil(L/64)*(2*P*N + 3) floats) stay in
+    # a kept buffer: back-to-back calls queue without a host wait, reuse the
+    # buffer in stream order and give bitwise the same gradients each time
+    ssd.ssd_release_scratch()
+    b, L, H, P, G, N = 1, 1000, 8, 64, 1, 128
+    si = inputs.make_scan(b, L, H, P, G, N, dtype=inputs.BF16, seed=77, init_std=0.3)
+    t = staging.scan_tensors(si, DEV)
+    gen = torch.Generator().manual_seed(78)
+    dy = torch.randn((b, L, H, P), generator=gen).to(torch.bfloat16).to(DEV)
+    df = torch.randn((b, H, P, N), generator=gen).to(DEV)
+    first = ssd.ssd_scan_bwd(**t, dout=dy, dfinal_state=df)
+    torch.cuda.synchronize()
+    first = {k: v.clone() for k, v in first.items() if v is not None}
+    outs = [ssd.ssd_scan_bwd(**t, dout=dy, dfinal_state=df) for _ in range(4)]
+    torch.cuda.synchronize()
+    n, nbytes = ssd.ssd_scratch_stats()
+    need = b * H * ((L + 63) // 64) * (2 * P * N + 3) * 4
+    say("backward scratch kept:", n, "buffers,", nbytes, "bytes; needs", need)
+    assert n >= 1 and nbytes >= need
+    for g in outs:
+        for k, v in first.items():
+            assert torch.equal(g[k], v), k
+    ssd.ssd_release_scratch()
+    assert ssd.ssd_scratch_stats() == (0, 0)
